@@ -1,0 +1,444 @@
+"""Pins of the fp64 oracle to things other than itself (closed forms, library routines, brute force
+in 40-digit arithmetic, exact identities, the pages' printed numbers, hand-derived fixtures).
+
+Each test names the oracle function it pins and what would break it (a dropped term, a wrong sign,
+a wrong index, a transposed operand).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import ledger
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------------------------------------
+# scalar formats (pinned to numpy's IEEE binary16 conversions)
+# ------------------------------------------------------------------------------------------------
+
+def test_f16_decode_all_bit_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    L = oracle.lib()
+    got = np.array([L.orc_f16_to_f64(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_f64_to_f16_round_nearest_even():
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 5, 20000),
+        # exact ties between neighbouring binary16 values (mantissa + half ulp)
+        (np.arange(1, 2000) + 0.5) * 2.0 ** -10, (np.arange(1, 2000) + 0.5) * 2.0 ** -24,
+        [65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26,
+         5.96e-8, 6.1e-5, -0.0, 0.0, -3.0e-8],
+    ])
+    ref = xs.astype(np.float16).view(np.uint16)
+    L = oracle.lib()
+    got = np.array([L.orc_f64_to_f16(float(x)) for x in xs], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------------------------------------
+# RoPE: closed forms, complex-number formulation, invariants
+# ------------------------------------------------------------------------------------------------
+
+def test_rope_closed_forms():
+    # d = 2: theta_0 = base^0 = 1, so position n rotates (1, 0) to (cos n, sin n).
+    for n in (0, 1, 5, 1000, 32767):
+        out = oracle.rope(np.array([1.0, 0.0]), n, 10000.0)
+        assert out[0] == pytest.approx(math.cos(n), abs=1e-12)
+        assert out[1] == pytest.approx(math.sin(n), abs=1e-12)
+    # d = 4, base 10000: theta_1 = 10000^(-1/2) = 0.01; the pair of index 1 is (x_1, x_3).
+    for n in (3, 77, 4096):
+        out = oracle.rope(np.array([0.0, 1.0, 0.0, 0.0]), n, 10000.0)
+        assert out[0] == 0.0 and out[2] == 0.0
+        assert out[1] == pytest.approx(math.cos(0.01 * n), abs=1e-12)
+        assert out[3] == pytest.approx(math.sin(0.01 * n), abs=1e-12)
+
+
+def test_rope_equals_complex_multiplication():
+    rng = np.random.default_rng(1)
+    for d in (8, 64, 128):
+        x = rng.standard_normal(d)
+        half = d // 2
+        freqs = np.array([10000.0 ** (-(2.0 * i) / d) for i in range(half)])
+        for n in (0, 1, 17, 4095, 32767):
+            z = (x[:half] + 1j * x[half:]) * np.exp(1j * n * freqs)
+            out = oracle.rope(x, n)
+            assert np.allclose(out[:half], z.real, atol=1e-11, rtol=0)
+            assert np.allclose(out[half:], z.imag, atol=1e-11, rtol=0)
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(2)
+    d = 64
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    assert np.array_equal(oracle.rope(k, 0), k)                     # position 0 is the identity
+    for n in (1, 100, 30000):
+        assert np.linalg.norm(oracle.rope(k, n)) == pytest.approx(np.linalg.norm(k), rel=1e-13)
+    # only the relative position matters: <R(m) q, R(n) k> = <R(m+D) q, R(n+D) k>
+    for m, n, D in ((5, 9, 100), (0, 4000, 123), (31000, 12, 7)):
+        a = oracle.rope(q, m) @ oracle.rope(k, n)
+        b = oracle.rope(q, m + D) @ oracle.rope(k, n + D)
+        assert a == pytest.approx(b, rel=1e-9, abs=1e-9)
+
+
+# ------------------------------------------------------------------------------------------------
+# decode attention
+# ------------------------------------------------------------------------------------------------
+
+def _rand_layer(rng, B, H, d, T, ranks, rv, dtype=np.float64):
+    Rk = int(np.sum(ranks))
+    zk = rng.standard_normal((B, T, Rk)).astype(dtype)
+    zv = rng.standard_normal((B, T, rv)).astype(dtype)
+    bk = rng.standard_normal((Rk, d)) / 3.0
+    bv = rng.standard_normal((rv, H * d)) / 3.0
+    q = rng.standard_normal((B, H, d))
+    return zk, zv, bk, bv, q
+
+
+def test_latent_order_equals_explicit_order():
+    """The value reordering P_h (Z_v B_v^h) = (P_h Z_v) B_v^h is exact (associativity)."""
+    rng = np.random.default_rng(3)
+    for (B, H, d, T, ranks, rv) in ((2, 3, 8, 37, [1, 4, 8], 5), (1, 4, 64, 256, [16] * 4, 64),
+                                   (2, 2, 16, 130, [3, 16], 32)):
+        zk, zv, bk, bv, q = _rand_layer(rng, B, H, d, T, ranks, rv)
+        a = oracle.decode_latent(zk, zv, bk, bv, q, ranks, form="latent")
+        b = oracle.decode_latent(zk, zv, bk, bv, q, ranks, form="explicit")
+        assert np.max(np.abs(a - b)) <= 1e-12 * np.sqrt(np.mean(a ** 2))
+
+
+def _rope_complex(x, positions, base=10000.0):
+    """Rotate rows x[n] (last axis d) to positions[n] with the complex formulation."""
+    d = x.shape[-1]
+    half = d // 2
+    freqs = np.array([base ** (-(2.0 * i) / d) for i in range(half)])
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * positions[:, None] * freqs[None, :])
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def test_identity_factors_reproduce_sdpa():
+    """Full rank with identity factors is textbook RoPE attention (torch SDPA in fp64 on CPU)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(4)
+    B, H, d, T = 2, 3, 16, 45
+    K = rng.standard_normal((B, T, H * d))
+    V = rng.standard_normal((B, T, H * d))
+    q = rng.standard_normal((B, H, d))
+    ranks = [d] * H
+    bk = np.concatenate([np.eye(d)] * H)                 # B_k[h] = I_d
+    bv = np.eye(H * d)                                    # B_v = I_{H d}: head h takes its block
+    lat = oracle.decode_latent(K, V, bk, bv, q, ranks)
+    dense = oracle.decode_dense(K, V, q)
+    pos = np.arange(T, dtype=np.float64)
+    ref = np.empty((B, H, d))
+    for b in range(B):
+        for h in range(H):
+            kr = _rope_complex(K[b, :, h * d:(h + 1) * d], pos)
+            qt = torch.tensor(q[b, h][None, None, None, :])
+            kt = torch.tensor(kr[None, None])
+            vt = torch.tensor(V[b, :, h * d:(h + 1) * d][None, None])
+            ref[b, h] = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0, 0].numpy()
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(lat - ref)) <= 1e-12 * rms
+    assert np.max(np.abs(dense - ref)) <= 1e-12 * rms
+
+
+def _brute_force_mp(zk, zv, bk, bv, q, ranks, base, scale):
+    """Straight definition in 40-digit arithmetic: build K_h and V_h explicitly, rotate with 2x2
+    rotation matrices, softmax, weighted sum."""
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 40
+    B, T, _ = zk.shape
+    H, d = len(ranks), bk.shape[1]
+    out = np.empty((B, H, d))
+    koff = np.concatenate([[0], np.cumsum(ranks)])
+    for b in range(B):
+        for h in range(H):
+            scores = []
+            for n in range(T):
+                kt = [mp.fsum(mp.mpf(zk[b, n, c]) * mp.mpf(bk[c, j]) for c in range(koff[h], koff[h + 1]))
+                      for j in range(d)]
+                kr = [None] * d
+                for i in range(d // 2):
+                    ang = n * mp.power(mp.mpf(base), mp.mpf(-2 * i) / d)
+                    c, s = mp.cos(ang), mp.sin(ang)
+                    kr[i] = c * kt[i] - s * kt[i + d // 2]
+                    kr[i + d // 2] = s * kt[i] + c * kt[i + d // 2]
+                scores.append(mp.mpf(scale) * mp.fsum(mp.mpf(q[b, h, j]) * kr[j] for j in range(d)))
+            m = max(scores)
+            w = [mp.exp(s - m) for s in scores]
+            Z = mp.fsum(w)
+            for j in range(d):
+                vals = [mp.fsum(mp.mpf(zv[b, n, c]) * mp.mpf(bv[c, h * d + j]) for c in range(zv.shape[2]))
+                        for n in range(T)]
+                out[b, h, j] = float(mp.fsum(w[n] * vals[n] for n in range(T)) / Z)
+    return out
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 4, 1, [2], 3), (1, 2, 4, 3, [1, 3], 2), (2, 2, 8, 17, [4, 1], 5), (1, 2, 8, 2, [8, 8], 16),
+])
+def test_brute_force_tiny(shape):
+    B, H, d, T, ranks, rv = shape
+    rng = np.random.default_rng(sum(ranks) * 31 + T)
+    zk, zv, bk, bv, q = _rand_layer(rng, B, H, d, T, ranks, rv)
+    base, scale = 10000.0, 1.0 / math.sqrt(d)
+    ref = _brute_force_mp(zk, zv, bk, bv, q, ranks, base, scale)
+    got = oracle.decode_latent(zk, zv, bk, bv, q, ranks, rope_base=base, scale=scale)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+    # a different base and scale go through the same definition
+    ref2 = _brute_force_mp(zk, zv, bk, bv, q, ranks, 500.0, 0.3)
+    got2 = oracle.decode_latent(zk, zv, bk, bv, q, ranks, rope_base=500.0, scale=0.3)
+    assert np.max(np.abs(got2 - ref2)) <= 1e-12 * max(1.0, np.max(np.abs(ref2)))
+
+
+def test_closed_forms():
+    rng = np.random.default_rng(5)
+    B, H, d, ranks, rv = 2, 3, 16, [2, 5, 16], 7
+    # one cached token: the output is that token's value, o_h = Z_v[0] B_v^h
+    zk, zv, bk, bv, q = _rand_layer(rng, B, H, d, 1, ranks, rv)
+    got = oracle.decode_latent(zk, zv, bk, bv, q, ranks)
+    ref = (zv[:, 0, :] @ bv).reshape(B, H, d)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    # zero query: uniform attention, o_h = mean_n(Z_v[n]) B_v^h
+    zk, zv, bk, bv, q = _rand_layer(rng, B, H, d, 50, ranks, rv)
+    got = oracle.decode_latent(zk, zv, bk, bv, np.zeros_like(q), ranks)
+    ref = (zv.mean(axis=1) @ bv).reshape(B, H, d)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    # one dominating score: a key parallel to the rotated-back query with a huge norm
+    T = 40
+    zk, zv, bk, bv, q = _rand_layer(rng, 1, 1, 8, T, [8], 4)
+    bk = np.eye(8)
+    star = 23
+    zk[0, :, :] *= 1e-3
+    zk[0, star, :] = oracle.rope(q[0, 0], -star) * 60.0    # R(star) k = 60 q -> score 60|q|^2/sqrt(8)
+    got = oracle.decode_latent(zk, zv, bk, bv, q, [8])
+    ref = zv[0, star] @ bv
+    assert np.allclose(got[0, 0], ref, rtol=0, atol=1e-9)
+
+
+def test_pairs_subset_matches_full():
+    rng = np.random.default_rng(6)
+    zk, zv, bk, bv, q = _rand_layer(rng, 3, 4, 16, 33, [4, 8, 12, 16], 24)
+    full = oracle.decode_latent(zk, zv, bk, bv, q, [4, 8, 12, 16])
+    pairs = [(2, 3), (0, 0), (1, 2)]
+    sub = oracle.decode_latent(zk, zv, bk, bv, q, [4, 8, 12, 16], pairs=pairs)
+    for i, (b, h) in enumerate(pairs):
+        assert np.array_equal(sub[i], full[b, h])
+
+
+def test_low_precision_inputs_widen_exactly():
+    rng = np.random.default_rng(8)
+    zk, zv, bk, bv, q = _rand_layer(rng, 1, 2, 16, 20, [4, 8], 8)
+    z16k, z16v = zk.astype(np.float16), zv.astype(np.float16)
+    a = oracle.decode_latent(z16k, z16v, bk, bv, q, [4, 8])
+    b = oracle.decode_latent(z16k.astype(np.float64), z16v.astype(np.float64), bk, bv, q, [4, 8])
+    assert np.array_equal(a, b)
+    from rank_kv_cache_amd.synth import to_bf16_bits, bf16_bits_to_f32
+    kb, vb = to_bf16_bits(zk.astype(np.float32)), to_bf16_bits(zv.astype(np.float32))
+    c = oracle.decode_latent(kb, vb, bk, bv, q, [4, 8], bf16=True)
+    d = oracle.decode_latent(bf16_bits_to_f32(kb).astype(np.float64),
+                             bf16_bits_to_f32(vb).astype(np.float64), bk, bv, q, [4, 8])
+    assert np.array_equal(c, d)
+
+
+# ------------------------------------------------------------------------------------------------
+# Hadamard rotation
+# ------------------------------------------------------------------------------------------------
+
+def test_hadamard_textbook_and_orthogonal():
+    assert np.allclose(oracle.hadamard(2), np.array([[1, 1], [1, -1]]) / math.sqrt(2), atol=0, rtol=1e-15)
+    h4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]]) / 2.0
+    assert np.array_equal(oracle.hadamard(4), h4)
+    for n in (1, 2, 4, 8, 16, 32, 64):
+        Hm = oracle.hadamard(n)
+        assert np.allclose(Hm @ Hm.T, np.eye(n), atol=1e-15, rtol=0)
+        assert np.allclose(np.abs(Hm), 1 / math.sqrt(n), rtol=1e-15, atol=0)
+        if n >= 2:   # Sylvester recursion H_2n = [[H, H], [H, -H]] / sqrt(2)
+            Hh = oracle.hadamard(n // 2)
+            rec = np.block([[Hh, Hh], [Hh, -Hh]]) / math.sqrt(2)
+            assert np.allclose(Hm, rec, atol=1e-15, rtol=0)
+
+
+def test_hadamard_block_rule():
+    # min(64, largest power of two dividing the width)
+    for w, b in ((1, 1), (7, 1), (12, 4), (24, 8), (36, 4), (48, 16), (4, 4), (16, 16),
+                 (256, 64), (768, 64), (320, 64), (96, 32), (6, 2)):
+        assert oracle.hadamard_block(w) == b
+
+
+def test_segments_and_bits():
+    segs = oracle.latent_segments([16, 48], 0.25)
+    assert segs.tolist() == [[0, 4], [4, 12], [16, 12], [28, 36]]
+    bits = oracle.channel_bits([16, 48], 0.25)
+    assert bits.tolist() == [4] * 4 + [3] * 12 + [4] * 12 + [3] * 36
+    assert oracle.n_hi(1024, 0.25) == 256 and oracle.n_hi(20, 0.2) == 4 and oracle.n_hi(16, 0.2) == 4
+    assert oracle.n_hi(10, 0.0) == 0 and oracle.n_hi(10, 1.0) == 10
+
+
+def test_rotation_absorbs_exactly():
+    """Z B = (Z H)(H^T B) for the block-diagonal orthogonal rotation."""
+    rng = np.random.default_rng(9)
+    ranks = [16, 32, 48, 64]
+    segs = oracle.latent_segments(ranks, 0.25)
+    Z = rng.standard_normal((50, sum(ranks)))
+    Bm = rng.standard_normal((sum(ranks), 128))
+    Zr = oracle.rotate_rows(Z, segs)
+    Br = oracle.rotate_factor(Bm, segs)
+    assert np.allclose(Zr @ Br, Z @ Bm, atol=1e-12, rtol=0)
+    # and it is the block-diagonal matrix built from hadamard(): compare with a dense product
+    Hfull = np.zeros((sum(ranks), sum(ranks)))
+    for s0, w in segs:
+        b = oracle.hadamard_block(int(w))
+        for j0 in range(s0, s0 + w, b):
+            Hfull[j0:j0 + b, j0:j0 + b] = oracle.hadamard(b)
+    assert np.allclose(Zr, Z @ Hfull, atol=1e-13, rtol=0)
+    assert np.allclose(Br, Hfull.T @ Bm, atol=1e-13, rtol=0)
+
+
+def test_rotation_fp16_storage_rule():
+    rng = np.random.default_rng(10)
+    ranks = [16, 32, 48, 64]
+    segs = oracle.latent_segments(ranks, 0.25)
+    Z16 = (rng.standard_normal((40, sum(ranks))) * 3).astype(np.float16)
+    got = oracle.rotate_rows(Z16, segs)
+    exact = oracle.rotate_rows(Z16.astype(np.float64), segs)
+    # blocks of 1, 4, 16 and 64 have power-of-two scales: one rounding of the exact value
+    blocks = np.zeros(sum(ranks), int)
+    for s0, w in segs:
+        blocks[s0:s0 + w] = oracle.hadamard_block(int(w))
+    one_round = np.isin(blocks, (1, 4, 16, 64))
+    assert np.array_equal(got[:, one_round].view(np.uint16),
+                          exact[:, one_round].astype(np.float16).view(np.uint16))
+    # blocks of 2, 8, 32: exact sum times fp64(1/sqrt(b)), then one more rounding to fp16
+    assert np.all(np.abs(got.astype(np.float64) - exact) <= 2.0 ** -10 * np.abs(exact) + 2.0 ** -24)
+    B16 = (rng.standard_normal((sum(ranks), 64)) / 4).astype(np.float16)
+    gotb = oracle.rotate_factor(B16, segs)
+    exb = oracle.rotate_factor(B16.astype(np.float64), segs)
+    assert np.array_equal(gotb[one_round].view(np.uint16), exb[one_round].astype(np.float16).view(np.uint16))
+
+
+# ------------------------------------------------------------------------------------------------
+# quantiser (hand-derived fixtures + bounds + round trip)
+# ------------------------------------------------------------------------------------------------
+
+def _expand(case, key_pattern, key_list, key_fill):
+    if key_pattern in case:
+        pat = case[key_pattern]
+        return [pat[t % len(pat)] for t in range(64)]
+    vals = list(case[key_list])
+    return vals + [case[key_fill]] * (64 - len(vals))
+
+
+def _f16(v):
+    return np.float16(-0.0) if v == "-0" else np.float16(v)
+
+
+@pytest.mark.parametrize("name", ["ramp3", "ramp4", "ties3", "scale_rounding3", "constant3", "negzero3"])
+def test_quantiser_golden(name):
+    with open(os.path.join(GOLDEN, "q43_groups.json")) as f:
+        case = json.load(f)[name]
+    x = np.array([_f16(v) for v in _expand(case, "x_pattern", "x", "x_fill")], dtype=np.float16)
+    bits = case["bits"]
+    codes, s16, z16 = oracle.quantize_group(x, bits)
+    assert s16 == int(case["scale"], 16) and z16 == int(case["zero"], 16)
+    want_codes = _expand(case, "codes_pattern", "codes", "code_fill")
+    assert oracle.unpack_codes(codes, bits).tolist() == want_codes
+    if "bytes" in case:
+        assert [int(b) for b in codes] == [int(b, 16) for b in case["bytes"]]
+    if "bytes_pattern" in case:
+        pat = [int(b, 16) for b in case["bytes_pattern"]]
+        assert [int(b) for b in codes] == [pat[i % len(pat)] for i in range(32)]
+    if "dequant" in case or "dequant_pattern" in case:
+        want = [int(v, 16) for v in _expand(case, "dequant_pattern", "dequant", "dequant_fill")]
+        got = [oracle.dequant_value(c, s16, z16) for c in want_codes]
+        assert got == want
+
+
+def test_quantiser_bounds_random():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        bits = 4 if trial % 2 else 3
+        x = (rng.standard_normal(64) * 10.0 ** rng.uniform(-3, 2)).astype(np.float16)
+        codes, s16, z16 = oracle.quantize_group(x, bits)
+        q = oracle.unpack_codes(codes, bits)
+        assert q.min() >= 0 and q.max() <= (1 << bits) - 1
+        s = float(np.uint16(s16).view(np.float16))
+        xh = np.array([oracle.dequant_value(c, s16, z16) for c in q], np.uint16).view(np.float16)
+        err = np.abs(xh.astype(np.float64) - x.astype(np.float64))
+        # half a step, plus the scale's own fp16 rounding over at most 2^bits - 1 steps, plus the
+        # final fp16 rounding of the dequantised value
+        bound = s / 2 + ((1 << bits) - 1) * s * 2.0 ** -11 + np.abs(x.astype(np.float64)) * 2.0 ** -10 + 2.0 ** -24
+        assert np.all(err <= bound)
+
+
+def test_q43_pack_roundtrip_and_tail():
+    rng = np.random.default_rng(12)
+    ranks = [16, 48]
+    bits = oracle.channel_bits(ranks, 0.25)
+    B, T, cap = 2, 64 * 3 + 21, 64 * 5
+    x = (rng.standard_normal((B, T, sum(ranks))) * 0.3).astype(np.float16)
+    codes, meta, tail = oracle.q43_pack(x, bits, cap)
+    assert codes.shape == (B, cap // 64, oracle.q43_block_bytes(bits))
+    assert oracle.q43_block_bytes(bits) == 16 * 32 + 48 * 24
+    xh = oracle.q43_unpack(codes, meta, tail, bits, T, cap)
+    # complete groups: exactly the per-group quantise/dequantise; tail rows: unchanged
+    for b in range(B):
+        off = 0
+        for c in range(sum(ranks)):
+            for g in range(T // 64):
+                cg, s16, z16 = oracle.quantize_group(x[b, g * 64:(g + 1) * 64, c], int(bits[c]))
+                blk = codes[b, g, off:off + 8 * int(bits[c])]
+                assert np.array_equal(blk, cg)
+                assert meta[b, g, c, 0] == s16 and meta[b, g, c, 1] == z16
+                qs = oracle.unpack_codes(cg, int(bits[c]))
+                want = [oracle.dequant_value(v, s16, z16) for v in qs]
+                assert xh[b, g * 64:(g + 1) * 64, c].view(np.uint16).tolist() == want
+            off += 8 * int(bits[c])
+    assert np.array_equal(xh[:, 192:], x[:, 192:])
+    part = oracle.q43_unpack(codes, meta, tail, bits, T, cap, t0=100, t1=200)
+    assert np.array_equal(part, xh[:, 100:200])
+
+
+# ------------------------------------------------------------------------------------------------
+# ledger: the pages' printed numbers
+# ------------------------------------------------------------------------------------------------
+
+def test_ledger_printed_values():
+    with open(os.path.join(GOLDEN, "ledger_values.json")) as f:
+        g = json.load(f)
+    i = g["mean_bits_top20"]["inputs"]
+    assert ledger.mean_bits(i["top_fraction"], i["bits_hi"], i["bits_lo"]) == pytest.approx(3.2, abs=1e-12)
+    for k in ("ratio_rank25_bits3p2", "ratio_rank40_bits3p2", "ratio_rank25_fp16"):
+        i = g[k]["inputs"]
+        assert ledger.ratio_vs_fp16(i["retained_fraction"], i["bits"]) == pytest.approx(g[k]["value"], abs=1e-9)
+    i = g["whole_model_3_exempt"]["inputs"]
+    assert ledger.whole_model_ratio(i["n_layers"], i["n_exempt"], i["layer_ratio"]) == pytest.approx(
+        g["whole_model_3_exempt"]["value"], abs=g["whole_model_3_exempt"]["tolerance"])
+    i = g["joint_over_headwise_reconstruction"]["inputs"]
+    for H in i["heads"]:
+        hd = ledger.explicit_reconstruction_mults(1000, H, i["head_dim"], i["retained_fraction"], "headwise")
+        jd = ledger.explicit_reconstruction_mults(1000, H, i["head_dim"], i["retained_fraction"], "joint")
+        assert jd / hd == pytest.approx(H, rel=1e-12)
+
+
+def test_ledger_model_bytes_consistent():
+    # a whole model of latent layers at retained fraction 0.25 and 3.2 bits is 20x smaller than fp16
+    H, d, L = 32, 128, 32
+    lay = [dict(dense=False, heads=H, head_dim=d, key_ranks=[32] * H, value_rank=1024, bits=3.2)] * L
+    dense = [dict(dense=True, heads=H, head_dim=d)] * L
+    r = ledger.model_payload_bytes(4, 1000, dense) / ledger.model_payload_bytes(4, 1000, lay)
+    assert r == pytest.approx(20.0, rel=1e-12)
+    mixed = dense[:3] + lay[3:]
+    r2 = ledger.model_payload_bytes(4, 1000, dense) / ledger.model_payload_bytes(4, 1000, mixed)
+    assert r2 == pytest.approx(ledger.whole_model_ratio(32, 3, 20.0), rel=1e-12)
