@@ -1,0 +1,185 @@
+/*
+ * starkv.h -- C ABI of the MI355X (gfx950) latent-KV decode-attention library.
+ *
+ * The library implements the decode-time data path of STAR-KV (Bhatnagar et al., "STAR-KV:
+ * Low-Rank KV Cache Compression via Soft Thresholding for Adaptive Rank Control"): keys are
+ * cached per head as pre-RoPE latents Z_k[h] (T x r_k[h]) with a constant up factor B_k[h]
+ * (r_k[h] x d); values are cached as one joint latent Z_v (T x r_v) shared by all heads, with up
+ * factor B_v (r_v x H*d). A decode step appends the new token's latents and attends from the
+ * latents without ever writing a full-width K or V (Zhou, "STAR-KV reading notes", sections 2.2,
+ * 5.1, 5.3 and Algorithm 2; gist.science explainer, "Technisches Resuemee", Methodik 2-3).
+ *
+ * Conventions shared by every entry point
+ *  - All pointers to bulk data are DEVICE pointers owned by the caller; descriptor structs and
+ *    key_ranks are HOST memory read during the call only. The library never allocates, frees or
+ *    synchronises, and keeps no pointer after it returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is enqueued on it.
+ *  - Validation runs on the host before anything is enqueued: a non-OK return means nothing was
+ *    enqueued and no buffer was touched. A failed launch returns STARKV_ERR_DEVICE. Faults inside
+ *    kernels surface at the caller's next synchronisation of the stream.
+ *  - Shapes: num_heads in [1, 32]; head_dim 64 or 128; key and value ranks multiples of 16 with
+ *    r_k[h] <= head_dim and 16 <= r_v <= 2048 (latent layers); capacity a multiple of 64.
+ *  - Bulk pointers must be 16-byte aligned.
+ *  - Calls that write the same buffers must not overlap in time (use one stream per cache).
+ *
+ * Cache layouts (element type = cache_dtype for F32/F16/BF16; fp16 tails for Q43):
+ *  - latent layer, F32/F16/BF16:
+ *      zk: [B][capacity][R_k], R_k = sum_h r_k[h]; per token the heads' latents are concatenated
+ *          in head order (token-major).
+ *      zv: [B][capacity/64][r_v][64]: channel-major inside each 64-token block, so the 64 values
+ *          of one channel in one block are contiguous.
+ *      zk_meta, zv_meta, zk_tail, zv_tail: unused (may be NULL).
+ *  - dense (exempt) layer, F32/F16/BF16: zk = K, zv = V, both [B][capacity][H*d] token-major;
+ *      keys are stored pre-RoPE.
+ *  - latent layer, Q43 (mixed 4/3-bit, see starkv_layer): for each latent (zk with C = R_k
+ *      channels, zv with C = r_v), channel j of a latent of width r is "hi" (q_bits_hi bits) when
+ *      j < ceil(q_top_fraction * r), else "lo" (q_bits_lo bits); per 64-token block:
+ *      zk / zv:           [B][capacity/64][block_bytes], channel c occupying 8*bits(c) bytes at
+ *                         offset sum_{c'<c} 8*bits(c'). 4-bit: token t in byte t/2, low nibble for
+ *                         even t. 3-bit: bytes 0..15 hold the low two bits (token t in byte t/4 at
+ *                         bit 2*(t%4)), bytes 16..23 the third bit (token t in byte 16+t/8, bit t%8).
+ *      zk_meta / zv_meta: [B][capacity/64][C][2] fp16 (scale, zero).
+ *      zk_tail / zv_tail: [B][64][C] fp16: rows of the unfinished last group.
+ *    Use starkv_cache_bytes() for every buffer size.
+ */
+#ifndef STARKV_H
+#define STARKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STARKV_OK = 0,
+    STARKV_ERR_NULL = 1,         /* a required pointer is NULL */
+    STARKV_ERR_SHAPE = 2,        /* a size is negative, zero where it must not be, or inconsistent */
+    STARKV_ERR_RANK_ALIGN = 3,   /* a rank is not a multiple of 16, or exceeds its bound */
+    STARKV_ERR_DTYPE = 4,        /* unknown dtype or unsupported cache/factor combination */
+    STARKV_ERR_MISALIGNED = 5,   /* a bulk pointer is not 16-byte aligned */
+    STARKV_ERR_CAPACITY = 6,     /* capacity not a multiple of 64, or a range beyond capacity */
+    STARKV_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than starkv_decode_workspace_bytes */
+    STARKV_ERR_UNSUPPORTED = 8,  /* valid request outside what the kernels implement */
+    STARKV_ERR_DEVICE = 9        /* a HIP call or kernel launch failed */
+} starkv_status;
+
+typedef enum { STARKV_F32 = 0, STARKV_F16 = 1, STARKV_BF16 = 2, STARKV_Q43 = 3 } starkv_dtype;
+
+/* One attention layer. Host memory. */
+typedef struct {
+    int32_t num_heads;           /* H */
+    int32_t head_dim;            /* d (64 or 128) */
+    const int32_t *key_ranks;    /* [H] per-head key ranks r_k[h] (latent layers; NULL if dense) */
+    int32_t value_rank;          /* joint value rank r_v (latent layers; ignored if dense) */
+    int32_t dense;               /* 1: exempt layer with full-width K/V; 0: latent layer */
+    int32_t cache_dtype;         /* starkv_dtype: F32, F16, BF16, or Q43 (latent layers only) */
+    int32_t factor_dtype;        /* starkv_dtype of B_k, B_v: F32 with F32 caches, F16 with F16 and
+                                    Q43 caches, BF16 with BF16 caches */
+    double rope_base;            /* RoPE base (10000 for LLaMA); must be > 1 */
+    float sm_scale;              /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+    float q_top_fraction;        /* Q43: fraction of each latent's leading channels at q_bits_hi */
+    int32_t q_bits_hi;           /* Q43: 4 */
+    int32_t q_bits_lo;           /* Q43: 3 */
+    int32_t q_group;             /* Q43: tokens per quantisation group; must be 64 */
+} starkv_layer;
+
+/* Caller-owned device buffers of one layer's cache (see layouts above). */
+typedef struct {
+    int32_t batch;               /* B */
+    int32_t capacity;            /* tokens per sequence the buffers hold; multiple of 64 */
+    void *zk, *zv;
+    void *zk_meta, *zv_meta;     /* Q43 only */
+    void *zk_tail, *zv_tail;     /* Q43 only */
+} starkv_cache;
+
+/* Byte sizes of the six cache buffers {zk, zv, zk_meta, zv_meta, zk_tail, zv_tail} for a layer,
+ * batch and capacity (0 for buffers the layout does not use). Pure host arithmetic. */
+starkv_status starkv_cache_bytes(const starkv_layer *layer, int32_t batch, int32_t capacity,
+                                 size_t out_bytes[6]);
+
+/*
+ * Append n_new tokens per sequence at positions [pos, pos + n_new) (Zhou notes, Algorithm 2
+ * steps 1-3: the new token's latents, already in the rotated basis when rotation is used, are
+ * quantised if enabled and appended).
+ *   zk_new: [B][n_new][R_k] (dense: [B][n_new][H*d]); zv_new: [B][n_new][r_v] (dense: H*d), in
+ *   the cache element type (fp16 for Q43). Must not alias the cache.
+ * Q43: a 64-token group is quantised when it completes (its earlier rows are read from the tail
+ * buffer); rows of an unfinished group are written to the tail. Appends must therefore be made in
+ * increasing, gap-free positions. fp caches accept any range.
+ * Errors: NULL, SHAPE (pos < 0, n_new < 0), CAPACITY (pos + n_new > capacity), DTYPE, MISALIGNED.
+ * n_new == 0 or batch == 0 returns OK without enqueuing.
+ */
+starkv_status starkv_append_latents(const starkv_layer *layer, const starkv_cache *cache,
+                                    int64_t pos, int64_t n_new, const void *zk_new,
+                                    const void *zv_new, void *stream);
+
+/* Workspace bytes starkv_decode_attn needs for this layer, batch, seq_len and split request
+ * (num_splits 0 = the library's choice). Returns 0 for invalid descriptors. */
+size_t starkv_decode_workspace_bytes(const starkv_layer *layer, int32_t batch, int64_t seq_len,
+                                     int32_t num_splits);
+
+/*
+ * Single-token decode attention over the first seq_len cached tokens of every sequence
+ * (Zhou notes, Algorithm 2 steps 4-7, section 5.3):
+ *   s_{h,n} = scale * q_h . RoPE_n(Z_k[h][n] B_k[h]),  p = softmax_n(s),
+ *   out_h   = (sum_n p_{h,n} Z_v[n]) B_v[:, h*d:(h+1)*d]
+ * (dense layers: out_h = sum_n p_{h,n} V_h[n] with K, V full width).
+ * RoPE is LLaMA rotate-half: pair (i, i+d/2) of the key at cache position n is rotated by the
+ * angle n * rope_base^(-2i/d). Split-K over the sequence with a log-sum-exp merge.
+ *   q:   [B][H][d] fp32, already rotated to the query's own position.
+ *   bk:  [R_k][d] factor_dtype (heads' factors stacked in head order); NULL for dense layers.
+ *   bv:  [r_v][H*d] factor_dtype; NULL for dense layers.
+ *   out: [B][H][d] fp32, per-head attention output before the output projection.
+ *   num_splits: 0 = library choice; otherwise the number of sequence splits (>= 1).
+ *   workspace: device scratch of at least starkv_decode_workspace_bytes(...) bytes; contents on
+ *   entry are ignored and clobbered.
+ * For Q43 caches seq_len must equal the number of tokens appended so far (the unfinished group is
+ * read from the tail). out and workspace must not alias any input.
+ * Errors: NULL, SHAPE (seq_len < 1), CAPACITY (seq_len > capacity), DTYPE, MISALIGNED, WORKSPACE,
+ * UNSUPPORTED. batch == 0 returns OK without enqueuing.
+ */
+starkv_status starkv_decode_attn(const starkv_layer *layer, const starkv_cache *cache,
+                                 int64_t seq_len, const float *q, const void *bk, const void *bv,
+                                 float *out, int32_t num_splits, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/*
+ * Read cached tokens [t0, t1) back in token-major order: zk_out [B][t1-t0][R_k] (dense: H*d) and
+ * zv_out [B][t1-t0][r_v] (dense: H*d). Element type: fp16 for Q43 (codes of complete groups are
+ * dequantised as binary16(fmaf(code, scale, zero)); rows of the unfinished group come from the
+ * tail), otherwise the cache element type (a plain gather). seq_len is the number of tokens
+ * appended so far (Q43: decides which groups are complete). Either output may be NULL to skip it.
+ * Errors: NULL (cache buffers), SHAPE (t0 < 0 or t0 > t1), CAPACITY (t1 > seq_len or seq_len >
+ * capacity), DTYPE, MISALIGNED.
+ */
+starkv_status starkv_dequant(const starkv_layer *layer, const starkv_cache *cache,
+                             int64_t seq_len, int64_t t0, int64_t t1, void *zk_out, void *zv_out,
+                             void *stream);
+
+/*
+ * Offline preparation: absorb the blockwise Hadamard rotation (Zhou notes, section 6.1 / Fig. 5).
+ * Each latent (every head's key latent for which = 0, the joint value latent for which = 1) is
+ * split into its first ceil(q_top_fraction * r) channels and the rest; each part of width w is
+ * rotated by blockdiag(H_b, ...) with b = min(64, largest power of two dividing w) and H_b the
+ * normalised Sylvester-Hadamard matrix. kind 0 rotates latent rows (dst = src . H, src/dst
+ * [n][C]); kind 1 rotates factor rows (dst = H^T . src, src/dst [C][n] with n = head_dim for keys,
+ * H*d for values). fp16 in and out: each output is binary16 of (the exact signed sum of the
+ * inputs) times the fp64 value of 1/sqrt(b). src and dst must not alias.
+ * Errors: NULL, SHAPE (n < 0), DTYPE (not fp16), RANK_ALIGN, MISALIGNED.
+ */
+starkv_status starkv_hadamard_rotate(const starkv_layer *layer, int32_t which, int32_t kind,
+                                     int64_t n, const void *src, void *dst, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *starkv_status_string(starkv_status status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t starkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STARKV_H */

@@ -1,0 +1,458 @@
+// api.cpp -- host side of the C ABI declared in include/starkv.h: argument validation (entirely
+// before anything is enqueued), the split planner, workspace carving and kernel launches.
+
+#include "starkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "common.hpp"
+
+namespace starkv {
+hipError_t launch_latent_split(const LatentDecodeParams& p, int elem, int ntv, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, hipStream_t st);
+hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
+hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
+                            const int16_t* rank, int elem, hipStream_t st);
+hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
+
+hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
+hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st);
+}  // namespace starkv
+
+using namespace starkv;
+
+namespace {
+
+constexpr int kTargetWorkgroups = 256;   // MI355X compute units: one decode workgroup per CU
+constexpr int kMaxSplits = 256;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int elem_bytes(int dt) { return dt == STARKV_F32 ? 4 : 2; }
+
+inline int elem_kind(int dt) {
+    return dt == STARKV_F32 ? kF32 : dt == STARKV_BF16 ? kBF16 : kF16;
+}
+
+struct LayerInfo {
+    int H = 0, D = 0, rv = 0, Rk = 0;
+    bool dense = false, q43 = false;
+    int cache_dt = 0, factor_dt = 0;
+    int16_t koff[kMaxHeads + 1] = {0};
+    int16_t rank[kMaxHeads] = {0};
+};
+
+// Validates the layer descriptor (host arithmetic only).
+starkv_status check_layer(const starkv_layer* L, LayerInfo* out) {
+    if (!L) return STARKV_ERR_NULL;
+    LayerInfo li;
+    li.H = L->num_heads;
+    li.D = L->head_dim;
+    li.dense = L->dense != 0;
+    li.cache_dt = L->cache_dtype;
+    li.factor_dt = L->factor_dtype;
+    if (li.H < 1 || li.D < 2 || (li.D & 1)) return STARKV_ERR_SHAPE;
+    if (!(L->rope_base > 1.0) || !std::isfinite(L->rope_base)) return STARKV_ERR_SHAPE;
+    if (std::isnan(L->sm_scale) || std::isinf(L->sm_scale)) return STARKV_ERR_SHAPE;
+    if (li.cache_dt < STARKV_F32 || li.cache_dt > STARKV_Q43) return STARKV_ERR_DTYPE;
+    if (li.H > kMaxHeads || (li.D != 64 && li.D != 128)) return STARKV_ERR_UNSUPPORTED;
+    if (li.dense) {
+        if (li.cache_dt == STARKV_Q43) return STARKV_ERR_DTYPE;
+        *out = li;
+        return STARKV_OK;
+    }
+    if (!L->key_ranks) return STARKV_ERR_NULL;
+    const int want_factor = li.cache_dt == STARKV_Q43 ? STARKV_F16 : li.cache_dt;
+    if (li.factor_dt != want_factor) return STARKV_ERR_DTYPE;
+    int off = 0;
+    for (int h = 0; h < li.H; ++h) {
+        const int r = L->key_ranks[h];
+        if (r < 16 || r > li.D || (r % 16)) return STARKV_ERR_RANK_ALIGN;
+        li.koff[h] = static_cast<int16_t>(off);
+        li.rank[h] = static_cast<int16_t>(r);
+        off += r;
+    }
+    li.koff[li.H] = static_cast<int16_t>(off);
+    li.Rk = off;
+    li.rv = L->value_rank;
+    if (li.rv < 16 || (li.rv % 16) || li.rv > 2048) return STARKV_ERR_RANK_ALIGN;
+    if (li.rv > 1280) return STARKV_ERR_UNSUPPORTED;
+    if (li.cache_dt == STARKV_Q43) {
+        li.q43 = true;
+        if (L->q_group != 64) return STARKV_ERR_UNSUPPORTED;
+        if (L->q_bits_hi != 4 || L->q_bits_lo != 3) return STARKV_ERR_UNSUPPORTED;
+        if (!(L->q_top_fraction >= 0.0f && L->q_top_fraction <= 1.0f)) return STARKV_ERR_SHAPE;
+    }
+    *out = li;
+    return STARKV_OK;
+}
+
+starkv_status check_cache(const starkv_cache* c, const LayerInfo& li) {
+    if (!c) return STARKV_ERR_NULL;
+    if (c->batch < 0 || c->capacity < 0) return STARKV_ERR_SHAPE;
+    if (c->capacity == 0 || (c->capacity % kTile)) return STARKV_ERR_CAPACITY;
+    if (c->batch == 0) return STARKV_OK;
+    if (!c->zk || !c->zv) return STARKV_ERR_NULL;
+    if (!aligned16(c->zk) || !aligned16(c->zv)) return STARKV_ERR_MISALIGNED;
+    if (li.q43) {
+        if (!c->zk_meta || !c->zv_meta || !c->zk_tail || !c->zv_tail) return STARKV_ERR_NULL;
+        if (!aligned16(c->zk_meta) || !aligned16(c->zv_meta) || !aligned16(c->zk_tail) ||
+            !aligned16(c->zv_tail))
+            return STARKV_ERR_MISALIGNED;
+    }
+    return STARKV_OK;
+}
+
+// Key-phase schedule: the heads are dealt to kKeyWaveGroups waves so that their rank sums
+// (MFMA work) are balanced: longest-processing-time-first greedy.
+void plan_heads(const LayerInfo& li, LatentDecodeParams* p) {
+    std::vector<int> order(li.H);
+    for (int h = 0; h < li.H; ++h) order[h] = h;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return li.rank[a] > li.rank[b]; });
+    int load[kKeyWaveGroups] = {0};
+    for (int g = 0; g < kKeyWaveGroups; ++g) p->sched_n[g] = 0;
+    for (int h : order) {
+        int g = 0;
+        for (int k = 1; k < kKeyWaveGroups; ++k)
+            if (load[k] < load[g]) g = k;
+        p->sched[g][p->sched_n[g]++] = static_cast<int8_t>(h);
+        load[g] += li.rank[h];
+    }
+}
+
+int plan_splits(int B, int64_t seq_len, int requested) {
+    const int ntiles = static_cast<int>((seq_len + kTile - 1) / kTile);
+    int S = requested > 0 ? requested : (kTargetWorkgroups + std::max(B, 1) - 1) / std::max(B, 1);
+    S = std::max(1, std::min({S, ntiles, kMaxSplits}));
+    return S;
+}
+
+struct WorkspaceLayout {
+    size_t bkt = 0, ml = 0, acc = 0, a = 0, total = 0;
+    int S = 1, tps = 1;
+};
+
+WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, int requested) {
+    WorkspaceLayout w;
+    w.S = plan_splits(B, seq_len, requested);
+    const int ntiles = static_cast<int>((seq_len + kTile - 1) / kTile);
+    w.tps = (ntiles + w.S - 1) / w.S;
+    const int width = li.dense ? li.D : li.rv;
+    size_t off = 0;
+    if (!li.dense) {
+        w.bkt = off;
+        off += align_up(static_cast<size_t>(li.Rk) * li.D * elem_bytes(li.factor_dt));
+    }
+    w.ml = off;
+    off += align_up(static_cast<size_t>(B) * w.S * li.H * 2 * sizeof(float));
+    w.acc = off;
+    off += align_up(static_cast<size_t>(B) * w.S * li.H * width * sizeof(float));
+    if (!li.dense) {
+        w.a = off;
+        off += align_up(static_cast<size_t>(B) * li.H * li.rv * sizeof(float));
+    }
+    w.total = off;
+    return w;
+}
+
+void fill_rope(double base, int D, double* rev) {
+    for (int i = 0; i < D / 2; ++i)
+        rev[i] = std::pow(base, (-2.0 * i) / D) / (2.0 * M_PI);
+}
+
+float q_scale_of(const starkv_layer* L, int D) {
+    const double scale = L->sm_scale > 0.0f ? static_cast<double>(L->sm_scale) : 1.0 / std::sqrt(D);
+    return static_cast<float>(scale * 1.4426950408889634);   // log2(e): softmax done in base 2
+}
+
+inline starkv_status dev(hipError_t e) { return e == hipSuccess ? STARKV_OK : STARKV_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t starkv_version(void) { return 100; }
+
+const char* starkv_status_string(starkv_status s) {
+    switch (s) {
+    case STARKV_OK: return "ok";
+    case STARKV_ERR_NULL: return "a required pointer is NULL";
+    case STARKV_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case STARKV_ERR_RANK_ALIGN: return "a rank is not a multiple of 16 or exceeds its bound";
+    case STARKV_ERR_DTYPE: return "unknown dtype or unsupported cache/factor dtype combination";
+    case STARKV_ERR_MISALIGNED: return "a bulk pointer is not 16-byte aligned";
+    case STARKV_ERR_CAPACITY: return "capacity not a multiple of 64, or a range beyond capacity";
+    case STARKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case STARKV_ERR_UNSUPPORTED: return "request outside what the kernels implement";
+    case STARKV_ERR_DEVICE: return "a HIP call or kernel launch failed";
+    }
+    return "unknown status";
+}
+
+starkv_status starkv_cache_bytes(const starkv_layer* layer, int32_t batch, int32_t capacity,
+                                 size_t out_bytes[6]) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if (!out_bytes) return STARKV_ERR_NULL;
+    if (batch < 0 || capacity < 0) return STARKV_ERR_SHAPE;
+    if (capacity == 0 || capacity % kTile) return STARKV_ERR_CAPACITY;
+    for (int i = 0; i < 6; ++i) out_bytes[i] = 0;
+    const size_t Bc = static_cast<size_t>(batch) * capacity;
+    if (li.dense) {
+        out_bytes[0] = out_bytes[1] = Bc * li.H * li.D * elem_bytes(li.cache_dt);
+        return STARKV_OK;
+    }
+    if (!li.q43) {
+        out_bytes[0] = Bc * li.Rk * elem_bytes(li.cache_dt);
+        out_bytes[1] = Bc * li.rv * elem_bytes(li.cache_dt);
+        return STARKV_OK;
+    }
+    return STARKV_ERR_UNSUPPORTED;
+}
+
+size_t starkv_decode_workspace_bytes(const starkv_layer* layer, int32_t batch, int64_t seq_len,
+                                     int32_t num_splits) {
+    LayerInfo li;
+    if (check_layer(layer, &li) != STARKV_OK || batch < 0 || seq_len < 1 || num_splits < 0)
+        return 0;
+    return workspace_layout(li, batch, seq_len, num_splits).total;
+}
+
+starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cache* cache,
+                                    int64_t pos, int64_t n_new, const void* zk_new,
+                                    const void* zv_new, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if ((s = check_cache(cache, li)) != STARKV_OK) return s;
+    if (pos < 0 || n_new < 0) return STARKV_ERR_SHAPE;
+    if (pos + n_new > cache->capacity) return STARKV_ERR_CAPACITY;
+    if (n_new == 0 || cache->batch == 0) return STARKV_OK;
+    if (!zk_new || !zv_new) return STARKV_ERR_NULL;
+    if (!aligned16(zk_new) || !aligned16(zv_new)) return STARKV_ERR_MISALIGNED;
+    if (li.q43) return STARKV_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int B = cache->batch;
+    const int es = elem_bytes(li.cache_dt);
+    const long long cap = cache->capacity;
+    if (li.dense) {
+        const long long row = static_cast<long long>(li.H) * li.D * es;
+        for (int which = 0; which < 2; ++which) {
+            RowCopyParams p;
+            p.src = static_cast<const char*>(which ? zv_new : zk_new);
+            p.dst = static_cast<char*>(which ? cache->zv : cache->zk);
+            p.src_seq_stride = n_new * row;
+            p.dst_seq_stride = cap * row;
+            p.src_off = 0;
+            p.dst_off = pos * row;
+            p.bytes = n_new * row;
+            if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
+        }
+        return STARKV_OK;
+    }
+    const long long krow = static_cast<long long>(li.Rk) * es;
+    RowCopyParams p;
+    p.src = static_cast<const char*>(zk_new);
+    p.dst = static_cast<char*>(cache->zk);
+    p.src_seq_stride = n_new * krow;
+    p.dst_seq_stride = cap * krow;
+    p.src_off = 0;
+    p.dst_off = pos * krow;
+    p.bytes = n_new * krow;
+    if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
+    BlockXposeParams x;
+    x.src = zv_new;
+    x.dst = cache->zv;
+    x.B = B;
+    x.C = li.rv;
+    x.cap = cache->capacity;
+    x.t_begin = pos;
+    x.t_end = pos + n_new;
+    x.row0 = pos;
+    x.rows_per_seq = n_new;
+    x.blk_first = static_cast<int>(pos / kTile);
+    x.to_blocks = 1;
+    return dev(launch_block_transpose(x, es, st));
+}
+
+starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* cache,
+                                 int64_t seq_len, const float* q, const void* bk, const void* bv,
+                                 float* out, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if ((s = check_cache(cache, li)) != STARKV_OK) return s;
+    if (seq_len < 1 || num_splits < 0) return STARKV_ERR_SHAPE;
+    if (seq_len > cache->capacity) return STARKV_ERR_CAPACITY;
+    if (cache->batch == 0) return STARKV_OK;
+    if (!q || !out) return STARKV_ERR_NULL;
+    if (!li.dense && (!bk || !bv)) return STARKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return STARKV_ERR_MISALIGNED;
+    if (!li.dense && (!aligned16(bk) || !aligned16(bv))) return STARKV_ERR_MISALIGNED;
+    const int B = cache->batch;
+    const WorkspaceLayout w = workspace_layout(li, B, seq_len, num_splits);
+    if (!workspace || workspace_bytes < w.total) return STARKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return STARKV_ERR_MISALIGNED;
+    if (li.q43) return STARKV_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const int ntiles = static_cast<int>((seq_len + kTile - 1) / kTile);
+    const int active = (ntiles + w.tps - 1) / w.tps;
+
+    if (li.dense) {
+        DenseDecodeParams p;
+        p.k = cache->zk;
+        p.v = cache->zv;
+        p.q = q;
+        p.ws_ml = reinterpret_cast<float*>(ws + w.ml);
+        p.ws_acc = reinterpret_cast<float*>(ws + w.acc);
+        p.B = B;
+        p.H = li.H;
+        p.D = li.D;
+        p.cap = cache->capacity;
+        p.seq_len = static_cast<int>(seq_len);
+        p.S = w.S;
+        p.tiles_per_split = w.tps;
+        p.q_scale = q_scale_of(layer, li.D);
+        fill_rope(layer->rope_base, li.D, p.rope_rev);
+        if ((s = dev(launch_dense_split(p, elem_kind(li.cache_dt), st))) != STARKV_OK) return s;
+        MergeParams m;
+        m.ws_ml = p.ws_ml;
+        m.ws_acc = p.ws_acc;
+        m.ws_a = out;
+        m.B = B;
+        m.H = li.H;
+        m.S = w.S;
+        m.W = li.D;
+        m.active_splits = active;
+        return dev(launch_merge(m, st));
+    }
+
+    const int ek = elem_kind(li.cache_dt);
+    void* bkt = ws + w.bkt;
+    if ((s = dev(launch_pack_keys(bk, bkt, li.D, li.H, li.koff, li.rank, ek, st))) != STARKV_OK)
+        return s;
+    LatentDecodeParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.zk = cache->zk;
+    p.zv = cache->zv;
+    p.bkt = bkt;
+    p.q = q;
+    p.ws_ml = reinterpret_cast<float*>(ws + w.ml);
+    p.ws_acc = reinterpret_cast<float*>(ws + w.acc);
+    p.B = B;
+    p.H = li.H;
+    p.D = li.D;
+    p.Rk = li.Rk;
+    p.rv = li.rv;
+    p.cap = cache->capacity;
+    p.seq_len = static_cast<int>(seq_len);
+    p.S = w.S;
+    p.tiles_per_split = w.tps;
+    p.q_scale = q_scale_of(layer, li.D);
+    for (int h = 0; h <= li.H; ++h) p.koff[h] = li.koff[h];
+    for (int h = 0; h < li.H; ++h) p.rank[h] = li.rank[h];
+    plan_heads(li, &p);
+    fill_rope(layer->rope_base, li.D, p.rope_rev);
+    const int ntv = (li.rv + 255) / 256;
+    if ((s = dev(launch_latent_split(p, ek, ntv, st))) != STARKV_OK) return s;
+    MergeParams m;
+    m.ws_ml = p.ws_ml;
+    m.ws_acc = p.ws_acc;
+    m.ws_a = reinterpret_cast<float*>(ws + w.a);
+    m.B = B;
+    m.H = li.H;
+    m.S = w.S;
+    m.W = li.rv;
+    m.active_splits = active;
+    if ((s = dev(launch_merge(m, st))) != STARKV_OK) return s;
+    ProjectParams pr;
+    pr.ws_a = m.ws_a;
+    pr.bv = bv;
+    pr.out = out;
+    pr.B = B;
+    pr.H = li.H;
+    pr.D = li.D;
+    pr.rv = li.rv;
+    return dev(launch_project(pr, ek, st));
+}
+
+starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cache,
+                             int64_t seq_len, int64_t t0, int64_t t1, void* zk_out, void* zv_out,
+                             void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if ((s = check_cache(cache, li)) != STARKV_OK) return s;
+    if (seq_len < 0 || t0 < 0 || t0 > t1) return STARKV_ERR_SHAPE;
+    if (seq_len > cache->capacity || t1 > seq_len) return STARKV_ERR_CAPACITY;
+    if ((zk_out && !aligned16(zk_out)) || (zv_out && !aligned16(zv_out))) return STARKV_ERR_MISALIGNED;
+    if (cache->batch == 0 || t0 == t1) return STARKV_OK;
+    if (li.q43) return STARKV_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int B = cache->batch;
+    const int es = elem_bytes(li.cache_dt);
+    const long long cap = cache->capacity, n = t1 - t0;
+    const long long krow = static_cast<long long>(li.dense ? li.H * li.D : li.Rk) * es;
+    if (zk_out) {
+        RowCopyParams p;
+        p.src = static_cast<const char*>(cache->zk);
+        p.dst = static_cast<char*>(zk_out);
+        p.src_seq_stride = cap * krow;
+        p.dst_seq_stride = n * krow;
+        p.src_off = t0 * krow;
+        p.dst_off = 0;
+        p.bytes = n * krow;
+        if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
+    }
+    if (zv_out) {
+        if (li.dense) {
+            RowCopyParams p;
+            p.src = static_cast<const char*>(cache->zv);
+            p.dst = static_cast<char*>(zv_out);
+            p.src_seq_stride = cap * krow;
+            p.dst_seq_stride = n * krow;
+            p.src_off = t0 * krow;
+            p.dst_off = 0;
+            p.bytes = n * krow;
+            return dev(launch_copy_rows(p, B, st));
+        }
+        BlockXposeParams x;
+        x.src = cache->zv;
+        x.dst = zv_out;
+        x.B = B;
+        x.C = li.rv;
+        x.cap = cache->capacity;
+        x.t_begin = t0;
+        x.t_end = t1;
+        x.row0 = t0;
+        x.rows_per_seq = n;
+        x.blk_first = static_cast<int>(t0 / kTile);
+        x.to_blocks = 0;
+        return dev(launch_block_transpose(x, es, st));
+    }
+    return STARKV_OK;
+}
+
+starkv_status starkv_hadamard_rotate(const starkv_layer* layer, int32_t which, int32_t kind,
+                                     int64_t n, const void* src, void* dst, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    (void)which; (void)kind; (void)n; (void)src; (void)dst; (void)stream;
+    return STARKV_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// common.hpp -- element traits, MFMA fragment helpers and kernel parameter blocks shared by the
+// HIP kernels of the latent-KV decode library and its host planner. gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace starkv {
+
+// ------------------------------------------------------------------------------------------------
+// Element types. Storage is F32 (float), F16 (_Float16) or BF16 (raw bits in uint16_t).
+// ------------------------------------------------------------------------------------------------
+enum ElemKind { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// fp32 -> bf16 bits, nearest-even (finite inputs).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <int K> struct Elem;
+template <> struct Elem<kF32> {
+    using storage = float;
+    using frag = f32x8;                 // 8 consecutive K elements per lane, 32 bytes
+    static constexpr int bytes = 4;
+};
+template <> struct Elem<kF16> {
+    using storage = _Float16;
+    using frag = f16x8;                 // 16 bytes
+    static constexpr int bytes = 2;
+};
+template <> struct Elem<kBF16> {
+    using storage = uint16_t;
+    using frag = bf16x8;                // 16 bytes
+    static constexpr int bytes = 2;
+};
+
+// Load 8 consecutive elements (16-byte aligned for 16-bit types, 32-byte for fp32).
+template <int K>
+__device__ __forceinline__ typename Elem<K>::frag load_frag(const void* base, size_t elem_off) {
+    using F = typename Elem<K>::frag;
+    return *reinterpret_cast<const F*>(static_cast<const char*>(base) + elem_off * Elem<K>::bytes);
+}
+
+template <int K>
+__device__ __forceinline__ typename Elem<K>::frag zero_frag() {
+    typename Elem<K>::frag f;
+    for (int i = 0; i < 8; ++i) f[i] = 0;
+    return f;
+}
+
+// ------------------------------------------------------------------------------------------------
+// 32x32 output tile, K = 16 per step. Operand convention (both operands): lane l supplies row
+// (A) / column (B) l % 32 and the 8 K-slots 8*(l/32) .. 8*(l/32)+7. The fp16/bf16 forms are one
+// v_mfma_f32_32x32x16_{f16,bf16}; the fp32 form issues eight v_mfma_f32_32x32x2_f32, step j
+// contracting slot j of both lane halves (K index j and 8+j), which covers the same 16 K values.
+// Accumulator: register r of lane l holds row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
+// ------------------------------------------------------------------------------------------------
+template <int K>
+__device__ __forceinline__ f32x16 mma32(const typename Elem<K>::frag& a,
+                                        const typename Elem<K>::frag& b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mma32<kF16>(const f16x8& a, const f16x8& b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mma32<kBF16>(const bf16x8& a, const bf16x8& b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mma32<kF32>(const f32x8& a, const f32x8& b, f32x16 c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Wave-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// cos and sin of 2*pi*x for x in [0, 1) (hardware v_cos_f32 / v_sin_f32 take revolutions).
+__device__ __forceinline__ void sincos_rev(float x, float* c, float* s) {
+    *c = __builtin_amdgcn_cosf(x);
+    *s = __builtin_amdgcn_sinf(x);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Parameter blocks (passed by value; each stays well under the 4 KB kernel-argument limit).
+// ------------------------------------------------------------------------------------------------
+constexpr int kMaxHeads = 32;
+constexpr int kTile = 64;              // tokens per tile == tokens per cache block
+constexpr int kKeyWaveGroups = 4;      // waves per 32-token sub-tile in the key phase
+
+struct LatentDecodeParams {
+    const void* zk;        // [B][cap][Rk]
+    const void* zv;        // [B][cap/64][rv][64]
+    const void* bkt;       // packed key-factor fragments (see pack kernel)
+    const float* q;        // [B][H][D]
+    float* ws_ml;          // [B][S][H][2]  (running max in log2 units, sum)
+    float* ws_acc;         // [B][S][H][rv]
+    int B, H, D, Rk, rv, cap, seq_len, S, tiles_per_split;
+    float q_scale;         // softmax scale * log2(e)
+    int16_t koff[kMaxHeads + 1];
+    int16_t rank[kMaxHeads];
+    int8_t sched[kKeyWaveGroups][kMaxHeads];   // heads of each key-wave group
+    int8_t sched_n[kKeyWaveGroups];
+    double rope_rev[64];   // theta_i / (2 pi): RoPE frequency in revolutions per position
+};
+
+struct MergeParams {
+    const float* ws_ml;    // [B][S][H][2]
+    const float* ws_acc;   // [B][S][H][W]
+    float* ws_a;           // [B][H][W] merged, normalised
+    int B, H, S, W, active_splits;
+};
+
+struct ProjectParams {
+    const float* ws_a;     // [B][H][rv]
+    const void* bv;        // [rv][H*D]
+    float* out;            // [B][H][D]
+    int B, H, D, rv;
+};
+
+struct DenseDecodeParams {
+    const void* k;         // [B][cap][H*D]
+    const void* v;         // [B][cap][H*D]
+    const float* q;        // [B][H][D]
+    float* ws_ml;          // [B][S][H][2]
+    float* ws_acc;         // [B][S][H][D]
+    int B, H, D, cap, seq_len, S, tiles_per_split;
+    float q_scale;
+    double rope_rev[64];
+};
+
+// Copy one contiguous byte range per sequence: dst[b*dst_seq_stride + dst_off + i] =
+// src[b*src_seq_stride + src_off + i] for i < bytes (a multiple of 16, 16-byte aligned).
+struct RowCopyParams {
+    const char* src;
+    char* dst;
+    long long src_seq_stride, dst_seq_stride;
+    long long src_off, dst_off;
+    long long bytes;
+};
+
+// Value-latent row <-> block transpose. to_blocks = 1: rows[b][t - row0][c] ->
+// blocks[b][t/64][c][t%64] for absolute tokens t in [t_begin, t_end); to_blocks = 0: reverse.
+struct BlockXposeParams {
+    const void* src;
+    void* dst;
+    int B, C, cap;
+    long long t_begin, t_end;
+    long long row0;             // absolute token of row 0 of the row-major side
+    long long rows_per_seq;     // rows per sequence on the row-major side
+    int blk_first;              // first 64-token block touched
+    int to_blocks;
+};
+
+}  // namespace starkv

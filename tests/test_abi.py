@@ -1,0 +1,143 @@
+"""The C ABI on the CPU: the library loads, exports every function include/starkv.h declares, and
+rejects invalid arguments with the documented status before anything is enqueued (so none of
+these calls reaches the GPU; device pointers below are never dereferenced)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import rank_kv_cache_amd as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "starkv.h")
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation rejects first
+MISAL = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(starkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = sk.lib()
+    decl = declared_functions()
+    assert set(decl) == set(sk.EXPORTED_SYMBOLS)
+    for name in decl:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sk.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (starkv_[a-z_]+)$", out, flags=re.M))
+    assert set(decl) <= exported
+    assert sk.starkv_version() == 100
+    for code in range(10):
+        assert sk.starkv_status_string(code)
+
+
+def _latent(**kw):
+    base = dict(num_heads=4, head_dim=128, key_ranks=(16, 32, 48, 64), value_rank=256,
+                cache_dtype=sk.F16)
+    base.update(kw)
+    return sk.Layer(**base)
+
+
+def _cache(**kw):
+    base = dict(batch=2, capacity=256, zk=FAKE, zv=FAKE)
+    base.update(kw)
+    return sk.Cache(**base)
+
+
+def st_decode(layer, cache, seq_len=100, q=FAKE, bk=FAKE, bv=FAKE, out=FAKE, ns=0, ws=FAKE,
+              nws=1 << 40):
+    return sk.starkv_decode_attn(layer, cache, seq_len, q, bk, bv, out, ns, ws, nws, check=False)
+
+
+def test_decode_validation():
+    E = {n: i for i, n in enumerate(["OK", "NULL", "SHAPE", "RANK", "DTYPE", "MISAL", "CAP", "WS",
+                                     "UNSUP", "DEV"])}
+    L, Cc = _latent(), _cache()
+    assert st_decode(None, Cc) == E["NULL"]
+    assert st_decode(L, None) == E["NULL"]
+    assert st_decode(_latent(num_heads=0), Cc) == E["SHAPE"]
+    assert st_decode(_latent(head_dim=63), Cc) == E["SHAPE"]
+    assert st_decode(_latent(rope_base=1.0), Cc) == E["SHAPE"]
+    assert st_decode(_latent(rope_base=float("nan")), Cc) == E["SHAPE"]
+    assert st_decode(_latent(cache_dtype=7), Cc) == E["DTYPE"]
+    assert st_decode(_latent(factor_dtype=sk.F32), Cc) == E["DTYPE"]
+    assert st_decode(_latent(cache_dtype=sk.Q43, factor_dtype=sk.BF16), Cc) == E["DTYPE"]
+    assert st_decode(_latent(key_ranks=(16, 32, 40, 64)), Cc) == E["RANK"]
+    assert st_decode(_latent(key_ranks=(16, 32, 48, 144)), Cc) == E["RANK"]
+    assert st_decode(_latent(key_ranks=(0, 32, 48, 64)), Cc) == E["RANK"]
+    assert st_decode(_latent(value_rank=100), Cc) == E["RANK"]
+    assert st_decode(_latent(value_rank=4096), Cc) == E["RANK"]
+    assert st_decode(_latent(value_rank=1536), Cc) == E["UNSUP"]
+    assert st_decode(_latent(num_heads=40, key_ranks=(16,) * 40), Cc) == E["UNSUP"]
+    assert st_decode(_latent(head_dim=96), Cc) == E["UNSUP"]
+    assert st_decode(L, _cache(capacity=100)) == E["CAP"]
+    assert st_decode(L, _cache(capacity=0)) == E["CAP"]
+    assert st_decode(L, _cache(batch=-1)) == E["SHAPE"]
+    assert st_decode(L, _cache(zk=None)) == E["NULL"]
+    assert st_decode(L, _cache(zv=MISAL)) == E["MISAL"]
+    assert st_decode(L, Cc, seq_len=0) == E["SHAPE"]
+    assert st_decode(L, Cc, seq_len=257) == E["CAP"]
+    assert st_decode(L, Cc, q=None) == E["NULL"]
+    assert st_decode(L, Cc, bk=None) == E["NULL"]
+    assert st_decode(L, Cc, out=MISAL) == E["MISAL"]
+    assert st_decode(L, Cc, ns=-1) == E["SHAPE"]
+    assert st_decode(L, Cc, ws=None) == E["WS"]
+    need = sk.starkv_decode_workspace_bytes(L, 2, 100, 0)
+    assert need > 0
+    assert st_decode(L, Cc, nws=need - 1) == E["WS"]
+    assert st_decode(L, Cc, ws=MISAL) == E["MISAL"]
+    q43 = _latent(cache_dtype=sk.Q43)
+    assert st_decode(q43, Cc) == E["NULL"]                 # meta / tail buffers missing
+    assert st_decode(_latent(cache_dtype=sk.Q43, q_group=32), Cc) == E["UNSUP"]
+    # empty batch: nothing to do, OK without touching anything
+    assert st_decode(L, _cache(batch=0, zk=None, zv=None), q=None, out=None, ws=None) == E["OK"]
+    dense = sk.Layer(num_heads=4, head_dim=128, dense=True, cache_dtype=sk.F16)
+    assert st_decode(dense, Cc, bk=None, bv=None, ws=None) == E["WS"]
+    assert st_decode(sk.Layer(num_heads=4, head_dim=128, dense=True, cache_dtype=sk.Q43), Cc) == E["DTYPE"]
+
+
+def test_append_and_dequant_validation():
+    L, Cc = _latent(), _cache()
+    ap = lambda *a, **k: sk.starkv_append_latents(*a, check=False, **k)
+    assert ap(L, Cc, -1, 4, FAKE, FAKE) == 2
+    assert ap(L, Cc, 0, -4, FAKE, FAKE) == 2
+    assert ap(L, Cc, 250, 7, FAKE, FAKE) == 6
+    assert ap(L, Cc, 0, 4, None, FAKE) == 1
+    assert ap(L, Cc, 0, 4, FAKE, MISAL) == 5
+    assert ap(L, Cc, 10, 0, None, None) == 0               # nothing to append
+    assert ap(L, _cache(batch=0, zk=None, zv=None), 0, 4, None, None) == 0
+    dq = lambda *a: sk.starkv_dequant(*a, check=False)
+    assert dq(L, Cc, 100, -1, 5, FAKE, FAKE) == 2
+    assert dq(L, Cc, 100, 6, 5, FAKE, FAKE) == 2
+    assert dq(L, Cc, 100, 0, 101, FAKE, FAKE) == 6
+    assert dq(L, Cc, 300, 0, 10, FAKE, FAKE) == 6
+    assert dq(L, Cc, 100, 0, 10, MISAL, None) == 5
+    assert dq(L, Cc, 100, 7, 7, FAKE, FAKE) == 0           # empty range
+
+
+def test_cache_bytes():
+    L = _latent()
+    s = sk.starkv_cache_bytes(L, 3, 128)
+    assert s[0] == 3 * 128 * 160 * 2 and s[1] == 3 * 128 * 256 * 2 and s[2:] == [0, 0, 0, 0]
+    Lf = _latent(cache_dtype=sk.F32, factor_dtype=sk.F32)
+    assert sk.starkv_cache_bytes(Lf, 1, 64)[0] == 64 * 160 * 4
+    D = sk.Layer(num_heads=32, head_dim=128, dense=True, cache_dtype=sk.F16)
+    s = sk.starkv_cache_bytes(D, 2, 64)
+    assert s[0] == s[1] == 2 * 64 * 4096 * 2
+    with pytest.raises(sk.StarkvError):
+        sk.starkv_cache_bytes(L, 1, 100)
+
+
+def test_workspace_sizes_and_planner():
+    L = _latent()
+    # default: splits = ceil(256 / B) capped by the tile count
+    w16 = sk.starkv_decode_workspace_bytes(L, 16, 32768, 0)
+    w1 = sk.starkv_decode_workspace_bytes(L, 16, 32768, 1)
+    assert w16 > w1 > 0
+    assert sk.starkv_decode_workspace_bytes(L, 16, 0, 0) == 0
+    assert sk.starkv_decode_workspace_bytes(None, 16, 10, 0) == 0
