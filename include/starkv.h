@@ -146,6 +146,19 @@ starkv_status starkv_decode_attn(const starkv_layer *layer, const starkv_cache *
                                  size_t workspace_bytes, void *stream);
 
 /*
+ * starkv_decode_attn with kernel timing for profiling tools: event_begin and event_end
+ * (hipEvent_t passed as void*, created by the caller, may be NULL) are recorded on `stream`
+ * immediately before and after the launch of the main per-split kernel, so their elapsed time is
+ * that kernel's duration. Everything else is identical to starkv_decode_attn (same validation,
+ * same kernels, same results). Extra error: STARKV_ERR_DEVICE if recording an event fails.
+ */
+starkv_status starkv_decode_attn_timed(const starkv_layer *layer, const starkv_cache *cache,
+                                       int64_t seq_len, const float *q, const void *bk,
+                                       const void *bv, float *out, int32_t num_splits,
+                                       void *workspace, size_t workspace_bytes, void *stream,
+                                       void *event_begin, void *event_end);
+
+/*
  * Read cached tokens [t0, t1) back in token-major order: zk_out [B][t1-t0][R_k] (dense: H*d) and
  * zv_out [B][t1-t0][r_v] (dense: H*d). Element type: fp16 for Q43 (codes of complete groups are
  * dequantised as binary16(fmaf(code, scale, zero)); rows of the unfinished group come from the

@@ -19,7 +19,7 @@ __all__ = [
     "F32", "F16", "BF16", "Q43", "StarkvError", "Layer", "Cache", "lib", "library_path",
     "starkv_version", "starkv_status_string", "starkv_cache_bytes", "starkv_append_latents",
     "starkv_decode_workspace_bytes", "starkv_decode_attn", "starkv_dequant",
-    "starkv_hadamard_rotate", "EXPORTED_SYMBOLS",
+    "starkv_hadamard_rotate", "starkv_decode_attn_timed", "EXPORTED_SYMBOLS",
 ]
 
 F32, F16, BF16, Q43 = 0, 1, 2, 3
@@ -27,7 +27,7 @@ _STATUS = ["OK", "ERR_NULL", "ERR_SHAPE", "ERR_RANK_ALIGN", "ERR_DTYPE", "ERR_MI
            "ERR_CAPACITY", "ERR_WORKSPACE", "ERR_UNSUPPORTED", "ERR_DEVICE"]
 
 EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decode_workspace_bytes",
-                    "starkv_decode_attn", "starkv_dequant", "starkv_hadamard_rotate",
+                    "starkv_decode_attn", "starkv_decode_attn_timed", "starkv_dequant", "starkv_hadamard_rotate",
                     "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,8 @@ def lib():
         L.starkv_decode_workspace_bytes.argtypes = [LP, i32, i64, i32]
         L.starkv_decode_attn.restype = C.c_int
         L.starkv_decode_attn.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.starkv_decode_attn_timed.restype = C.c_int
+        L.starkv_decode_attn_timed.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp, vp, vp]
         L.starkv_dequant.restype = C.c_int
         L.starkv_dequant.argtypes = [LP, CP, i64, i64, i64, vp, vp, vp]
         L.starkv_hadamard_rotate.restype = C.c_int
@@ -206,6 +208,17 @@ def starkv_decode_attn(layer, cache, seq_len, q, bk, bv, out, num_splits=0, work
                                   int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "starkv_decode_attn")
+    return st
+
+
+def starkv_decode_attn_timed(layer, cache, seq_len, q, bk, bv, out, num_splits=0, workspace=None,
+                             workspace_bytes=0, stream=None, event_begin=None, event_end=None,
+                             check=True):
+    st = lib().starkv_decode_attn_timed(_layer_ptr(layer), _cache_ptr(cache), seq_len, _ptr(q),
+                                        _ptr(bk), _ptr(bv), _ptr(out), num_splits, _ptr(workspace),
+                                        int(workspace_bytes), _stream(stream), event_begin, event_end)
+    if check:
+        _check(st, "starkv_decode_attn_timed")
     return st
 
 

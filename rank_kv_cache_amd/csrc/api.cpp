@@ -286,10 +286,10 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
     return dev(launch_block_transpose(x, es, st));
 }
 
-starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* cache,
+static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* cache,
                                  int64_t seq_len, const float* q, const void* bk, const void* bv,
                                  float* out, int32_t num_splits, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 size_t workspace_bytes, void* stream, void* ev0, void* ev1) {
     LayerInfo li;
     starkv_status s = check_layer(layer, &li);
     if (s != STARKV_OK) return s;
@@ -327,7 +327,9 @@ starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* 
         p.tiles_per_split = w.tps;
         p.q_scale = q_scale_of(layer, li.D);
         fill_rope(layer->rope_base, li.D, p.rope_rev);
+        if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
         if ((s = dev(launch_dense_split(p, elem_kind(li.cache_dt), st))) != STARKV_OK) return s;
+        if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
         MergeParams m;
         m.ws_ml = p.ws_ml;
         m.ws_acc = p.ws_acc;
@@ -367,7 +369,9 @@ starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* 
     plan_heads(li, &p);
     fill_rope(layer->rope_base, li.D, p.rope_rev);
     const int ntv = (li.rv + 255) / 256;
+    if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
     if ((s = dev(launch_latent_split(p, ek, ntv, st))) != STARKV_OK) return s;
+    if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
     MergeParams m;
     m.ws_ml = p.ws_ml;
     m.ws_acc = p.ws_acc;
@@ -387,6 +391,23 @@ starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* 
     pr.D = li.D;
     pr.rv = li.rv;
     return dev(launch_project(pr, ek, st));
+}
+
+starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* cache,
+                                 int64_t seq_len, const float* q, const void* bk, const void* bv,
+                                 float* out, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return decode_impl(layer, cache, seq_len, q, bk, bv, out, num_splits, workspace,
+                       workspace_bytes, stream, nullptr, nullptr);
+}
+
+starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_cache* cache,
+                                       int64_t seq_len, const float* q, const void* bk,
+                                       const void* bv, float* out, int32_t num_splits,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       void* event_begin, void* event_end) {
+    return decode_impl(layer, cache, seq_len, q, bk, bv, out, num_splits, workspace,
+                       workspace_bytes, stream, event_begin, event_end);
 }
 
 starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cache,
