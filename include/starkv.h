@@ -23,11 +23,15 @@
  *  - Calls that write the same buffers must not overlap in time (use one stream per cache).
  *
  * Cache layouts (element type = cache_dtype for F32/F16/BF16; fp16 tails for Q43):
- *  - latent layer, F32/F16/BF16:
- *      zk: [B][capacity][R_k], R_k = sum_h r_k[h]; per token the heads' latents are concatenated
- *          in head order (token-major).
- *      zv: [B][capacity/64][r_v][64]: channel-major inside each 64-token block, so the 64 values
- *          of one channel in one block are contiguous.
+ *  - latent layer, F32/F16/BF16: channel c of a latent (key: R_k = sum_h r_k[h] channels, the
+ *      heads' latents concatenated in head order; value: r_v channels) at cache token t lives in
+ *      64-token block t/64 and 16-channel group c/16, 1024 elements per (block, group):
+ *      zk: [B][capacity/64][R_k/16][64][16]     element (t%64, c%16): tokens rows of 16 channels
+ *      zv: [B][capacity/64][r_v/16][4][16][16]  element ((t%64)/16, c%16, t%16): runs of 16
+ *          consecutive tokens per channel.
+ *      Each lane load of 8 consecutive elements is one MFMA operand fragment. Use
+ *      starkv_append_latents / starkv_dequant to write / read rows; the layout is an internal
+ *      detail of this version.
  *      zk_meta, zv_meta, zk_tail, zv_tail: unused (may be NULL).
  *  - dense (exempt) layer, F32/F16/BF16: zk = K, zv = V, both [B][capacity][H*d] token-major;
  *      keys are stored pre-RoPE.
@@ -132,7 +136,9 @@ size_t starkv_decode_workspace_bytes(const starkv_layer *layer, int32_t batch, i
  *   bk:  [R_k][d] factor_dtype (heads' factors stacked in head order); NULL for dense layers.
  *   bv:  [r_v][H*d] factor_dtype; NULL for dense layers.
  *   out: [B][H][d] fp32, per-head attention output before the output projection.
- *   num_splits: 0 = library choice; otherwise the number of sequence splits (>= 1).
+ *   num_splits: 0 = library choice; otherwise the requested number of sequence splits whose
+ *   partial results are merged (raised when needed so that no split exceeds 256 blocks of 64
+ *   tokens, lowered to the number of blocks).
  *   workspace: device scratch of at least starkv_decode_workspace_bytes(...) bytes; contents on
  *   entry are ignored and clobbered.
  * For Q43 caches seq_len must equal the number of tokens appended so far (the unfinished group is
@@ -146,17 +152,19 @@ starkv_status starkv_decode_attn(const starkv_layer *layer, const starkv_cache *
                                  size_t workspace_bytes, void *stream);
 
 /*
- * starkv_decode_attn with kernel timing for profiling tools: event_begin and event_end
- * (hipEvent_t passed as void*, created by the caller, may be NULL) are recorded on `stream`
- * immediately before and after the launch of the main per-split kernel, so their elapsed time is
- * that kernel's duration. Everything else is identical to starkv_decode_attn (same validation,
- * same kernels, same results). Extra error: STARKV_ERR_DEVICE if recording an event fails.
+ * starkv_decode_attn with kernel timing for profiling tools: event_begin, event_mid and event_end
+ * (hipEvent_t passed as void*, created by the caller, each may be NULL) are recorded on `stream`
+ * immediately before the kernel that streams the key latents, between it and the kernel that
+ * streams the value latents, and after that one (dense layers: before and after the single
+ * attention kernel, event_mid right after it). Everything else is identical to starkv_decode_attn
+ * (same validation, same kernels, same results). Extra error: STARKV_ERR_DEVICE if recording an
+ * event fails.
  */
 starkv_status starkv_decode_attn_timed(const starkv_layer *layer, const starkv_cache *cache,
                                        int64_t seq_len, const float *q, const void *bk,
                                        const void *bv, float *out, int32_t num_splits,
                                        void *workspace, size_t workspace_bytes, void *stream,
-                                       void *event_begin, void *event_end);
+                                       void *event_begin, void *event_mid, void *event_end);
 
 /*
  * Read cached tokens [t0, t1) back in token-major order: zk_out [B][t1-t0][R_k] (dense: H*d) and

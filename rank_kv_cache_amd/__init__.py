@@ -82,7 +82,7 @@ def lib():
         L.starkv_decode_attn.restype = C.c_int
         L.starkv_decode_attn.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp]
         L.starkv_decode_attn_timed.restype = C.c_int
-        L.starkv_decode_attn_timed.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp, vp, vp]
+        L.starkv_decode_attn_timed.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp, vp, vp, vp]
         L.starkv_dequant.restype = C.c_int
         L.starkv_dequant.argtypes = [LP, CP, i64, i64, i64, vp, vp, vp]
         L.starkv_hadamard_rotate.restype = C.c_int
@@ -212,11 +212,12 @@ def starkv_decode_attn(layer, cache, seq_len, q, bk, bv, out, num_splits=0, work
 
 
 def starkv_decode_attn_timed(layer, cache, seq_len, q, bk, bv, out, num_splits=0, workspace=None,
-                             workspace_bytes=0, stream=None, event_begin=None, event_end=None,
-                             check=True):
+                             workspace_bytes=0, stream=None, event_begin=None, event_mid=None,
+                             event_end=None, check=True):
     st = lib().starkv_decode_attn_timed(_layer_ptr(layer), _cache_ptr(cache), seq_len, _ptr(q),
                                         _ptr(bk), _ptr(bv), _ptr(out), num_splits, _ptr(workspace),
-                                        int(workspace_bytes), _stream(stream), event_begin, event_end)
+                                        int(workspace_bytes), _stream(stream), event_begin,
+                                        event_mid, event_end)
     if check:
         _check(st, "starkv_decode_attn_timed")
     return st

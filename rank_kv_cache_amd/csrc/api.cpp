@@ -14,7 +14,10 @@
 #include "common.hpp"
 
 namespace starkv {
-hipError_t launch_latent_split(const LatentDecodeParams& p, int elem, int ntv, hipStream_t st);
+hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
+                                hipStream_t st);
+hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, hipStream_t st);
+int value_chunk_channels();
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
@@ -23,15 +26,18 @@ hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t 
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
 hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st);
+hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st);
 }  // namespace starkv
 
 using namespace starkv;
 
 namespace {
 
-constexpr int kTargetWorkgroups = 256;   // MI355X compute units: one decode workgroup per CU
+constexpr int kTargetWorkgroups = 256;   // MI355X compute units: one score workgroup per CU
+constexpr int kValueTargetWorkgroups = 768;   // three 4-wave value workgroups per CU
 constexpr int kMaxSplits = 256;
 constexpr size_t kAlign = 256;
+constexpr int64_t kSmallAppend = 16;     // appends of up to this many tokens use one fused launch
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -85,7 +91,6 @@ starkv_status check_layer(const starkv_layer* L, LayerInfo* out) {
     li.Rk = off;
     li.rv = L->value_rank;
     if (li.rv < 16 || (li.rv % 16) || li.rv > 2048) return STARKV_ERR_RANK_ALIGN;
-    if (li.rv > 1280) return STARKV_ERR_UNSUPPORTED;
     if (li.cache_dt == STARKV_Q43) {
         li.q43 = true;
         if (L->q_group != 64) return STARKV_ERR_UNSUPPORTED;
@@ -112,22 +117,70 @@ starkv_status check_cache(const starkv_cache* c, const LayerInfo& li) {
     return STARKV_OK;
 }
 
-// Key-phase schedule: the heads are dealt to kKeyWaveGroups waves so that their rank sums
-// (MFMA work) are balanced: longest-processing-time-first greedy.
-void plan_heads(const LayerInfo& li, LatentDecodeParams* p) {
+// Score-kernel head groups: the heads are dealt to G groups with balanced rank sums
+// (longest-processing-time-first greedy); G is the smallest count whose largest group's factor
+// fragments fit the LDS budget of one workgroup.
+struct ScorePlan {
+    int G = 1, splits = 1, bpw = 1, maxks = 1;
+    int8_t order[kMaxHeads] = {0};
+    int8_t gstart[kMaxGroups + 1] = {0};
+};
+
+bool plan_groups(const LayerInfo& li, int G, ScorePlan* sp) {
     std::vector<int> order(li.H);
     for (int h = 0; h < li.H; ++h) order[h] = h;
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return li.rank[a] > li.rank[b]; });
-    int load[kKeyWaveGroups] = {0};
-    for (int g = 0; g < kKeyWaveGroups; ++g) p->sched_n[g] = 0;
+    std::vector<std::vector<int>> groups(G);
+    std::vector<int> load(G, 0);
     for (int h : order) {
         int g = 0;
-        for (int k = 1; k < kKeyWaveGroups; ++k)
+        for (int k = 1; k < G; ++k)
             if (load[k] < load[g]) g = k;
-        p->sched[g][p->sched_n[g]++] = static_cast<int8_t>(h);
+        groups[g].push_back(h);
         load[g] += li.rank[h];
     }
+    const int esz = elem_bytes(li.factor_dt);
+    int pos = 0;
+    for (int g = 0; g < G; ++g) {
+        if (static_cast<size_t>(load[g]) * li.D * esz > static_cast<size_t>(kFragLdsBytes)) return false;
+        sp->gstart[g] = static_cast<int8_t>(pos);
+        for (int h : groups[g]) sp->order[pos++] = static_cast<int8_t>(h);
+    }
+    sp->gstart[G] = static_cast<int8_t>(pos);
+    sp->G = G;
+    return true;
+}
+
+ScorePlan plan_scores(const LayerInfo& li, int B, int nblk) {
+    ScorePlan sp;
+    int G = 1;
+    while (G <= std::min(kMaxGroups, li.H) && !plan_groups(li, G, &sp)) ++G;
+    int maxr = 0;
+    for (int h = 0; h < li.H; ++h) maxr = std::max(maxr, static_cast<int>(li.rank[h]));
+    sp.maxks = maxr / 16;
+    const int per = std::max(1, B) * sp.G;
+    int S = (kTargetWorkgroups + per - 1) / per;
+    S = std::max(1, std::min(S, nblk));
+    sp.bpw = (nblk + S - 1) / S;
+    sp.splits = (nblk + sp.bpw - 1) / sp.bpw;
+    return sp;
+}
+
+struct ValuePlan {
+    int chunks = 1, splits = 1, bps = 1;
+};
+
+ValuePlan plan_values(const LayerInfo& li, int B, int nblk, int requested) {
+    ValuePlan vp;
+    vp.chunks = (li.rv + value_chunk_channels() - 1) / value_chunk_channels();
+    const int per = std::max(1, B) * vp.chunks;
+    int S = requested > 0 ? requested : (kValueTargetWorkgroups + per - 1) / per;
+    S = std::max({1, std::min(S, nblk), (nblk + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit});
+    S = std::min(S, kMaxSplits);
+    vp.bps = (nblk + S - 1) / S;
+    vp.splits = (nblk + vp.bps - 1) / vp.bps;
+    return vp;
 }
 
 int plan_splits(int B, int64_t seq_len, int requested) {
@@ -138,29 +191,45 @@ int plan_splits(int B, int64_t seq_len, int requested) {
 }
 
 struct WorkspaceLayout {
-    size_t bkt = 0, ml = 0, acc = 0, a = 0, total = 0;
-    int S = 1, tps = 1;
+    size_t bkt = 0, P = 0, stats = 0, ml = 0, acc = 0, a = 0, total = 0;
+    int S = 1, tps = 1, nblk = 1;
+    ScorePlan sp;
+    ValuePlan vp;
 };
 
 WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, int requested) {
     WorkspaceLayout w;
-    w.S = plan_splits(B, seq_len, requested);
-    const int ntiles = static_cast<int>((seq_len + kTile - 1) / kTile);
-    w.tps = (ntiles + w.S - 1) / w.S;
-    const int width = li.dense ? li.D : li.rv;
+    const int nblk = static_cast<int>((seq_len + kTile - 1) / kTile);
+    w.nblk = nblk;
     size_t off = 0;
-    if (!li.dense) {
-        w.bkt = off;
-        off += align_up(static_cast<size_t>(li.Rk) * li.D * elem_bytes(li.factor_dt));
+    if (li.dense) {
+        w.S = plan_splits(B, seq_len, requested);
+        w.tps = (nblk + w.S - 1) / w.S;
+        w.ml = off;
+        off += align_up(static_cast<size_t>(B) * w.S * li.H * 2 * sizeof(float));
+        w.acc = off;
+        off += align_up(static_cast<size_t>(B) * w.S * li.H * li.D * sizeof(float));
+        w.total = off;
+        return w;
     }
+    w.sp = plan_scores(li, B, nblk);
+    w.vp = plan_values(li, B, nblk, requested);
+    w.S = w.vp.splits;
+    w.tps = w.vp.bps;
+    const size_t Tp = static_cast<size_t>(nblk) * kTile;
+    const size_t pesz = li.cache_dt == STARKV_F32 ? 4 : 2;
+    w.bkt = off;
+    off += align_up(static_cast<size_t>(li.Rk) * li.D * elem_bytes(li.factor_dt));
+    w.P = off;
+    off += align_up(static_cast<size_t>(B) * li.H * Tp * pesz);
+    w.stats = off;
+    off += align_up(static_cast<size_t>(B) * li.H * nblk * 2 * sizeof(float));
     w.ml = off;
     off += align_up(static_cast<size_t>(B) * w.S * li.H * 2 * sizeof(float));
     w.acc = off;
-    off += align_up(static_cast<size_t>(B) * w.S * li.H * width * sizeof(float));
-    if (!li.dense) {
-        w.a = off;
-        off += align_up(static_cast<size_t>(B) * li.H * li.rv * sizeof(float));
-    }
+    off += align_up(static_cast<size_t>(B) * w.S * li.H * li.rv * sizeof(float));
+    w.a = off;
+    off += align_up(static_cast<size_t>(B) * li.H * li.rv * sizeof(float));
     w.total = off;
     return w;
 }
@@ -245,8 +314,8 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int B = cache->batch;
     const int es = elem_bytes(li.cache_dt);
-    const long long cap = cache->capacity;
     if (li.dense) {
+        const long long cap = cache->capacity;
         const long long row = static_cast<long long>(li.H) * li.D * es;
         for (int which = 0; which < 2; ++which) {
             RowCopyParams p;
@@ -261,41 +330,52 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
         }
         return STARKV_OK;
     }
-    const long long krow = static_cast<long long>(li.Rk) * es;
-    RowCopyParams p;
-    p.src = static_cast<const char*>(zk_new);
-    p.dst = static_cast<char*>(cache->zk);
-    p.src_seq_stride = n_new * krow;
-    p.dst_seq_stride = cap * krow;
-    p.src_off = 0;
-    p.dst_off = pos * krow;
-    p.bytes = n_new * krow;
-    if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
-    BlockXposeParams x;
-    x.src = zv_new;
-    x.dst = cache->zv;
-    x.B = B;
-    x.C = li.rv;
-    x.cap = cache->capacity;
-    x.t_begin = pos;
-    x.t_end = pos + n_new;
-    x.row0 = pos;
-    x.rows_per_seq = n_new;
-    x.blk_first = static_cast<int>(pos / kTile);
-    x.to_blocks = 1;
-    return dev(launch_block_transpose(x, es, st));
+    if (n_new <= kSmallAppend) {
+        AppendSmallParams a;
+        a.zk_src = zk_new;
+        a.zv_src = zv_new;
+        a.zk = cache->zk;
+        a.zv = cache->zv;
+        a.B = B;
+        a.Rk = li.Rk;
+        a.rv = li.rv;
+        a.nblk_cap = cache->capacity / kTile;
+        a.pos = pos;
+        a.n = n_new;
+        return dev(launch_append_small(a, es, st));
+    }
+    for (int which = 0; which < 2; ++which) {
+        BlockXposeParams x;
+        x.src = which ? zv_new : zk_new;
+        x.dst = which ? cache->zv : cache->zk;
+        x.B = B;
+        x.C = which ? li.rv : li.Rk;
+        x.nblk_cap = cache->capacity / kTile;
+        x.t_begin = pos;
+        x.t_end = pos + n_new;
+        x.row0 = pos;
+        x.rows_per_seq = n_new;
+        x.blk_first = static_cast<int>(pos / kTile);
+        x.to_blocks = 1;
+        x.layout = which;
+        if ((s = dev(launch_block_transpose(x, es, st))) != STARKV_OK) return s;
+    }
+    return STARKV_OK;
 }
 
 static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* cache,
                                  int64_t seq_len, const float* q, const void* bk, const void* bv,
                                  float* out, int32_t num_splits, void* workspace,
-                                 size_t workspace_bytes, void* stream, void* ev0, void* ev1) {
+                                 size_t workspace_bytes, void* stream, void* ev0, void* evm,
+                                 void* ev1) {
     LayerInfo li;
     starkv_status s = check_layer(layer, &li);
     if (s != STARKV_OK) return s;
     if ((s = check_cache(cache, li)) != STARKV_OK) return s;
     if (seq_len < 1 || num_splits < 0) return STARKV_ERR_SHAPE;
     if (seq_len > cache->capacity) return STARKV_ERR_CAPACITY;
+    if (seq_len > static_cast<int64_t>(kMaxSplits) * kMaxBlocksPerSplit * kTile)
+        return STARKV_ERR_UNSUPPORTED;
     if (cache->batch == 0) return STARKV_OK;
     if (!q || !out) return STARKV_ERR_NULL;
     if (!li.dense && (!bk || !bv)) return STARKV_ERR_NULL;
@@ -308,10 +388,8 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     if (li.q43) return STARKV_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
-    const int ntiles = static_cast<int>((seq_len + kTile - 1) / kTile);
-    const int active = (ntiles + w.tps - 1) / w.tps;
-
     if (li.dense) {
+        const int active = (w.nblk + w.tps - 1) / w.tps;
         DenseDecodeParams p;
         p.k = cache->zk;
         p.v = cache->zv;
@@ -329,6 +407,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
         fill_rope(layer->rope_base, li.D, p.rope_rev);
         if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
         if ((s = dev(launch_dense_split(p, elem_kind(li.cache_dt), st))) != STARKV_OK) return s;
+        if (evm && (s = dev(hipEventRecord(static_cast<hipEvent_t>(evm), st))) != STARKV_OK) return s;
         if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
         MergeParams m;
         m.ws_ml = p.ws_ml;
@@ -346,41 +425,58 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     void* bkt = ws + w.bkt;
     if ((s = dev(launch_pack_keys(bk, bkt, li.D, li.H, li.koff, li.rank, ek, st))) != STARKV_OK)
         return s;
-    LatentDecodeParams p;
-    std::memset(&p, 0, sizeof(p));
-    p.zk = cache->zk;
-    p.zv = cache->zv;
-    p.bkt = bkt;
-    p.q = q;
-    p.ws_ml = reinterpret_cast<float*>(ws + w.ml);
-    p.ws_acc = reinterpret_cast<float*>(ws + w.acc);
-    p.B = B;
-    p.H = li.H;
-    p.D = li.D;
-    p.Rk = li.Rk;
-    p.rv = li.rv;
-    p.cap = cache->capacity;
-    p.seq_len = static_cast<int>(seq_len);
-    p.S = w.S;
-    p.tiles_per_split = w.tps;
-    p.q_scale = q_scale_of(layer, li.D);
-    for (int h = 0; h <= li.H; ++h) p.koff[h] = li.koff[h];
-    for (int h = 0; h < li.H; ++h) p.rank[h] = li.rank[h];
-    plan_heads(li, &p);
-    fill_rope(layer->rope_base, li.D, p.rope_rev);
-    const int ntv = (li.rv + 255) / 256;
+    ScoreParams sp;
+    std::memset(&sp, 0, sizeof(sp));
+    sp.zk = cache->zk;
+    sp.bkt = bkt;
+    sp.q = q;
+    sp.P = ws + w.P;
+    sp.stats = reinterpret_cast<float*>(ws + w.stats);
+    sp.B = B;
+    sp.H = li.H;
+    sp.D = li.D;
+    sp.Rk = li.Rk;
+    sp.nblk_cap = cache->capacity / kTile;
+    sp.seq_len = static_cast<int>(seq_len);
+    sp.nblk = w.nblk;
+    sp.Tp = w.nblk * kTile;
+    sp.blocks_per_wg = w.sp.bpw;
+    sp.q_scale = q_scale_of(layer, li.D);
+    for (int h = 0; h < li.H; ++h) sp.order[h] = w.sp.order[h];
+    for (int g = 0; g <= w.sp.G; ++g) sp.gstart[g] = w.sp.gstart[g];
+    for (int h = 0; h <= li.H; ++h) sp.koff[h] = li.koff[h];
+    for (int h = 0; h < li.H; ++h) sp.rank[h] = li.rank[h];
+    fill_rope(layer->rope_base, li.D, sp.rope_rev);
     if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
-    if ((s = dev(launch_latent_split(p, ek, ntv, st))) != STARKV_OK) return s;
+    if ((s = dev(launch_latent_scores(sp, ek, w.sp.G, w.sp.splits, w.sp.maxks, st))) != STARKV_OK)
+        return s;
+    if (evm && (s = dev(hipEventRecord(static_cast<hipEvent_t>(evm), st))) != STARKV_OK) return s;
+    ValueParams vp;
+    vp.zv = cache->zv;
+    vp.P = sp.P;
+    vp.stats = sp.stats;
+    vp.ws_ml = reinterpret_cast<float*>(ws + w.ml);
+    vp.ws_acc = reinterpret_cast<float*>(ws + w.acc);
+    vp.B = B;
+    vp.H = li.H;
+    vp.rv = li.rv;
+    vp.nblk_cap = sp.nblk_cap;
+    vp.seq_len = sp.seq_len;
+    vp.nblk = w.nblk;
+    vp.Tp = sp.Tp;
+    vp.S = w.vp.splits;
+    vp.blocks_per_split = w.vp.bps;
+    if ((s = dev(launch_latent_values(vp, ek, w.vp.chunks, st))) != STARKV_OK) return s;
     if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
     MergeParams m;
-    m.ws_ml = p.ws_ml;
-    m.ws_acc = p.ws_acc;
+    m.ws_ml = vp.ws_ml;
+    m.ws_acc = vp.ws_acc;
     m.ws_a = reinterpret_cast<float*>(ws + w.a);
     m.B = B;
     m.H = li.H;
-    m.S = w.S;
+    m.S = w.vp.splits;
     m.W = li.rv;
-    m.active_splits = active;
+    m.active_splits = w.vp.splits;
     if ((s = dev(launch_merge(m, st))) != STARKV_OK) return s;
     ProjectParams pr;
     pr.ws_a = m.ws_a;
@@ -398,16 +494,16 @@ starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* 
                                  float* out, int32_t num_splits, void* workspace,
                                  size_t workspace_bytes, void* stream) {
     return decode_impl(layer, cache, seq_len, q, bk, bv, out, num_splits, workspace,
-                       workspace_bytes, stream, nullptr, nullptr);
+                       workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
 starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_cache* cache,
                                        int64_t seq_len, const float* q, const void* bk,
                                        const void* bv, float* out, int32_t num_splits,
                                        void* workspace, size_t workspace_bytes, void* stream,
-                                       void* event_begin, void* event_end) {
+                                       void* event_begin, void* event_mid, void* event_end) {
     return decode_impl(layer, cache, seq_len, q, bk, bv, out, num_splits, workspace,
-                       workspace_bytes, stream, event_begin, event_end);
+                       workspace_bytes, stream, event_begin, event_mid, event_end);
 }
 
 starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cache,
@@ -426,43 +522,40 @@ starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cach
     const int B = cache->batch;
     const int es = elem_bytes(li.cache_dt);
     const long long cap = cache->capacity, n = t1 - t0;
-    const long long krow = static_cast<long long>(li.dense ? li.H * li.D : li.Rk) * es;
-    if (zk_out) {
-        RowCopyParams p;
-        p.src = static_cast<const char*>(cache->zk);
-        p.dst = static_cast<char*>(zk_out);
-        p.src_seq_stride = cap * krow;
-        p.dst_seq_stride = n * krow;
-        p.src_off = t0 * krow;
-        p.dst_off = 0;
-        p.bytes = n * krow;
-        if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
-    }
-    if (zv_out) {
-        if (li.dense) {
+    if (li.dense) {
+        const long long row = static_cast<long long>(li.H) * li.D * es;
+        for (int which = 0; which < 2; ++which) {
+            void* outp = which ? zv_out : zk_out;
+            if (!outp) continue;
             RowCopyParams p;
-            p.src = static_cast<const char*>(cache->zv);
-            p.dst = static_cast<char*>(zv_out);
-            p.src_seq_stride = cap * krow;
-            p.dst_seq_stride = n * krow;
-            p.src_off = t0 * krow;
+            p.src = static_cast<const char*>(which ? cache->zv : cache->zk);
+            p.dst = static_cast<char*>(outp);
+            p.src_seq_stride = cap * row;
+            p.dst_seq_stride = n * row;
+            p.src_off = t0 * row;
             p.dst_off = 0;
-            p.bytes = n * krow;
-            return dev(launch_copy_rows(p, B, st));
+            p.bytes = n * row;
+            if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
         }
+        return STARKV_OK;
+    }
+    for (int which = 0; which < 2; ++which) {
+        void* outp = which ? zv_out : zk_out;
+        if (!outp) continue;
         BlockXposeParams x;
-        x.src = cache->zv;
-        x.dst = zv_out;
+        x.src = which ? cache->zv : cache->zk;
+        x.dst = outp;
         x.B = B;
-        x.C = li.rv;
-        x.cap = cache->capacity;
+        x.C = which ? li.rv : li.Rk;
+        x.nblk_cap = cache->capacity / kTile;
         x.t_begin = t0;
         x.t_end = t1;
         x.row0 = t0;
         x.rows_per_seq = n;
         x.blk_first = static_cast<int>(t0 / kTile);
         x.to_blocks = 0;
-        return dev(launch_block_transpose(x, es, st));
+        x.layout = which;
+        if ((s = dev(launch_block_transpose(x, es, st))) != STARKV_OK) return s;
     }
     return STARKV_OK;
 }

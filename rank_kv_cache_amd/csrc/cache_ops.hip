@@ -1,9 +1,10 @@
 // cache_ops.hip -- cache maintenance kernels (gfx950): append new tokens' latents (Zhou, STAR-KV
 // reading notes, Algorithm 2 steps 1-3) and read cached tokens back in token-major order.
 //
-// Layouts: token-major rows [B][cap][C] for key latents and for dense K/V; channel-major 64-token
-// blocks [B][cap/64][C][64] for the joint value latent. The block transposes go through LDS so
-// that both the row side and the block side are accessed with coalesced loads and stores.
+// Layouts: token-major rows [B][cap][H*d] for dense K/V; 64-token blocks of 16-channel groups for
+// the latents (key: token-major inside a group, value: 16-token runs per channel inside a group;
+// see zk_block_index / zv_block_index). The block transposes go through LDS so that both the row
+// side and the block side are accessed in order.
 
 #include "common.hpp"
 
@@ -19,48 +20,99 @@ __global__ __launch_bounds__(256) void copy_rows(const RowCopyParams p) {
         d[i] = s[i];
 }
 
-// Row <-> block transpose of the value latent, one (64-token block, 64-channel chunk) per
-// workgroup.
+// Token-major rows <-> block layout (key or value latent), one (64-token block, 64-channel chunk,
+// sequence) per workgroup, staged through an LDS tile so both sides are accessed in order.
 template <typename E>
 __global__ __launch_bounds__(256) void block_transpose(const BlockXposeParams p) {
-    __shared__ E tile[64][65];
+    __shared__ E tile[64][65];                        // [token in block][channel in chunk]
     const int blk = p.blk_first + blockIdx.x;
     const int c0 = blockIdx.y * 64;
     const int b = blockIdx.z;
     const long long tb = (long long)blk * 64;
-    const size_t nblk = (size_t)p.cap / 64;
     const E* src = static_cast<const E*>(p.src);
     E* dst = static_cast<E*>(p.dst);
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int ncg = min(64, p.C - c0) >> 4;            // 16-channel groups in this chunk
+    const size_t gbase = ((size_t)b * p.nblk_cap + blk) * (size_t)(p.C >> 4) + (size_t)(c0 >> 4);
+    // element e of the chunk's contiguous block-layout range -> (token, channel)
+    auto decode = [&](int e, int* tok, int* ch) {
+        const int gl = e >> 10, w = e & 1023;
+        if (p.layout == 0) {                          // [t][k]
+            *tok = w >> 4;
+            *ch = 16 * gl + (w & 15);
+        } else {                                      // [u][k][v]
+            *tok = 16 * (w >> 8) + (w & 15);
+            *ch = 16 * gl + ((w >> 4) & 15);
+        }
+    };
     if (p.to_blocks) {
-        for (int r = ty; r < 64; r += 4) {             // r: token in block, tx: channel
+        for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+            const int r = e >> 6, cc = e & 63;          // r: token in block, cc: channel
             const long long t = tb + r;
-            const int c = c0 + tx;
-            if (t >= p.t_begin && t < p.t_end && c < p.C)
-                tile[r][tx] = src[((size_t)b * p.rows_per_seq + (t - p.row0)) * p.C + c];
+            if (t >= p.t_begin && t < p.t_end && c0 + cc < p.C)
+                tile[r][cc] = src[((size_t)b * p.rows_per_seq + (t - p.row0)) * p.C + c0 + cc];
         }
         __syncthreads();
-        for (int r = ty; r < 64; r += 4) {             // r: channel in chunk, tx: token in block
-            const long long t = tb + tx;
-            const int c = c0 + r;
-            if (t >= p.t_begin && t < p.t_end && c < p.C)
-                dst[(((size_t)b * nblk + blk) * p.C + c) * 64 + tx] = tile[tx][r];
+        for (int e = threadIdx.x; e < ncg * 1024; e += 256) {
+            int tok, ch;
+            decode(e, &tok, &ch);
+            const long long t = tb + tok;
+            if (t >= p.t_begin && t < p.t_end) dst[gbase * 1024 + e] = tile[tok][ch];
         }
     } else {
-        for (int r = ty; r < 64; r += 4) {             // r: channel, tx: token in block
-            const long long t = tb + tx;
-            const int c = c0 + r;
-            if (t >= p.t_begin && t < p.t_end && c < p.C)
-                tile[tx][r] = src[(((size_t)b * nblk + blk) * p.C + c) * 64 + tx];
+        for (int e = threadIdx.x; e < ncg * 1024; e += 256) {
+            int tok, ch;
+            decode(e, &tok, &ch);
+            const long long t = tb + tok;
+            if (t >= p.t_begin && t < p.t_end) tile[tok][ch] = src[gbase * 1024 + e];
         }
         __syncthreads();
-        for (int r = ty; r < 64; r += 4) {             // r: token, tx: channel
+        for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+            const int r = e >> 6, cc = e & 63;
             const long long t = tb + r;
-            const int c = c0 + tx;
-            if (t >= p.t_begin && t < p.t_end && c < p.C)
-                dst[((size_t)b * p.rows_per_seq + (t - p.row0)) * p.C + c] = tile[r][tx];
+            if (t >= p.t_begin && t < p.t_end && c0 + cc < p.C)
+                dst[((size_t)b * p.rows_per_seq + (t - p.row0)) * p.C + c0 + cc] = tile[r][cc];
         }
     }
+}
+
+// Append of a few tokens to both latents in one launch: thread per (sequence, token, run of 8
+// channels). A run is contiguous in the key layout (one vector store) and strided by 16 elements
+// in the value layout.
+template <typename E>
+__global__ __launch_bounds__(256) void append_small(const AppendSmallParams p) {
+    struct __attribute__((aligned(16))) Run { E v[8]; };
+    const int runs_k = p.Rk >> 3, runs_v = p.rv >> 3;
+    const long long per_tok = runs_k + runs_v;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.B * p.n * per_tok) return;
+    const int run = (int)(idx % per_tok);
+    const long long bt = idx / per_tok;
+    const int t = (int)(bt % p.n);
+    const int b = (int)(bt / p.n);
+    const long long tok = p.pos + t;
+    if (run < runs_k) {
+        const int c = run * 8;
+        const Run v = *reinterpret_cast<const Run*>(static_cast<const E*>(p.zk_src) + (bt * p.Rk + c));
+        *reinterpret_cast<Run*>(static_cast<E*>(p.zk) + zk_block_index(b, p.nblk_cap, p.Rk, tok, c)) = v;
+    } else {
+        const int c = (run - runs_k) * 8;
+        const Run v = *reinterpret_cast<const Run*>(static_cast<const E*>(p.zv_src) + (bt * p.rv + c));
+        E* dst = static_cast<E*>(p.zv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[zv_block_index(b, p.nblk_cap, p.rv, tok, c + e)] = v.v[e];
+    }
+}
+
+hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st) {
+    const long long n = (long long)p.B * p.n * ((p.Rk + p.rv) / 8);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(append_small<uint16_t>, grid, dim3(256), 0, st, p);
+    else if (elem_bytes == 4)
+        hipLaunchKernelGGL(append_small<uint32_t>, grid, dim3(256), 0, st, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st) {

@@ -110,23 +110,49 @@ __device__ __forceinline__ void sincos_rev(float x, float* c, float* s) {
 // Parameter blocks (passed by value; each stays well under the 4 KB kernel-argument limit).
 // ------------------------------------------------------------------------------------------------
 constexpr int kMaxHeads = 32;
-constexpr int kTile = 64;              // tokens per tile == tokens per cache block
-constexpr int kKeyWaveGroups = 4;      // waves per 32-token sub-tile in the key phase
+constexpr int kTile = 64;              // tokens per cache block
+constexpr int kScoreWaves = 8;         // waves per score workgroup
+constexpr int kFragLdsBytes = 96 * 1024;   // key-factor fragments of one head group in LDS
+constexpr int kMaxGroups = 8;
+constexpr int kValueWaves = 4;         // waves per value workgroup
+constexpr int kMaxBlocksPerSplit = 256;
 
-struct LatentDecodeParams {
-    const void* zk;        // [B][cap][Rk]
-    const void* zv;        // [B][cap/64][rv][64]
-    const void* bkt;       // packed key-factor fragments (see pack kernel)
+// Latent cache block layouts (64-token blocks, 16-channel groups of 1024 elements):
+//   key latent   zk[b][blk][g][t][k]      t < 64 token in block, k < 16 channel in group
+//   value latent zv[b][blk][g][u][k][v]   u < 4, v < 16: token 16u + v, k < 16 channel in group
+// so that one 16-byte lane load of eight consecutive elements feeds an MFMA operand fragment and
+// the 64 lanes of a wave read 1 KB (key) or two 512-byte runs (value) of contiguous memory.
+__host__ __device__ inline size_t zk_block_index(size_t b, size_t nblk_cap, int C, long long t, int c) {
+    return ((b * nblk_cap + (size_t)(t >> 6)) * (size_t)(C >> 4) + (size_t)(c >> 4)) * 1024 +
+           (size_t)(t & 63) * 16 + (size_t)(c & 15);
+}
+__host__ __device__ inline size_t zv_block_index(size_t b, size_t nblk_cap, int C, long long t, int c) {
+    return ((b * nblk_cap + (size_t)(t >> 6)) * (size_t)(C >> 4) + (size_t)(c >> 4)) * 1024 +
+           (size_t)((t & 63) >> 4) * 256 + (size_t)(c & 15) * 16 + (size_t)(t & 15);
+}
+
+struct ScoreParams {
+    const void* zk;        // key latent, block layout
+    const void* bkt;       // key factors in MFMA fragment order (head h at koff[h] * D)
     const float* q;        // [B][H][D]
-    float* ws_ml;          // [B][S][H][2]  (running max in log2 units, sum)
-    float* ws_acc;         // [B][S][H][rv]
-    int B, H, D, Rk, rv, cap, seq_len, S, tiles_per_split;
+    void* P;               // [B][H][Tp] probabilities, relative to each block's maximum
+    float* stats;          // [B][H][nblk][2] per block: max (log2 units), sum of probabilities
+    int B, H, D, Rk, nblk_cap, seq_len, nblk, Tp, blocks_per_wg;
     float q_scale;         // softmax scale * log2(e)
+    int8_t order[kMaxHeads];          // heads grouped: group g = order[gstart[g] .. gstart[g+1])
+    int8_t gstart[kMaxGroups + 1];
     int16_t koff[kMaxHeads + 1];
     int16_t rank[kMaxHeads];
-    int8_t sched[kKeyWaveGroups][kMaxHeads];   // heads of each key-wave group
-    int8_t sched_n[kKeyWaveGroups];
     double rope_rev[64];   // theta_i / (2 pi): RoPE frequency in revolutions per position
+};
+
+struct ValueParams {
+    const void* zv;        // value latent, block layout
+    const void* P;         // [B][H][Tp]
+    const float* stats;    // [B][H][nblk][2]
+    float* ws_ml;          // [B][S][H][2]   (max in log2 units, sum)
+    float* ws_acc;         // [B][S][H][rv]
+    int B, H, rv, nblk_cap, seq_len, nblk, Tp, S, blocks_per_split;
 };
 
 struct MergeParams {
@@ -164,17 +190,27 @@ struct RowCopyParams {
     long long bytes;
 };
 
-// Value-latent row <-> block transpose. to_blocks = 1: rows[b][t - row0][c] ->
-// blocks[b][t/64][c][t%64] for absolute tokens t in [t_begin, t_end); to_blocks = 0: reverse.
+// Token-major rows <-> block layout of a latent (layout 0: key, 1: value). to_blocks = 1:
+// rows[b][t - row0][c] -> blocks for absolute tokens t in [t_begin, t_end); 0: the reverse.
 struct BlockXposeParams {
     const void* src;
     void* dst;
-    int B, C, cap;
+    int B, C, nblk_cap;
     long long t_begin, t_end;
     long long row0;             // absolute token of row 0 of the row-major side
     long long rows_per_seq;     // rows per sequence on the row-major side
     int blk_first;              // first 64-token block touched
     int to_blocks;
+    int layout;
+};
+
+struct AppendSmallParams {
+    const void* zk_src;         // [B][n][Rk] rows
+    const void* zv_src;         // [B][n][rv] rows
+    void* zk;
+    void* zv;
+    int B, Rk, rv, nblk_cap;
+    long long pos, n;
 };
 
 }  // namespace starkv

@@ -3,315 +3,488 @@
 // Computes, for every sequence b and head h (Zhou, STAR-KV reading notes, Algorithm 2 steps 4-7
 // and section 5.3):
 //   s_n   = scale * q_h . RoPE_n(Z_k[h][n] B_k[h])        keys rebuilt per tile in registers
-//   p     = softmax_n(s)                                  online over tiles, split-K over n
+//   p     = softmax_n(s)
 //   out_h = (sum_n p_n Z_v[n]) B_v[:, h*d:(h+1)*d]        values summed in latent space
 // No full-width K or V is ever written to memory.
 //
-// Kernel 1 (latent_decode_split): one workgroup per (split, sequence), 8 waves. For each 64-token
-// tile of its split:
-//   * RoPE table: cos/sin of n*theta_i for the tile's 64 positions into LDS (angles in fp64,
-//     reduced to one revolution, then the hardware sin/cos).
-//   * key phase: waves 0-3 take tokens 0-31 of the tile, waves 4-7 tokens 32-63; each wave owns a
-//     rank-balanced subset of heads. Per head, K~^T (d x 32 tokens) = B_k[h]^T Z_k[h]^T on MFMA
-//     32x32x16 (A = packed factor fragments, B = latent rows loaded straight from HBM), then the
-//     rotate-half RoPE and the dot with q are done in registers: a lane holds 64 of the 128
-//     reconstructed dims of one token, with each RoPE partner (i, i+d/2) in the same lane, so the
-//     dot needs one cross-half swap. Scores (log2 domain) go to LDS.
-//   * softmax phase: each head's 64 scores are reduced with wave shuffles; running max/sum are
-//     kept per head; probabilities (fp16 for fp16 caches, hi+lo bf16 pair for bf16, fp32 for fp32)
-//     go to LDS with the rescale factor of the running accumulator.
-//   * value phase: Acc[H x r_v] += P[H x 64] Z_v[64 x r_v] on MFMA, all heads in one contraction
-//     (the stacking of the notes' section 5.3); wave w owns r_v columns 32*(w + 8k). Z_v is stored
-//     channel-major inside each 64-token block so every lane loads 8 consecutive tokens of one
-//     channel with one 16-byte load.
-//   At the end the split's (max, sum, Acc) partial goes to the workspace.
-// Kernel 2 (merge_splits): log-sum-exp weighted merge of the splits per (b, h), normalised.
-// Kernel 3 (project_heads): out[b][h] = a[b][h] . B_v[:, h*d:(h+1)*d] for all b at once.
+// Four kernels per call:
+//  1. pack_key_factors: B_k into MFMA A-operand fragment order (one 16-byte run per lane).
+//  2. latent_scores: one workgroup per (split of the sequence, head group, sequence). The group's
+//     factor fragments are staged once in LDS; each wave walks 64-token blocks and, per head,
+//     rebuilds K~^T (d x 64 tokens) = B_k^T Z_k^T on MFMA 32x32x16 (A = factor fragments from
+//     LDS, B = latent fragments streamed from HBM one unit ahead in registers), applies RoPE and
+//     the dot with q in registers, and writes the block's probabilities p = exp2(s - m_blk)
+//     (relative to the block maximum) plus (m_blk, sum p). RoPE at position n0 + j (n0 = first
+//     token of a 32-token MFMA column tile, j = lane's column) is split as R_{n0+j} = R_{n0} R_j:
+//     the query is rotated back by n0 once per (head, tile) and the constant rotation by j*theta
+//     is kept in registers, so no per-token trigonometry runs in the hot loop.
+//  3. latent_values: one workgroup per (split, channel chunk, sequence): per-head split maximum
+//     M and sum L from the block statistics, then Acc[H x r_v] += (p * 2^(m_blk - M)) Z_v on MFMA
+//     with all heads stacked into one 32-row operand (notes, section 5.3), Z_v fragments
+//     streamed one block ahead in registers. Writes (M, L, Acc) per split.
+//  4. merge_splits: log-sum-exp weighted merge of the splits per (b, h), normalised.
+//  5. project_heads: out[b][h] = a[b][h] . B_v[:, h*d:(h+1)*d] for all b at once.
 
 #include "common.hpp"
 
 namespace starkv {
 
 // ------------------------------------------------------------------------------------------------
-// Probability tile storage in LDS, per element kind, and the value-side MFMA that consumes it.
-// Row = head (32 rows), column = token in tile (64).
+// 1. Key-factor packing: for head h (rank r, offset ko), fragment f = mt*(r/16) + ks, lane l holds
+// B_k[ko + 16*ks + 8*(l/32) + j][32*mt + l%32], j = 0..7, at element ko*D + (f*64 + l)*8 + j.
+// One thread per 8-element lane run.
 // ------------------------------------------------------------------------------------------------
-template <int K> struct ProbTile;
-
-template <> struct ProbTile<kF16> {
-    static constexpr int kStride = kTile + 8;                // halves per row (144 bytes)
-    _Float16 p[kMaxHeads * kStride];
-    __device__ void zero(int tid, int nthreads) {
-        for (int i = tid; i < kMaxHeads * kStride; i += nthreads) p[i] = (_Float16)0.0f;
-    }
-    __device__ void store(int h, int t, float v) { p[h * kStride + t] = (_Float16)v; }
-    __device__ f32x16 mma(int row, int tcol, const f16x8& z, f32x16 acc) const {
-        f16x8 a = *reinterpret_cast<const f16x8*>(&p[row * kStride + tcol]);
-        return mma32<kF16>(a, z, acc);
-    }
+struct PackParams {
+    const void* bk;
+    void* bkt;
+    int D, H, Rk;
+    int16_t koff[kMaxHeads + 1];
+    int16_t rank[kMaxHeads];
 };
 
-template <> struct ProbTile<kBF16> {
-    // p = hi + lo with both parts bf16: the pair carries ~16 significant bits, so the bf16 path
-    // keeps the probabilities as precise as the fp16 path does.
-    static constexpr int kStride = kTile + 8;
-    uint16_t hi[kMaxHeads * kStride];
-    uint16_t lo[kMaxHeads * kStride];
-    __device__ void zero(int tid, int nthreads) {
-        for (int i = tid; i < kMaxHeads * kStride; i += nthreads) { hi[i] = 0; lo[i] = 0; }
-    }
-    __device__ void store(int h, int t, float v) {
-        uint16_t a = float_to_bf16_bits(v);
-        hi[h * kStride + t] = a;
-        lo[h * kStride + t] = float_to_bf16_bits(v - bf16_bits_to_float(a));
-    }
-    __device__ f32x16 mma(int row, int tcol, const bf16x8& z, f32x16 acc) const {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(&hi[row * kStride + tcol]);
-        bf16x8 b = *reinterpret_cast<const bf16x8*>(&lo[row * kStride + tcol]);
-        acc = mma32<kBF16>(a, z, acc);
-        return mma32<kBF16>(b, z, acc);
-    }
-};
-
-template <> struct ProbTile<kF32> {
-    static constexpr int kStride = kTile + 4;
-    float p[kMaxHeads * kStride];
-    __device__ void zero(int tid, int nthreads) {
-        for (int i = tid; i < kMaxHeads * kStride; i += nthreads) p[i] = 0.0f;
-    }
-    __device__ void store(int h, int t, float v) { p[h * kStride + t] = v; }
-    __device__ f32x16 mma(int row, int tcol, const f32x8& z, f32x16 acc) const {
-        const f32x4* src = reinterpret_cast<const f32x4*>(&p[row * kStride + tcol]);
-        f32x4 a0 = src[0], a1 = src[1];
-        f32x8 a;
-        for (int i = 0; i < 4; ++i) { a[i] = a0[i]; a[4 + i] = a1[i]; }
-        return mma32<kF32>(a, z, acc);
-    }
-};
+template <int K>
+__global__ __launch_bounds__(256) void pack_key_factors(const PackParams p) {
+    using T = typename Elem<K>::storage;
+    const int run = blockIdx.x * 256 + threadIdx.x;        // run index over Rk*D/8
+    if (run >= p.Rk * p.D / 8) return;
+    const int e0 = run * 8;
+    int h = 0;
+    while (h + 1 < p.H && e0 >= p.koff[h + 1] * p.D) ++h;
+    const int ko = p.koff[h], nks = p.rank[h] >> 4;
+    const int local = e0 - ko * p.D;                         // element inside the head's block
+    const int l = (local >> 3) & 63;
+    const int f = local >> 9;
+    const int mt = f / nks, ks = f - mt * nks;
+    const int dim = 32 * mt + (l & 31);
+    const int r0 = ko + 16 * ks + 8 * (l >> 5);
+    const T* src = static_cast<const T*>(p.bk);
+    T v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[(size_t)(r0 + j) * p.D + dim];
+    T* dst = static_cast<T*>(p.bkt) + e0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = v[j];
+}
 
 // ------------------------------------------------------------------------------------------------
-// Kernel 1
+// 2. Scores.
 // ------------------------------------------------------------------------------------------------
-template <int D, int NTV, int K>
-__global__ __launch_bounds__(512, 1) void latent_decode_split(const LatentDecodeParams p) {
-    constexpr int MT = D / 32;          // 32-row tiles of head dims
-    constexpr int HMT = MT / 2;         // tiles holding the first half of the dims
+template <int K> struct PStore;
+template <> struct PStore<kF32> { using T = float; };
+template <> struct PStore<kF16> { using T = _Float16; };
+template <> struct PStore<kBF16> { using T = _Float16; };
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int K, int MAXKS>
+__global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
     constexpr int NF = D / 2;           // RoPE frequencies
-    constexpr int TRIG_STRIDE = 2 * NF + 4;
-    constexpr int SC_STRIDE = kTile + 4;
+    constexpr int HMT = D / 64;         // m-tile pairs (mt, mt + HMT)
     using Fr = typename Elem<K>::frag;
+    using T = typename Elem<K>::storage;
+    using PT = typename PStore<K>::T;
 
-    __shared__ __attribute__((aligned(16))) float s_trig[kTile * TRIG_STRIDE];
+    __shared__ __attribute__((aligned(32))) T s_bk[kFragLdsBytes / sizeof(T)];
     __shared__ __attribute__((aligned(16))) float s_q[kMaxHeads * D];
-    __shared__ __attribute__((aligned(16))) float s_score[kMaxHeads * SC_STRIDE];
-    __shared__ __attribute__((aligned(16))) float s_alpha[kMaxHeads];
-    __shared__ __attribute__((aligned(16))) ProbTile<K> s_p;
+    __shared__ __attribute__((aligned(16))) float s_qr[kScoreWaves][2][D];
+    __shared__ int s_slot[kMaxHeads + 1];
+
+    // small per-layer tables, copied out of the kernel arguments so that every dynamic index
+    // reads LDS (indexing the by-value argument block would make the compiler copy it to scratch)
+    __shared__ double s_rev[64];
+    __shared__ int s_head[kMaxHeads], s_rank[kMaxHeads], s_kgrp[kMaxHeads];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int half = lane >> 5;
+    const int j = lane & 31;
+    const int split = blockIdx.x;
+    const int grp = blockIdx.y;
+    const int b = blockIdx.z;
+    const int hs0 = p.gstart[grp];
+    const int ng = p.gstart[grp + 1] - hs0;
+    const int H = p.H;
+    const int seq_len = p.seq_len;
+    const int Tp = p.Tp;
+    const int nblk = p.nblk;
+    const float q_scale = p.q_scale;
+    const T* __restrict__ zk = static_cast<const T*>(p.zk);
+    const T* __restrict__ bkt = static_cast<const T*>(p.bkt);
+    const float* __restrict__ qg = p.q;
+    PT* __restrict__ Pout = static_cast<PT*>(p.P);
+    float* __restrict__ stats = p.stats;
+    const size_t kgroups = (size_t)(p.Rk >> 4);
+    const size_t blk_base = (size_t)b * p.nblk_cap;
+
+    if (tid < 64) s_rev[tid] = tid < NF ? p.rope_rev[tid] : 0.0;
+    if (tid < ng) {
+        const int h = p.order[hs0 + tid];
+        s_head[tid] = h;
+        s_rank[tid] = p.rank[h];
+        s_kgrp[tid] = p.koff[h] >> 4;
+    }
+    // ---- stage the group's factor fragments and (scaled) queries ----
+    if (tid == 0) {
+        int off = 0;
+        for (int s = 0; s < ng; ++s) {
+            s_slot[s] = off;
+            off += p.rank[p.order[hs0 + s]] * D;
+        }
+        s_slot[ng] = off;
+    }
+    __syncthreads();
+    for (int s = 0; s < ng; ++s) {
+        const int h = s_head[s];
+        const int n8 = s_rank[s] * D / 8;
+        const Fr* src = reinterpret_cast<const Fr*>(bkt + (size_t)s_kgrp[s] * 16 * D);
+        Fr* dst = reinterpret_cast<Fr*>(&s_bk[s_slot[s]]);
+        for (int i = tid; i < n8; i += 512) dst[i] = src[i];
+        for (int i = tid; i < D; i += 512) s_q[s * D + i] = qg[((size_t)b * H + h) * D + i] * q_scale;
+    }
+
+    // ---- constant rotation by j*theta_i for this lane's column j and its frequencies ----
+    // Frequencies held by the lane: i = 32*pp + 8*g + 4*half + r, pp < HMT, g < 4, r < 4.
+    float cj[HMT][4][4], sj[HMT][4][4];
+#pragma unroll
+    for (int pp = 0; pp < HMT; ++pp)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 32 * pp + 8 * g + 4 * half + r;
+                const double rev = (double)j * s_rev[i];
+                sincos_rev((float)(rev - floor(rev)), &cj[pp][g][r], &sj[pp][g][r]);
+            }
+    __syncthreads();
+
+    const int blk_begin = split * p.blocks_per_wg;
+    const int blk_end = min(nblk, blk_begin + p.blocks_per_wg);
+    const int my_blocks = blk_begin + wave < blk_end ? (blk_end - blk_begin - wave + kScoreWaves - 1) / kScoreWaves : 0;
+    const int nunits = my_blocks * ng;
+
+    // latent fragments of one unit (head, 64-token block): [column tile][rank step]
+    Fr zA[2][MAXKS], zB[2][MAXKS];
+
+    auto load_unit = [&](Fr (&z)[2][MAXKS], int u) {
+        const int blk = blk_begin + wave + kScoreWaves * (u / ng);
+        const int s = u - (u / ng) * ng;
+        const int nks = s_rank[s] >> 4;
+        const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
+        // Every slot is loaded (steps past the head's rank repeat its last step, a cache hit), so
+        // the number of loads in flight is static and the compiler's wait counts stay exact:
+        // loads are retired in order, and a data-dependent count would force a full drain.
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < MAXKS; ++ks)
+                z[nt][ks] = load_frag<K>(zk, base + (size_t)min(ks, nks - 1) * 1024 + nt * 512);
+    };
+
+    float cb[2] = {1.0f, 1.0f}, sb[2] = {0.0f, 0.0f};     // rotation by n0*theta_lane (lane < NF)
+
+    auto compute_unit = [&](const Fr (&z)[2][MAXKS], int u) {
+        const int blk = blk_begin + wave + kScoreWaves * (u / ng);
+        const int s = u - (u / ng) * ng;
+        const int h = s_head[s];
+        const int nks = s_rank[s] >> 4;
+        if (s == 0 && lane < NF) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const double rev = (double)(blk * 64 + 32 * nt) * s_rev[lane];
+                sincos_rev((float)(rev - floor(rev)), &cb[nt], &sb[nt]);
+            }
+        }
+        // q' = R_{n0}^T q for both column tiles, wave-private LDS
+        if (lane < NF) {
+            const float q1 = s_q[s * D + lane], q2 = s_q[s * D + lane + NF];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                s_qr[wave][nt][lane] = q1 * cb[nt] + q2 * sb[nt];
+                s_qr[wave][nt][lane + NF] = q2 * cb[nt] - q1 * sb[nt];
+            }
+        }
+        wave_sync_lds();
+        const T* fr = &s_bk[s_slot[s]];
+        float sc[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+            for (int pp = 0; pp < HMT; ++pp) {
+                f32x16 acc0, acc1;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { acc0[r] = 0.0f; acc1[r] = 0.0f; }
+#pragma unroll
+                for (int ks = 0; ks < MAXKS; ++ks) {
+                    if (ks < nks) {
+                        const Fr a0 = *reinterpret_cast<const Fr*>(fr + ((pp * nks + ks) * 64 + lane) * 8);
+                        const Fr a1 = *reinterpret_cast<const Fr*>(fr + (((pp + HMT) * nks + ks) * 64 + lane) * 8);
+                        acc0 = mma32<K>(a0, z[nt][ks], acc0);
+                        acc1 = mma32<K>(a1, z[nt][ks], acc1);
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int i0 = 32 * pp + 8 * g + 4 * half;
+                    const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0]);
+                    const f32x4 q2 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0 + NF]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float a = acc0[4 * g + r], bb = acc1[4 * g + r];
+                        const float c = cj[pp][g][r], sn = sj[pp][g][r];
+                        sc[nt] += q1[r] * (a * c - bb * sn) + q2[r] * (bb * c + a * sn);
+                    }
+                }
+                // consume the dot here, so the compiler cannot sink every pass's RoPE arithmetic
+                // past all the MFMA chains (which would keep all accumulators live at once)
+                asm volatile("" : "+v"(sc[nt]));
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sc[nt] += __shfl_xor(sc[nt], 32, 64);
+        const int tok = blk * 64 + lane;
+        float my = half ? sc[1] : sc[0];
+        if (tok >= seq_len) my = -INFINITY;
+        const float m = wave_max(my);
+        const float pr = __builtin_amdgcn_exp2f(my - m);
+        const float l = wave_sum(pr);
+        Pout[((size_t)b * H + h) * Tp + tok] = (PT)pr;
+        if (lane == 0) {
+            float* st = stats + (((size_t)b * H + h) * nblk + blk) * 2;
+            st[0] = m;
+            st[1] = l;
+        }
+        wave_sync_lds();
+    };
+
+    // Two-deep software pipeline over units. Prefetches past the last unit reload the last one
+    // (a cache hit) instead of being skipped, for the same reason as in load_unit.
+    if (nunits > 0) load_unit(zA, 0);
+    for (int u = 0; u < nunits; u += 2) {
+        load_unit(zB, min(u + 1, nunits - 1));
+        compute_unit(zA, u);
+        load_unit(zA, min(u + 2, nunits - 1));
+        if (u + 1 < nunits) compute_unit(zB, u + 1);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// 3. Values. Wave w of workgroup (split, chunk, b) owns channel tiles nt = (chunk*kValueWaves + w)
+// * NTW + k, k < NTW (32 channels each). A operand = probabilities (row = head), B operand = Z_v.
+// ------------------------------------------------------------------------------------------------
+template <int K> struct ProbFrag;
+
+template <> struct ProbFrag<kF16> {
+    using Raw = f16x8;
+    __device__ static Raw load(const void* P, size_t i) { return *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(P) + i); }
+    __device__ static Raw zero() { Raw r; for (int e = 0; e < 8; ++e) r[e] = (_Float16)0.0f; return r; }
+    struct Op { f16x8 v; };
+    __device__ static Op scale(const Raw& r, float f) {
+        Op o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.v[e] = (_Float16)((float)r[e] * f);
+        return o;
+    }
+    __device__ static f32x16 mma(const Op& a, const f16x8& z, f32x16 acc) { return mma32<kF16>(a.v, z, acc); }
+};
+
+template <> struct ProbFrag<kBF16> {
+    // probabilities are stored as fp16; the bf16 operand is split into hi + lo so that the pair
+    // keeps the ~16 significant bits of the scaled probability.
+    using Raw = f16x8;
+    __device__ static Raw load(const void* P, size_t i) { return *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(P) + i); }
+    __device__ static Raw zero() { Raw r; for (int e = 0; e < 8; ++e) r[e] = (_Float16)0.0f; return r; }
+    struct Op { bf16x8 hi, lo; };
+    __device__ static Op scale(const Raw& r, float f) {
+        Op o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = (float)r[e] * f;
+            const uint16_t hb = float_to_bf16_bits(v);
+            const uint16_t lb = float_to_bf16_bits(v - bf16_bits_to_float(hb));
+            o.hi[e] = __builtin_bit_cast(__bf16, hb);
+            o.lo[e] = __builtin_bit_cast(__bf16, lb);
+        }
+        return o;
+    }
+    __device__ static f32x16 mma(const Op& a, const bf16x8& z, f32x16 acc) {
+        acc = mma32<kBF16>(a.hi, z, acc);
+        return mma32<kBF16>(a.lo, z, acc);
+    }
+};
+
+template <> struct ProbFrag<kF32> {
+    using Raw = f32x8;
+    __device__ static Raw load(const void* P, size_t i) {
+        const f32x4* s = reinterpret_cast<const f32x4*>(static_cast<const float*>(P) + i);
+        const f32x4 a = s[0], c = s[1];
+        Raw r;
+        for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[4 + e] = c[e]; }
+        return r;
+    }
+    __device__ static Raw zero() { Raw r; for (int e = 0; e < 8; ++e) r[e] = 0.0f; return r; }
+    struct Op { f32x8 v; };
+    __device__ static Op scale(const Raw& r, float f) {
+        Op o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.v[e] = r[e] * f;
+        return o;
+    }
+    __device__ static f32x16 mma(const Op& a, const f32x8& z, f32x16 acc) { return mma32<kF32>(a.v, z, acc); }
+};
+
+template <int K, int NTW>
+__global__ __launch_bounds__(256) void latent_values(const ValueParams p) {
+    using Fr = typename Elem<K>::frag;
+    using PF = ProbFrag<K>;
+    __shared__ float s_f[kMaxHeads][kMaxBlocksPerSplit];
+    __shared__ float s_M[kMaxHeads], s_L[kMaxHeads];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int half = lane >> 5;
     const int split = blockIdx.x;
-    const int b = blockIdx.y;
-    const int H = p.H, rv = p.rv;
-    const int ntiles = (p.seq_len + kTile - 1) / kTile;
-    const int tile_begin = split * p.tiles_per_split;
-    const int tile_end = min(ntiles, tile_begin + p.tiles_per_split);
+    const int chunk = blockIdx.y;
+    const int b = blockIdx.z;
+    const int H = p.H;
+    const int blk_begin = split * p.blocks_per_split;
+    const int blk_end = min(p.nblk, blk_begin + p.blocks_per_split);
+    const int nb = blk_end - blk_begin;
 
-    for (int i = tid; i < H * D; i += 512) s_q[i] = p.q[(size_t)b * H * D + i] * p.q_scale;
-    s_p.zero(tid, 512);
-    if (tid < kMaxHeads) s_alpha[tid] = 1.0f;
-
-    float m_run[4], l_run[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { m_run[j] = -INFINITY; l_run[j] = 0.0f; }
-    f32x16 accv[NTV];
-#pragma unroll
-    for (int k = 0; k < NTV; ++k)
-        for (int r = 0; r < 16; ++r) accv[k][r] = 0.0f;
+    // ---- split statistics per head: M = max m_blk, f_blk = 2^(m_blk - M), L = sum f_blk l_blk ----
+    for (int h = wave; h < H; h += kValueWaves) {
+        const float* st = p.stats + ((size_t)b * H + h) * p.nblk * 2;
+        float M = -INFINITY;
+        for (int i = lane; i < nb; i += 64) M = fmaxf(M, st[(blk_begin + i) * 2]);
+        M = wave_max(M);
+        float L = 0.0f;
+        for (int i = lane; i < nb; i += 64) {
+            const float f = __builtin_amdgcn_exp2f(st[(blk_begin + i) * 2] - M);
+            s_f[h][i] = f;
+            L += f * st[(blk_begin + i) * 2 + 1];
+        }
+        L = wave_sum(L);
+        if (lane == 0) { s_M[h] = M; s_L[h] = L; }
+    }
     __syncthreads();
 
-    const int st = wave / kKeyWaveGroups;     // key sub-tile (32 tokens)
-    const int grp = wave % kKeyWaveGroups;
-    const int nsched = p.sched_n[grp];
-    const int tok = 32 * st + (lane & 31);    // this lane's token inside the tile (key phase)
-    const size_t nblk = (size_t)p.cap / kTile;
+    const int hrow = lane & 31;
+    const bool hvalid = hrow < H;
+    const int cgroups = p.rv >> 4;
+    int ch[NTW];
+    bool chok[NTW];
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) {
+        ch[k] = ((chunk * kValueWaves + wave) * NTW + k) * 32 + (lane & 31);
+        chok[k] = ch[k] < p.rv;
+    }
+    f32x16 acc[NTW];
+#pragma unroll
+    for (int k = 0; k < NTW; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
 
-    for (int tile = tile_begin; tile < tile_end; ++tile) {
-        const int t0 = tile * kTile;
+    typename PF::Raw pA[4], pB[4];
+    Fr zA[NTW][4], zB[NTW][4];
+    const size_t prow = ((size_t)b * H + (hvalid ? hrow : 0)) * p.Tp + 8 * half;
 
-        // ---- RoPE table for positions t0 .. t0+63 ----
-        for (int e = tid; e < kTile * NF; e += 512) {
-            const int j = e / NF, i = e - j * NF;
-            const double rev = (double)(t0 + j) * p.rope_rev[i];
-            const float x = (float)(rev - floor(rev));
-            float c, s;
-            sincos_rev(x, &c, &s);
-            s_trig[j * TRIG_STRIDE + 2 * i] = c;
-            s_trig[j * TRIG_STRIDE + 2 * i + 1] = s;
+    auto load_blk = [&](typename PF::Raw (&pr)[4], Fr (&z)[NTW][4], int blk) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            pr[ks] = hvalid ? PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks) : PF::zero();
+        const size_t bbase = ((size_t)b * p.nblk_cap + blk) * cgroups;
+#pragma unroll
+        for (int k = 0; k < NTW; ++k)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                z[k][ks] = chok[k] ? load_frag<K>(p.zv, (bbase + (ch[k] >> 4)) * 1024 + ks * 256 +
+                                                        (ch[k] & 15) * 16 + 8 * half)
+                                   : zero_frag<K>();
+    };
+    auto compute_blk = [&](const typename PF::Raw (&pr)[4], Fr (&z)[NTW][4], int blk) {
+        const float f = hvalid ? s_f[hrow][blk - blk_begin] : 0.0f;
+        if ((blk + 1) * 64 > p.seq_len) {                  // ragged last block: zero the tail
+#pragma unroll
+            for (int k = 0; k < NTW; ++k)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (blk * 64 + 16 * ks + 8 * half + e >= p.seq_len) z[k][ks][e] = 0;
         }
-        __syncthreads();
-
-        // ---- key phase ----
-        {
-            float tc[HMT][4][4], ts[HMT][4][4];
 #pragma unroll
-            for (int mt = 0; mt < HMT; ++mt)
+        for (int ks = 0; ks < 4; ++ks) {
+            const typename PF::Op a = PF::scale(pr[ks], f);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4* row = reinterpret_cast<const f32x4*>(
-                        &s_trig[tok * TRIG_STRIDE + 2 * (32 * mt + 8 * g + 4 * half)]);
-                    const f32x4 v0 = row[0], v1 = row[1];
-                    tc[mt][g][0] = v0[0]; ts[mt][g][0] = v0[1];
-                    tc[mt][g][1] = v0[2]; ts[mt][g][1] = v0[3];
-                    tc[mt][g][2] = v1[0]; ts[mt][g][2] = v1[1];
-                    tc[mt][g][3] = v1[2]; ts[mt][g][3] = v1[3];
-                }
-            const bool valid = (t0 + tok) < p.seq_len;
-            const size_t zrow = ((size_t)b * p.cap + t0 + tok) * p.Rk;
-            for (int si = 0; si < nsched; ++si) {
-                const int h = p.sched[grp][si];
-                const int ko = p.koff[h];
-                const int nks = p.rank[h] >> 4;
-                f32x16 acc[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
-                const size_t fbase = (size_t)ko * D;
-                for (int ks = 0; ks < nks; ++ks) {
-                    const Fr bz = load_frag<K>(p.zk, zrow + ko + 16 * ks + 8 * half);
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const Fr a = load_frag<K>(p.bkt, fbase + ((size_t)(mt * nks + ks) * 64 + lane) * 8);
-                        acc[mt] = mma32<K>(a, bz, acc[mt]);
-                    }
-                }
-                const float* qh = &s_q[h * D];
-                float sc = 0.0f;
-#pragma unroll
-                for (int mt = 0; mt < HMT; ++mt)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int i0 = 32 * mt + 8 * g + 4 * half;
-                        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qh[i0]);
-                        const f32x4 q2 = *reinterpret_cast<const f32x4*>(&qh[i0 + NF]);
-#pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) {
-                            const float a = acc[mt][4 * g + r4], bb = acc[mt + HMT][4 * g + r4];
-                            const float c = tc[mt][g][r4], s = ts[mt][g][r4];
-                            sc += q1[r4] * (a * c - bb * s) + q2[r4] * (bb * c + a * s);
-                        }
-                    }
-                sc += __shfl_xor(sc, 32, 64);
-                if (lane < 32) s_score[h * SC_STRIDE + tok] = valid ? sc : -INFINITY;
-            }
+            for (int k = 0; k < NTW; ++k) acc[k] = PF::mma(a, z[k][ks], acc[k]);
         }
-        __syncthreads();
+    };
 
-        // ---- softmax phase: wave w owns heads w, w+8, w+16, w+24 ----
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int h = wave + 8 * j;
-            if (h < H) {
-                const float v = s_score[h * SC_STRIDE + lane];
-                const float m_new = fmaxf(m_run[j], wave_max(v));
-                const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_new);
-                const float pr = __builtin_amdgcn_exp2f(v - m_new);
-                l_run[j] = l_run[j] * alpha + wave_sum(pr);
-                m_run[j] = m_new;
-                s_p.store(h, lane, pr);
-                if (lane == 0) s_alpha[h] = alpha;
-            }
-        }
-        __syncthreads();
-
-        // ---- value phase ----
-        const bool partial = (t0 + kTile) > p.seq_len;
-#pragma unroll
-        for (int k = 0; k < NTV; ++k) {
-            const int nt = wave + 8 * k;
-            if (nt * 32 < rv) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 al = *reinterpret_cast<const f32x4*>(&s_alpha[8 * g + 4 * half]);
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) accv[k][4 * g + r4] *= al[r4];
-                }
-                const int ch = nt * 32 + (lane & 31);
-                const bool ch_ok = ch < rv;
-                const size_t zvb = (((size_t)b * nblk + tile) * rv + (ch_ok ? ch : 0)) * kTile;
-#pragma unroll
-                for (int ks = 0; ks < kTile / 16; ++ks) {
-                    const int tt = 16 * ks + 8 * half;
-                    Fr z = ch_ok ? load_frag<K>(p.zv, zvb + tt) : zero_frag<K>();
-                    if (partial) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (t0 + tt + e >= p.seq_len) z[e] = 0;
-                    }
-                    accv[k] = s_p.mma(lane & 31, tt, z, accv[k]);
-                }
-            }
-        }
+    if (nb > 0) load_blk(pA, zA, blk_begin);
+    for (int blk = blk_begin; blk < blk_end; blk += 2) {
+        if (blk + 1 < blk_end) load_blk(pB, zB, blk + 1);
+        compute_blk(pA, zA, blk);
+        if (blk + 2 < blk_end) load_blk(pA, zA, blk + 2);
+        if (blk + 1 < blk_end) compute_blk(pB, zB, blk + 1);
     }
 
-    // ---- partial results of this split ----
     const size_t part = (size_t)b * p.S + split;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int h = wave + 8 * j;
-        if (h < H && lane == 0) {
-            p.ws_ml[(part * H + h) * 2 + 0] = m_run[j];
-            p.ws_ml[(part * H + h) * 2 + 1] = l_run[j];
+    for (int k = 0; k < NTW; ++k) {
+        if (!chok[k]) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int h = acc_row(r, lane);
+            if (h < H) p.ws_acc[(part * H + h) * p.rv + ch[k]] = acc[k][r];
         }
     }
-#pragma unroll
-    for (int k = 0; k < NTV; ++k) {
-        const int nt = wave + 8 * k;
-        const int ch = nt * 32 + (lane & 31);
-        if (nt * 32 < rv && ch < rv) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int h = acc_row(r, lane);
-                if (h < H) p.ws_acc[(part * H + h) * rv + ch] = accv[k][r];
-            }
-        }
+    if (chunk == 0 && tid < H) {
+        p.ws_ml[(part * H + tid) * 2 + 0] = s_M[tid];
+        p.ws_ml[(part * H + tid) * 2 + 1] = s_L[tid];
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// Kernel 2: log-sum-exp merge of the splits, one workgroup per (b, h). Row width W.
+// 4. Log-sum-exp merge of the splits: thread per (b, h, 4 channels); the split weights
+// w_s = 2^(M_s - M) / sum_s 2^(M_s - M) L_s are recomputed per thread from the (small) split
+// statistics. Row width W (a multiple of 4).
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_splits(const MergeParams p) {
-    __shared__ float s_w[256];
-    __shared__ float s_inv_l;
-    const int bh = blockIdx.x;
+    const int W4 = p.W >> 2;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.B * p.H * W4) return;
+    const int c4 = (int)(idx % W4);
+    const int bh = (int)(idx / W4);
     const int b = bh / p.H, h = bh - b * p.H;
     const int S = p.active_splits;
-    if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[(((size_t)b * p.S + s) * p.H + h) * 2]);
-        float L = 0.0f;
-        for (int s = 0; s < S; ++s) {
-            const size_t o = (((size_t)b * p.S + s) * p.H + h) * 2;
-            const float w = __builtin_amdgcn_exp2f(p.ws_ml[o] - M);
-            s_w[s] = w;
-            L += w * p.ws_ml[o + 1];
-        }
-        s_inv_l = 1.0f / L;
+    const float* ml = p.ws_ml + ((size_t)b * p.S * p.H + h) * 2;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(size_t)s * p.H * 2]);
+    float L = 0.0f;
+    for (int s = 0; s < S; ++s) L += __builtin_amdgcn_exp2f(ml[(size_t)s * p.H * 2] - M) * ml[(size_t)s * p.H * 2 + 1];
+    const float inv_l = 1.0f / L;
+    const f32x4* acc = reinterpret_cast<const f32x4*>(p.ws_acc + ((size_t)b * p.S * p.H + h) * p.W) + c4;
+    const size_t sstride = (size_t)p.H * W4;
+    f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int s = 0; s < S; ++s) {
+        const float w = __builtin_amdgcn_exp2f(ml[(size_t)s * p.H * 2] - M) * inv_l;
+        const f32x4 v = acc[s * sstride];
+        a += w * v;
     }
-    __syncthreads();
-    const float inv_l = s_inv_l;
-    for (int c = threadIdx.x; c < p.W; c += 256) {
-        float a = 0.0f;
-        for (int s = 0; s < S; ++s) a += s_w[s] * p.ws_acc[(((size_t)b * p.S + s) * p.H + h) * p.W + c];
-        p.ws_a[((size_t)b * p.H + h) * p.W + c] = a * inv_l;
-    }
+    reinterpret_cast<f32x4*>(p.ws_a + ((size_t)b * p.H + h) * p.W)[c4] = a;
 }
 
 // ------------------------------------------------------------------------------------------------
-// Kernel 3: out[b][h][j0..j0+15] = sum_c a[b][h][c] * B_v[c][h*D + j], all b (chunks of 32).
-// Thread (cs = tid / 16, jj = tid % 16) sums channels c = cs + 16*k; LDS reduces over cs.
+// 5. Output projection: out[b][h][j] = sum_c a[b][h][c] * B_v[c][h*D + j]. Workgroup (h, 64-column
+// tile, chunk of 8 batches), 16 waves; wave w sums the channels c = w + 16*i with lane = column
+// (coalesced 128-byte rows of B_v) and the 8 batches' a[.][h][c] broadcast from LDS; the waves'
+// partial sums are reduced through LDS.
 // ------------------------------------------------------------------------------------------------
 template <int K>
 __device__ __forceinline__ float load_scalar(const void* base, size_t i);
@@ -325,120 +498,116 @@ template <> __device__ __forceinline__ float load_scalar<kBF16>(const void* base
     return bf16_bits_to_float(static_cast<const uint16_t*>(base)[i]);
 }
 
+constexpr int kProjBatch = 8;
+constexpr int kProjMaxRv = 2048;
+constexpr int kProjWaves = 16;
+
 template <int K>
-__global__ __launch_bounds__(256) void project_heads(const ProjectParams p) {
-    constexpr int BCH = 32;
-    __shared__ float s_red[16][BCH][17];
+__global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
+    __shared__ __attribute__((aligned(16))) float s_a[kProjMaxRv * kProjBatch];
+    __shared__ float s_red[kProjWaves][kProjBatch][64];
     const int h = blockIdx.x;
-    const int j0 = blockIdx.y * 16;
     const int tid = threadIdx.x;
-    const int jj = tid & 15, cs = tid >> 4;
-    const size_t HD = (size_t)p.H * p.D;
-    for (int b0 = 0; b0 < p.B; b0 += BCH) {
-        const int nb = min(BCH, p.B - b0);
-        float acc[BCH];
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) acc[i] = 0.0f;
-        for (int c = cs; c < p.rv; c += 16) {
-            const float w = load_scalar<K>(p.bv, (size_t)c * HD + (size_t)h * p.D + j0 + jj);
-            const float* arow = p.ws_a + ((size_t)b0 * p.H + h) * p.rv + c;
-#pragma unroll
-            for (int i = 0; i < BCH; ++i)
-                if (i < nb) acc[i] += arow[(size_t)i * p.H * p.rv] * w;
-        }
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) s_red[cs][i][jj] = acc[i];
-        __syncthreads();
-        for (int e = tid; e < nb * 16; e += 256) {
-            const int i = e >> 4, j = e & 15;
-            float v = 0.0f;
-            for (int k = 0; k < 16; ++k) v += s_red[k][i][j];
-            p.out[((size_t)(b0 + i) * p.H + h) * p.D + j0 + j] = v;
-        }
-        __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = blockIdx.y * 64 + lane;
+    const int b0 = blockIdx.z * kProjBatch;
+    const int nb = min(kProjBatch, p.B - b0);
+    for (int e = tid; e < kProjBatch * p.rv; e += 1024) {
+        const int bi = e / p.rv, c = e - bi * p.rv;
+        s_a[c * kProjBatch + bi] = bi < nb ? p.ws_a[((size_t)(b0 + bi) * p.H + h) * p.rv + c] : 0.0f;
     }
-}
-
-// ------------------------------------------------------------------------------------------------
-// Packing of the key factors into MFMA A-operand fragments: for head h (rank r, offset ko),
-// fragment (mt, ks) lane l holds B_k[ko + 16*ks + 8*(l/32) + j][32*mt + l%32], j = 0..7, stored
-// at ((ko*D) + ((mt*(r/16) + ks)*64 + l)*8 + j). One workgroup per head.
-// ------------------------------------------------------------------------------------------------
-struct PackParams {
-    const void* bk;
-    void* bkt;
-    int D, H;
-    int16_t koff[kMaxHeads + 1];
-    int16_t rank[kMaxHeads];
-};
-
-template <int K>
-__global__ __launch_bounds__(256) void pack_key_factors(const PackParams p) {
-    using T = typename Elem<K>::storage;
-    const int h = blockIdx.x;
-    const int ko = p.koff[h], nks = p.rank[h] >> 4;
-    const int total = p.D * p.rank[h];
-    const T* src = static_cast<const T*>(p.bk);
-    T* dst = static_cast<T*>(p.bkt) + (size_t)ko * p.D;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-        const int j = idx & 7;
-        const int l = (idx >> 3) & 63;
-        const int frag = idx >> 9;           // mt * nks + ks
-        const int mt = frag / nks, ks = frag - mt * nks;
-        const int dim = 32 * mt + (l & 31);
-        const int rr = 16 * ks + 8 * (l >> 5) + j;
-        dst[idx] = src[(size_t)(ko + rr) * p.D + dim];
+    __syncthreads();
+    float acc[kProjBatch];
+#pragma unroll
+    for (int i = 0; i < kProjBatch; ++i) acc[i] = 0.0f;
+    const bool colok = col < p.D;
+    const size_t HD = (size_t)p.H * p.D;
+    const size_t cbase = (size_t)h * p.D + (colok ? col : 0);
+#pragma unroll 8
+    for (int c = wave; c < p.rv; c += kProjWaves) {
+        const float w = load_scalar<K>(p.bv, (size_t)c * HD + cbase);
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_a[c * kProjBatch]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_a[c * kProjBatch + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[e] += a0[e] * w;
+            acc[4 + e] += a1[e] * w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kProjBatch; ++i) s_red[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (tid < kProjBatch * 64) {
+        const int i = tid >> 6, jc = tid & 63;
+        const int c2 = blockIdx.y * 64 + jc;
+        if (i < nb && c2 < p.D) {
+            float v = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kProjWaves; ++k) v += s_red[k][i][jc];
+            p.out[((size_t)(b0 + i) * p.H + h) * p.D + c2] = v;
+        }
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // Host launchers
 // ------------------------------------------------------------------------------------------------
-template <int D, int NTV, int K>
-static hipError_t launch_split_t(const LatentDecodeParams& p, hipStream_t st) {
-    hipLaunchKernelGGL((latent_decode_split<D, NTV, K>), dim3(p.S, p.B), dim3(512), 0, st, p);
+template <int D, int K, int MAXKS>
+static hipError_t launch_scores_t(const ScoreParams& p, int groups, int splits, hipStream_t st) {
+    hipLaunchKernelGGL((latent_scores<D, K, MAXKS>), dim3(splits, groups, p.B), dim3(512), 0, st, p);
     return hipGetLastError();
 }
 
 template <int D, int K>
-static hipError_t launch_split_d(const LatentDecodeParams& p, int ntv, hipStream_t st) {
-    switch (ntv) {
-    case 1: return launch_split_t<D, 1, K>(p, st);
-    case 2: return launch_split_t<D, 2, K>(p, st);
-    case 3: return launch_split_t<D, 3, K>(p, st);
-    case 4: return launch_split_t<D, 4, K>(p, st);
-    case 5: return launch_split_t<D, 5, K>(p, st);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <int K>
-static hipError_t launch_split_k(const LatentDecodeParams& p, int ntv, hipStream_t st) {
-    if (p.D == 128) return launch_split_d<128, K>(p, ntv, st);
-    if (p.D == 64) return launch_split_d<64, K>(p, ntv, st);
+static hipError_t launch_scores_d(const ScoreParams& p, int groups, int splits, int maxks, hipStream_t st) {
+    if (maxks <= 4) return launch_scores_t<D, K, 4>(p, groups, splits, st);
+    if (D == 128 && maxks <= 8) return launch_scores_t<D, K, (D == 128 ? 8 : 4)>(p, groups, splits, st);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_latent_split(const LatentDecodeParams& p, int elem, int ntv, hipStream_t st) {
+template <int K>
+static hipError_t launch_scores_k(const ScoreParams& p, int groups, int splits, int maxks, hipStream_t st) {
+    if (p.D == 128) return launch_scores_d<128, K>(p, groups, splits, maxks, st);
+    if (p.D == 64) return launch_scores_d<64, K>(p, groups, splits, maxks, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
+                                hipStream_t st) {
     switch (elem) {
-    case kF32: return launch_split_k<kF32>(p, ntv, st);
-    case kF16: return launch_split_k<kF16>(p, ntv, st);
-    case kBF16: return launch_split_k<kBF16>(p, ntv, st);
+    case kF32: return launch_scores_k<kF32>(p, groups, splits, maxks, st);
+    case kF16: return launch_scores_k<kF16>(p, groups, splits, maxks, st);
+    case kBF16: return launch_scores_k<kBF16>(p, groups, splits, maxks, st);
     default: return hipErrorInvalidValue;
     }
 }
 
+constexpr int kValueNTW = 2;
+int value_chunk_channels() { return kValueWaves * kValueNTW * 32; }
+
+hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, hipStream_t st) {
+    const dim3 grid(p.S, chunks, p.B);
+    switch (elem) {
+    case kF32: hipLaunchKernelGGL((latent_values<kF32, kValueNTW>), grid, dim3(256), 0, st, p); break;
+    case kF16: hipLaunchKernelGGL((latent_values<kF16, kValueNTW>), grid, dim3(256), 0, st, p); break;
+    case kBF16: hipLaunchKernelGGL((latent_values<kBF16, kValueNTW>), grid, dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_merge(const MergeParams& p, hipStream_t st) {
-    hipLaunchKernelGGL(merge_splits, dim3(p.B * p.H), dim3(256), 0, st, p);
+    const long long n = (long long)p.B * p.H * (p.W / 4);
+    hipLaunchKernelGGL(merge_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st) {
-    const dim3 grid(p.H, p.D / 16);
+    const dim3 grid(p.H, (p.D + 63) / 64, (p.B + kProjBatch - 1) / kProjBatch);
     switch (elem) {
-    case kF32: hipLaunchKernelGGL(project_heads<kF32>, grid, dim3(256), 0, st, p); break;
-    case kF16: hipLaunchKernelGGL(project_heads<kF16>, grid, dim3(256), 0, st, p); break;
-    case kBF16: hipLaunchKernelGGL(project_heads<kBF16>, grid, dim3(256), 0, st, p); break;
+    case kF32: hipLaunchKernelGGL(project_heads<kF32>, grid, dim3(1024), 0, st, p); break;
+    case kF16: hipLaunchKernelGGL(project_heads<kF16>, grid, dim3(1024), 0, st, p); break;
+    case kBF16: hipLaunchKernelGGL(project_heads<kBF16>, grid, dim3(1024), 0, st, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -451,12 +620,15 @@ hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16
     p.bkt = bkt;
     p.D = D;
     p.H = H;
+    p.Rk = koff[H];
     for (int h = 0; h <= H; ++h) p.koff[h] = koff[h];
     for (int h = 0; h < H; ++h) p.rank[h] = rank[h];
+    const int runs = p.Rk * D / 8;
+    const dim3 grid((runs + 255) / 256);
     switch (elem) {
-    case kF32: hipLaunchKernelGGL(pack_key_factors<kF32>, dim3(H), dim3(256), 0, st, p); break;
-    case kF16: hipLaunchKernelGGL(pack_key_factors<kF16>, dim3(H), dim3(256), 0, st, p); break;
-    case kBF16: hipLaunchKernelGGL(pack_key_factors<kBF16>, dim3(H), dim3(256), 0, st, p); break;
+    case kF32: hipLaunchKernelGGL(pack_key_factors<kF32>, grid, dim3(256), 0, st, p); break;
+    case kF16: hipLaunchKernelGGL(pack_key_factors<kF16>, grid, dim3(256), 0, st, p); break;
+    case kBF16: hipLaunchKernelGGL(pack_key_factors<kBF16>, grid, dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

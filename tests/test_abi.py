@@ -72,7 +72,7 @@ def test_decode_validation():
     assert st_decode(_latent(key_ranks=(0, 32, 48, 64)), Cc) == E["RANK"]
     assert st_decode(_latent(value_rank=100), Cc) == E["RANK"]
     assert st_decode(_latent(value_rank=4096), Cc) == E["RANK"]
-    assert st_decode(_latent(value_rank=1536), Cc) == E["UNSUP"]
+    assert st_decode(_latent(value_rank=2064), Cc) == E["RANK"]
     assert st_decode(_latent(num_heads=40, key_ranks=(16,) * 40), Cc) == E["UNSUP"]
     assert st_decode(_latent(head_dim=96), Cc) == E["UNSUP"]
     assert st_decode(L, _cache(capacity=100)) == E["CAP"]
