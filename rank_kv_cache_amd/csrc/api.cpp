@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kTargetWorkgroups = 256;   // MI355X compute units: one score workgroup per CU
 constexpr int kValueTargetWorkgroups = 768;   // three 4-wave value workgroups per CU
+constexpr int kMaxScoreRounds = 4;
 constexpr int kMaxSplits = 256;
 constexpr size_t kAlign = 256;
 constexpr int64_t kSmallAppend = 16;     // appends of up to this many tokens use one fused launch
@@ -154,14 +155,28 @@ bool plan_groups(const LayerInfo& li, int G, ScorePlan* sp) {
 
 ScorePlan plan_scores(const LayerInfo& li, int B, int nblk) {
     ScorePlan sp;
+    // one head per group always fits (a rank-d head needs at most d * d * 4 bytes of fragments)
     int G = 1;
-    while (G <= std::min(kMaxGroups, li.H) && !plan_groups(li, G, &sp)) ++G;
+    while (G < li.H && !plan_groups(li, G, &sp)) ++G;
+    if (G == li.H) plan_groups(li, G, &sp);
     int maxr = 0;
     for (int h = 0; h < li.H; ++h) maxr = std::max(maxr, static_cast<int>(li.rank[h]));
     sp.maxks = maxr / 16;
+    // One score workgroup fills a CU. Choose the split count so that the grid's last round of
+    // workgroups is as full as possible, preferring fewer rounds (each workgroup pays a prologue).
     const int per = std::max(1, B) * sp.G;
-    int S = (kTargetWorkgroups + per - 1) / per;
-    S = std::max(1, std::min(S, nblk));
+    int S = 1;
+    double best = -1.0;
+    for (int rounds = 1; rounds <= kMaxScoreRounds; ++rounds) {
+        const int s_try = std::max(1, std::min(nblk, rounds * kTargetWorkgroups / per));
+        const int wgs = per * s_try;
+        const int used = (wgs + kTargetWorkgroups - 1) / kTargetWorkgroups;
+        const double eff = static_cast<double>(wgs) / (used * kTargetWorkgroups);
+        if (eff > best + 0.02) {
+            best = eff;
+            S = s_try;
+        }
+    }
     sp.bpw = (nblk + S - 1) / S;
     sp.splits = (nblk + sp.bpw - 1) / sp.bpw;
     return sp;

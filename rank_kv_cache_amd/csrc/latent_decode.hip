@@ -25,6 +25,8 @@
 //  4. merge_splits: log-sum-exp weighted merge of the splits per (b, h), normalised.
 //  5. project_heads: out[b][h] = a[b][h] . B_v[:, h*d:(h+1)*d] for all b at once.
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace starkv {
@@ -211,38 +213,53 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         wave_sync_lds();
         const T* fr = &s_bk[s_slot[s]];
         float sc[2] = {0.0f, 0.0f};
+        // Key rebuild + RoPE + dot for a head of NKS rank steps, as straight-line code: the rank
+        // is dispatched once per unit, so no branch separates the MFMA chains from the RoPE
+        // arithmetic and the scheduler can overlap one pass's MFMAs with another's VALU work.
+        auto core = [&](auto nks_c) {
+            constexpr int NKS = decltype(nks_c)::value;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
-            for (int pp = 0; pp < HMT; ++pp) {
-                f32x16 acc0, acc1;
+                for (int pp = 0; pp < HMT; ++pp) {
+                    f32x16 acc0, acc1;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) { acc0[r] = 0.0f; acc1[r] = 0.0f; }
+                    for (int r = 0; r < 16; ++r) { acc0[r] = 0.0f; acc1[r] = 0.0f; }
 #pragma unroll
-                for (int ks = 0; ks < MAXKS; ++ks) {
-                    if (ks < nks) {
-                        const Fr a0 = *reinterpret_cast<const Fr*>(fr + ((pp * nks + ks) * 64 + lane) * 8);
-                        const Fr a1 = *reinterpret_cast<const Fr*>(fr + (((pp + HMT) * nks + ks) * 64 + lane) * 8);
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const Fr a0 = *reinterpret_cast<const Fr*>(fr + ((pp * NKS + ks) * 64 + lane) * 8);
+                        const Fr a1 = *reinterpret_cast<const Fr*>(fr + (((pp + HMT) * NKS + ks) * 64 + lane) * 8);
                         acc0 = mma32<K>(a0, z[nt][ks], acc0);
                         acc1 = mma32<K>(a1, z[nt][ks], acc1);
                     }
-                }
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int i0 = 32 * pp + 8 * g + 4 * half;
-                    const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0]);
-                    const f32x4 q2 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0 + NF]);
+                    for (int g = 0; g < 4; ++g) {
+                        const int i0 = 32 * pp + 8 * g + 4 * half;
+                        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0]);
+                        const f32x4 q2 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0 + NF]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float a = acc0[4 * g + r], bb = acc1[4 * g + r];
-                        const float c = cj[pp][g][r], sn = sj[pp][g][r];
-                        sc[nt] += q1[r] * (a * c - bb * sn) + q2[r] * (bb * c + a * sn);
+                        for (int r = 0; r < 4; ++r) {
+                            const float a = acc0[4 * g + r], bb = acc1[4 * g + r];
+                            const float c = cj[pp][g][r], sn = sj[pp][g][r];
+                            sc[nt] = fmaf(q1[r], fmaf(-bb, sn, a * c), sc[nt]);
+                            sc[nt] = fmaf(q2[r], fmaf(a, sn, bb * c), sc[nt]);
+                        }
                     }
+                    // consume the dot here, so the compiler cannot sink every pass's RoPE
+                    // arithmetic past all the MFMA chains (all accumulators would stay live)
+                    asm volatile("" : "+v"(sc[nt]));
                 }
-                // consume the dot here, so the compiler cannot sink every pass's RoPE arithmetic
-                // past all the MFMA chains (which would keep all accumulators live at once)
-                asm volatile("" : "+v"(sc[nt]));
             }
+        };
+        switch (nks) {
+        case 1: core(std::integral_constant<int, 1>{}); break;
+        case 2: core(std::integral_constant<int, 2>{}); break;
+        case 3: core(std::integral_constant<int, 3>{}); break;
+        case 4: core(std::integral_constant<int, (MAXKS >= 4 ? 4 : 1)>{}); break;
+        case 5: core(std::integral_constant<int, (MAXKS >= 5 ? 5 : 1)>{}); break;
+        case 6: core(std::integral_constant<int, (MAXKS >= 6 ? 6 : 1)>{}); break;
+        case 7: core(std::integral_constant<int, (MAXKS >= 7 ? 7 : 1)>{}); break;
+        default: core(std::integral_constant<int, MAXKS>{}); break;
         }
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) sc[nt] += __shfl_xor(sc[nt], 32, 64);
@@ -253,11 +270,9 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         const float pr = __builtin_amdgcn_exp2f(my - m);
         const float l = wave_sum(pr);
         Pout[((size_t)b * H + h) * Tp + tok] = (PT)pr;
-        if (lane == 0) {
-            float* st = stats + (((size_t)b * H + h) * nblk + blk) * 2;
-            st[0] = m;
-            st[1] = l;
-        }
+        // every lane stores (even lanes m, odd lanes l, to the same two words): no branch, so
+        // the count of memory operations in flight stays static
+        stats[(((size_t)b * H + h) * nblk + blk) * 2 + (lane & 1)] = (lane & 1) ? l : m;
         wave_sync_lds();
     };
 
@@ -346,42 +361,49 @@ __global__ __launch_bounds__(256) void latent_values(const ValueParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
     const int split = blockIdx.x;
     const int chunk = blockIdx.y;
     const int b = blockIdx.z;
     const int H = p.H;
+    const int seq_len = p.seq_len;
     const int blk_begin = split * p.blocks_per_split;
     const int blk_end = min(p.nblk, blk_begin + p.blocks_per_split);
     const int nb = blk_end - blk_begin;
 
-    // ---- split statistics per head: M = max m_blk, f_blk = 2^(m_blk - M), L = sum f_blk l_blk ----
+    // ---- split statistics per head: M = max m_blk, f_blk = 2^(m_blk - M), L = sum f l ----
     for (int h = wave; h < H; h += kValueWaves) {
-        const float* st = p.stats + ((size_t)b * H + h) * p.nblk * 2;
+        const float* st = p.stats + (((size_t)b * H + h) * p.nblk + blk_begin) * 2;
         float M = -INFINITY;
-        for (int i = lane; i < nb; i += 64) M = fmaxf(M, st[(blk_begin + i) * 2]);
+        for (int i = lane; i < nb; i += 64) M = fmaxf(M, st[2 * i]);
         M = wave_max(M);
         float L = 0.0f;
         for (int i = lane; i < nb; i += 64) {
-            const float f = __builtin_amdgcn_exp2f(st[(blk_begin + i) * 2] - M);
+            const float f = __builtin_amdgcn_exp2f(st[2 * i] - M);
             s_f[h][i] = f;
-            L += f * st[(blk_begin + i) * 2 + 1];
+            L += f * st[2 * i + 1];
         }
         L = wave_sum(L);
         if (lane == 0) { s_M[h] = M; s_L[h] = L; }
     }
     __syncthreads();
 
+    // Rows (heads) >= H and channels >= r_v only feed output rows / columns that are never
+    // stored, so their operands are loaded from a clamped valid address without masking; all
+    // loads are unconditional, which keeps the compiler's in-order wait counts exact.
     const int hrow = lane & 31;
     const bool hvalid = hrow < H;
     const int cgroups = p.rv >> 4;
     int ch[NTW];
     bool chok[NTW];
+    size_t zoff[NTW];
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {
         ch[k] = ((chunk * kValueWaves + wave) * NTW + k) * 32 + (lane & 31);
         chok[k] = ch[k] < p.rv;
+        const int cc = min(ch[k], p.rv - 1);
+        zoff[k] = (size_t)(cc >> 4) * 1024 + (cc & 15) * 16 + 8 * half;
     }
     f32x16 acc[NTW];
 #pragma unroll
@@ -391,31 +413,27 @@ __global__ __launch_bounds__(256) void latent_values(const ValueParams p) {
 
     typename PF::Raw pA[4], pB[4];
     Fr zA[NTW][4], zB[NTW][4];
-    const size_t prow = ((size_t)b * H + (hvalid ? hrow : 0)) * p.Tp + 8 * half;
+    const size_t prow = ((size_t)b * H + min(hrow, H - 1)) * p.Tp + 8 * half;
 
     auto load_blk = [&](typename PF::Raw (&pr)[4], Fr (&z)[NTW][4], int blk) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            pr[ks] = hvalid ? PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks) : PF::zero();
-        const size_t bbase = ((size_t)b * p.nblk_cap + blk) * cgroups;
+        for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
+        const size_t bbase = ((size_t)b * p.nblk_cap + blk) * cgroups * 1024;
 #pragma unroll
         for (int k = 0; k < NTW; ++k)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                z[k][ks] = chok[k] ? load_frag<K>(p.zv, (bbase + (ch[k] >> 4)) * 1024 + ks * 256 +
-                                                        (ch[k] & 15) * 16 + 8 * half)
-                                   : zero_frag<K>();
+            for (int ks = 0; ks < 4; ++ks) z[k][ks] = load_frag<K>(p.zv, bbase + zoff[k] + ks * 256);
     };
     auto compute_blk = [&](const typename PF::Raw (&pr)[4], Fr (&z)[NTW][4], int blk) {
         const float f = hvalid ? s_f[hrow][blk - blk_begin] : 0.0f;
-        if ((blk + 1) * 64 > p.seq_len) {                  // ragged last block: zero the tail
+        if ((blk + 1) * 64 > seq_len) {                    // ragged last block: zero the tail
 #pragma unroll
             for (int k = 0; k < NTW; ++k)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        if (blk * 64 + 16 * ks + 8 * half + e >= p.seq_len) z[k][ks][e] = 0;
+                        if (blk * 64 + 16 * ks + 8 * half + e >= seq_len) z[k][ks][e] = 0;
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -427,9 +445,9 @@ __global__ __launch_bounds__(256) void latent_values(const ValueParams p) {
 
     if (nb > 0) load_blk(pA, zA, blk_begin);
     for (int blk = blk_begin; blk < blk_end; blk += 2) {
-        if (blk + 1 < blk_end) load_blk(pB, zB, blk + 1);
+        load_blk(pB, zB, min(blk + 1, blk_end - 1));
         compute_blk(pA, zA, blk);
-        if (blk + 2 < blk_end) load_blk(pA, zA, blk + 2);
+        load_blk(pA, zA, min(blk + 2, blk_end - 1));
         if (blk + 1 < blk_end) compute_blk(pB, zB, blk + 1);
     }
 
