@@ -169,8 +169,8 @@ starkv_status starkv_decode_attn_timed(const starkv_layer *layer, const starkv_c
 /*
  * Read cached tokens [t0, t1) back in token-major order: zk_out [B][t1-t0][R_k] (dense: H*d) and
  * zv_out [B][t1-t0][r_v] (dense: H*d). Element type: fp16 for Q43 (codes of complete groups are
- * dequantised as binary16(fmaf(code, scale, zero)); rows of the unfinished group come from the
- * tail), otherwise the cache element type (a plain gather). seq_len is the number of tokens
+ * dequantised as binary16(code * scale + zero), the exact value rounded once to nearest-even;
+ * rows of the unfinished group come from the tail), otherwise the cache element type (a plain gather). seq_len is the number of tokens
  * appended so far (Q43: decides which groups are complete). Either output may be NULL to skip it.
  * Errors: NULL (cache buffers), SHAPE (t0 < 0 or t0 > t1), CAPACITY (t1 > seq_len or seq_len >
  * capacity), DTYPE, MISALIGNED.

@@ -505,7 +505,9 @@ int orc_rotate_factor_f16(int C, int ncols, int nseg, const int *seg, const uint
 /*   s16      = binary16(s) (nearest-even);   z16 = binary16(mn), -0 stored as +0               */
 /*   code     = 0 if s16 == 0, else clamp(rint((float(x) - z) / s), 0, 2^bits - 1) with z, s    */
 /*              the fp32 values of z16, s16; fp32 subtract and divide, rint ties to even        */
-/*   dequant  = binary16(fmaf(code, s, z))                          one fp32 fused multiply-add */
+/*   dequant  = binary16(code * s + z), the exact value rounded once (nearest-even). Every   */
+/*              binary16 is an integer multiple of 2^-24 and |code * s + z| < 2^21, so the     */
+/*              exact value is an integer times 2^-24 below 2^45 and fp64 holds it exactly.    */
 /*                                                                                              */
 /* Packed layout of one channel's 64 codes (little-endian bytes):                               */
 /*   4 bits: 32 bytes; token t sits in byte t/2, low nibble for even t.                         */
@@ -572,8 +574,8 @@ int orc_unpack_code(const uint8_t *codes, int bits, int t)
 
 uint16_t orc_dequant_value(int code, uint16_t s16, uint16_t z16)
 {
-    float r = fmaf((float)code, f16_to_f32(s16), f16_to_f32(z16));
-    return orc_f64_to_f16((double)r);
+    double exact = (double)code * orc_f16_to_f64(s16) + orc_f16_to_f64(z16);
+    return orc_f64_to_f16(exact);
 }
 
 /* Bytes of one 64-token block of a latent whose channel c has bits[c] bits: sum of 8*bits. */

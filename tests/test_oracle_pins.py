@@ -365,6 +365,25 @@ def test_quantiser_golden(name):
         assert got == want
 
 
+def test_dequant_is_single_rounding_of_exact_value():
+    """x^ = binary16(q*s + z) rounded once: pinned to exact rational arithmetic (Python
+    fractions) followed by numpy's nearest-even binary16 conversion, over random codes and random
+    finite binary16 scales and zero points, including subnormals and values near the overflow."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    bits = rng.integers(0, 0x7C00, size=4000).astype(np.uint16)          # finite, non-negative
+    zbits = rng.integers(0, 0xFC00, size=4000).astype(np.uint16)
+    zbits = np.where((zbits >= 0x7C00) & (zbits < 0x8000), zbits - 0x7C00, zbits).astype(np.uint16)
+    for i in range(4000):
+        q = int(rng.integers(0, 16))
+        s = Fraction(float(bits[i:i + 1].view(np.float16)[0]))
+        z = Fraction(float(zbits[i:i + 1].view(np.float16)[0]))
+        exact = q * s + z
+        want = np.array([float(exact)], dtype=np.float64).astype(np.float16).view(np.uint16)[0]
+        assert float(exact) == exact                                 # representable in fp64
+        assert oracle.dequant_value(q, int(bits[i]), int(zbits[i])) == int(want), (q, bits[i], zbits[i])
+
+
 def test_quantiser_bounds_random():
     rng = np.random.default_rng(11)
     for trial in range(300):
