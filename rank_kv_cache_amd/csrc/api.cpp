@@ -27,6 +27,8 @@ hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
 hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st);
+hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t st);
+hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st);
 }  // namespace starkv
 
 using namespace starkv;
@@ -54,6 +56,7 @@ struct LayerInfo {
     int H = 0, D = 0, rv = 0, Rk = 0;
     bool dense = false, q43 = false;
     int cache_dt = 0, factor_dt = 0;
+    double top_fraction = 0.0;
     int16_t koff[kMaxHeads + 1] = {0};
     int16_t rank[kMaxHeads] = {0};
 };
@@ -97,6 +100,8 @@ starkv_status check_layer(const starkv_layer* L, LayerInfo* out) {
         if (L->q_group != 64) return STARKV_ERR_UNSUPPORTED;
         if (L->q_bits_hi != 4 || L->q_bits_lo != 3) return STARKV_ERR_UNSUPPORTED;
         if (!(L->q_top_fraction >= 0.0f && L->q_top_fraction <= 1.0f)) return STARKV_ERR_SHAPE;
+        if (li.Rk > kMaxKeyGroups * 16) return STARKV_ERR_UNSUPPORTED;
+        li.top_fraction = L->q_top_fraction;
     }
     *out = li;
     return STARKV_OK;
@@ -117,6 +122,38 @@ starkv_status check_cache(const starkv_cache* c, const LayerInfo& li) {
     }
     return STARKV_OK;
 }
+
+// Channels of a latent of width r kept at 4 bits: the leading ceil(top_fraction * r) (a 1e-9
+// guard keeps products that are integers in exact arithmetic from being pushed up).
+int q43_hi_channels(int r, double frac) {
+    const int n = static_cast<int>(std::ceil(frac * r - 1e-9));
+    return std::max(0, std::min(r, n));
+}
+
+void q43_layouts(const LayerInfo& li, Q43Layout* K, Q43Layout* V) {
+    std::memset(K, 0, sizeof(*K));
+    std::memset(V, 0, sizeof(*V));
+    K->C = li.Rk;
+    K->is_key = 1;
+    int off = 0, g = 0;
+    for (int h = 0; h < li.H; ++h) {
+        const int r = li.rank[h];
+        const int nh = q43_hi_channels(r, li.top_fraction);
+        for (int k = 0; k < r / 16; ++k, ++g) {
+            const int n = std::max(0, std::min(16, nh - 16 * k));
+            K->gn[g] = static_cast<uint8_t>(n);
+            K->goff[g] = off;
+            off += 384 + 8 * n;
+        }
+    }
+    K->block_bytes = off;
+    V->C = li.rv;
+    V->is_key = 0;
+    V->n_hi = q43_hi_channels(li.rv, li.top_fraction);
+    V->block_bytes = 32 * V->n_hi + 24 * (li.rv - V->n_hi);
+}
+
+constexpr size_t kQ43CodePad = 32;   // readers load aligned windows that may pass a block's end
 
 // Score-kernel head groups: the heads are dealt to G groups with balanced rank sums
 // (longest-processing-time-first greedy); G is the smallest count whose largest group's factor
@@ -302,7 +339,16 @@ starkv_status starkv_cache_bytes(const starkv_layer* layer, int32_t batch, int32
         out_bytes[1] = Bc * li.rv * elem_bytes(li.cache_dt);
         return STARKV_OK;
     }
-    return STARKV_ERR_UNSUPPORTED;
+    Q43Layout K, V;
+    q43_layouts(li, &K, &V);
+    const size_t nb = static_cast<size_t>(batch) * (capacity / kTile);
+    out_bytes[0] = nb * K.block_bytes + kQ43CodePad;
+    out_bytes[1] = nb * V.block_bytes + kQ43CodePad;
+    out_bytes[2] = nb * li.Rk * 4;
+    out_bytes[3] = nb * li.rv * 4;
+    out_bytes[4] = static_cast<size_t>(batch) * kTile * li.Rk * 2;
+    out_bytes[5] = static_cast<size_t>(batch) * kTile * li.rv * 2;
+    return STARKV_OK;
 }
 
 size_t starkv_decode_workspace_bytes(const starkv_layer* layer, int32_t batch, int64_t seq_len,
@@ -325,10 +371,48 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
     if (n_new == 0 || cache->batch == 0) return STARKV_OK;
     if (!zk_new || !zv_new) return STARKV_ERR_NULL;
     if (!aligned16(zk_new) || !aligned16(zv_new)) return STARKV_ERR_MISALIGNED;
-    if (li.q43) return STARKV_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int B = cache->batch;
     const int es = elem_bytes(li.cache_dt);
+    if (li.q43) {
+        // complete the groups this append finishes (quantise), then keep the rows of the
+        // unfinished group in the tail
+        Q43Layout K, V;
+        q43_layouts(li, &K, &V);
+        const int g_first = static_cast<int>(pos / kTile);
+        const int ngroups = static_cast<int>((pos + n_new) / kTile) - g_first;
+        for (int which = 0; which < 2; ++which) {
+            Q43QuantParams q;
+            q.L = which ? V : K;
+            q.src = which ? zv_new : zk_new;
+            q.tail = which ? cache->zv_tail : cache->zk_tail;
+            q.codes = which ? cache->zv : cache->zk;
+            q.meta = which ? cache->zv_meta : cache->zk_meta;
+            q.B = B;
+            q.nblk_cap = cache->capacity / kTile;
+            q.g_first = g_first;
+            q.pos = pos;
+            q.n = n_new;
+            if ((s = dev(launch_q43_quantize(q, ngroups, st))) != STARKV_OK) return s;
+        }
+        const int64_t t_begin = std::max<int64_t>(pos, (pos + n_new) / kTile * kTile);
+        const int64_t t_end = pos + n_new;
+        if (t_end > t_begin) {
+            for (int which = 0; which < 2; ++which) {
+                const long long row = static_cast<long long>(which ? li.rv : li.Rk) * 2;
+                RowCopyParams p;
+                p.src = static_cast<const char*>(which ? zv_new : zk_new);
+                p.dst = static_cast<char*>(which ? cache->zv_tail : cache->zk_tail);
+                p.src_seq_stride = n_new * row;
+                p.dst_seq_stride = kTile * row;
+                p.src_off = (t_begin - pos) * row;
+                p.dst_off = (t_begin % kTile) * row;
+                p.bytes = (t_end - t_begin) * row;
+                if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
+            }
+        }
+        return STARKV_OK;
+    }
     if (li.dense) {
         const long long cap = cache->capacity;
         const long long row = static_cast<long long>(li.H) * li.D * es;
@@ -532,11 +616,31 @@ starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cach
     if (seq_len > cache->capacity || t1 > seq_len) return STARKV_ERR_CAPACITY;
     if ((zk_out && !aligned16(zk_out)) || (zv_out && !aligned16(zv_out))) return STARKV_ERR_MISALIGNED;
     if (cache->batch == 0 || t0 == t1) return STARKV_OK;
-    if (li.q43) return STARKV_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int B = cache->batch;
     const int es = elem_bytes(li.cache_dt);
     const long long cap = cache->capacity, n = t1 - t0;
+    if (li.q43) {
+        Q43Layout K, V;
+        q43_layouts(li, &K, &V);
+        for (int which = 0; which < 2; ++which) {
+            void* outp = which ? zv_out : zk_out;
+            if (!outp) continue;
+            Q43ReadParams r;
+            r.L = which ? V : K;
+            r.codes = which ? cache->zv : cache->zk;
+            r.meta = which ? cache->zv_meta : cache->zk_meta;
+            r.tail = which ? cache->zv_tail : cache->zk_tail;
+            r.out = outp;
+            r.B = B;
+            r.nblk_cap = cache->capacity / kTile;
+            r.t0 = t0;
+            r.t1 = t1;
+            r.full_tokens = seq_len / kTile * kTile;
+            if ((s = dev(launch_q43_readback(r, st))) != STARKV_OK) return s;
+        }
+        return STARKV_OK;
+    }
     if (li.dense) {
         const long long row = static_cast<long long>(li.H) * li.D * es;
         for (int which = 0; which < 2; ++which) {

@@ -213,4 +213,42 @@ struct AppendSmallParams {
     long long pos, n;
 };
 
+// Mixed 4/3-bit code layout of one latent (see quant.hip for the byte layout).
+constexpr int kMaxKeyGroups = 256;          // R_k <= 4096
+struct Q43Layout {
+    int C;                      // channels of the latent
+    int block_bytes;            // code bytes per 64-token block
+    int is_key;                 // 1: token-major key layout, 0: channel-major value layout
+    int n_hi;                   // value latent: channels [0, n_hi) are 4-bit
+    int32_t goff[kMaxKeyGroups];   // key latent: byte offset of 16-channel group g in a block
+    uint8_t gn[kMaxKeyGroups];     // key latent: 4-bit channels at the start of group g
+};
+
+__host__ __device__ inline bool q43_is_hi(const Q43Layout& L, int c) {
+    return L.is_key ? (c & 15) < L.gn[c >> 4] : c < L.n_hi;
+}
+__host__ __device__ inline int q43_value_run_offset(const Q43Layout& L, int c) {
+    return c < L.n_hi ? 32 * c : 32 * L.n_hi + 24 * (c - L.n_hi);
+}
+
+struct Q43QuantParams {
+    Q43Layout L;
+    const void* src;            // new rows [B][n][C] binary16
+    const void* tail;           // [B][64][C] binary16
+    void* codes;                // [B][cap/64][block_bytes]
+    void* meta;                 // [B][cap/64][C][2] binary16
+    int B, nblk_cap, g_first;
+    long long pos, n;
+};
+
+struct Q43ReadParams {
+    Q43Layout L;
+    const void* codes;
+    const void* meta;
+    const void* tail;
+    void* out;                  // [B][t1 - t0][C] binary16
+    int B, nblk_cap;
+    long long t0, t1, full_tokens;   // tokens below full_tokens sit in complete groups
+};
+
 }  // namespace starkv

@@ -1,0 +1,231 @@
+// quant.hip -- mixed 4/3-bit latent cache (gfx950): quantise whole 64-token groups on append and
+// read them back (Zhou, STAR-KV reading notes, section 6.1 and Algorithm 2 step 3: the new
+// token's latents are quantised, then appended; low-rank-aware mixed precision keeps the leading
+// channels of each latent at 4 bits and the rest at 3 bits).
+//
+// Per (channel, 64-token group), asymmetric with a binary16 scale and zero point:
+//   s = (max - min) / (2^bits - 1) in fp32, s16 = binary16(s) (0 when max == min),
+//   z16 = binary16(min) (a zero is stored as +0),
+//   q = 0 if s16 == 0, else clamp(rint_even((x - z16) / s16), 0, 2^bits - 1), fp32 arithmetic,
+//   x^ = binary16(q * s16 + z16), the exact value rounded once (one fp16 FMA).
+//
+// Code layouts of one 64-token block (bytes per block: Q43Layout::block_bytes):
+//  * key latent (token-major, consumed as MFMA operands of eight channels of one token): 16-channel
+//    groups, group g at byte goff[g], holding 64 rows of 48 + n bits (n = gn[g] = 4-bit channels
+//    at the start of the group); row t starts at bit t * (48 + n) of the group; in a row, bits
+//    3e .. 3e+2 are the low three bits of channel e, and bit 48 + e the fourth bit of channel
+//    e < n. Bits are little-endian in little-endian 32-bit words.
+//  * value latent (channel-major, consumed as operands of eight tokens of one channel): channel c
+//    at byte 32c (4-bit, c < n_hi) or 32 n_hi + 24 (c - n_hi) (3-bit); 4-bit run: token t in
+//    byte t/2, low nibble for even t; 3-bit run: bytes 0..15 hold the low two bits (token t at
+//    bits 2(t%4) of byte t/4), bytes 16..23 the third bit (token t at bit t%8 of byte 16 + t/8).
+//  * meta [B][cap/64][C][2] binary16 (scale, zero); tail [B][64][C] binary16 holds the rows of
+//    the unfinished group.
+
+#include "common.hpp"
+
+namespace starkv {
+
+__device__ __forceinline__ uint16_t f16_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+__device__ __forceinline__ _Float16 bits_f16(uint16_t u) { return __builtin_bit_cast(_Float16, u); }
+
+// Quantiser of one value (see the header comment); IEEE fp32 subtract, divide and rint.
+__device__ __forceinline__ int q43_code(_Float16 x, uint16_t s16, uint16_t z16, int qmax) {
+    if ((s16 & 0x7fffu) == 0) return 0;
+    const float v = ((float)x - (float)bits_f16(z16)) / (float)bits_f16(s16);
+    float r = __builtin_rintf(v);
+    r = fminf(fmaxf(r, 0.0f), (float)qmax);
+    return (int)r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// Quantise complete groups: workgroup per (group, 64-channel chunk, sequence). The group's 64 rows
+// are gathered from the tail (tokens appended by earlier calls) and the new rows.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void q43_quantize(const Q43QuantParams p) {
+    __shared__ _Float16 x[64][65];
+    __shared__ float s_mn[4][64], s_mx[4][64];
+    __shared__ uint16_t s_s[64], s_z[64];
+    __shared__ uint8_t code[64][65];
+    __shared__ uint32_t words[4][136];
+
+    const Q43Layout& L = p.L;
+    const int tid = threadIdx.x;
+    const int g = p.g_first + blockIdx.x;
+    const int c0 = blockIdx.y * 64;
+    const int b = blockIdx.z;
+    const int C = L.C;
+    const long long tok0 = (long long)g * 64;
+    const _Float16* src = static_cast<const _Float16*>(p.src);
+    const _Float16* tail = static_cast<const _Float16*>(p.tail);
+
+    for (int e = tid; e < 64 * 64; e += 256) {
+        const int t = e >> 6, cc = e & 63, c = c0 + cc;
+        const long long tok = tok0 + t;
+        _Float16 v = (_Float16)0.0f;
+        if (c < C)
+            v = tok < p.pos ? tail[((size_t)b * 64 + t) * C + c]
+                            : src[((size_t)b * p.n + (tok - p.pos)) * C + c];
+        x[t][cc] = v;
+    }
+    __syncthreads();
+    {
+        const int cc = tid & 63, part = tid >> 6;
+        float mn = INFINITY, mx = -INFINITY;
+        for (int t = 16 * part; t < 16 * part + 16; ++t) {
+            const float v = (float)x[t][cc];
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+        }
+        s_mn[part][cc] = mn;
+        s_mx[part][cc] = mx;
+    }
+    __syncthreads();
+    if (tid < 64 && c0 + tid < C) {
+        const int c = c0 + tid;
+        float mn = s_mn[0][tid], mx = s_mx[0][tid];
+        for (int k = 1; k < 4; ++k) {
+            mn = fminf(mn, s_mn[k][tid]);
+            mx = fmaxf(mx, s_mx[k][tid]);
+        }
+        const int qmax = q43_is_hi(L, c) ? 15 : 7;
+        const float diff = mx - mn;
+        const uint16_t s16 = diff == 0.0f ? 0 : f16_bits((_Float16)(diff / (float)qmax));
+        uint16_t z16 = f16_bits((_Float16)mn);
+        if (z16 == 0x8000u) z16 = 0;
+        s_s[tid] = s16;
+        s_z[tid] = z16;
+        uint16_t* meta = static_cast<uint16_t*>(p.meta) + (((size_t)b * p.nblk_cap + g) * C + c) * 2;
+        meta[0] = s16;
+        meta[1] = z16;
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * 64; e += 256) {
+        const int t = e >> 6, cc = e & 63, c = c0 + cc;
+        code[t][cc] = c < C ? (uint8_t)q43_code(x[t][cc], s_s[cc], s_z[cc], q43_is_hi(L, c) ? 15 : 7) : 0;
+    }
+    __syncthreads();
+
+    uint8_t* blk = static_cast<uint8_t*>(p.codes) + ((size_t)b * p.nblk_cap + g) * L.block_bytes;
+    if (!L.is_key) {
+        // value latent: thread per channel writes its whole run
+        if (tid < 64 && c0 + tid < C) {
+            const int c = c0 + tid;
+            uint32_t* run = reinterpret_cast<uint32_t*>(blk + q43_value_run_offset(L, c));
+            if (q43_is_hi(L, c)) {
+                for (int w = 0; w < 8; ++w) {
+                    uint32_t v = 0;
+                    for (int k = 0; k < 8; ++k) v |= (uint32_t)code[8 * w + k][tid] << (4 * k);
+                    run[w] = v;
+                }
+            } else {
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t v = 0;
+                    for (int k = 0; k < 16; ++k) v |= (uint32_t)(code[16 * w + k][tid] & 3u) << (2 * k);
+                    run[w] = v;
+                }
+                for (int w = 0; w < 2; ++w) {
+                    uint32_t v = 0;
+                    for (int k = 0; k < 32; ++k) v |= (uint32_t)((code[32 * w + k][tid] >> 2) & 1u) << k;
+                    run[4 + w] = v;
+                }
+            }
+        }
+        return;
+    }
+    // key latent: thread (group gl in chunk, token t) ORs its row into an LDS image of the group
+    for (int e = tid; e < 4 * 136; e += 256) (&words[0][0])[e] = 0u;
+    __syncthreads();
+    const int gl = tid >> 6, t = tid & 63;
+    const int g16 = (c0 >> 4) + gl;
+    const bool gok = c0 + 16 * gl < C;
+    int n = 0;
+    if (gok) {
+        n = L.gn[g16];
+        uint64_t row = 0;
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t q = code[t][16 * gl + e];
+            row |= (uint64_t)(q & 7u) << (3 * e);
+            if (e < n) row |= (uint64_t)((q >> 3) & 1u) << (48 + e);
+        }
+        const int bit = t * (48 + n);
+        const int w0 = bit >> 5, sh = bit & 31;
+        // the row's bits i land at bit sh + i of words w0, w0 + 1, w0 + 2
+        atomicOr(&words[gl][w0], (uint32_t)(row << sh));
+        atomicOr(&words[gl][w0 + 1], (uint32_t)(row >> (32 - sh)));
+        if (sh) atomicOr(&words[gl][w0 + 2], (uint32_t)(row >> (64 - sh)));
+    }
+    __syncthreads();
+    if (gok) {
+        const int nwords = (384 + 8 * n) / 4;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(blk + L.goff[g16]);
+        for (int w = t; w < nwords; w += 64) dst[w] = words[gl][w];
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Read-back: rows [t0, t1) of a latent as binary16, thread per (sequence, token, 8 channels).
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int q43_key_code(const uint8_t* blk, const Q43Layout& L, int c, int t) {
+    const int g16 = c >> 4, e = c & 15, n = L.gn[g16];
+    const uint8_t* gb = blk + L.goff[g16];
+    const int rowbit = t * (48 + n);
+    auto bit = [&](int i) -> uint32_t { return (gb[i >> 3] >> (i & 7)) & 1u; };
+    uint32_t q = bit(rowbit + 3 * e) | (bit(rowbit + 3 * e + 1) << 1) | (bit(rowbit + 3 * e + 2) << 2);
+    if (e < n) q |= bit(rowbit + 48 + e) << 3;
+    return (int)q;
+}
+
+__device__ __forceinline__ int q43_value_code(const uint8_t* blk, const Q43Layout& L, int c, int t) {
+    const uint8_t* run = blk + q43_value_run_offset(L, c);
+    if (q43_is_hi(L, c)) return (run[t >> 1] >> (4 * (t & 1))) & 15;
+    return ((run[t >> 2] >> (2 * (t & 3))) & 3) | (((run[16 + (t >> 3)] >> (t & 7)) & 1) << 2);
+}
+
+__device__ __forceinline__ _Float16 q43_dequant(int q, uint16_t s16, uint16_t z16) {
+    return __builtin_fmaf16((_Float16)q, bits_f16(s16), bits_f16(z16));
+}
+
+__global__ __launch_bounds__(256) void q43_readback(const Q43ReadParams p) {
+    const Q43Layout& L = p.L;
+    const int runs = L.C >> 3;
+    const long long n = p.t1 - p.t0;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.B * n * runs) return;
+    const int run = (int)(idx % runs);
+    const long long bt = idx / runs;
+    const long long tok = p.t0 + bt % n;
+    const int b = (int)(bt / n);
+    const int c = run * 8;
+    _Float16 v[8];
+    if (tok < p.full_tokens) {
+        const int g = (int)(tok >> 6), t = (int)(tok & 63);
+        const uint8_t* blk = static_cast<const uint8_t*>(p.codes) + ((size_t)b * p.nblk_cap + g) * L.block_bytes;
+        const uint16_t* meta = static_cast<const uint16_t*>(p.meta) + (((size_t)b * p.nblk_cap + g) * L.C + c) * 2;
+        for (int e = 0; e < 8; ++e) {
+            const int q = L.is_key ? q43_key_code(blk, L, c + e, t) : q43_value_code(blk, L, c + e, t);
+            v[e] = q43_dequant(q, meta[2 * e], meta[2 * e + 1]);
+        }
+    } else {
+        const _Float16* tail = static_cast<const _Float16*>(p.tail) + ((size_t)b * 64 + (tok & 63)) * L.C + c;
+        for (int e = 0; e < 8; ++e) v[e] = tail[e];
+    }
+    _Float16* dst = static_cast<_Float16*>(p.out) + (size_t)bt * L.C + c;
+    for (int e = 0; e < 8; ++e) dst[e] = v[e];
+}
+
+hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t st) {
+    if (ngroups <= 0) return hipSuccess;
+    const dim3 grid(ngroups, (p.L.C + 63) / 64, p.B);
+    hipLaunchKernelGGL(q43_quantize, grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st) {
+    const long long n = (long long)p.B * (p.t1 - p.t0) * (p.L.C / 8);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(q43_readback, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace starkv
