@@ -36,13 +36,22 @@
  *  - dense (exempt) layer, F32/F16/BF16: zk = K, zv = V, both [B][capacity][H*d] token-major;
  *      keys are stored pre-RoPE.
  *  - latent layer, Q43 (mixed 4/3-bit, see starkv_layer): for each latent (zk with C = R_k
- *      channels, zv with C = r_v), channel j of a latent of width r is "hi" (q_bits_hi bits) when
- *      j < ceil(q_top_fraction * r), else "lo" (q_bits_lo bits); per 64-token block:
- *      zk / zv:           [B][capacity/64][block_bytes], channel c occupying 8*bits(c) bytes at
- *                         offset sum_{c'<c} 8*bits(c'). 4-bit: token t in byte t/2, low nibble for
- *                         even t. 3-bit: bytes 0..15 hold the low two bits (token t in byte t/4 at
- *                         bit 2*(t%4)), bytes 16..23 the third bit (token t in byte 16+t/8, bit t%8).
- *      zk_meta / zv_meta: [B][capacity/64][C][2] fp16 (scale, zero).
+ *      channels, the heads' latents concatenated; zv with C = r_v), channel j of a latent of
+ *      width r (each head's key latent, the value latent) is "hi" (q_bits_hi = 4 bits) when
+ *      j < ceil(q_top_fraction * r), else "lo" (q_bits_lo = 3 bits). Per 64-token block:
+ *      zk:  [B][capacity/64][key_block_bytes]: 16-channel groups in channel order, group g
+ *           holding 64 token rows of 48 + n_g bits (n_g = 4-bit channels at the start of the
+ *           group); row t starts at bit t*(48 + n_g) of the group; bits 3e..3e+2 of a row are
+ *           the low three bits of channel e of the group, bit 48+e the fourth bit of channel
+ *           e < n_g. key_block_bytes = 24*R_k + 8*(number of 4-bit key channels).
+ *      zv:  [B][capacity/64][value_block_bytes]: channel c's 64 codes at byte 32c when 4-bit,
+ *           32*n_hi + 24*(c - n_hi) when 3-bit. 4-bit: token t in byte t/2, low nibble for even
+ *           t. 3-bit: bytes 0..15 hold the low two bits (token t in byte t/4 at bit 2*(t%4)),
+ *           bytes 16..23 the third bit (token t in byte 16 + t/8, bit t%8).
+ *      Bits are little-endian in little-endian bytes; both code buffers carry 32 bytes of
+ *      padding at the end (readers load aligned windows).
+ *      zk_meta / zv_meta: [B][capacity/64][2][C] fp16: per block the scales of all channels,
+ *           then their zero points.
  *      zk_tail / zv_tail: [B][64][C] fp16: rows of the unfinished last group.
  *    Use starkv_cache_bytes() for every buffer size.
  */

@@ -484,7 +484,6 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     const WorkspaceLayout w = workspace_layout(li, B, seq_len, num_splits);
     if (!workspace || workspace_bytes < w.total) return STARKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return STARKV_ERR_MISALIGNED;
-    if (li.q43) return STARKV_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
     if (li.dense) {
@@ -546,8 +545,17 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     for (int h = 0; h <= li.H; ++h) sp.koff[h] = li.koff[h];
     for (int h = 0; h < li.H; ++h) sp.rank[h] = li.rank[h];
     fill_rope(layer->rope_base, li.D, sp.rope_rev);
+    Q43Layout qk, qv;
+    if (li.q43) {
+        q43_layouts(li, &qk, &qv);
+        sp.zk_meta = cache->zk_meta;
+        sp.zk_tail = cache->zk_tail;
+        sp.full_blocks = static_cast<int>(seq_len / kTile);
+        sp.ql = qk;
+    }
+    const int stream_kind = li.q43 ? -1 : ek;     // -1: mixed 4/3-bit codes, dequantised in-kernel
     if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
-    if ((s = dev(launch_latent_scores(sp, ek, w.sp.G, w.sp.splits, w.sp.maxks, st))) != STARKV_OK)
+    if ((s = dev(launch_latent_scores(sp, stream_kind, w.sp.G, w.sp.splits, w.sp.maxks, st))) != STARKV_OK)
         return s;
     if (evm && (s = dev(hipEventRecord(static_cast<hipEvent_t>(evm), st))) != STARKV_OK) return s;
     ValueParams vp;
@@ -565,7 +573,12 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     vp.Tp = sp.Tp;
     vp.S = w.vp.splits;
     vp.blocks_per_split = w.vp.bps;
-    if ((s = dev(launch_latent_values(vp, ek, w.vp.chunks, st))) != STARKV_OK) return s;
+    vp.zv_meta = cache->zv_meta;
+    vp.zv_tail = cache->zv_tail;
+    vp.full_blocks = static_cast<int>(seq_len / kTile);
+    vp.block_bytes = li.q43 ? qv.block_bytes : 0;
+    vp.n_hi = li.q43 ? qv.n_hi : 0;
+    if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, st))) != STARKV_OK) return s;
     if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
     MergeParams m;
     m.ws_ml = vp.ws_ml;

@@ -131,6 +131,24 @@ __host__ __device__ inline size_t zv_block_index(size_t b, size_t nblk_cap, int 
            (size_t)((t & 63) >> 4) * 256 + (size_t)(c & 15) * 16 + (size_t)(t & 15);
 }
 
+// Mixed 4/3-bit code layout of one latent (see quant.hip for the byte layout).
+constexpr int kMaxKeyGroups = 256;          // R_k <= 4096
+struct Q43Layout {
+    int C;                      // channels of the latent
+    int block_bytes;            // code bytes per 64-token block
+    int is_key;                 // 1: token-major key layout, 0: channel-major value layout
+    int n_hi;                   // value latent: channels [0, n_hi) are 4-bit
+    int32_t goff[kMaxKeyGroups];   // key latent: byte offset of 16-channel group g in a block
+    uint8_t gn[kMaxKeyGroups];     // key latent: 4-bit channels at the start of group g
+};
+
+__host__ __device__ inline bool q43_is_hi(const Q43Layout& L, int c) {
+    return L.is_key ? (c & 15) < L.gn[c >> 4] : c < L.n_hi;
+}
+__host__ __device__ inline int q43_value_run_offset(const Q43Layout& L, int c) {
+    return c < L.n_hi ? 32 * c : 32 * L.n_hi + 24 * (c - L.n_hi);
+}
+
 struct ScoreParams {
     const void* zk;        // key latent, block layout
     const void* bkt;       // key factors in MFMA fragment order (head h at koff[h] * D)
@@ -144,6 +162,11 @@ struct ScoreParams {
     int16_t koff[kMaxHeads + 1];
     int16_t rank[kMaxHeads];
     double rope_rev[64];   // theta_i / (2 pi): RoPE frequency in revolutions per position
+    // mixed 4/3-bit key cache only: codes in zk, scales / zero points, binary16 tail rows
+    const void* zk_meta;   // [B][cap/64][2][Rk]
+    const void* zk_tail;   // [B][64][Rk]
+    int full_blocks;       // blocks [0, full_blocks) are quantised, block full_blocks is the tail
+    Q43Layout ql;
 };
 
 struct ValueParams {
@@ -153,6 +176,11 @@ struct ValueParams {
     float* ws_ml;          // [B][S][H][2]   (max in log2 units, sum)
     float* ws_acc;         // [B][S][H][rv]
     int B, H, rv, nblk_cap, seq_len, nblk, Tp, S, blocks_per_split;
+    // mixed 4/3-bit value cache only
+    const void* zv_meta;   // [B][cap/64][2][rv]
+    const void* zv_tail;   // [B][64][rv]
+    int full_blocks;
+    int block_bytes, n_hi;
 };
 
 struct MergeParams {
@@ -213,30 +241,12 @@ struct AppendSmallParams {
     long long pos, n;
 };
 
-// Mixed 4/3-bit code layout of one latent (see quant.hip for the byte layout).
-constexpr int kMaxKeyGroups = 256;          // R_k <= 4096
-struct Q43Layout {
-    int C;                      // channels of the latent
-    int block_bytes;            // code bytes per 64-token block
-    int is_key;                 // 1: token-major key layout, 0: channel-major value layout
-    int n_hi;                   // value latent: channels [0, n_hi) are 4-bit
-    int32_t goff[kMaxKeyGroups];   // key latent: byte offset of 16-channel group g in a block
-    uint8_t gn[kMaxKeyGroups];     // key latent: 4-bit channels at the start of group g
-};
-
-__host__ __device__ inline bool q43_is_hi(const Q43Layout& L, int c) {
-    return L.is_key ? (c & 15) < L.gn[c >> 4] : c < L.n_hi;
-}
-__host__ __device__ inline int q43_value_run_offset(const Q43Layout& L, int c) {
-    return c < L.n_hi ? 32 * c : 32 * L.n_hi + 24 * (c - L.n_hi);
-}
-
 struct Q43QuantParams {
     Q43Layout L;
     const void* src;            // new rows [B][n][C] binary16
     const void* tail;           // [B][64][C] binary16
     void* codes;                // [B][cap/64][block_bytes]
-    void* meta;                 // [B][cap/64][C][2] binary16
+    void* meta;                 // [B][cap/64][2][C] binary16 (scales, then zero points)
     int B, nblk_cap, g_first;
     long long pos, n;
 };

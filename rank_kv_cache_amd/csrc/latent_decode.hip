@@ -82,13 +82,58 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, int K, int MAXKS>
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Eight mixed 4/3-bit key codes of one token (one 16-channel group, channels 8*half .. +7) to an
+// fp16 MFMA operand fragment. w0..w2: the aligned 96-bit window holding the token's row, sh: the
+// row's first bit in the window, n: 4-bit channels at the start of the group; sc / zc: the scales
+// and zero points of the eight channels, two per word. Each value is binary16(q*s + z) rounded
+// once (one fp16 FMA per pair); q is formed exactly as binary16(1024 + q) - 1024.
+__device__ __forceinline__ f16x8 q43_key_frag(uint32_t w0, uint32_t w1, uint32_t w2, int sh, int n,
+                                             int half, const u32x4& sc, const u32x4& zc) {
+    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
+    const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
+    const uint32_t low24 = (half ? __builtin_amdgcn_alignbit(hi, lo, 24) : lo) & 0xffffffu;
+    const int m = min(max(n - 8 * half, 0), 8);
+    const uint32_t ext = (hi >> (16 + 8 * half)) & ((1u << m) - 1u);
+    f16x8 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = 2 * k;
+        const uint32_t q0 = ((low24 >> (3 * e)) & 7u) | (((ext >> e) & 1u) << 3);
+        const uint32_t q1 = ((low24 >> (3 * e + 3)) & 7u) | (((ext >> (e + 1)) & 1u) << 3);
+        const uint32_t bits = 0x64006400u | q0 | (q1 << 16);
+        const f16x2 qv = __builtin_bit_cast(f16x2, bits) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+        // vector elements are copied to scalars first: a bit cast applied directly to an
+        // element of an ext_vector value has been compiled as a cast of element 0
+        const uint32_t sk = sc[k], zk = zc[k];
+        const f16x2 r = __builtin_elementwise_fma(qv, __builtin_bit_cast(f16x2, sk),
+                                                  __builtin_bit_cast(f16x2, zk));
+        out[e] = r[0];
+        out[e + 1] = r[1];
+    }
+    return out;
+}
+
+// Latent source of the score kernel: binary16/bf16/fp32 fragments straight from the block layout,
+// or (QK) mixed 4/3-bit code windows plus scales / zero points, dequantised in registers.
+template <int K, int MAXKS, bool QK> struct KeyBuf;
+template <int K, int MAXKS> struct KeyBuf<K, MAXKS, false> {
+    typename Elem<K>::frag z[2][MAXKS];
+};
+template <int K, int MAXKS> struct KeyBuf<K, MAXKS, true> {
+    uint32_t w[2][MAXKS][3];
+    u32x4 sc[MAXKS], zc[MAXKS];
+};
+
+template <int D, int K, int MAXKS, bool QK>
 __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
     constexpr int NF = D / 2;           // RoPE frequencies
     constexpr int HMT = D / 64;         // m-tile pairs (mt, mt + HMT)
     using Fr = typename Elem<K>::frag;
     using T = typename Elem<K>::storage;
     using PT = typename PStore<K>::T;
+    using Buf = KeyBuf<K, MAXKS, QK>;
 
     __shared__ __attribute__((aligned(32))) T s_bk[kFragLdsBytes / sizeof(T)];
     __shared__ __attribute__((aligned(16))) float s_q[kMaxHeads * D];
@@ -99,6 +144,7 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
     // reads LDS (indexing the by-value argument block would make the compiler copy it to scratch)
     __shared__ double s_rev[64];
     __shared__ int s_head[kMaxHeads], s_rank[kMaxHeads], s_kgrp[kMaxHeads];
+    __shared__ int s_goff[QK ? kMaxHeads : 1][8], s_gn[QK ? kMaxHeads : 1][8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -120,8 +166,13 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
     const float* __restrict__ qg = p.q;
     PT* __restrict__ Pout = static_cast<PT*>(p.P);
     float* __restrict__ stats = p.stats;
-    const size_t kgroups = (size_t)(p.Rk >> 4);
+    const int Rk = p.Rk;
+    const size_t kgroups = (size_t)(Rk >> 4);
     const size_t blk_base = (size_t)b * p.nblk_cap;
+    const uint32_t* __restrict__ qcodes = static_cast<const uint32_t*>(p.zk);
+    const uint16_t* __restrict__ qmeta = static_cast<const uint16_t*>(p.zk_meta);
+    const T* __restrict__ qtail = static_cast<const T*>(p.zk_tail);
+    const size_t qblock_words = (size_t)(p.ql.block_bytes >> 2);
 
     if (tid < 64) s_rev[tid] = tid < NF ? p.rope_rev[tid] : 0.0;
     if (tid < ng) {
@@ -129,6 +180,13 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         s_head[tid] = h;
         s_rank[tid] = p.rank[h];
         s_kgrp[tid] = p.koff[h] >> 4;
+    }
+    if (QK && tid < 8 * ng) {
+        const int sl = tid >> 3, k = tid & 7;
+        const int h = p.order[hs0 + sl];
+        const int g16 = min((p.koff[h] >> 4) + k, (int)kgroups - 1);
+        s_goff[sl][k] = p.ql.goff[g16];
+        s_gn[sl][k] = p.ql.gn[g16];
     }
     // ---- stage the group's factor fragments and (scaled) queries ----
     if (tid == 0) {
@@ -166,32 +224,53 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
 
     const int blk_begin = split * p.blocks_per_wg;
     const int blk_end = min(nblk, blk_begin + p.blocks_per_wg);
-    const int my_blocks = blk_begin + wave < blk_end ? (blk_end - blk_begin - wave + kScoreWaves - 1) / kScoreWaves : 0;
+    // the pipelined loop covers the blocks stored in the main layout (all blocks for binary16 /
+    // bf16 / fp32 caches; the quantised groups for a mixed-precision cache, whose partial last
+    // block is read from the binary16 tail afterwards)
+    const int main_end = QK ? min(blk_end, p.full_blocks) : blk_end;
+    const int my_blocks = blk_begin + wave < main_end ? (main_end - blk_begin - wave + kScoreWaves - 1) / kScoreWaves : 0;
     const int nunits = my_blocks * ng;
 
-    // latent fragments of one unit (head, 64-token block): [column tile][rank step]
-    Fr zA[2][MAXKS], zB[2][MAXKS];
-
-    auto load_unit = [&](Fr (&z)[2][MAXKS], int u) {
+    auto load_unit = [&](Buf& z, int u) __attribute__((always_inline)) {
         const int blk = blk_begin + wave + kScoreWaves * (u / ng);
         const int s = u - (u / ng) * ng;
         const int nks = s_rank[s] >> 4;
-        const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
         // Every slot is loaded (steps past the head's rank repeat its last step, a cache hit), so
         // the number of loads in flight is static and the compiler's wait counts stay exact:
         // loads are retired in order, and a data-dependent count would force a full drain.
+        if constexpr (!QK) {
+            const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int ks = 0; ks < MAXKS; ++ks)
-                z[nt][ks] = load_frag<K>(zk, base + (size_t)min(ks, nks - 1) * 1024 + nt * 512);
+                for (int ks = 0; ks < MAXKS; ++ks)
+                    z.z[nt][ks] = load_frag<K>(zk, base + (size_t)min(ks, nks - 1) * 1024 + nt * 512);
+        } else {
+            const uint32_t* blkw = qcodes + (blk_base + blk) * qblock_words;
+            const uint16_t* meta = qmeta + (blk_base + blk) * 2 * (size_t)Rk;
+#pragma unroll
+            for (int ks = 0; ks < MAXKS; ++ks) {
+                const int k = min(ks, nks - 1);
+                const int n = s_gn[s][k];
+                const int c0 = 16 * (s_kgrp[s] + k) + 8 * half;
+                z.sc[ks] = *reinterpret_cast<const u32x4*>(meta + c0);
+                z.zc[ks] = *reinterpret_cast<const u32x4*>(meta + Rk + c0);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int rb = 8 * s_goff[s][k] + (32 * nt + j) * (48 + n);
+                    const uint32_t* wp = blkw + (rb >> 5);
+                    z.w[nt][ks][0] = wp[0];
+                    z.w[nt][ks][1] = wp[1];
+                    z.w[nt][ks][2] = wp[2];
+                }
+            }
+        }
     };
 
     float cb[2] = {1.0f, 1.0f}, sb[2] = {0.0f, 0.0f};     // rotation by n0*theta_lane (lane < NF)
 
-    auto compute_unit = [&](const Fr (&z)[2][MAXKS], int u) {
-        const int blk = blk_begin + wave + kScoreWaves * (u / ng);
-        const int s = u - (u / ng) * ng;
+    // One unit: head slot s over 64-token block blk. frag(nt, ks) supplies the latent operand.
+    auto unit = [&](int blk, int s, auto&& frag) __attribute__((always_inline)) {
         const int h = s_head[s];
         const int nks = s_rank[s] >> 4;
         if (s == 0 && lane < NF) {
@@ -216,8 +295,13 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         // Key rebuild + RoPE + dot for a head of NKS rank steps, as straight-line code: the rank
         // is dispatched once per unit, so no branch separates the MFMA chains from the RoPE
         // arithmetic and the scheduler can overlap one pass's MFMAs with another's VALU work.
-        auto core = [&](auto nks_c) {
+        auto core = [&](auto nks_c) __attribute__((always_inline)) {
             constexpr int NKS = decltype(nks_c)::value;
+            Fr z[2][NKS];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) z[nt][ks] = frag(nt, ks);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
@@ -253,8 +337,8 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         };
         switch (nks) {
         case 1: core(std::integral_constant<int, 1>{}); break;
-        case 2: core(std::integral_constant<int, 2>{}); break;
-        case 3: core(std::integral_constant<int, 3>{}); break;
+        case 2: core(std::integral_constant<int, (MAXKS >= 2 ? 2 : 1)>{}); break;
+        case 3: core(std::integral_constant<int, (MAXKS >= 3 ? 3 : 1)>{}); break;
         case 4: core(std::integral_constant<int, (MAXKS >= 4 ? 4 : 1)>{}); break;
         case 5: core(std::integral_constant<int, (MAXKS >= 5 ? 5 : 1)>{}); break;
         case 6: core(std::integral_constant<int, (MAXKS >= 6 ? 6 : 1)>{}); break;
@@ -276,14 +360,44 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         wave_sync_lds();
     };
 
+    auto compute_unit = [&](const Buf& z, int u) __attribute__((always_inline)) {
+        const int blk = blk_begin + wave + kScoreWaves * (u / ng);
+        const int s = u - (u / ng) * ng;
+        if constexpr (!QK) {
+            unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) { return z.z[nt][ks]; });
+        } else {
+            unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
+                const int n = s_gn[s][ks];
+                const int rb = 8 * s_goff[s][ks] + (32 * nt + j) * (48 + n);
+                return q43_key_frag(z.w[nt][ks][0], z.w[nt][ks][1], z.w[nt][ks][2], rb & 31, n,
+                                    half, z.sc[ks], z.zc[ks]);
+            });
+        }
+    };
+
     // Two-deep software pipeline over units. Prefetches past the last unit reload the last one
     // (a cache hit) instead of being skipped, for the same reason as in load_unit.
+    Buf zA, zB;
     if (nunits > 0) load_unit(zA, 0);
     for (int u = 0; u < nunits; u += 2) {
         load_unit(zB, min(u + 1, nunits - 1));
         compute_unit(zA, u);
         load_unit(zA, min(u + 2, nunits - 1));
         if (u + 1 < nunits) compute_unit(zB, u + 1);
+    }
+
+    if constexpr (QK) {
+        // the partial last block of a mixed-precision cache: its rows are still binary16 in the
+        // tail buffer [B][64][Rk], token-major
+        const int tb = p.full_blocks;
+        if (tb < blk_end && tb >= blk_begin && (tb - blk_begin) % kScoreWaves == wave) {
+            for (int s = 0; s < ng; ++s) {
+                const T* rowp = qtail + ((size_t)b * 64 + j) * Rk + 16 * s_kgrp[s] + 8 * half;
+                unit(tb, s, [&](int nt, int ks) __attribute__((always_inline)) {
+                    return load_frag<K>(rowp, (size_t)(32 * nt) * Rk + 16 * ks);
+                });
+            }
+        }
     }
 }
 
@@ -352,9 +466,48 @@ template <> struct ProbFrag<kF32> {
     __device__ static f32x16 mma(const Op& a, const f32x8& z, f32x16 acc) { return mma32<kF32>(a.v, z, acc); }
 };
 
-template <int K, int NTW>
+// Eight mixed 4/3-bit value codes (tokens 16*ks + 8*half .. +7 of one channel) to an fp16 MFMA
+// operand fragment. run: the channel's 64 codes as eight words (4-bit: a nibble per token; 3-bit:
+// words 0..3 the low two bits, words 4..5 the third bit); s2 / z2: the channel's scale and zero
+// point in both halves. Each value is binary16(q*s + z) rounded once.
+__device__ __forceinline__ f16x8 q43_value_frag(const uint32_t (&run)[8], bool hi4, int ks, int half,
+                                               uint32_t s2, uint32_t z2) {
+    uint32_t q[8];
+    if (hi4) {
+        const uint32_t w = half ? run[2 * ks + 1] : run[2 * ks];   // static register indices
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = (w >> (4 * e)) & 15u;
+    } else {
+        const uint32_t w2 = run[ks] >> (16 * half);
+        const uint32_t w1 = run[4 + (ks >> 1)] >> (16 * (ks & 1) + 8 * half);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = ((w2 >> (2 * e)) & 3u) | (((w1 >> e) & 1u) << 2);
+    }
+    f16x8 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t bits = 0x64006400u | q[2 * k] | (q[2 * k + 1] << 16);
+        const f16x2 qv = __builtin_bit_cast(f16x2, bits) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+        const f16x2 r = __builtin_elementwise_fma(qv, __builtin_bit_cast(f16x2, s2), __builtin_bit_cast(f16x2, z2));
+        out[2 * k] = r[0];
+        out[2 * k + 1] = r[1];
+    }
+    return out;
+}
+
+template <int K, int MAXC, bool QV> struct ValBuf;
+template <int K, int NTW> struct ValBuf<K, NTW, false> {
+    typename Elem<K>::frag z[NTW][4];
+};
+template <int K, int NTW> struct ValBuf<K, NTW, true> {
+    uint32_t run[NTW][8];
+    uint32_t s2[NTW], z2[NTW];
+};
+
+template <int K, int NTW, bool QV>
 __global__ __launch_bounds__(256) void latent_values(const ValueParams p) {
     using Fr = typename Elem<K>::frag;
+    using Buf = ValBuf<K, NTW, QV>;
     using PF = ProbFrag<K>;
     __shared__ float s_f[kMaxHeads][kMaxBlocksPerSplit];
     __shared__ float s_M[kMaxHeads], s_L[kMaxHeads];
@@ -412,43 +565,104 @@ __global__ __launch_bounds__(256) void latent_values(const ValueParams p) {
         for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
 
     typename PF::Raw pA[4], pB[4];
-    Fr zA[NTW][4], zB[NTW][4];
+    Buf zA, zB;
     const size_t prow = ((size_t)b * H + min(hrow, H - 1)) * p.Tp + 8 * half;
+    // mixed 4/3-bit cache: per lane, the channel's run offset and width are fixed
+    const uint8_t* __restrict__ qcodes = static_cast<const uint8_t*>(p.zv);
+    const uint16_t* __restrict__ qmeta = static_cast<const uint16_t*>(p.zv_meta);
+    int roff[NTW];
+    bool hi4[NTW];
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) {
+        const int cc = min(ch[k], p.rv - 1);
+        hi4[k] = cc < p.n_hi;
+        roff[k] = cc < p.n_hi ? 32 * cc : 32 * p.n_hi + 24 * (cc - p.n_hi);
+    }
+    const int main_end = QV ? min(blk_end, p.full_blocks) : blk_end;
 
-    auto load_blk = [&](typename PF::Raw (&pr)[4], Fr (&z)[NTW][4], int blk) {
+    auto load_blk = [&](typename PF::Raw (&pr)[4], Buf& z, int blk) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
-        const size_t bbase = ((size_t)b * p.nblk_cap + blk) * cgroups * 1024;
-#pragma unroll
-        for (int k = 0; k < NTW; ++k)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) z[k][ks] = load_frag<K>(p.zv, bbase + zoff[k] + ks * 256);
-    };
-    auto compute_blk = [&](const typename PF::Raw (&pr)[4], Fr (&z)[NTW][4], int blk) {
-        const float f = hvalid ? s_f[hrow][blk - blk_begin] : 0.0f;
-        if ((blk + 1) * 64 > seq_len) {                    // ragged last block: zero the tail
+        if constexpr (!QV) {
+            const size_t bbase = ((size_t)b * p.nblk_cap + blk) * cgroups * 1024;
 #pragma unroll
             for (int k = 0; k < NTW; ++k)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < 4; ++ks) z.z[k][ks] = load_frag<K>(p.zv, bbase + zoff[k] + ks * 256);
+        } else {
+            const size_t bb = ((size_t)b * p.nblk_cap + blk);
+            const uint8_t* blkp = qcodes + bb * p.block_bytes;
+            const uint16_t* meta = qmeta + bb * 2 * p.rv;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (blk * 64 + 16 * ks + 8 * half + e >= seq_len) z[k][ks][e] = 0;
+            for (int k = 0; k < NTW; ++k) {
+                // the 3-bit runs are 24 bytes; the eight-word window may read into the next run or
+                // the buffer's padding, which is never used
+                const uint2* w = reinterpret_cast<const uint2*>(blkp + roff[k]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint2 v = w[i];
+                    z.run[k][2 * i] = v.x;
+                    z.run[k][2 * i + 1] = v.y;
+                }
+                const int cc = min(ch[k], p.rv - 1);
+                const uint32_t sv = meta[cc], zv = meta[p.rv + cc];
+                z.s2[k] = sv | (sv << 16);
+                z.z2[k] = zv | (zv << 16);
+            }
         }
+    };
+    // Fr frag(k, ks) of the block's latent operand; zero past the sequence end
+    auto accumulate = [&](const typename PF::Raw (&pr)[4], int blk, auto&& frag) __attribute__((always_inline)) {
+        const float f = hvalid ? s_f[hrow][blk - blk_begin] : 0.0f;
+        const bool ragged = (blk + 1) * 64 > seq_len;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const typename PF::Op a = PF::scale(pr[ks], f);
 #pragma unroll
-            for (int k = 0; k < NTW; ++k) acc[k] = PF::mma(a, z[k][ks], acc[k]);
+            for (int k = 0; k < NTW; ++k) {
+                Fr zf = frag(k, ks);
+                if (ragged) {                              // ragged last block: zero the tail
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (blk * 64 + 16 * ks + 8 * half + e >= seq_len) zf[e] = 0;
+                }
+                acc[k] = PF::mma(a, zf, acc[k]);
+            }
+        }
+    };
+    auto compute_blk = [&](const typename PF::Raw (&pr)[4], const Buf& z, int blk) __attribute__((always_inline)) {
+        if constexpr (!QV) {
+            accumulate(pr, blk, [&](int k, int ks) __attribute__((always_inline)) { return z.z[k][ks]; });
+        } else {
+            accumulate(pr, blk, [&](int k, int ks) __attribute__((always_inline)) {
+                return q43_value_frag(z.run[k], hi4[k], ks, half, z.s2[k], z.z2[k]);
+            });
         }
     };
 
-    if (nb > 0) load_blk(pA, zA, blk_begin);
-    for (int blk = blk_begin; blk < blk_end; blk += 2) {
-        load_blk(pB, zB, min(blk + 1, blk_end - 1));
+    if (main_end > blk_begin) load_blk(pA, zA, blk_begin);
+    for (int blk = blk_begin; blk < main_end; blk += 2) {
+        load_blk(pB, zB, min(blk + 1, main_end - 1));
         compute_blk(pA, zA, blk);
-        load_blk(pA, zA, min(blk + 2, blk_end - 1));
-        if (blk + 1 < blk_end) compute_blk(pB, zB, blk + 1);
+        load_blk(pA, zA, min(blk + 2, main_end - 1));
+        if (blk + 1 < main_end) compute_blk(pB, zB, blk + 1);
+    }
+    if constexpr (QV) {
+        // the partial last block of a mixed-precision cache: binary16 rows in the tail [B][64][rv]
+        if (main_end < blk_end) {
+            const int blk = main_end;
+            typename PF::Raw pr[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
+            const _Float16* tail = static_cast<const _Float16*>(p.zv_tail) + (size_t)b * 64 * p.rv;
+            accumulate(pr, blk, [&](int k, int ks) __attribute__((always_inline)) {
+                const int cc = min(ch[k], p.rv - 1);
+                Fr zf;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zf[e] = tail[(size_t)(16 * ks + 8 * half + e) * p.rv + cc];
+                return zf;
+            });
+        }
     }
 
     const size_t part = (size_t)b * p.S + split;
@@ -570,32 +784,34 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
 // ------------------------------------------------------------------------------------------------
 // Host launchers
 // ------------------------------------------------------------------------------------------------
-template <int D, int K, int MAXKS>
+template <int D, int K, int MAXKS, bool QK>
 static hipError_t launch_scores_t(const ScoreParams& p, int groups, int splits, hipStream_t st) {
-    hipLaunchKernelGGL((latent_scores<D, K, MAXKS>), dim3(splits, groups, p.B), dim3(512), 0, st, p);
+    hipLaunchKernelGGL((latent_scores<D, K, MAXKS, QK>), dim3(splits, groups, p.B), dim3(512), 0, st, p);
     return hipGetLastError();
 }
 
-template <int D, int K>
+template <int D, int K, bool QK>
 static hipError_t launch_scores_d(const ScoreParams& p, int groups, int splits, int maxks, hipStream_t st) {
-    if (maxks <= 4) return launch_scores_t<D, K, 4>(p, groups, splits, st);
-    if (D == 128 && maxks <= 8) return launch_scores_t<D, K, (D == 128 ? 8 : 4)>(p, groups, splits, st);
+    if (maxks <= 4) return launch_scores_t<D, K, 4, QK>(p, groups, splits, st);
+    if (D == 128 && maxks <= 8) return launch_scores_t<D, K, (D == 128 ? 8 : 4), QK>(p, groups, splits, st);
     return hipErrorInvalidValue;
 }
 
-template <int K>
+template <int K, bool QK>
 static hipError_t launch_scores_k(const ScoreParams& p, int groups, int splits, int maxks, hipStream_t st) {
-    if (p.D == 128) return launch_scores_d<128, K>(p, groups, splits, maxks, st);
-    if (p.D == 64) return launch_scores_d<64, K>(p, groups, splits, maxks, st);
+    if (p.D == 128) return launch_scores_d<128, K, QK>(p, groups, splits, maxks, st);
+    if (p.D == 64) return launch_scores_d<64, K, QK>(p, groups, splits, maxks, st);
     return hipErrorInvalidValue;
 }
 
+// elem: kF32 / kF16 / kBF16, or -1 for a mixed 4/3-bit key cache (binary16 factors)
 hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
                                 hipStream_t st) {
     switch (elem) {
-    case kF32: return launch_scores_k<kF32>(p, groups, splits, maxks, st);
-    case kF16: return launch_scores_k<kF16>(p, groups, splits, maxks, st);
-    case kBF16: return launch_scores_k<kBF16>(p, groups, splits, maxks, st);
+    case kF32: return launch_scores_k<kF32, false>(p, groups, splits, maxks, st);
+    case kF16: return launch_scores_k<kF16, false>(p, groups, splits, maxks, st);
+    case kBF16: return launch_scores_k<kBF16, false>(p, groups, splits, maxks, st);
+    case -1: return launch_scores_k<kF16, true>(p, groups, splits, maxks, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -606,9 +822,10 @@ int value_chunk_channels() { return kValueWaves * kValueNTW * 32; }
 hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, hipStream_t st) {
     const dim3 grid(p.S, chunks, p.B);
     switch (elem) {
-    case kF32: hipLaunchKernelGGL((latent_values<kF32, kValueNTW>), grid, dim3(256), 0, st, p); break;
-    case kF16: hipLaunchKernelGGL((latent_values<kF16, kValueNTW>), grid, dim3(256), 0, st, p); break;
-    case kBF16: hipLaunchKernelGGL((latent_values<kBF16, kValueNTW>), grid, dim3(256), 0, st, p); break;
+    case kF32: hipLaunchKernelGGL((latent_values<kF32, kValueNTW, false>), grid, dim3(256), 0, st, p); break;
+    case kF16: hipLaunchKernelGGL((latent_values<kF16, kValueNTW, false>), grid, dim3(256), 0, st, p); break;
+    case kBF16: hipLaunchKernelGGL((latent_values<kBF16, kValueNTW, false>), grid, dim3(256), 0, st, p); break;
+    case -1: hipLaunchKernelGGL((latent_values<kF16, kValueNTW, true>), grid, dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

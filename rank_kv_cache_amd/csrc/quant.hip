@@ -19,8 +19,9 @@
 //    at byte 32c (4-bit, c < n_hi) or 32 n_hi + 24 (c - n_hi) (3-bit); 4-bit run: token t in
 //    byte t/2, low nibble for even t; 3-bit run: bytes 0..15 hold the low two bits (token t at
 //    bits 2(t%4) of byte t/4), bytes 16..23 the third bit (token t at bit t%8 of byte 16 + t/8).
-//  * meta [B][cap/64][C][2] binary16 (scale, zero); tail [B][64][C] binary16 holds the rows of
-//    the unfinished group.
+//  * meta [B][cap/64][2][C] binary16: per block a row of scales, then a row of zero points (so
+//    that the scales, and the zero points, of neighbouring channels pair up in one word);
+//    tail [B][64][C] binary16 holds the rows of the unfinished group.
 
 #include "common.hpp"
 
@@ -95,9 +96,9 @@ __global__ __launch_bounds__(256) void q43_quantize(const Q43QuantParams p) {
         if (z16 == 0x8000u) z16 = 0;
         s_s[tid] = s16;
         s_z[tid] = z16;
-        uint16_t* meta = static_cast<uint16_t*>(p.meta) + (((size_t)b * p.nblk_cap + g) * C + c) * 2;
+        uint16_t* meta = static_cast<uint16_t*>(p.meta) + ((size_t)b * p.nblk_cap + g) * 2 * C + c;
         meta[0] = s16;
-        meta[1] = z16;
+        meta[C] = z16;
     }
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += 256) {
@@ -201,10 +202,10 @@ __global__ __launch_bounds__(256) void q43_readback(const Q43ReadParams p) {
     if (tok < p.full_tokens) {
         const int g = (int)(tok >> 6), t = (int)(tok & 63);
         const uint8_t* blk = static_cast<const uint8_t*>(p.codes) + ((size_t)b * p.nblk_cap + g) * L.block_bytes;
-        const uint16_t* meta = static_cast<const uint16_t*>(p.meta) + (((size_t)b * p.nblk_cap + g) * L.C + c) * 2;
+        const uint16_t* meta = static_cast<const uint16_t*>(p.meta) + ((size_t)b * p.nblk_cap + g) * 2 * L.C + c;
         for (int e = 0; e < 8; ++e) {
             const int q = L.is_key ? q43_key_code(blk, L, c + e, t) : q43_value_code(blk, L, c + e, t);
-            v[e] = q43_dequant(q, meta[2 * e], meta[2 * e + 1]);
+            v[e] = q43_dequant(q, meta[e], meta[L.C + e]);
         }
     } else {
         const _Float16* tail = static_cast<const _Float16*>(p.tail) + ((size_t)b * 64 + (tok & 63)) * L.C + c;

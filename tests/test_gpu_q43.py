@@ -115,8 +115,9 @@ def test_q43_append_dequant_bit_exact(chunks):
     # metadata and packed bytes of the complete groups
     full = T // 64
     sizes = sk.starkv_cache_bytes(L, B, cap)
-    meta_k = cache.zk_meta.cpu().numpy().view(np.uint16).reshape(B, cap // 64, sum(ranks), 2)
-    meta_v = cache.zv_meta.cpu().numpy().view(np.uint16).reshape(B, cap // 64, rv, 2)
+    # library meta layout: per block a row of scales then a row of zero points
+    meta_k = cache.zk_meta.cpu().numpy().view(np.uint16).reshape(B, cap // 64, 2, sum(ranks)).transpose(0, 1, 3, 2)
+    meta_v = cache.zv_meta.cpu().numpy().view(np.uint16).reshape(B, cap // 64, 2, rv).transpose(0, 1, 3, 2)
     assert np.array_equal(meta_k[:, :full], mk[:, :full])
     assert np.array_equal(meta_v[:, :full], mv[:, :full])
     vbytes = cv.shape[2]
@@ -127,3 +128,86 @@ def test_q43_append_dequant_bit_exact(chunks):
     for b in range(B):
         for g in range(full):
             assert np.array_equal(gk[b, g], _key_rows_layout(ck[b, g], bits_k, cap // 64)), (b, g)
+
+
+def _q43_reference(ld, zk16, zv16, q, ranks, rv, T, cap, pairs=None):
+    """Oracle attention on the oracle's own quantise -> dequantise of the same binary16 rows."""
+    bits_k = oracle.channel_bits(ranks, FRAC)
+    bits_v = oracle.channel_bits([rv], FRAC)
+    ck, mk, tk = oracle.q43_pack(zk16, bits_k, cap)
+    cv, mv, tv = oracle.q43_pack(zv16, bits_v, cap)
+    dk = oracle.q43_unpack(ck, mk, tk, bits_k, T, cap)
+    dv = oracle.q43_unpack(cv, mv, tv, bits_v, T, cap)
+    return oracle.decode_latent(dk, dv, ld.bk, ld.bv, q, ranks, pairs=pairs)
+
+
+def _gpu_decode(L, cache, T, q, bk, bv, num_splits=0):
+    import torch
+    from rank_kv_cache_amd import buffers
+    B = cache.batch
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    ws, nws = buffers.alloc_workspace(L, B, T, num_splits)
+    ws.fill_(0xFF)
+    sk.starkv_decode_attn(L, cache, T, buffers.to_device(np.ascontiguousarray(q, np.float32)),
+                          buffers.to_device(bk), buffers.to_device(bv), out, num_splits, ws, nws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_q43_decode_parity_rotated():
+    """Blockwise-Hadamard-rotated latents and factors (rotation by the oracle, as offline
+    preparation), mixed 4/3-bit cache built by chunked appends, decode at several lengths
+    including a partial last group."""
+    from rank_kv_cache_amd import buffers
+    from gpu_support import rel_err
+    H, d, B = 6, 128, 2
+    ranks = [16, 48, 32, 64, 16, 80]
+    rv = 272
+    T, cap = 64 * 3 + 21, 64 * 5
+    w = synth.Workload("qd", batch=B, heads=H, head_dim=d, seq_len=T, dtype="f16", layer_seed=71,
+                       cache_seed=72, value_rank=rv, power=0.5)
+    ld = synth.draw_layer(w, key_ranks=ranks)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = synth.draw_queries(72, 0, B, H, d)
+    seg_k = oracle.latent_segments(ranks, FRAC)
+    seg_v = oracle.latent_segments([rv], FRAC)
+    zk_r, zv_r = oracle.rotate_rows(zk, seg_k), oracle.rotate_rows(zv, seg_v)
+    ld.bk = oracle.rotate_factor(ld.bk, seg_k)
+    ld.bv = oracle.rotate_factor(ld.bv, seg_v)
+    L = q43_layer(H, d, ranks, rv)
+    cache = buffers.alloc_cache(L, B, cap, fill=0xFF)
+    _append(L, cache, zk_r, zv_r, [61, 3, 64, 70, 1, 1, 13])
+    for Tq in (T, 192, 64):
+        ref = _q43_reference(ld, zk_r[:, :Tq], zv_r[:, :Tq], q, ranks, rv, Tq, cap)
+        for S in (0, 1, 3):
+            got = _gpu_decode(L, cache, Tq, q, ld.bk, ld.bv, S)
+            e = rel_err(got, ref)
+            say(f"[q43 decode] T={Tq} splits={S} rel err {e:.3e}")
+            assert np.all(np.isfinite(got)) and e <= 1e-2
+            assert e <= 2e-3          # same dequantised values: only fp32 vs fp64 arithmetic differs
+
+
+def test_q43_decode_full_size_sampled():
+    """The quantised LongChat-shaped workload at full size (B=16, T=16384) in the library's
+    default launch configuration; the oracle evaluates sampled (sequence, head) pairs on its own
+    dequantisation of the same rows. (Latents are not rotated here: the rotation is absorbed into
+    the factors offline and does not reach the kernels.)"""
+    from rank_kv_cache_amd import buffers
+    from gpu_support import rel_err
+    w = synth.WORKLOADS["longchat_b16_t16384_q43"]
+    ld = synth.draw_layer(w)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = synth.draw_queries(w.cache_seed, 0, w.batch, w.heads, w.head_dim)
+    ranks, rv = ld.key_ranks, ld.value_rank
+    L = q43_layer(w.heads, w.head_dim, ranks, rv)
+    cache = buffers.alloc_cache(L, w.batch, w.seq_len)
+    _append(L, cache, zk, zv, [w.seq_len])
+    got = _gpu_decode(L, cache, w.seq_len, q, ld.bk, ld.bv)
+    rng = np.random.default_rng(7)
+    sel_b = [0, w.batch - 1]
+    pairs = [(0, 0), (1, w.heads - 1)] + [(int(rng.integers(0, 2)), int(h)) for h in rng.integers(0, w.heads, 6)]
+    ref = _q43_reference(ld, zk[sel_b], zv[sel_b], q[sel_b], ranks, rv, w.seq_len, w.seq_len, pairs=pairs)
+    sub = np.stack([got[sel_b[b], h] for b, h in pairs])
+    e = rel_err(sub, ref)
+    say(f"[q43 full] sampled {len(pairs)} pairs rel err {e:.3e}")
+    assert np.all(np.isfinite(got)) and e <= 1e-2
