@@ -1,19 +1,22 @@
 """Benchmark of single-token decode attention over a low-rank latent KV cache on one MI355X.
 
-A step is one decode step of one attention layer for the whole batch: append the new token's key
-and value latents at the last position (starkv_append_latents), then attend from the latent
-cache over all T cached tokens (starkv_decode_attn: split kernel, log-sum-exp merge, per-head B_v
-projection). Inputs are synthetic (seeded), already resident in HBM when timing starts.
+A step is one decode step for the whole batch. For a single-layer workload: append the new token's
+key and value latents at the last position (starkv_append_latents), then attend from the latent
+cache over all T cached tokens (starkv_decode_attn: score kernel, value kernel, log-sum-exp merge,
+per-head B_v projection). For the 32-layer model step the same is done for every layer in order,
+the three exempt layers attending over full-width fp16 K/V. Inputs are synthetic (seeded) and
+already resident in HBM when timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 Prints one JSON line. ``value`` is decode tokens per second (one new token per sequence per step,
-B / step time). ``roofline`` prices the dominant kernel against MI355X's 8 TB/s HBM. The two
-streaming kernels are the score kernel (reads the key latents, B * T * R_k elements) and the value
-kernel (reads the value latent, B * T * r_v elements); each one's algorithmic bytes are divided by
-its average duration from HIP events recorded around its launch on the launch stream, and the
-slower one is reported (both appear under ``kernels``). ``cpu_baseline`` times the fp64 CPU oracle on a bounded
-sample of (sequence, head) pairs of the same workload, scaled to the whole workload.
+B / step time). ``roofline`` prices the dominant kernel against MI355X's 8 TB/s HBM: each
+streaming kernel's algorithmic bytes (latent bytes it must read: key latents for the score kernel,
+value latent for the value kernel, codes plus scales / zero points for a mixed 4/3-bit cache,
+K and V for an exempt layer) are divided by its duration from HIP events recorded around its
+launch on the launch stream; the kernel with the largest total time is reported (all appear under
+``kernels``). ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
+pairs of the same workload, scaled to the whole workload.
 """
 from __future__ import annotations
 
@@ -33,6 +36,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, AMD datasheet
 DEFAULT_WORKLOAD = "longchat_b16_t32768_f16"
+MODEL_WORKLOAD = "model32_b32_t8192_f16"
 METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=16 T=32K"
 
 
@@ -74,33 +78,217 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def cpu_baseline(ld, zk, zv, q, B, H, budget_s: float):
-    """Time the fp64 oracle on (b, h) pairs until about ``budget_s`` seconds of wall time have
-    been spent; scale to all B*H pairs and report decode tokens/s of the whole workload."""
+class LayerRun:
+    """One layer's device state for the benchmark: cache prefilled with T-1 tokens, the new
+    token's rows, factors, query, output, and the algorithmic bytes of its streaming kernels."""
+
+    def __init__(self, layer, cache, new_k, new_v, bk, bv, q, out, T, dense, key_bytes,
+                 value_bytes):
+        self.layer, self.cache, self.new_k, self.new_v = layer, cache, new_k, new_v
+        self.bk, self.bv, self.q, self.out, self.T = bk, bv, q, out, T
+        self.dense, self.key_bytes, self.value_bytes = dense, key_bytes, value_bytes
+
+
+class OracleSample:
+    """Accumulates oracle wall time on sampled (sequence, head) pairs, scaled per layer."""
+
+    def __init__(self):
+        self.full_s = 0.0
+        self.spent = 0.0
+        self.pairs = 0
+        self.total_pairs = 0
+
+    def time_pairs(self, fn, B, H, budget_s, seed, extra_per_seq=None):
+        """fn(pairs) runs the oracle on a list of (b, h); extra_per_seq(b) times per-sequence
+        preparation (dequantisation) that the oracle repeats for each sequence it touches."""
+        import oracle
+        thr = oracle.threads()
+        rng = np.random.default_rng(seed)
+        order = rng.permutation(B * H)
+        done, spent, chunk = 0, 0.0, max(1, thr)
+        while done < B * H and spent < budget_s:
+            sel = order[done:done + chunk]
+            pairs = [(int(i) // H, int(i) % H) for i in sel]
+            t0 = time.perf_counter()
+            fn(pairs)
+            spent += time.perf_counter() - t0
+            done += len(sel)
+            per_pair = spent / done
+            chunk = int(min(max(chunk, (budget_s - spent) / max(per_pair, 1e-9)), B * H - done))
+            if chunk <= 0:
+                break
+        full = spent * (B * H) / done
+        if extra_per_seq is not None:
+            t0 = time.perf_counter()
+            extra_per_seq(0)
+            e = time.perf_counter() - t0
+            spent += e
+            full += e * B
+        self.full_s += full
+        self.spent += spent
+        self.pairs += done
+        self.total_pairs += B * H
+        return full
+
+
+def cache_capacity(T):
+    return ((T + 63) // 64) * 64
+
+
+def latent_kernel_bytes(sk, layer, B, T, Rk, rv, esz, quantized):
+    """Algorithmic bytes one launch of the score / value kernel must read."""
+    if not quantized:
+        return B * T * Rk * esz, B * T * rv * esz
+    cap = cache_capacity(T)
+    sizes = sk.starkv_cache_bytes(layer, B, cap)
+    pad = 32                                          # readers' window padding after the blocks
+    nb_cap = cap // 64
+    kbb = (sizes[0] - pad) // (B * nb_cap)
+    vbb = (sizes[1] - pad) // (B * nb_cap)
+    full, tail = T // 64, T % 64
+    kb = B * (full * (kbb + 4 * Rk) + tail * Rk * 2)
+    vb = B * (full * (vbb + 4 * rv) + tail * rv * 2)
+    return kb, vb
+
+
+def build_latent_run(sk, buffers, layer, zk, zv, bk_h, bv_h, q_h, T, bf16, quantized):
+    import torch
+    B = zk.shape[0]
+    cap = cache_capacity(T)
+    cache = buffers.alloc_cache(layer, B, cap)
+    dzk = buffers.to_device(zk, bf16=bf16)
+    dzv = buffers.to_device(zv, bf16=bf16)
+    sk.starkv_append_latents(layer, cache, 0, T - 1, dzk[:, :T - 1].contiguous(),
+                             dzv[:, :T - 1].contiguous())
+    new_k = dzk[:, T - 1:].contiguous()
+    new_v = dzv[:, T - 1:].contiguous()
+    del dzk, dzv
+    H, d = q_h.shape[1], q_h.shape[2]
+    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    esz = zk.dtype.itemsize
+    kb, vb = latent_kernel_bytes(sk, layer, B, T, zk.shape[2], zv.shape[2], esz, quantized)
+    return LayerRun(layer, cache, new_k, new_v, buffers.to_device(bk_h, bf16=bf16),
+                    buffers.to_device(bv_h, bf16=bf16), buffers.to_device(q_h), out, T, False,
+                    kb, vb)
+
+
+def build_dense_run(sk, buffers, layer, k, v, q_h, T):
+    import torch
+    B = k.shape[0]
+    cache = buffers.alloc_cache(layer, B, cache_capacity(T))
+    dk = buffers.to_device(k)
+    dv = buffers.to_device(v)
+    sk.starkv_append_latents(layer, cache, 0, T - 1, dk[:, :T - 1].contiguous(),
+                             dv[:, :T - 1].contiguous())
+    new_k = dk[:, T - 1:].contiguous()
+    new_v = dv[:, T - 1:].contiguous()
+    del dk, dv
+    H, d = q_h.shape[1], q_h.shape[2]
+    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    kvb = B * T * k.shape[2] * k.dtype.itemsize
+    return LayerRun(layer, cache, new_k, new_v, None, None, buffers.to_device(q_h), out, T, True,
+                    kvb, kvb)
+
+
+def setup_single(a, sk, buffers, synth, sample):
+    w = synth.WORKLOADS[a.workload]
+    B, H, d, T = w.batch, w.heads, w.head_dim, w.seq_len
+    t_gen = time.perf_counter()
+    ld = synth.draw_layer(w)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = synth.draw_queries(w.cache_seed, 0, B, H, d)
+    Rk, rv = int(ld.key_ranks.sum()), ld.value_rank
+    log(f"[bench] {w.name}: B={B} H={H} d={d} T={T} R_k={Rk} r_v={rv} {w.dtype}"
+        f"{' mixed 4/3-bit cache' if w.quantized else ''}; generated "
+        f"{(zk.nbytes + zv.nbytes) / 1e9:.2f} GB in {time.perf_counter() - t_gen:.1f} s")
+    if w.quantized:
+        # Latents enter the cache already in the rotated basis (the rotation is folded into the
+        # down-projection ahead of the cache); rows of the synthetic generator stand in for them.
+        layer = sk.Layer(num_heads=H, head_dim=d, key_ranks=tuple(int(r) for r in ld.key_ranks),
+                         value_rank=rv, cache_dtype=sk.Q43, rope_base=w.rope_base)
+    else:
+        dt_code = {"f32": sk.F32, "f16": sk.F16, "bf16": sk.BF16}[w.dtype]
+        layer = sk.Layer(num_heads=H, head_dim=d, key_ranks=tuple(int(r) for r in ld.key_ranks),
+                         value_rank=rv, cache_dtype=dt_code, rope_base=w.rope_base)
+    bf16 = w.dtype == "bf16"
+    run = build_latent_run(sk, buffers, layer, zk, zv, ld.bk, ld.bv, q, T, bf16, w.quantized)
+    if sample is not None:
+        sample_latent_layer(sample, w, ld, zk, zv, q, a.cpu_budget, w.quantized, seed=2024)
+    desc = {"workload": w.name, "batch": B, "heads": H, "head_dim": d, "seq_len": T,
+            "key_rank_sum": Rk, "value_rank": rv,
+            "latent_dtype": "q43" if w.quantized else w.dtype, "layers": 1}
+    return [run], desc, "f16" if w.quantized else w.dtype, B
+
+
+def sample_latent_layer(sample, w, ld, zk, zv, q, budget, quantized, seed):
     import oracle
     oracle.lib()
-    thr = oracle.threads()
-    rng = np.random.default_rng(2024)
-    order = rng.permutation(B * H)
-    done, spent = 0, 0.0
-    chunk = max(1, thr)
-    while done < B * H and spent < budget_s:
-        sel = order[done:done + chunk]
-        pairs = [(int(i) // H, int(i) % H) for i in sel]
-        t0 = time.perf_counter()
-        oracle.decode_latent(zk, zv, ld.bk, ld.bv, q, ld.key_ranks, pairs=pairs)
-        spent += time.perf_counter() - t0
-        done += len(sel)
-        per_pair = spent / done
-        chunk = int(min(max(chunk, (budget_s - spent) / max(per_pair, 1e-9)), B * H - done))
-        chunk = max(chunk, 0)
-        if chunk == 0:
-            break
-    full_s = spent * (B * H) / done
-    return {"value": B / full_s, "unit": "tokens/s", "cores": thr, "kind": "oracle",
-            "sample": f"{done} of {B * H} (sequence, head) pairs of the same workload, full T, fp64 "
-                      f"latent form, {spent:.1f} s wall on {thr} threads; scaled to all pairs "
-                      f"({full_s:.1f} s per step)"}
+    if not quantized:
+        sample.time_pairs(lambda pairs: oracle.decode_latent(zk, zv, ld.bk, ld.bv, q, ld.key_ranks,
+                                                             pairs=pairs),
+                          w.batch, w.heads, budget, seed)
+        return
+    # the oracle's mixed 4/3-bit path: the cache is quantised once when it is built (not timed);
+    # a step dequantises every sequence (timed once, scaled by B) and attends on the result
+    T = zk.shape[1]
+    cap = cache_capacity(T)
+    bits_k = oracle.channel_bits(ld.key_ranks, 0.25)
+    bits_v = oracle.channel_bits([ld.value_rank], 0.25)
+    pk = oracle.q43_pack(zk, bits_k, cap)
+    pv = oracle.q43_pack(zv, bits_v, cap)
+    dk = oracle.q43_unpack(*pk, bits_k, T, cap)
+    dv = oracle.q43_unpack(*pv, bits_v, T, cap)
+
+    def unpack_one(b):
+        oracle.q43_unpack(*(x[b:b + 1] for x in pk), bits_k, T, cap)
+        oracle.q43_unpack(*(x[b:b + 1] for x in pv), bits_v, T, cap)
+
+    sample.time_pairs(lambda pairs: oracle.decode_latent(dk, dv, ld.bk, ld.bv, q, ld.key_ranks,
+                                                         pairs=pairs),
+                      w.batch, w.heads, budget, seed, extra_per_seq=unpack_one)
+
+
+def setup_model(a, sk, buffers, synth, sample):
+    import oracle
+    spec = synth.MODEL_STEP
+    layers = synth.model_layers()
+    B, H, d, T = spec["batch"], spec["heads"], spec["head_dim"], spec["seq_len"]
+    runs = []
+    latent_bytes = dense_bytes = 0
+    t_gen = time.perf_counter()
+    per_layer_budget = a.cpu_budget / len(layers)
+    for ml in layers:
+        w = ml.workload
+        q = synth.draw_queries(spec["seed"], ml.index, B, H, d)
+        if ml.dense:
+            k, v = synth.draw_dense_cache(spec["seed"], ml.index, B, T, H * d, spec["dtype"])
+            layer = sk.Layer(num_heads=H, head_dim=d, dense=True, cache_dtype=sk.F16)
+            runs.append(build_dense_run(sk, buffers, layer, k, v, q, T))
+            dense_bytes += 2 * k.nbytes
+            if sample is not None:
+                sample.time_pairs(lambda pairs: oracle.decode_dense(k, v, q, pairs=pairs), B, H,
+                                  per_layer_budget, 100 + ml.index)
+            del k, v
+        else:
+            ld = synth.draw_model_layer(ml)
+            zk, zv = synth.draw_latent_cache(w, ld, layer=ml.index)
+            layer = sk.Layer(num_heads=H, head_dim=d, key_ranks=tuple(int(r) for r in ld.key_ranks),
+                             value_rank=ld.value_rank, cache_dtype=sk.F16)
+            runs.append(build_latent_run(sk, buffers, layer, zk, zv, ld.bk, ld.bv, q, T, False,
+                                         False))
+            latent_bytes += zk.nbytes + zv.nbytes
+            if sample is not None:
+                sample.time_pairs(lambda pairs: oracle.decode_latent(zk, zv, ld.bk, ld.bv, q,
+                                                                     ld.key_ranks, pairs=pairs),
+                                  B, H, per_layer_budget, 100 + ml.index)
+            del zk, zv
+        log(f"[bench] layer {ml.index:2d} {'dense' if ml.dense else 'latent'} ready "
+            f"({time.perf_counter() - t_gen:.1f} s)")
+    desc = {"workload": spec["name"], "batch": B, "heads": H, "head_dim": d, "seq_len": T,
+            "layers": len(layers), "dense_layers": list(spec["dense_layers"]),
+            "latent_dtype": spec["dtype"], "latent_gb": round(latent_bytes / 1e9, 2),
+            "dense_gb": round(dense_bytes / 1e9, 2)}
+    return runs, desc, spec["dtype"], B
 
 
 def main(argv=None):
@@ -108,7 +296,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="a single-layer workload name, or " + MODEL_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's split planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle wall seconds")
@@ -127,53 +316,35 @@ def main(argv=None):
     from rank_kv_cache_amd import buffers, synth
     sk.lib()                                              # fails loudly if the library is missing
 
-    w = synth.WORKLOADS[a.workload]
-    if w.quantized:
-        raise SystemExit("quantized workloads are not benchmarked by this script yet")
-    B, H, d, T = w.batch, w.heads, w.head_dim, w.seq_len
-    t_gen = time.perf_counter()
-    ld = synth.draw_layer(w)
-    zk, zv = synth.draw_latent_cache(w, ld)
-    q = synth.draw_queries(w.cache_seed, 0, B, H, d)
-    Rk, rv = int(ld.key_ranks.sum()), ld.value_rank
-    esz = zk.dtype.itemsize
-    log(f"[bench] {w.name}: B={B} H={H} d={d} T={T} R_k={Rk} r_v={rv} {w.dtype}; "
-        f"generated {(zk.nbytes + zv.nbytes) / 1e9:.2f} GB in {time.perf_counter() - t_gen:.1f} s")
-
-    dt_code = {"f32": sk.F32, "f16": sk.F16, "bf16": sk.BF16}[w.dtype]
-    layer = sk.Layer(num_heads=H, head_dim=d, key_ranks=tuple(int(r) for r in ld.key_ranks),
-                     value_rank=rv, cache_dtype=dt_code, rope_base=w.rope_base)
-    bf16 = w.dtype == "bf16"
-    cap = ((T + 63) // 64) * 64
-    cache = buffers.alloc_cache(layer, B, cap)
-    # prefill T-1 tokens; the step appends token T-1 and attends over T
-    dzk = buffers.to_device(zk, bf16=bf16)
-    dzv = buffers.to_device(zv, bf16=bf16)
-    sk.starkv_append_latents(layer, cache, 0, T - 1, dzk[:, :T - 1].contiguous(),
-                             dzv[:, :T - 1].contiguous())
-    new_k = dzk[:, T - 1:].contiguous()
-    new_v = dzv[:, T - 1:].contiguous()
-    del dzk, dzv
-    bk = buffers.to_device(ld.bk, bf16=bf16)
-    bv = buffers.to_device(ld.bv, bf16=bf16)
-    dq = buffers.to_device(q)
-    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
-    ws, nws = buffers.alloc_workspace(layer, B, T, a.splits)
+    sample = None if a.no_cpu_baseline else OracleSample()
+    if a.workload == MODEL_WORKLOAD:
+        runs, desc, dtype, B = setup_model(a, sk, buffers, synth, sample)
+    elif a.workload in synth.WORKLOADS:
+        runs, desc, dtype, B = setup_single(a, sk, buffers, synth, sample)
+    else:
+        raise SystemExit(f"unknown workload {a.workload!r}; choose from "
+                         f"{sorted(synth.WORKLOADS) + [MODEL_WORKLOAD]}")
+    ws_bytes = max(sk.starkv_decode_workspace_bytes(r.layer, B, r.T, a.splits) for r in runs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     hip = HipEvents()
-    ev = hip.create(3 * a.steps)
+    nl = len(runs)
+    ev = hip.create(3 * nl * a.steps)
 
     def step(i=None):
-        sk.starkv_append_latents(layer, cache, T - 1, 1, new_k, new_v, stream=stream)
-        if i is None:
-            sk.starkv_decode_attn(layer, cache, T, dq, bk, bv, out, a.splits, ws, nws,
-                                  stream=stream)
-        else:
-            sk.starkv_decode_attn_timed(layer, cache, T, dq, bk, bv, out, a.splits, ws, nws,
-                                        stream=stream, event_begin=ev[3 * i],
-                                        event_mid=ev[3 * i + 1], event_end=ev[3 * i + 2])
+        for li, r in enumerate(runs):
+            sk.starkv_append_latents(r.layer, r.cache, r.T - 1, 1, r.new_k, r.new_v, stream=stream)
+            if i is None:
+                sk.starkv_decode_attn(r.layer, r.cache, r.T, r.q, r.bk, r.bv, r.out, a.splits, ws,
+                                      ws_bytes, stream=stream)
+            else:
+                e = 3 * (i * nl + li)
+                sk.starkv_decode_attn_timed(r.layer, r.cache, r.T, r.q, r.bk, r.bv, r.out,
+                                            a.splits, ws, ws_bytes, stream=stream,
+                                            event_begin=ev[e], event_mid=ev[e + 1],
+                                            event_end=ev[e + 2])
 
     for _ in range(a.warmup):
         step()
@@ -184,31 +355,58 @@ def main(argv=None):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    score_ms = [hip.elapsed_ms(ev[3 * i], ev[3 * i + 1]) for i in range(a.steps)]
-    value_ms = [hip.elapsed_ms(ev[3 * i + 1], ev[3 * i + 2]) for i in range(a.steps)]
-    hip.destroy(ev)
     log(f"[bench] timed {a.steps} steps in {elapsed * 1e3:.2f} ms")
 
-    res = out.cpu().numpy()
-    if not np.all(np.isfinite(res)):
-        raise SystemExit("non-finite attention output")
+    # per-step kernel time by kind, summed over layers
+    k_ms = {"latent_scores": [0.0] * a.steps, "latent_values": [0.0] * a.steps,
+            "dense_attention": [0.0] * a.steps}
+    k_bytes = {"latent_scores": 0, "latent_values": 0, "dense_attention": 0}
+    k_launches = {"latent_scores": 0, "latent_values": 0, "dense_attention": 0}
+    for li, r in enumerate(runs):
+        if r.dense:
+            k_bytes["dense_attention"] += 2 * r.key_bytes
+            k_launches["dense_attention"] += 1
+        else:
+            k_bytes["latent_scores"] += r.key_bytes
+            k_bytes["latent_values"] += r.value_bytes
+            k_launches["latent_scores"] += 1
+            k_launches["latent_values"] += 1
+        for i in range(a.steps):
+            e = 3 * (i * nl + li)
+            if r.dense:
+                k_ms["dense_attention"][i] += hip.elapsed_ms(ev[e], ev[e + 1])
+            else:
+                k_ms["latent_scores"][i] += hip.elapsed_ms(ev[e], ev[e + 1])
+                k_ms["latent_values"][i] += hip.elapsed_ms(ev[e + 1], ev[e + 2])
+    hip.destroy(ev)
+
+    for r in runs:
+        res = r.out.cpu().numpy()
+        if not np.all(np.isfinite(res)):
+            raise SystemExit("non-finite attention output")
 
     ms_per_step = elapsed * 1e3 / a.steps
-    score_avg, value_avg = statistics.fmean(score_ms), statistics.fmean(value_ms)
-    key_bytes = B * T * Rk * esz                          # per launch of the score kernel
-    val_bytes = B * T * rv * esz                          # per launch of the value kernel
-    latent_bytes = key_bytes + val_bytes
-    kernels = {
-        "latent_scores": {"alg_bytes_per_launch": key_bytes, "avg_us": score_avg * 1e3,
-                          "median_us": statistics.median(score_ms) * 1e3,
-                          "gbs": key_bytes / (score_avg * 1e-3) / 1e9},
-        "latent_values": {"alg_bytes_per_launch": val_bytes, "avg_us": value_avg * 1e3,
-                          "median_us": statistics.median(value_ms) * 1e3,
-                          "gbs": val_bytes / (value_avg * 1e-3) / 1e9},
-    }
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    stream_gbs = latent_bytes / ((score_avg + value_avg) * 1e-3) / 1e9
-    step_gbs = latent_bytes / (ms_per_step * 1e-3) / 1e9
+    kernels = {}
+    for k in k_ms:
+        if k_launches[k] == 0:
+            continue
+        avg = statistics.fmean(k_ms[k])
+        kernels[k] = {"alg_bytes_per_step": k_bytes[k], "launches_per_step": k_launches[k],
+                      "avg_us_per_step": avg * 1e3,
+                      "avg_us_per_launch": avg * 1e3 / k_launches[k],
+                      "median_us_per_step": statistics.median(k_ms[k]) * 1e3,
+                      "gbs": k_bytes[k] / (avg * 1e-3) / 1e9}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us_per_step"])
+    total_bytes = sum(k_bytes.values())
+    stream_ms = sum(statistics.fmean(k_ms[k]) for k in kernels)
+    step_gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
+    desc.update({"splits": a.splits or "planner",
+                 "kv_gb_per_step": round(total_bytes / 1e9, 3),
+                 "kv_gbs_per_step": round(step_gbs, 1),
+                 "kv_hbm_frac_per_step": round(step_gbs / HBM_PEAK_GBS, 4),
+                 "kv_gbs_stream_kernels": round(total_bytes / (stream_ms * 1e-3) / 1e9, 1),
+                 "cached_tokens_per_s": B * runs[0].T / (ms_per_step * 1e-3)})
+    dk = kernels[dom]
     rec = {
         "metric": METRIC,
         "value": B / (ms_per_step * 1e-3),
@@ -220,25 +418,24 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "heads": H, "head_dim": d, "seq_len": T,
-                   "key_rank_sum": Rk, "value_rank": rv, "latent_dtype": w.dtype,
-                   "splits": a.splits or "planner",
-                   "latent_gbs_per_step": round(step_gbs, 1),
-                   "latent_hbm_frac_per_step": round(step_gbs / HBM_PEAK_GBS, 4),
-                   "latent_gbs_stream_kernels": round(stream_gbs, 1),
-                   "cached_tokens_per_s": B * T / (ms_per_step * 1e-3)},
+        "config": desc,
         "roofline": {"bound": "hbm", "kernel": dom,
-                     "achieved": kernels[dom]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": kernels[dom]["gbs"] / HBM_PEAK_GBS, "traffic": None,
-                     "kernel_avg_us": kernels[dom]["avg_us"],
-                     "alg_bytes_per_launch": kernels[dom]["alg_bytes_per_launch"]},
+                     "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "kernel_avg_us": dk["avg_us_per_launch"],
+                     "alg_bytes_per_launch": dk["alg_bytes_per_step"] // dk["launches_per_step"]},
         "kernels": kernels,
     }
-    if not a.no_cpu_baseline:
-        log(f"[bench] timing the oracle for ~{a.cpu_budget:.0f} s")
-        rec["cpu_baseline"] = cpu_baseline(ld, zk, zv, q, B, H, a.cpu_budget)
+    if sample is not None and sample.pairs:
+        import oracle
+        thr = oracle.threads()
+        rec["cpu_baseline"] = {
+            "value": B / sample.full_s, "unit": "tokens/s", "cores": thr, "kind": "oracle",
+            "sample": f"{sample.pairs} of {sample.total_pairs} (sequence, head, layer) pairs of the "
+                      f"same workload, full T, fp64, {sample.spent:.1f} s wall on {thr} threads; "
+                      f"scaled per layer to all pairs ({sample.full_s:.1f} s per step)"}
     print(json.dumps(rec), flush=True)
     return 0
 
