@@ -235,11 +235,18 @@ ValuePlan plan_values(const LayerInfo& li, int B, int nblk, int requested) {
     return vp;
 }
 
+// Exempt-layer splits: about three 4-wave workgroups per compute unit (the kernel's register
+// use allows three waves per SIMD). Each split is a whole number of 64-token blocks and no split
+// is empty.
+constexpr int kDenseTargetWorkgroups = 768;
+
 int plan_splits(int B, int64_t seq_len, int requested) {
     const int ntiles = static_cast<int>((seq_len + kTile - 1) / kTile);
-    int S = requested > 0 ? requested : (kTargetWorkgroups + std::max(B, 1) - 1) / std::max(B, 1);
+    int S = requested > 0 ? requested
+                          : (kDenseTargetWorkgroups + std::max(B, 1) - 1) / std::max(B, 1);
     S = std::max(1, std::min({S, ntiles, kMaxSplits}));
-    return S;
+    const int tps = (ntiles + S - 1) / S;
+    return (ntiles + tps - 1) / tps;
 }
 
 struct WorkspaceLayout {
