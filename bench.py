@@ -301,6 +301,10 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's split planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle wall seconds")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, stream this many MiB through one elementwise copy "
+                         "kernel (reads and writes that many bytes once): the reference for "
+                         "scaling HBM byte counters")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -327,6 +331,16 @@ def main(argv=None):
     ws_bytes = max(sk.starkv_decode_workspace_bytes(r.layer, B, r.T, a.splits) for r in runs)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
+
+    if a.copy_probe_mib > 0:
+        n = a.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {a.copy_probe_mib} MiB read + {a.copy_probe_mib} MiB written")
+        del src, dst
 
     stream = torch.cuda.current_stream()
     hip = HipEvents()

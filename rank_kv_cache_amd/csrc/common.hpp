@@ -111,7 +111,6 @@ __device__ __forceinline__ void sincos_rev(float x, float* c, float* s) {
 // ------------------------------------------------------------------------------------------------
 constexpr int kMaxHeads = 32;
 constexpr int kTile = 64;              // tokens per cache block
-constexpr int kScoreWaves = 8;         // waves per score workgroup
 constexpr int kFragLdsBytes = 96 * 1024;   // key-factor fragments of one head group in LDS
 constexpr int kMaxGroups = 32;
 constexpr int kValueWaves = 4;         // waves per value workgroup

@@ -126,8 +126,15 @@ template <int K, int MAXKS> struct KeyBuf<K, MAXKS, true> {
     u32x4 sc[MAXKS], zc[MAXKS];
 };
 
+// Waves per score workgroup: twelve (three per SIMD, at most 168 VGPRs each) where a unit's
+// registers allow it (16-bit latents, ranks up to 64), else eight with a two-deep register
+// pipeline over units.
+template <int K, int MAXKS, bool QK>
+constexpr int score_waves() { return (QK || MAXKS > 4 || K == kF32) ? 8 : 12; }
+
 template <int D, int K, int MAXKS, bool QK>
-__global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
+__global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_scores(const ScoreParams p) {
+    constexpr int NW = score_waves<K, MAXKS, QK>();
     constexpr int NF = D / 2;           // RoPE frequencies
     constexpr int HMT = D / 64;         // m-tile pairs (mt, mt + HMT)
     using Fr = typename Elem<K>::frag;
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
 
     __shared__ __attribute__((aligned(32))) T s_bk[kFragLdsBytes / sizeof(T)];
     __shared__ __attribute__((aligned(16))) float s_q[kMaxHeads * D];
-    __shared__ __attribute__((aligned(16))) float s_qr[kScoreWaves][2][D];
+    __shared__ __attribute__((aligned(16))) float s_qr[NW][2][D];
     __shared__ int s_slot[kMaxHeads + 1];
 
     // small per-layer tables, copied out of the kernel arguments so that every dynamic index
@@ -203,8 +210,8 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         const int n8 = s_rank[s] * D / 8;
         const Fr* src = reinterpret_cast<const Fr*>(bkt + (size_t)s_kgrp[s] * 16 * D);
         Fr* dst = reinterpret_cast<Fr*>(&s_bk[s_slot[s]]);
-        for (int i = tid; i < n8; i += 512) dst[i] = src[i];
-        for (int i = tid; i < D; i += 512) s_q[s * D + i] = qg[((size_t)b * H + h) * D + i] * q_scale;
+        for (int i = tid; i < n8; i += 64 * NW) dst[i] = src[i];
+        for (int i = tid; i < D; i += 64 * NW) s_q[s * D + i] = qg[((size_t)b * H + h) * D + i] * q_scale;
     }
 
     // ---- constant rotation by j*theta_i for this lane's column j and its frequencies ----
@@ -228,11 +235,11 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
     // bf16 / fp32 caches; the quantised groups for a mixed-precision cache, whose partial last
     // block is read from the binary16 tail afterwards)
     const int main_end = QK ? min(blk_end, p.full_blocks) : blk_end;
-    const int my_blocks = blk_begin + wave < main_end ? (main_end - blk_begin - wave + kScoreWaves - 1) / kScoreWaves : 0;
+    const int my_blocks = blk_begin + wave < main_end ? (main_end - blk_begin - wave + NW - 1) / NW : 0;
     const int nunits = my_blocks * ng;
 
     auto load_unit = [&](Buf& z, int u) __attribute__((always_inline)) {
-        const int blk = blk_begin + wave + kScoreWaves * (u / ng);
+        const int blk = blk_begin + wave + NW * (u / ng);
         const int s = u - (u / ng) * ng;
         const int nks = s_rank[s] >> 4;
         // Every slot is loaded (steps past the head's rank repeat its last step, a cache hit), so
@@ -361,7 +368,7 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
     };
 
     auto compute_unit = [&](const Buf& z, int u) __attribute__((always_inline)) {
-        const int blk = blk_begin + wave + kScoreWaves * (u / ng);
+        const int blk = blk_begin + wave + NW * (u / ng);
         const int s = u - (u / ng) * ng;
         if constexpr (!QK) {
             unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) { return z.z[nt][ks]; });
@@ -375,22 +382,32 @@ __global__ __launch_bounds__(512, 1) void latent_scores(const ScoreParams p) {
         }
     };
 
-    // Two-deep software pipeline over units. Prefetches past the last unit reload the last one
-    // (a cache hit) instead of being skipped, for the same reason as in load_unit.
-    Buf zA, zB;
-    if (nunits > 0) load_unit(zA, 0);
-    for (int u = 0; u < nunits; u += 2) {
-        load_unit(zB, min(u + 1, nunits - 1));
-        compute_unit(zA, u);
-        load_unit(zA, min(u + 2, nunits - 1));
-        if (u + 1 < nunits) compute_unit(zB, u + 1);
+    if constexpr (NW == 12) {
+        // One unit at a time: its loads are waited for inside it, and the other two waves of the
+        // SIMD cover the latency (a second register buffer would cost a wave per SIMD).
+        Buf zA;
+        for (int u = 0; u < nunits; ++u) {
+            load_unit(zA, u);
+            compute_unit(zA, u);
+        }
+    } else {
+        // Two-deep software pipeline over units. Prefetches past the last unit reload the last
+        // one (a cache hit) instead of being skipped, for the same reason as in load_unit.
+        Buf zA, zB;
+        if (nunits > 0) load_unit(zA, 0);
+        for (int u = 0; u < nunits; u += 2) {
+            load_unit(zB, min(u + 1, nunits - 1));
+            compute_unit(zA, u);
+            load_unit(zA, min(u + 2, nunits - 1));
+            if (u + 1 < nunits) compute_unit(zB, u + 1);
+        }
     }
 
     if constexpr (QK) {
         // the partial last block of a mixed-precision cache: its rows are still binary16 in the
         // tail buffer [B][64][Rk], token-major
         const int tb = p.full_blocks;
-        if (tb < blk_end && tb >= blk_begin && (tb - blk_begin) % kScoreWaves == wave) {
+        if (tb < blk_end && tb >= blk_begin && (tb - blk_begin) % NW == wave) {
             for (int s = 0; s < ng; ++s) {
                 const T* rowp = qtail + ((size_t)b * 64 + j) * Rk + 16 * s_kgrp[s] + 8 * half;
                 unit(tb, s, [&](int nt, int ks) __attribute__((always_inline)) {
@@ -786,7 +803,8 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
 // ------------------------------------------------------------------------------------------------
 template <int D, int K, int MAXKS, bool QK>
 static hipError_t launch_scores_t(const ScoreParams& p, int groups, int splits, hipStream_t st) {
-    hipLaunchKernelGGL((latent_scores<D, K, MAXKS, QK>), dim3(splits, groups, p.B), dim3(512), 0, st, p);
+    hipLaunchKernelGGL((latent_scores<D, K, MAXKS, QK>), dim3(splits, groups, p.B),
+                       dim3(64 * score_waves<K, MAXKS, QK>()), 0, st, p);
     return hipGetLastError();
 }
 
