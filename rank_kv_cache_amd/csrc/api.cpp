@@ -36,7 +36,7 @@ using namespace starkv;
 namespace {
 
 constexpr int kTargetWorkgroups = 256;   // MI355X compute units: one score workgroup per CU
-constexpr int kValueTargetWorkgroups = 768;   // three 4-wave value workgroups per CU
+constexpr int kValueTargetWorkgroups = 512;   // two 4-wave value workgroups per CU
 constexpr int kMaxScoreRounds = 4;
 constexpr int kMaxSplits = 256;
 constexpr size_t kAlign = 256;

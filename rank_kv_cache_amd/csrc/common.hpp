@@ -88,16 +88,49 @@ __device__ __forceinline__ f32x16 mma32<kF32>(const f32x8& a, const f32x8& b, f3
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// Wave-wide reductions (64 lanes).
+// Lane exchanges without LDS traffic: DPP inside rows of 16 lanes, permlane swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// (v[lane], v[lane ^ 16]) and (v[lane], v[lane ^ 32]) in some order; op(a, b) of the pair is the
+// same in every lane for a commutative op
+struct LanePair { float a, b; };
+__device__ __forceinline__ LanePair swap16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair swap32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// v + v[lane ^ 32]
+__device__ __forceinline__ float add_xor32(float v) {
+    const LanePair p = swap32(v);
+    return p.a + p.b;
+}
+
+// Wave-wide reductions (64 lanes): lane ^ 1, ^ 2 (quad permutations), the other quad of eight
+// (half-row mirror), the other eight of sixteen (row mirror), then the row swaps.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    LanePair p = swap16(v);
+    v = fmaxf(p.a, p.b);
+    p = swap32(v);
+    return fmaxf(p.a, p.b);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    LanePair p = swap16(v);
+    v = p.a + p.b;
+    p = swap32(v);
+    return p.a + p.b;
 }
 
 // cos and sin of 2*pi*x for x in [0, 1) (hardware v_cos_f32 / v_sin_f32 take revolutions).

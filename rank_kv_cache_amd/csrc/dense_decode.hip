@@ -44,15 +44,11 @@ template <> __device__ __forceinline__ void load8<kBF16>(const void* base, size_
 }
 
 // Sum over aligned groups of LPH (4 or 8) lanes with DPP lane permutations.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
 template <int LPH>
 __device__ __forceinline__ float group_sum(float v) {
-    v += dpp_f32<0xB1>(v);                     // quad_perm [1,0,3,2]: partner lane ^ 1
-    v += dpp_f32<0x4E>(v);                     // quad_perm [2,3,0,1]: partner lane ^ 2
-    if constexpr (LPH == 8) v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of eight
+    v += dpp_mov<0xB1>(v);                     // quad_perm [1,0,3,2]: partner lane ^ 1
+    v += dpp_mov<0x4E>(v);                     // quad_perm [2,3,0,1]: partner lane ^ 2
+    if constexpr (LPH == 8) v += dpp_mov<0x141>(v);   // row_half_mirror: the other quad of eight
     return v;
 }
 

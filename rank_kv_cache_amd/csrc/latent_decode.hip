@@ -353,7 +353,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         default: core(std::integral_constant<int, MAXKS>{}); break;
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sc[nt] += __shfl_xor(sc[nt], 32, 64);
+        for (int nt = 0; nt < 2; ++nt) sc[nt] = add_xor32(sc[nt]);
         const int tok = blk * 64 + lane;
         float my = half ? sc[1] : sc[0];
         if (tok >= seq_len) my = -INFINITY;
@@ -522,7 +522,7 @@ template <int K, int NTW> struct ValBuf<K, NTW, true> {
 };
 
 template <int K, int NTW, bool QV>
-__global__ __launch_bounds__(256) void latent_values(const ValueParams p) {
+__global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     using Fr = typename Elem<K>::frag;
     using Buf = ValBuf<K, NTW, QV>;
     using PF = ProbFrag<K>;
@@ -834,7 +834,9 @@ hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int 
     }
 }
 
-constexpr int kValueNTW = 2;
+// Four 32-channel tiles per wave: each probability fragment a wave loads and scales feeds 16
+// MFMAs, and a block's probabilities are read by 8 waves rather than 16.
+constexpr int kValueNTW = 4;
 int value_chunk_channels() { return kValueWaves * kValueNTW * 32; }
 
 hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, hipStream_t st) {
