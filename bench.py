@@ -39,6 +39,19 @@ DEFAULT_WORKLOAD = "longchat_b16_t32768_f16"
 MODEL_WORKLOAD = "model32_b32_t8192_f16"
 METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=16 T=32K"
 
+# HBM bytes per launch (read + written) measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the
+# current kernels, scaled by the factors a plain copy of known size gives (FETCH x 2.0, WRITE x
+# 1.0); the counter summaries are under profiles/. Kernels without an entry report null.
+MEASURED_TRAFFIC = {
+    ("longchat_b16_t32768_f16", "latent_scores"): 1_431_900_000,
+    ("longchat_b16_t32768_f16", "latent_values"): 1_145_800_000,
+    ("longchat_b16_t16384_q43", "latent_scores"): 510_300_000,
+    ("longchat_b16_t16384_q43", "latent_values"): 179_700_000,
+    ("model32_b32_t8192_f16", "dense_attention"): 4_310_900_000,
+    ("model32_b32_t8192_f16", "latent_scores"): 1_029_600_000,     # mean over the latent layers
+    ("model32_b32_t8192_f16", "latent_values"): 628_400_000,       # mean over the latent layers
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -437,7 +450,8 @@ def main(argv=None):
         "config": desc,
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": dk["gbs"] / HBM_PEAK_GBS,
+                     "traffic": MEASURED_TRAFFIC.get((desc["workload"], dom)),
                      "kernel_avg_us": dk["avg_us_per_launch"],
                      "alg_bytes_per_launch": dk["alg_bytes_per_step"] // dk["launches_per_step"]},
         "kernels": kernels,

@@ -197,7 +197,11 @@ starkv_status starkv_dequant(const starkv_layer *layer, const starkv_cache *cach
  * [n][C]); kind 1 rotates factor rows (dst = H^T . src, src/dst [C][n] with n = head_dim for keys,
  * H*d for values). fp16 in and out: each output is binary16 of (the exact signed sum of the
  * inputs) times the fp64 value of 1/sqrt(b). src and dst must not alias.
- * Errors: NULL, SHAPE (n < 0), DTYPE (not fp16), RANK_ALIGN, MISALIGNED.
+ * The layer's top fraction picks the split; src and dst are caller-owned device buffers of n * C
+ * binary16 values (C = R_k for which = 0, r_v for which = 1), 2-byte aligned. n = 0 returns OK
+ * without enqueuing. Errors (before anything is enqueued): NULL, SHAPE (which or kind not 0/1,
+ * n < 0, or kind 1 with n other than the factor's column count), DTYPE (layer cache type not
+ * F16 or Q43), UNSUPPORTED (dense layer), RANK_ALIGN, MISALIGNED.
  */
 starkv_status starkv_hadamard_rotate(const starkv_layer *layer, int32_t which, int32_t kind,
                                      int64_t n, const void *src, void *dst, void *stream);

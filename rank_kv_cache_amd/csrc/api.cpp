@@ -29,6 +29,7 @@ hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hip
 hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t st);
 hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st);
+hipError_t launch_hadamard_rotate(const HadamardParams& p, hipStream_t st);
 }  // namespace starkv
 
 using namespace starkv;
@@ -704,8 +705,46 @@ starkv_status starkv_hadamard_rotate(const starkv_layer* layer, int32_t which, i
     LayerInfo li;
     starkv_status s = check_layer(layer, &li);
     if (s != STARKV_OK) return s;
-    (void)which; (void)kind; (void)n; (void)src; (void)dst; (void)stream;
-    return STARKV_ERR_UNSUPPORTED;
+    if (li.dense) return STARKV_ERR_UNSUPPORTED;
+    if ((which != 0 && which != 1) || (kind != 0 && kind != 1) || n < 0) return STARKV_ERR_SHAPE;
+    if (li.cache_dt != STARKV_F16 && li.cache_dt != STARKV_Q43) return STARKV_ERR_DTYPE;
+    if (kind == 1 && n != (which == 0 ? li.D : static_cast<int64_t>(li.H) * li.D))
+        return STARKV_ERR_SHAPE;
+    if (n == 0) return STARKV_OK;
+    if (!src || !dst) return STARKV_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(src) & 1) || (reinterpret_cast<uintptr_t>(dst) & 1))
+        return STARKV_ERR_MISALIGNED;
+    HadamardParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.src = static_cast<const uint16_t*>(src);
+    p.dst = static_cast<uint16_t*>(dst);
+    p.n = n;
+    p.kind = kind;
+    p.C = which == 0 ? li.Rk : li.rv;
+    // each latent splits into its leading 4-bit channels and the rest; each part of width w is
+    // rotated in blocks of b = min(64, largest power of two dividing w)
+    auto add = [&](int start, int w) {
+        if (w <= 0) return;
+        int b = 1;
+        while (b < 64 && w % (2 * b) == 0) b *= 2;
+        p.seg_start[p.nseg] = start;
+        p.seg_width[p.nseg] = w;
+        p.seg_block[p.nseg] = b;
+        p.seg_inv[p.nseg] = 1.0 / std::sqrt(static_cast<double>(b));
+        ++p.nseg;
+    };
+    if (which == 0) {
+        for (int h = 0; h < li.H; ++h) {
+            const int nh = q43_hi_channels(li.rank[h], li.top_fraction);
+            add(li.koff[h], nh);
+            add(li.koff[h] + nh, li.rank[h] - nh);
+        }
+    } else {
+        const int nh = q43_hi_channels(li.rv, li.top_fraction);
+        add(0, nh);
+        add(nh, li.rv - nh);
+    }
+    return dev(launch_hadamard_rotate(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

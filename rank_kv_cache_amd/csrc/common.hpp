@@ -283,6 +283,23 @@ struct Q43QuantParams {
     long long pos, n;
 };
 
+// Blockwise Hadamard rotation of binary16 rows (kind 0: latent rows dst = src . H, [n][C]) or
+// factor rows (kind 1: dst = H^T . src, [C][ncols]); segments (start, width) cover the channels,
+// each rotated by blockdiag(H_b) with its block size b.
+constexpr int kMaxRotSegments = 2 * kMaxHeads;
+struct HadamardParams {
+    const uint16_t* src;
+    uint16_t* dst;
+    long long n;               // rows (kind 0) or columns (kind 1)
+    int C;                     // channels
+    int kind;
+    int nseg;
+    int seg_start[kMaxRotSegments];
+    int seg_width[kMaxRotSegments];
+    int seg_block[kMaxRotSegments];
+    double seg_inv[kMaxRotSegments];   // fp64 value of 1 / sqrt(block size)
+};
+
 struct Q43ReadParams {
     Q43Layout L;
     const void* codes;

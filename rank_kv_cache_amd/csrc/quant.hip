@@ -215,6 +215,76 @@ __global__ __launch_bounds__(256) void q43_readback(const Q43ReadParams p) {
     for (int e = 0; e < 8; ++e) dst[e] = v[e];
 }
 
+// ------------------------------------------------------------------------------------------------
+// Offline preparation: blockwise Hadamard rotation (Zhou notes, section 6.1 / Fig. 5), binary16 in
+// and out. Output element = binary16(fp64(exact signed sum of the b inputs) * fp64(1 / sqrt(b))):
+// the sum of at most 64 binary16 values is exact in fp64 (each is an integer multiple of 2^-24 below
+// 2^16), so only the product and the final conversion round.
+// ------------------------------------------------------------------------------------------------
+
+// binary64 -> binary16, round to nearest, ties to even (IEEE 754 conversion, written out on bits).
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+    const int e = (int)((u >> 52) & 0x7ff);
+    uint64_t m = u & ((1ull << 52) - 1);
+    if (e == 0x7ff) return sign | (m ? 0x7e00u : 0x7c00u);          // NaN, infinity
+    if (e == 0) return sign;                                           // fp64 subnormals -> 0
+    const int E = e - 1023;                                            // unbiased exponent
+    if (E > 15) return sign | 0x7c00u;                                  // overflow
+    m |= 1ull << 52;                                                   // significand, 53 bits
+    // binary16 keeps 11 significant bits for normals (E >= -14); fewer below, down to 2^-24
+    const int shift = (E >= -14) ? 42 : 42 + (-14 - E);
+    if (shift > 53) return sign;                                        // below half of 2^-24
+    const uint64_t q = m >> shift;
+    const uint64_t rem = m & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    uint64_t r = q + ((rem > half || (rem == half && (q & 1))) ? 1 : 0);
+    uint32_t bits;
+    if (E >= -14) {
+        // r in [2^10, 2^11]; a carry to 2^11 moves to the next binade
+        int ee = E + 15;
+        if (r == (1ull << 11)) { r >>= 1; ++ee; }
+        if (ee >= 31) return sign | 0x7c00u;
+        bits = ((uint32_t)ee << 10) | (uint32_t)(r & 0x3ff);
+    } else {
+        bits = (uint32_t)r;                                            // subnormal (or 2^-14 on carry)
+    }
+    return sign | (uint16_t)bits;
+}
+
+__global__ __launch_bounds__(256) void hadamard_rotate(const HadamardParams p) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= p.n * p.C) return;
+    // kind 0: element (row, c) = idx / C, idx % C; kind 1: (c, col) = idx / n, idx % n
+    const long long outer = p.kind == 0 ? idx / p.C : idx / p.n;
+    const long long inner = p.kind == 0 ? idx % p.C : idx % p.n;
+    const int c = (int)(p.kind == 0 ? inner : outer);
+    int g = 0;
+    while (g + 1 < p.nseg && c >= p.seg_start[g + 1]) ++g;
+    const int s0 = p.seg_start[g], b = p.seg_block[g];
+    const double inv = p.seg_inv[g];
+    const bool in_seg = c >= s0 && c < s0 + p.seg_width[g];
+    const size_t out_i = (size_t)idx;
+    if (!in_seg) { p.dst[out_i] = p.src[out_i]; return; }
+    const int j0 = s0 + ((c - s0) / b) * b, i = c - j0;
+    double acc = 0.0;
+    for (int j = 0; j < b; ++j) {
+        const size_t src_i = p.kind == 0 ? (size_t)outer * p.C + (size_t)(j0 + j)
+                                         : (size_t)(j0 + j) * (size_t)p.n + (size_t)inner;
+        const double v = (double)bits_f16(p.src[src_i]);
+        acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -v : v;
+    }
+    p.dst[out_i] = f64_to_f16_rne(acc * inv);
+}
+
+hipError_t launch_hadamard_rotate(const HadamardParams& p, hipStream_t st) {
+    const long long total = p.n * p.C;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(hadamard_rotate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t st) {
     if (ngroups <= 0) return hipSuccess;
     const dim3 grid(ngroups, (p.L.C + 63) / 64, p.B);

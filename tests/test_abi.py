@@ -141,3 +141,20 @@ def test_workspace_sizes_and_planner():
     assert w16 > w1 > 0
     assert sk.starkv_decode_workspace_bytes(L, 16, 0, 0) == 0
     assert sk.starkv_decode_workspace_bytes(None, 16, 10, 0) == 0
+
+
+def test_hadamard_validation():
+    """Argument checks of the rotation happen on the host before anything is enqueued."""
+    L16 = sk.Layer(num_heads=2, head_dim=64, key_ranks=(16, 32), value_rank=64, cache_dtype=sk.F16)
+    L32 = sk.Layer(num_heads=2, head_dim=64, key_ranks=(16, 32), value_rank=64, cache_dtype=sk.F32)
+    dense = sk.Layer(num_heads=2, head_dim=64, dense=True, cache_dtype=sk.F16)
+    rot = lambda *a: sk.starkv_hadamard_rotate(*a, check=False)
+    assert rot(L16, 2, 0, 4, FAKE, FAKE) == 2                # which
+    assert rot(L16, 0, 2, 4, FAKE, FAKE) == 2                # kind
+    assert rot(L16, 0, 0, -1, FAKE, FAKE) == 2
+    assert rot(L16, 0, 1, 63, FAKE, FAKE) == 2               # factor rows need head_dim columns
+    assert rot(L16, 1, 1, 64, FAKE, FAKE) == 2               # value factor: H * d columns
+    assert rot(L32, 0, 0, 4, FAKE, FAKE) == 4                # binary16 only
+    assert rot(dense, 0, 0, 4, FAKE, FAKE) == 8
+    assert rot(L16, 0, 0, 4, None, FAKE) == 1
+    assert rot(L16, 0, 0, 0, None, None) == 0                # nothing to rotate

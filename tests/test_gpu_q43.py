@@ -211,3 +211,37 @@ def test_q43_decode_full_size_sampled():
     e = rel_err(sub, ref)
     say(f"[q43 full] sampled {len(pairs)} pairs rel err {e:.3e}")
     assert np.all(np.isfinite(got)) and e <= 1e-2
+
+
+@pytest.mark.parametrize("which,kind", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_hadamard_rotate_bit_exact(which, kind):
+    """Device blockwise Hadamard rotation of binary16 latent rows (kind 0) and factor rows (kind 1)
+    equals the oracle's rotation bit for bit: exact signed sums, one fp64 product with 1/sqrt(b),
+    one rounding to binary16. Ranks include widths whose block size is below 64 (hi parts of 4, 12
+    channels; r_v = 272 splits into 68 + 204)."""
+    import torch
+    from rank_kv_cache_amd import buffers
+    H, d = 6, 128
+    ranks = [16, 48, 32, 64, 16, 80]
+    rv = 272
+    L = q43_layer(H, d, ranks, rv)
+    rng = np.random.default_rng(90 + 2 * which + kind)
+    C = sum(ranks) if which == 0 else rv
+    segs = oracle.latent_segments(ranks if which == 0 else [rv], FRAC)
+    if kind == 0:
+        n = 37
+        x = (rng.standard_normal((n, C)) * 3.0).astype(np.float16)
+        x[0, :8] = np.array([65504, -65504, 6e-8, -6e-8, 0, -0.0, 1e-5, 2.0], np.float16)
+        want = oracle.rotate_rows(x, segs)
+    else:
+        n = d if which == 0 else H * d
+        x = (rng.standard_normal((C, n)) / np.sqrt(16)).astype(np.float16)
+        want = oracle.rotate_factor(x, segs)
+    src = buffers.to_device(x)
+    dst = torch.full(x.shape, float("nan"), dtype=torch.float16, device="cuda")
+    sk.starkv_hadamard_rotate(L, which, kind, n, src, dst)
+    torch.cuda.synchronize()
+    got = buffers.to_host(dst)
+    bad = np.argwhere(got.view(np.uint16) != want.view(np.uint16))
+    say(f"[hadamard] which={which} kind={kind} mismatches {len(bad)}")
+    assert len(bad) == 0, bad[:5]
