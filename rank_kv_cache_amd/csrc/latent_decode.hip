@@ -126,11 +126,15 @@ template <int K, int MAXKS> struct KeyBuf<K, MAXKS, true> {
     u32x4 sc[MAXKS], zc[MAXKS];
 };
 
-// Waves per score workgroup: twelve (three per SIMD, at most 168 VGPRs each) where a unit's
-// registers allow it (16-bit latents, ranks up to 64), else eight with a two-deep register
-// pipeline over units.
+// Waves per score workgroup: twelve (three per SIMD, at most 168 VGPRs each) for 16-bit latents,
+// else eight with a two-deep register pipeline over units.
 template <int K, int MAXKS, bool QK>
-constexpr int score_waves() { return (QK || MAXKS > 4 || K == kF32) ? 8 : 12; }
+constexpr int score_waves() { return (QK || K == kF32) ? 8 : 12; }
+// With ranks above 64 at twelve waves, a unit's latents for both 32-token column tiles do not fit
+// the register budget: the second tile's fragments are loaded once the first tile's MFMAs have
+// consumed theirs.
+template <int K, int MAXKS, bool QK>
+constexpr bool score_split_loads() { return score_waves<K, MAXKS, QK>() == 12 && MAXKS > 4; }
 
 template <int D, int K, int MAXKS, bool QK>
 __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_scores(const ScoreParams p) {
@@ -304,11 +308,14 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         // arithmetic and the scheduler can overlap one pass's MFMAs with another's VALU work.
         auto core = [&](auto nks_c) __attribute__((always_inline)) {
             constexpr int NKS = decltype(nks_c)::value;
+            constexpr bool SPLIT = score_split_loads<K, MAXKS, QK>();
             Fr z[2][NKS];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int ks = 0; ks < NKS; ++ks) z[0][ks] = frag(0, ks);
+            if constexpr (!SPLIT) {
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) z[nt][ks] = frag(nt, ks);
+                for (int ks = 0; ks < NKS; ++ks) z[1][ks] = frag(1, ks);
+            }
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
@@ -322,6 +329,14 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
                         const Fr a1 = *reinterpret_cast<const Fr*>(fr + (((pp + HMT) * NKS + ks) * 64 + lane) * 8);
                         acc0 = mma32<K>(a0, z[nt][ks], acc0);
                         acc1 = mma32<K>(a1, z[nt][ks], acc1);
+                    }
+                    if (SPLIT && nt == 0 && pp == HMT - 1) {
+                        // the first tile's fragments are dead: load the second tile's here, and
+                        // keep the scheduler from hoisting the loads above this point
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) z[1][ks] = frag(1, ks);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
@@ -382,7 +397,17 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         }
     };
 
-    if constexpr (NW == 12) {
+    if constexpr (score_split_loads<K, MAXKS, QK>()) {
+        // One unit at a time, latent fragments loaded inside the unit, per column tile.
+        for (int u = 0; u < nunits; ++u) {
+            const int blk = blk_begin + wave + NW * (u / ng);
+            const int s = u - (u / ng) * ng;
+            const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
+            unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
+                return load_frag<K>(zk, base + (size_t)ks * 1024 + nt * 512);
+            });
+        }
+    } else if constexpr (NW == 12) {
         // One unit at a time: its loads are waited for inside it, and the other two waves of the
         // SIMD cover the latency (a second register buffer would cost a wave per SIMD).
         Buf zA;
