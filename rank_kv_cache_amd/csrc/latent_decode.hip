@@ -115,26 +115,20 @@ __device__ __forceinline__ f16x8 q43_key_frag(uint32_t w0, uint32_t w1, uint32_t
     return out;
 }
 
-// Latent source of the score kernel: binary16/bf16/fp32 fragments straight from the block layout,
-// or (QK) mixed 4/3-bit code windows plus scales / zero points, dequantised in registers.
-template <int K, int MAXKS, bool QK> struct KeyBuf;
-template <int K, int MAXKS> struct KeyBuf<K, MAXKS, false> {
+// Latent fragments of one unit held in registers (the paths that load a whole unit at once).
+template <int K, int MAXKS> struct KeyBuf {
     typename Elem<K>::frag z[2][MAXKS];
 };
-template <int K, int MAXKS> struct KeyBuf<K, MAXKS, true> {
-    uint32_t w[2][MAXKS][3];
-    u32x4 sc[MAXKS], zc[MAXKS];
-};
 
-// Waves per score workgroup: twelve (three per SIMD, at most 168 VGPRs each) for 16-bit latents,
-// else eight with a two-deep register pipeline over units.
+// Waves per score workgroup: twelve (three per SIMD, at most 168 VGPRs each) for 16-bit and
+// mixed 4/3-bit latents, else eight with a two-deep register pipeline over units.
 template <int K, int MAXKS, bool QK>
-constexpr int score_waves() { return (QK || K == kF32) ? 8 : 12; }
-// With ranks above 64 at twelve waves, a unit's latents for both 32-token column tiles do not fit
-// the register budget: the second tile's fragments are loaded once the first tile's MFMAs have
-// consumed theirs.
+constexpr int score_waves() { return K == kF32 ? 8 : 12; }
+// With ranks above 64 (or code windows plus scales and zero points) at twelve waves, a unit's
+// latents for both 32-token column tiles do not fit the register budget: the second tile's
+// fragments are loaded once the first tile's MFMAs have consumed theirs.
 template <int K, int MAXKS, bool QK>
-constexpr bool score_split_loads() { return score_waves<K, MAXKS, QK>() == 12 && MAXKS > 4; }
+constexpr bool score_split_loads() { return score_waves<K, MAXKS, QK>() == 12 && (QK || MAXKS > 4); }
 
 template <int D, int K, int MAXKS, bool QK>
 __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_scores(const ScoreParams p) {
@@ -144,7 +138,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     using Fr = typename Elem<K>::frag;
     using T = typename Elem<K>::storage;
     using PT = typename PStore<K>::T;
-    using Buf = KeyBuf<K, MAXKS, QK>;
+    using Buf = KeyBuf<K, MAXKS>;
 
     __shared__ __attribute__((aligned(32))) T s_bk[kFragLdsBytes / sizeof(T)];
     __shared__ __attribute__((aligned(16))) float s_q[kMaxHeads * D];
@@ -249,33 +243,12 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         // Every slot is loaded (steps past the head's rank repeat its last step, a cache hit), so
         // the number of loads in flight is static and the compiler's wait counts stay exact:
         // loads are retired in order, and a data-dependent count would force a full drain.
-        if constexpr (!QK) {
-            const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
+        const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int ks = 0; ks < MAXKS; ++ks)
-                    z.z[nt][ks] = load_frag<K>(zk, base + (size_t)min(ks, nks - 1) * 1024 + nt * 512);
-        } else {
-            const uint32_t* blkw = qcodes + (blk_base + blk) * qblock_words;
-            const uint16_t* meta = qmeta + (blk_base + blk) * 2 * (size_t)Rk;
-#pragma unroll
-            for (int ks = 0; ks < MAXKS; ++ks) {
-                const int k = min(ks, nks - 1);
-                const int n = s_gn[s][k];
-                const int c0 = 16 * (s_kgrp[s] + k) + 8 * half;
-                z.sc[ks] = *reinterpret_cast<const u32x4*>(meta + c0);
-                z.zc[ks] = *reinterpret_cast<const u32x4*>(meta + Rk + c0);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int rb = 8 * s_goff[s][k] + (32 * nt + j) * (48 + n);
-                    const uint32_t* wp = blkw + (rb >> 5);
-                    z.w[nt][ks][0] = wp[0];
-                    z.w[nt][ks][1] = wp[1];
-                    z.w[nt][ks][2] = wp[2];
-                }
-            }
-        }
+            for (int ks = 0; ks < MAXKS; ++ks)
+                z.z[nt][ks] = load_frag<K>(zk, base + (size_t)min(ks, nks - 1) * 1024 + nt * 512);
     };
 
     float cb[2] = {1.0f, 1.0f}, sb[2] = {0.0f, 0.0f};     // rotation by n0*theta_lane (lane < NF)
@@ -385,19 +358,10 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     auto compute_unit = [&](const Buf& z, int u) __attribute__((always_inline)) {
         const int blk = blk_begin + wave + NW * (u / ng);
         const int s = u - (u / ng) * ng;
-        if constexpr (!QK) {
-            unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) { return z.z[nt][ks]; });
-        } else {
-            unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
-                const int n = s_gn[s][ks];
-                const int rb = 8 * s_goff[s][ks] + (32 * nt + j) * (48 + n);
-                return q43_key_frag(z.w[nt][ks][0], z.w[nt][ks][1], z.w[nt][ks][2], rb & 31, n,
-                                    half, z.sc[ks], z.zc[ks]);
-            });
-        }
+        unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) { return z.z[nt][ks]; });
     };
 
-    if constexpr (score_split_loads<K, MAXKS, QK>()) {
+    if constexpr (score_split_loads<K, MAXKS, QK>() && !QK) {
         // One unit at a time, latent fragments loaded inside the unit, per column tile.
         for (int u = 0; u < nunits; ++u) {
             const int blk = blk_begin + wave + NW * (u / ng);
@@ -405,6 +369,24 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
             const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
             unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
                 return load_frag<K>(zk, base + (size_t)ks * 1024 + nt * 512);
+            });
+        }
+    } else if constexpr (score_split_loads<K, MAXKS, QK>()) {
+        // Mixed 4/3-bit codes: the code window, scales and zero points of each fragment are
+        // loaded inside the unit, per column tile, and dequantised in registers.
+        for (int u = 0; u < nunits; ++u) {
+            const int blk = blk_begin + wave + NW * (u / ng);
+            const int s = u - (u / ng) * ng;
+            const uint32_t* blkw = qcodes + (blk_base + blk) * qblock_words;
+            const uint16_t* meta = qmeta + (blk_base + blk) * 2 * (size_t)Rk;
+            unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
+                const int n = s_gn[s][ks];
+                const int c0 = 16 * (s_kgrp[s] + ks) + 8 * half;
+                const u32x4 sc = *reinterpret_cast<const u32x4*>(meta + c0);
+                const u32x4 zc = *reinterpret_cast<const u32x4*>(meta + Rk + c0);
+                const int rb = 8 * s_goff[s][ks] + (32 * nt + j) * (48 + n);
+                const uint32_t* wp = blkw + (rb >> 5);
+                return q43_key_frag(wp[0], wp[1], wp[2], rb & 31, n, half, sc, zc);
             });
         }
     } else if constexpr (NW == 12) {
