@@ -151,7 +151,7 @@ size_t starkv_decode_workspace_bytes(const starkv_layer *layer, int32_t batch, i
  *   workspace: device scratch of at least starkv_decode_workspace_bytes(...) bytes; contents on
  *   entry are ignored and clobbered.
  * For Q43 caches seq_len must equal the number of tokens appended so far (the unfinished group is
- * read from the tail). out and workspace must not alias any input.
+ * read from the tail), or be a multiple of 64 not above it. out and workspace must not alias any input.
  * Errors: NULL, SHAPE (seq_len < 1), CAPACITY (seq_len > capacity), DTYPE, MISALIGNED, WORKSPACE,
  * UNSUPPORTED. batch == 0 returns OK without enqueuing.
  */

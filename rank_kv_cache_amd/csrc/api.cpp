@@ -251,7 +251,7 @@ int plan_splits(int B, int64_t seq_len, int requested) {
 }
 
 struct WorkspaceLayout {
-    size_t bkt = 0, P = 0, stats = 0, ml = 0, acc = 0, a = 0, total = 0;
+    size_t bkt = 0, P = 0, stats = 0, ml = 0, acc = 0, total = 0;
     int S = 1, tps = 1, nblk = 1;
     ScorePlan sp;
     ValuePlan vp;
@@ -288,8 +288,6 @@ WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, in
     off += align_up(static_cast<size_t>(B) * w.S * li.H * 2 * sizeof(float));
     w.acc = off;
     off += align_up(static_cast<size_t>(B) * w.S * li.H * li.rv * sizeof(float));
-    w.a = off;
-    off += align_up(static_cast<size_t>(B) * li.H * li.rv * sizeof(float));
     w.total = off;
     return w;
 }
@@ -588,18 +586,11 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     vp.n_hi = li.q43 ? qv.n_hi : 0;
     if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, st))) != STARKV_OK) return s;
     if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
-    MergeParams m;
-    m.ws_ml = vp.ws_ml;
-    m.ws_acc = vp.ws_acc;
-    m.ws_a = reinterpret_cast<float*>(ws + w.a);
-    m.B = B;
-    m.H = li.H;
-    m.S = w.vp.splits;
-    m.W = li.rv;
-    m.active_splits = w.vp.splits;
-    if ((s = dev(launch_merge(m, st))) != STARKV_OK) return s;
+    // the split merge happens inside the projection kernel, while it loads its inputs
     ProjectParams pr;
-    pr.ws_a = m.ws_a;
+    pr.ws_ml = vp.ws_ml;
+    pr.ws_acc = vp.ws_acc;
+    pr.S = w.vp.splits;
     pr.bv = bv;
     pr.out = out;
     pr.B = B;

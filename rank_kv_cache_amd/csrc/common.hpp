@@ -223,10 +223,11 @@ struct MergeParams {
 };
 
 struct ProjectParams {
-    const float* ws_a;     // [B][H][rv]
+    const float* ws_ml;    // [B][S][H][2] split (max, sum)
+    const float* ws_acc;   // [B][S][H][rv] split partial sums, merged while loading
     const void* bv;        // [rv][H*D]
     float* out;            // [B][H][D]
-    int B, H, D, rv;
+    int B, H, D, rv, S;
 };
 
 struct DenseDecodeParams {

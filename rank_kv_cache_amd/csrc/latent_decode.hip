@@ -22,8 +22,9 @@
 //     M and sum L from the block statistics, then Acc[H x r_v] += (p * 2^(m_blk - M)) Z_v on MFMA
 //     with all heads stacked into one 32-row operand (notes, section 5.3), Z_v fragments
 //     streamed one block ahead in registers. Writes (M, L, Acc) per split.
-//  4. merge_splits: log-sum-exp weighted merge of the splits per (b, h), normalised.
-//  5. project_heads: out[b][h] = a[b][h] . B_v[:, h*d:(h+1)*d] for all b at once.
+//  4. project_heads: merges the splits per (b, h) (log-sum-exp weights, normalised) while it
+//     loads them, then out[b][h] = a[b][h] . B_v[:, h*d:(h+1)*d] for a batch of sequences.
+//  merge_splits (the same merge as a kernel of its own) finishes the exempt-layer path.
 
 #include <type_traits>
 
@@ -737,8 +738,9 @@ __global__ __launch_bounds__(256) void merge_splits(const MergeParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// 5. Output projection: out[b][h][j] = sum_c a[b][h][c] * B_v[c][h*D + j]. Workgroup (h, 64-column
-// tile, chunk of 8 batches), 16 waves; wave w sums the channels c = w + 16*i with lane = column
+// 5. Output projection: out[b][h][j] = sum_c a[b][h][c] * B_v[c][h*D + j], where a is the split
+// merge a = sum_s 2^(M_s - M) Acc_s / sum_s 2^(M_s - M) L_s formed while loading. Workgroup (h,
+// 64-column tile, chunk of 8 batches), 16 waves; wave w sums the channels c = w + 16*i with lane = column
 // (coalesced 128-byte rows of B_v) and the 8 batches' a[.][h][c] broadcast from LDS; the waves'
 // partial sums are reduced through LDS.
 // ------------------------------------------------------------------------------------------------
@@ -757,20 +759,46 @@ template <> __device__ __forceinline__ float load_scalar<kBF16>(const void* base
 constexpr int kProjBatch = 8;
 constexpr int kProjMaxRv = 2048;
 constexpr int kProjWaves = 16;
+constexpr int kMaxProjSplits = 256;   // value splits merged while loading
 
 template <int K>
 __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
     __shared__ __attribute__((aligned(16))) float s_a[kProjMaxRv * kProjBatch];
     __shared__ float s_red[kProjWaves][kProjBatch][64];
+    __shared__ float s_w[kProjBatch][kMaxProjSplits];
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int col = blockIdx.y * 64 + lane;
     const int b0 = blockIdx.z * kProjBatch;
     const int nb = min(kProjBatch, p.B - b0);
+    // split weights w_s = 2^(M_s - M) / sum_s 2^(M_s - M) L_s for each of the batch's sequences
+    // (wave bi, lanes over the splits)
+    if (wave < kProjBatch) {
+        const int bi = wave;
+        const float* ml = p.ws_ml + ((size_t)(b0 + min(bi, nb - 1)) * p.S * p.H + h) * 2;
+        const size_t sstride = (size_t)p.H * 2;
+        float M = -INFINITY;
+        for (int s = lane; s < p.S; s += 64) M = fmaxf(M, ml[s * sstride]);
+        M = wave_max(M);
+        float L = 0.0f;
+        for (int s = lane; s < p.S; s += 64) L += __builtin_amdgcn_exp2f(ml[s * sstride] - M) * ml[s * sstride + 1];
+        L = wave_sum(L);
+        const float inv_l = 1.0f / L;
+        for (int s = lane; s < p.S; s += 64)
+            s_w[bi][s] = bi < nb ? __builtin_amdgcn_exp2f(ml[s * sstride] - M) * inv_l : 0.0f;
+    }
+    __syncthreads();
+    // merged, normalised latent output a[b][h][c] of the batch's sequences, channel-major in LDS
+    const size_t sacc = (size_t)p.H * p.rv;
     for (int e = tid; e < kProjBatch * p.rv; e += 1024) {
         const int bi = e / p.rv, c = e - bi * p.rv;
-        s_a[c * kProjBatch + bi] = bi < nb ? p.ws_a[((size_t)(b0 + bi) * p.H + h) * p.rv + c] : 0.0f;
+        float a = 0.0f;
+        if (bi < nb) {
+            const float* acc = p.ws_acc + ((size_t)(b0 + bi) * p.S * p.H + h) * p.rv + c;
+            for (int s = 0; s < p.S; ++s) a = fmaf(s_w[bi][s], acc[s * sacc], a);
+        }
+        s_a[c * kProjBatch + bi] = a;
     }
     __syncthreads();
     float acc[kProjBatch];

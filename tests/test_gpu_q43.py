@@ -245,3 +245,30 @@ def test_hadamard_rotate_bit_exact(which, kind):
     bad = np.argwhere(got.view(np.uint16) != want.view(np.uint16))
     say(f"[hadamard] which={which} kind={kind} mismatches {len(bad)}")
     assert len(bad) == 0, bad[:5]
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 130])
+def test_q43_decode_short_lengths(T):
+    """Quantised caches holding only a tail (T < 64), exactly one group, and one group plus a
+    short tail, built by 1-token appends at the end; decode over all appended tokens."""
+    from rank_kv_cache_amd import buffers
+    from gpu_support import rel_err
+    H, d, B = 6, 128, 2
+    ranks = [16, 48, 32, 64, 16, 80]
+    rv = 272
+    cap = 192
+    w = synth.Workload("qs", batch=B, heads=H, head_dim=d, seq_len=T, dtype="f16", layer_seed=81,
+                       cache_seed=82 + T, value_rank=rv, power=0.5)
+    ld = synth.draw_layer(w, key_ranks=ranks)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = synth.draw_queries(83, T, B, H, d)
+    L = q43_layer(H, d, ranks, rv)
+    cache = buffers.alloc_cache(L, B, cap, fill=0xFF)
+    chunks = [T] if T < 3 else [T - 2, 1, 1]
+    _append(L, cache, zk, zv, chunks)
+    ref = _q43_reference(ld, zk, zv, q, ranks, rv, T, cap)
+    for S in (0, 2):
+        got = _gpu_decode(L, cache, T, q, ld.bk, ld.bv, S)
+        e = rel_err(got, ref)
+        say(f"[q43 short] T={T} splits={S} rel err {e:.3e}")
+        assert np.all(np.isfinite(got)) and e <= 2e-3
