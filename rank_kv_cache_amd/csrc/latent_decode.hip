@@ -790,15 +790,25 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
     }
     __syncthreads();
     // merged, normalised latent output a[b][h][c] of the batch's sequences, channel-major in LDS
-    const size_t sacc = (size_t)p.H * p.rv;
-    for (int e = tid; e < kProjBatch * p.rv; e += 1024) {
-        const int bi = e / p.rv, c = e - bi * p.rv;
-        float a = 0.0f;
+    // four channels per thread (16-byte loads), four splits in flight per step
+    const size_t sacc4 = (size_t)p.H * p.rv / 4;
+    const int rv4 = p.rv >> 2;
+    for (int e = tid; e < kProjBatch * rv4; e += 1024) {
+        const int bi = e / rv4, c4 = e - bi * rv4;
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bi < nb) {
-            const float* acc = p.ws_acc + ((size_t)(b0 + bi) * p.S * p.H + h) * p.rv + c;
-            for (int s = 0; s < p.S; ++s) a = fmaf(s_w[bi][s], acc[s * sacc], a);
+            const f32x4* acc = reinterpret_cast<const f32x4*>(
+                p.ws_acc + ((size_t)(b0 + bi) * p.S * p.H + h) * p.rv) + c4;
+            int s = 0;
+            for (; s + 4 <= p.S; s += 4) {
+                const f32x4 v0 = acc[(s + 0) * sacc4], v1 = acc[(s + 1) * sacc4];
+                const f32x4 v2 = acc[(s + 2) * sacc4], v3 = acc[(s + 3) * sacc4];
+                a += s_w[bi][s] * v0 + s_w[bi][s + 1] * v1 + s_w[bi][s + 2] * v2 + s_w[bi][s + 3] * v3;
+            }
+            for (; s < p.S; ++s) a += s_w[bi][s] * acc[s * sacc4];
         }
-        s_a[c * kProjBatch + bi] = a;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s_a[(4 * c4 + k) * kProjBatch + bi] = a[k];
     }
     __syncthreads();
     float acc[kProjBatch];
