@@ -740,8 +740,8 @@ __global__ __launch_bounds__(256) void merge_splits(const MergeParams p) {
 // ------------------------------------------------------------------------------------------------
 // 5. Output projection: out[b][h][j] = sum_c a[b][h][c] * B_v[c][h*D + j], where a is the split
 // merge a = sum_s 2^(M_s - M) Acc_s / sum_s 2^(M_s - M) L_s formed while loading. Workgroup (h,
-// 64-column tile, chunk of 8 batches), 16 waves; wave w sums the channels c = w + 16*i with lane = column
-// (coalesced 128-byte rows of B_v) and the 8 batches' a[.][h][c] broadcast from LDS; the waves'
+// 64-column tile, chunk of 4 sequences), 16 waves; wave w sums the channels c = w + 16*i with lane = column
+// (coalesced 128-byte rows of B_v) and the 4 sequences' a[.][h][c] broadcast from LDS; the waves'
 // partial sums are reduced through LDS.
 // ------------------------------------------------------------------------------------------------
 template <int K>
@@ -756,7 +756,7 @@ template <> __device__ __forceinline__ float load_scalar<kBF16>(const void* base
     return bf16_bits_to_float(static_cast<const uint16_t*>(base)[i]);
 }
 
-constexpr int kProjBatch = 8;
+constexpr int kProjBatch = 4;     // sequences per workgroup (a multiple of 4)
 constexpr int kProjMaxRv = 2048;
 constexpr int kProjWaves = 16;
 constexpr int kMaxProjSplits = 256;   // value splits merged while loading
@@ -820,12 +820,11 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
 #pragma unroll 8
     for (int c = wave; c < p.rv; c += kProjWaves) {
         const float w = load_scalar<K>(p.bv, (size_t)c * HD + cbase);
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_a[c * kProjBatch]);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_a[c * kProjBatch + 4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[e] += a0[e] * w;
-            acc[4 + e] += a1[e] * w;
+        for (int k4 = 0; k4 < kProjBatch / 4; ++k4) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(&s_a[c * kProjBatch + 4 * k4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * k4 + e] += a4[e] * w;
         }
     }
 #pragma unroll
