@@ -47,10 +47,12 @@ template <> struct Elem<kBF16> {
 };
 
 // Load 8 consecutive elements (16-byte aligned for 16-bit types, 32-byte for fp32).
+// Latent fragments are streamed once: non-temporal loads keep them from displacing data that is
+// re-read (probabilities, block statistics, factor fragments) in the caches.
 template <int K>
 __device__ __forceinline__ typename Elem<K>::frag load_frag(const void* base, size_t elem_off) {
     using F = typename Elem<K>::frag;
-    return *reinterpret_cast<const F*>(static_cast<const char*>(base) + elem_off * Elem<K>::bytes);
+    return __builtin_nontemporal_load(reinterpret_cast<const F*>(static_cast<const char*>(base) + elem_off * Elem<K>::bytes));
 }
 
 template <int K>

@@ -20,21 +20,22 @@
 
 namespace starkv {
 
-// Eight consecutive elements as fp32 (16-byte loads; 32 bytes for fp32).
+// Eight consecutive elements as fp32 (16-byte loads; 32 bytes for fp32), non-temporal: K and V
+// are streamed once.
 template <int K> __device__ __forceinline__ void load8(const void* base, size_t i, float* out);
 template <> __device__ __forceinline__ void load8<kF32>(const void* base, size_t i, float* out) {
     const f32x4* s = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
-    const f32x4 a = s[0], b = s[1];
+    const f32x4 a = __builtin_nontemporal_load(s), b = __builtin_nontemporal_load(s + 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) { out[e] = a[e]; out[4 + e] = b[e]; }
 }
 template <> __device__ __forceinline__ void load8<kF16>(const void* base, size_t i, float* out) {
-    const f16x8 v = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(base) + i);
+    const f16x8 v = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(base) + i));
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
 }
 template <> __device__ __forceinline__ void load8<kBF16>(const void* base, size_t i, float* out) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + i);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + i));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const uint32_t w = v[e];
