@@ -16,8 +16,8 @@
 namespace starkv {
 hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
                                 hipStream_t st);
-hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, hipStream_t st);
-int value_chunk_channels();
+hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, hipStream_t st);
+int value_tiles_per_wave(int rv);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
@@ -221,12 +221,14 @@ ScorePlan plan_scores(const LayerInfo& li, int B, int nblk) {
 }
 
 struct ValuePlan {
-    int chunks = 1, splits = 1, bps = 1;
+    int chunks = 1, splits = 1, bps = 1, ntw = 4;
 };
 
 ValuePlan plan_values(const LayerInfo& li, int B, int nblk, int requested) {
     ValuePlan vp;
-    vp.chunks = (li.rv + value_chunk_channels() - 1) / value_chunk_channels();
+    vp.ntw = li.cache_dt == STARKV_F32 ? 2 : value_tiles_per_wave(li.rv);   // fp32 operands: 2 tiles fit
+    const int chunk_channels = kValueWaves * vp.ntw * 32;
+    vp.chunks = (li.rv + chunk_channels - 1) / chunk_channels;
     const int per = std::max(1, B) * vp.chunks;
     int S = requested > 0 ? requested : (kValueTargetWorkgroups + per - 1) / per;
     S = std::max({1, std::min(S, nblk), (nblk + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit});
@@ -584,7 +586,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     vp.full_blocks = static_cast<int>(seq_len / kTile);
     vp.block_bytes = li.q43 ? qv.block_bytes : 0;
     vp.n_hi = li.q43 ? qv.n_hi : 0;
-    if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, st))) != STARKV_OK) return s;
+    if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, st))) != STARKV_OK) return s;
     if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
     // the split merge happens inside the projection kernel, while it loads its inputs
     ProjectParams pr;

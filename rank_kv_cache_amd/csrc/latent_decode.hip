@@ -878,21 +878,33 @@ hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int 
     }
 }
 
-// Four 32-channel tiles per wave: each probability fragment a wave loads and scales feeds 16
-// MFMAs, and a block's probabilities are read by 8 waves rather than 16.
-constexpr int kValueNTW = 4;
-int value_chunk_channels() { return kValueWaves * kValueNTW * 32; }
+// 32-channel tiles per value wave: four where r_v fills whole 512-channel chunks (each probability
+// fragment a wave loads and scales then feeds 16 MFMAs, and a block's probabilities are read by
+// half as many waves), two where that would leave a partly empty chunk (e.g. r_v = 768, 1280).
+int value_tiles_per_wave(int rv) {
+    const int tiles = (rv + 31) / 32;
+    const int waste4 = ((tiles + 4 * kValueWaves - 1) / (4 * kValueWaves)) * 4 * kValueWaves - tiles;
+    const int waste2 = ((tiles + 2 * kValueWaves - 1) / (2 * kValueWaves)) * 2 * kValueWaves - tiles;
+    return waste2 < waste4 ? 2 : 4;
+}
 
-hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, hipStream_t st) {
+template <int NTW>
+static hipError_t launch_values_t(const ValueParams& p, int elem, int chunks, hipStream_t st) {
     const dim3 grid(p.S, chunks, p.B);
     switch (elem) {
-    case kF32: hipLaunchKernelGGL((latent_values<kF32, kValueNTW, false>), grid, dim3(256), 0, st, p); break;
-    case kF16: hipLaunchKernelGGL((latent_values<kF16, kValueNTW, false>), grid, dim3(256), 0, st, p); break;
-    case kBF16: hipLaunchKernelGGL((latent_values<kBF16, kValueNTW, false>), grid, dim3(256), 0, st, p); break;
-    case -1: hipLaunchKernelGGL((latent_values<kF16, kValueNTW, true>), grid, dim3(256), 0, st, p); break;
+    case kF32: hipLaunchKernelGGL((latent_values<kF32, NTW, false>), grid, dim3(256), 0, st, p); break;
+    case kF16: hipLaunchKernelGGL((latent_values<kF16, NTW, false>), grid, dim3(256), 0, st, p); break;
+    case kBF16: hipLaunchKernelGGL((latent_values<kBF16, NTW, false>), grid, dim3(256), 0, st, p); break;
+    case -1: hipLaunchKernelGGL((latent_values<kF16, NTW, true>), grid, dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, hipStream_t st) {
+    if (ntw == 4) return launch_values_t<4>(p, elem, chunks, st);
+    if (ntw == 2) return launch_values_t<2>(p, elem, chunks, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t st) {
