@@ -366,15 +366,16 @@ int orc_hadamard_block(int width)
     return b;
 }
 
-/* Number of high-precision ("hi") channels of a latent of width r: ceil(frac * r), computed with
- * a 1e-9 guard so that products that are integers in exact arithmetic are not pushed up by fp
- * representation error. */
+/* Number of high-precision ("hi") channels of a latent of width r: ceil(frac * r). Reading: the
+ * fraction is a decimal such as 0.25 or 0.2 that reaches the library as a binary32 parameter, so
+ * products within 1e-4 of an integer are taken as that integer (0.2f * 80 = 16.0000002 -> 16);
+ * any product farther from an integer is rounded up. */
 int orc_n_hi(int r, double frac)
 {
     if (r <= 0)
         return 0;
     double x = frac * (double)r;
-    int n = (int)ceil(x - 1e-9);
+    int n = (int)ceil(x - 1e-4);
     if (n < 0)
         n = 0;
     if (n > r)

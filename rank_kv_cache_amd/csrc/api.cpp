@@ -124,10 +124,11 @@ starkv_status check_cache(const starkv_cache* c, const LayerInfo& li) {
     return STARKV_OK;
 }
 
-// Channels of a latent of width r kept at 4 bits: the leading ceil(top_fraction * r) (a 1e-9
-// guard keeps products that are integers in exact arithmetic from being pushed up).
+// Channels of a latent of width r kept at 4 bits: the leading ceil(top_fraction * r). The
+// fraction arrives as binary32, so products within 1e-4 of an integer count as that integer
+// (0.2f * 80 = 16.0000002 gives 16, not 17).
 int q43_hi_channels(int r, double frac) {
-    const int n = static_cast<int>(std::ceil(frac * r - 1e-9));
+    const int n = static_cast<int>(std::ceil(frac * r - 1e-4));
     return std::max(0, std::min(r, n));
 }
 

@@ -284,6 +284,12 @@ def test_segments_and_bits():
     assert bits.tolist() == [4] * 4 + [3] * 12 + [4] * 12 + [3] * 36
     assert oracle.n_hi(1024, 0.25) == 256 and oracle.n_hi(20, 0.2) == 4 and oracle.n_hi(16, 0.2) == 4
     assert oracle.n_hi(10, 0.0) == 0 and oracle.n_hi(10, 1.0) == 10
+    # the fraction as the library receives it (binary32): ceil of the exact decimal product
+    for r in range(16, 1025, 16):
+        for frac in (0.2, 0.25, 0.3, 0.1):
+            exact = -(-r * round(frac * 100) // 100)            # ceil(r * frac) in integers
+            assert oracle.n_hi(r, float(np.float32(frac))) == exact, (r, frac)
+            assert oracle.n_hi(r, frac) == exact, (r, frac)
 
 
 def test_rotation_absorbs_exactly():
