@@ -206,6 +206,21 @@ starkv_status starkv_dequant(const starkv_layer *layer, const starkv_cache *cach
 starkv_status starkv_hadamard_rotate(const starkv_layer *layer, int32_t which, int32_t kind,
                                      int64_t n, const void *src, void *dst, void *stream);
 
+/*
+ * Output projection of the layer (Zhou notes, Algorithm 2 step 8; section 5.3 folds W_o after
+ * the value step): y[b] = concat_h(out[b][h]) . W_o, i.e. y[b][n] = sum_{h,j} out[b][h][j] *
+ * wo[h*d + j][n].
+ *   o:  [batch][H*d] fp32, the per-head outputs of starkv_decode_attn (its `out`), 4-byte aligned.
+ *   wo: [H*d][hidden] row-major, the layer's factor type (latent layers) or cache type (dense
+ *       layers); aligned to its element size.
+ *   y:  [batch][hidden] fp32.
+ * All device buffers are caller-owned; y must not alias o or wo. batch == 0 returns OK without
+ * enqueuing. Errors (before anything is enqueued): NULL, SHAPE (batch < 0, hidden < 1), DTYPE,
+ * MISALIGNED, UNSUPPORTED (H*d above 4096).
+ */
+starkv_status starkv_output_projection(const starkv_layer *layer, int32_t batch, const float *o,
+                                      const void *wo, int32_t hidden, float *y, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *starkv_status_string(starkv_status status);
 

@@ -231,6 +231,14 @@ def decode_dense(k, v, q, *, rope_base=10000.0, scale=None, pairs=None, bf16=Fal
 # Blockwise Hadamard rotation and mixed-precision bookkeeping
 # ----------------------------------------------------------------------------------------------
 
+def output_projection(out: np.ndarray, wo: np.ndarray, bf16: bool = False) -> np.ndarray:
+    """Notes, Algorithm 2 step 8: y[b] = concat_h(out[b][h]) . W_o in fp64 (a plain matrix
+    product). out [B, H, d]; wo [H*d, hidden] (fp64 / fp32 / fp16, or bf16 bits with bf16=True)."""
+    o = np.asarray(out, dtype=np.float64)
+    B = o.shape[0]
+    return o.reshape(B, -1) @ to_f64(np.asarray(wo), bf16)
+
+
 def hadamard(n: int) -> np.ndarray:
     out = np.empty((n, n), np.float64)
     if lib().orc_hadamard(n, _dp(out)) != 0:

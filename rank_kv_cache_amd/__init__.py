@@ -19,7 +19,8 @@ __all__ = [
     "F32", "F16", "BF16", "Q43", "StarkvError", "Layer", "Cache", "lib", "library_path",
     "starkv_version", "starkv_status_string", "starkv_cache_bytes", "starkv_append_latents",
     "starkv_decode_workspace_bytes", "starkv_decode_attn", "starkv_dequant",
-    "starkv_hadamard_rotate", "starkv_decode_attn_timed", "EXPORTED_SYMBOLS",
+    "starkv_hadamard_rotate", "starkv_decode_attn_timed", "starkv_output_projection",
+    "EXPORTED_SYMBOLS",
 ]
 
 F32, F16, BF16, Q43 = 0, 1, 2, 3
@@ -28,7 +29,7 @@ _STATUS = ["OK", "ERR_NULL", "ERR_SHAPE", "ERR_RANK_ALIGN", "ERR_DTYPE", "ERR_MI
 
 EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decode_workspace_bytes",
                     "starkv_decode_attn", "starkv_decode_attn_timed", "starkv_dequant", "starkv_hadamard_rotate",
-                    "starkv_status_string", "starkv_version"]
+                    "starkv_output_projection", "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libstarkv.so")
@@ -87,6 +88,8 @@ def lib():
         L.starkv_dequant.argtypes = [LP, CP, i64, i64, i64, vp, vp, vp]
         L.starkv_hadamard_rotate.restype = C.c_int
         L.starkv_hadamard_rotate.argtypes = [LP, i32, i32, i64, vp, vp, vp]
+        L.starkv_output_projection.restype = C.c_int
+        L.starkv_output_projection.argtypes = [LP, i32, vp, vp, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -236,4 +239,12 @@ def starkv_hadamard_rotate(layer, which, kind, n, src, dst, stream=None, check=T
                                       _stream(stream))
     if check:
         _check(st, "starkv_hadamard_rotate")
+    return st
+
+
+def starkv_output_projection(layer, batch, o, wo, hidden, y, stream=None, check=True):
+    st = lib().starkv_output_projection(_layer_ptr(layer), batch, _ptr(o), _ptr(wo), hidden,
+                                        _ptr(y), _stream(stream))
+    if check:
+        _check(st, "starkv_output_projection")
     return st

@@ -18,6 +18,8 @@ hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int 
                                 hipStream_t st);
 hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, hipStream_t st);
 int value_tiles_per_wave(int rv);
+int out_projection_max_width();
+hipError_t launch_out_projection(const OutProjParams& p, int elem, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
@@ -739,6 +741,31 @@ starkv_status starkv_hadamard_rotate(const starkv_layer* layer, int32_t which, i
         add(nh, li.rv - nh);
     }
     return dev(launch_hadamard_rotate(p, static_cast<hipStream_t>(stream)));
+}
+
+starkv_status starkv_output_projection(const starkv_layer* layer, int32_t batch, const float* o,
+                                      const void* wo, int32_t hidden, float* y, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if (batch < 0 || hidden < 1) return STARKV_ERR_SHAPE;
+    const int kd = li.H * li.D;
+    if (kd > out_projection_max_width()) return STARKV_ERR_UNSUPPORTED;
+    if (batch == 0) return STARKV_OK;
+    if (!o || !wo || !y) return STARKV_ERR_NULL;
+    const int wdt = li.dense ? li.cache_dt : li.factor_dt;    // the layer's weight type
+    const int esz = elem_bytes(wdt);
+    if ((reinterpret_cast<uintptr_t>(o) & 3) || (reinterpret_cast<uintptr_t>(y) & 3) ||
+        (reinterpret_cast<uintptr_t>(wo) & (esz - 1)))
+        return STARKV_ERR_MISALIGNED;
+    OutProjParams p;
+    p.o = o;
+    p.wo = wo;
+    p.y = y;
+    p.B = batch;
+    p.Kd = kd;
+    p.N = hidden;
+    return dev(launch_out_projection(p, elem_kind(wdt), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -232,6 +232,13 @@ struct ProjectParams {
     int B, H, D, rv, S;
 };
 
+struct OutProjParams {
+    const float* o;        // [B][Kd] per-head attention outputs, heads concatenated (Kd = H*D)
+    const void* wo;        // [Kd][N] output projection
+    float* y;              // [B][N]
+    int B, Kd, N;
+};
+
 struct DenseDecodeParams {
     const void* k;         // [B][cap][H*D]
     const void* v;         // [B][cap][H*D]

@@ -158,3 +158,17 @@ def test_hadamard_validation():
     assert rot(dense, 0, 0, 4, FAKE, FAKE) == 8
     assert rot(L16, 0, 0, 4, None, FAKE) == 1
     assert rot(L16, 0, 0, 0, None, None) == 0                # nothing to rotate
+
+
+def test_output_projection_validation():
+    L = _latent()
+    op = lambda *a: sk.starkv_output_projection(*a, check=False)
+    assert op(L, -1, FAKE, FAKE, 8, FAKE) == 2
+    assert op(L, 2, FAKE, FAKE, 0, FAKE) == 2
+    assert op(L, 2, None, FAKE, 8, FAKE) == 1
+    assert op(L, 2, FAKE, FAKE, 8, 0x10002) == 5
+    assert op(L, 0, None, None, 8, None) == 0               # nothing to project
+    wide = sk.Layer(num_heads=64, head_dim=128, key_ranks=(16,) * 64, value_rank=64,
+                    cache_dtype=sk.F16)
+    assert op(wide, 2, FAKE, FAKE, 8, FAKE) == 8            # H*d = 8192 exceeds the kernel's row
+    assert op(_latent(cache_dtype=sk.F32), 2, FAKE, 0x10002, 8, FAKE) == 5   # fp32 W_o unaligned

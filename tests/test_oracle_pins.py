@@ -467,3 +467,24 @@ def test_ledger_model_bytes_consistent():
     mixed = dense[:3] + lay[3:]
     r2 = ledger.model_payload_bytes(4, 1000, dense) / ledger.model_payload_bytes(4, 1000, mixed)
     assert r2 == pytest.approx(ledger.whole_model_ratio(32, 3, 20.0), rel=1e-12)
+
+
+def test_output_projection_pins():
+    """Alg. 2 step 8 (y = concat_h(o_h) W_o): identity W_o returns the heads' outputs; one cached
+    token reduces the whole chain to that token's value through B_v then W_o (the latent value
+    path and the projection compose as one matrix product); W_o with one nonzero block per head
+    picks that head's output."""
+    rng = np.random.default_rng(17)
+    B, H, d, ranks, rv = 2, 3, 8, [4, 8, 2], 6
+    zk, zv, bk, bv, q = _rand_layer(rng, B, H, d, 30, ranks, rv)
+    o = oracle.decode_latent(zk, zv, bk, bv, q, ranks)
+    assert np.array_equal(oracle.output_projection(o, np.eye(H * d)), o.reshape(B, H * d))
+    hidden = 5
+    wo = rng.standard_normal((H * d, hidden))
+    zk1, zv1, bk1, bv1, q1 = _rand_layer(rng, B, H, d, 1, ranks, rv)
+    y1 = oracle.output_projection(oracle.decode_latent(zk1, zv1, bk1, bv1, q1, ranks), wo)
+    assert np.allclose(y1, zv1[:, 0, :] @ (bv1 @ wo), rtol=0, atol=1e-12)
+    for h in range(H):
+        sel = np.zeros((H * d, d))
+        sel[h * d:(h + 1) * d] = np.eye(d)
+        assert np.array_equal(oracle.output_projection(o, sel), o[:, h, :])
