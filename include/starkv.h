@@ -207,19 +207,67 @@ starkv_status starkv_hadamard_rotate(const starkv_layer *layer, int32_t which, i
                                      int64_t n, const void *src, void *dst, void *stream);
 
 /*
- * Output projection of the layer (Zhou notes, Algorithm 2 step 8; section 5.3 folds W_o after
+ * Rows times weights on the matrix cores: the two dense products around decode attention share
+ * one kernel pair (a split over the inner dimension, then a fixed-order sum of the split partials
+ * fused with the store). Weights are output-major (row n holds output n's inputs contiguously,
+ * the layout of a linear layer's weight). The fp32 input rows are split into two 16-bit parts
+ * (hi = nearest 16-bit value, lo = nearest 16-bit value of the remainder) and both are
+ * multiplied with fp32 accumulation, so results are within a few fp32 rounding errors of the
+ * exact products; inputs must lie within the binary16 range for fp16 weights. Every workspace is
+ * caller-owned device scratch of at least the queried size, 16-byte aligned; contents on entry
+ * are ignored and clobbered.
+ */
+
+/* Workspace bytes for starkv_output_projection (0 for an invalid layer, batch < 1 or hidden < 1). */
+size_t starkv_output_projection_workspace_bytes(const starkv_layer *layer, int32_t batch,
+                                               int32_t hidden);
+
+/*
+ * Output projection of the layer (Zhou notes, Algorithm 2 step 8; section 5.3 applies W_o after
  * the value step): y[b] = concat_h(out[b][h]) . W_o, i.e. y[b][n] = sum_{h,j} out[b][h][j] *
- * wo[h*d + j][n].
- *   o:  [batch][H*d] fp32, the per-head outputs of starkv_decode_attn (its `out`), 4-byte aligned.
- *   wo: [H*d][hidden] row-major, the layer's factor type (latent layers) or cache type (dense
- *       layers); aligned to its element size.
- *   y:  [batch][hidden] fp32.
- * All device buffers are caller-owned; y must not alias o or wo. batch == 0 returns OK without
- * enqueuing. Errors (before anything is enqueued): NULL, SHAPE (batch < 0, hidden < 1), DTYPE,
- * MISALIGNED, UNSUPPORTED (H*d above 4096).
+ * wo[n][h*d + j].
+ *   o:  [batch][H*d] fp32, the per-head outputs of starkv_decode_attn (its `out`).
+ *   wo: [hidden][H*d] output-major (W_o transposed), the layer's factor type (latent layers) or
+ *       cache type (dense layers).
+ *   y:  [batch][hidden] fp32, 4-byte aligned; o, wo and the workspace 16-byte aligned.
+ * y must not alias o, wo or the workspace. batch == 0 returns OK without enqueuing.
+ * Errors (before anything is enqueued): NULL, SHAPE (batch < 0, hidden < 1), DTYPE, MISALIGNED,
+ * WORKSPACE.
  */
 starkv_status starkv_output_projection(const starkv_layer *layer, int32_t batch, const float *o,
-                                      const void *wo, int32_t hidden, float *y, void *stream);
+                                      const void *wo, int32_t hidden, float *y, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for starkv_append_tokens (0 for an invalid layer, batch < 1, n_new < 1 or
+ * model_dim < 64). Does not depend on pos. */
+size_t starkv_append_tokens_workspace_bytes(const starkv_layer *layer, int32_t batch,
+                                            int64_t n_new, int32_t model_dim);
+
+/*
+ * Fused append front-end (Zhou notes, Algorithm 2 steps 1-3): project the new tokens' hidden
+ * states to their key and value latents and append them, without writing the latents anywhere
+ * but the cache:
+ *   zk_new[b][t] = x[b][t] . A_k (A_k: the heads' key down-projections side by side, R_k columns)
+ *   zv_new[b][t] = x[b][t] . A_v (r_v columns)
+ * each output rounded once (nearest-even) to the cache element type (binary16 for Q43), then
+ * stored exactly as starkv_append_latents stores zk_new / zv_new (Q43: rows go to the tail and a
+ * group this call completes is quantised). For Q43 layers the blockwise rotation is absorbed into
+ * the weights by the caller (section 6.1: the down-projection takes the rotation), so A_k and A_v
+ * here are the rotated ones. Dense layers: A_k, A_v are the full key and value projections
+ * (H*d columns each) and the keys are stored pre-RoPE.
+ *   x:   [batch][n_new][model_dim] fp32 hidden states; model_dim a multiple of 64.
+ *   a_k: [R_k][model_dim] output-major (A_k transposed; dense: [H*d][model_dim]), a_v:
+ *        [r_v][model_dim] (dense: [H*d][model_dim]); factor type (latent) or cache type (dense).
+ * Q43 appends are processed one 64-token group at a time (a call spanning g groups makes about
+ * 2g launches); as with starkv_append_latents, Q43 appends must be made in increasing, gap-free
+ * positions. Errors (before anything is enqueued): NULL, SHAPE (pos < 0, n_new < 0,
+ * model_dim < 1), CAPACITY (pos + n_new > capacity), DTYPE, MISALIGNED, WORKSPACE, UNSUPPORTED
+ * (model_dim not a multiple of 64). n_new == 0 or batch == 0 returns OK without enqueuing.
+ */
+starkv_status starkv_append_tokens(const starkv_layer *layer, const starkv_cache *cache,
+                                   int64_t pos, int64_t n_new, const float *x, int32_t model_dim,
+                                   const void *a_k, const void *a_v, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *starkv_status_string(starkv_status status);

@@ -47,6 +47,10 @@ def lib():
         L.orc_f64_to_f16.argtypes = [C.c_double]
         L.orc_bf16_to_f64.restype = C.c_double
         L.orc_bf16_to_f64.argtypes = [C.c_uint16]
+        L.orc_f64_to_bf16.restype = C.c_uint16
+        L.orc_f64_to_bf16.argtypes = [C.c_double]
+        L.orc_round_array.restype = None
+        L.orc_round_array.argtypes = [C.c_long, dp, C.c_int, vp]
         L.orc_rope_theta.restype = C.c_double
         L.orc_rope_theta.argtypes = [C.c_int, C.c_int, C.c_double]
         L.orc_rope.restype = None
@@ -136,6 +140,20 @@ def f16_to_f64(bits: int) -> float:
 
 def f64_to_f16(x: float) -> int:
     return int(lib().orc_f64_to_f16(float(x)))
+
+
+def f64_to_bf16(x: float) -> int:
+    return int(lib().orc_f64_to_bf16(float(x)))
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round fp64 values once, nearest-even, to a storage type: "f32" (float32 array), "f16"
+    (float16 array) or "bf16" (uint16 bit patterns)."""
+    x64 = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    code = {"f32": F32, "f16": F16, "bf16": BF16}[dtype]
+    out = np.empty(x64.shape, {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16}[dtype])
+    lib().orc_round_array(x64.size, _dp(x64), code, _vp(out))
+    return out.view(np.float16) if dtype == "f16" else out
 
 
 # ----------------------------------------------------------------------------------------------
@@ -231,12 +249,26 @@ def decode_dense(k, v, q, *, rope_base=10000.0, scale=None, pairs=None, bf16=Fal
 # Blockwise Hadamard rotation and mixed-precision bookkeeping
 # ----------------------------------------------------------------------------------------------
 
-def output_projection(out: np.ndarray, wo: np.ndarray, bf16: bool = False) -> np.ndarray:
+def output_projection(out: np.ndarray, wo_t: np.ndarray, bf16: bool = False) -> np.ndarray:
     """Notes, Algorithm 2 step 8: y[b] = concat_h(out[b][h]) . W_o in fp64 (a plain matrix
-    product). out [B, H, d]; wo [H*d, hidden] (fp64 / fp32 / fp16, or bf16 bits with bf16=True)."""
+    product). out [B, H, d]; wo_t = W_o transposed, [hidden, H*d] (fp64 / fp32 / fp16, or bf16
+    bits with bf16=True)."""
     o = np.asarray(out, dtype=np.float64)
     B = o.shape[0]
-    return o.reshape(B, -1) @ to_f64(np.asarray(wo), bf16)
+    return o.reshape(B, -1) @ to_f64(np.asarray(wo_t), bf16).T
+
+
+def project_tokens(x: np.ndarray, a_k_t: np.ndarray, a_v_t: np.ndarray, dtype: str):
+    """Notes, Algorithm 2 steps 1-2: the new tokens' key and value latents x . A_k and x . A_v in
+    fp64 (plain matrix products; any rotation is already inside the weights), each rounded once
+    to the storage type ("f32", "f16", "bf16"; binary16 for a mixed 4/3-bit cache).
+    x [B, n, D]; a_k_t = A_k transposed [C_k, D], a_v_t [C_v, D] (fp64 / fp32 / fp16, or bf16
+    bits when dtype is "bf16"). Returns (zk [B, n, C_k], zv [B, n, C_v]) in the storage type."""
+    bf16 = dtype == "bf16"
+    x64 = np.asarray(x, dtype=np.float64)
+    zk = x64 @ to_f64(np.asarray(a_k_t), bf16).T
+    zv = x64 @ to_f64(np.asarray(a_v_t), bf16).T
+    return round_to_storage(zk, dtype), round_to_storage(zv, dtype)
 
 
 def hadamard(n: int) -> np.ndarray:

@@ -102,6 +102,48 @@ double orc_bf16_to_f64(uint16_t b)
     return (double)f;
 }
 
+/* Round any double to the nearest bfloat16 (8 significant bits, the binary32 exponent range),
+ * ties to even; overflow goes to infinity. Rounded directly from the double, never through
+ * binary32, so no second rounding. */
+uint16_t orc_f64_to_bf16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7fc0;
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127))   /* max finite + half an ulp ties to even -> inf */
+        return sign | 0x7f80;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);                                  /* a in [2^(e-1), 2^e) */
+    int q = e - 8;                                 /* bfloat16 keeps 8 significant bits */
+    if (q < -133)
+        q = -133;                                  /* subnormal spacing 2^-133 */
+    double v = ldexp(nearbyint(ldexp(a, -q)), q);
+    if (v == 0.0)
+        return sign;
+    int e2;
+    frexp(v, &e2);
+    int E = e2 + 126;                              /* biased exponent of v */
+    if (E >= 1)
+        return sign | (uint16_t)(E << 7) | (uint16_t)((uint32_t)ldexp(v, 8 - e2) - 128u);
+    return sign | (uint16_t)ldexp(v, 133);
+}
+
+/* Round n doubles once to the storage type dt (F32: binary32 nearest-even, F16, BF16). */
+void orc_round_array(long n, const double *x, int dt, void *out)
+{
+    for (long i = 0; i < n; ++i) {
+        if (dt == ORC_F32)
+            ((float *)out)[i] = (float)x[i];
+        else if (dt == ORC_F16)
+            ((uint16_t *)out)[i] = orc_f64_to_f16(x[i]);
+        else
+            ((uint16_t *)out)[i] = orc_f64_to_bf16(x[i]);
+    }
+}
+
 static double load_elem(const void *p, int dt, size_t i)
 {
     switch (dt) {

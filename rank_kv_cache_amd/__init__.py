@@ -20,6 +20,8 @@ __all__ = [
     "starkv_version", "starkv_status_string", "starkv_cache_bytes", "starkv_append_latents",
     "starkv_decode_workspace_bytes", "starkv_decode_attn", "starkv_dequant",
     "starkv_hadamard_rotate", "starkv_decode_attn_timed", "starkv_output_projection",
+    "starkv_output_projection_workspace_bytes", "starkv_append_tokens",
+    "starkv_append_tokens_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -29,7 +31,9 @@ _STATUS = ["OK", "ERR_NULL", "ERR_SHAPE", "ERR_RANK_ALIGN", "ERR_DTYPE", "ERR_MI
 
 EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decode_workspace_bytes",
                     "starkv_decode_attn", "starkv_decode_attn_timed", "starkv_dequant", "starkv_hadamard_rotate",
-                    "starkv_output_projection", "starkv_status_string", "starkv_version"]
+                    "starkv_output_projection", "starkv_output_projection_workspace_bytes",
+                    "starkv_append_tokens", "starkv_append_tokens_workspace_bytes",
+                    "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libstarkv.so")
@@ -89,7 +93,13 @@ def lib():
         L.starkv_hadamard_rotate.restype = C.c_int
         L.starkv_hadamard_rotate.argtypes = [LP, i32, i32, i64, vp, vp, vp]
         L.starkv_output_projection.restype = C.c_int
-        L.starkv_output_projection.argtypes = [LP, i32, vp, vp, i32, vp, vp]
+        L.starkv_output_projection.argtypes = [LP, i32, vp, vp, i32, vp, vp, sz, vp]
+        L.starkv_output_projection_workspace_bytes.restype = sz
+        L.starkv_output_projection_workspace_bytes.argtypes = [LP, i32, i32]
+        L.starkv_append_tokens.restype = C.c_int
+        L.starkv_append_tokens.argtypes = [LP, CP, i64, i64, vp, i32, vp, vp, vp, sz, vp]
+        L.starkv_append_tokens_workspace_bytes.restype = sz
+        L.starkv_append_tokens_workspace_bytes.argtypes = [LP, i32, i64, i32]
         _lib = L
     return _lib
 
@@ -242,9 +252,30 @@ def starkv_hadamard_rotate(layer, which, kind, n, src, dst, stream=None, check=T
     return st
 
 
-def starkv_output_projection(layer, batch, o, wo, hidden, y, stream=None, check=True):
+def starkv_output_projection_workspace_bytes(layer, batch, hidden) -> int:
+    return int(lib().starkv_output_projection_workspace_bytes(_layer_ptr(layer), batch, hidden))
+
+
+def starkv_output_projection(layer, batch, o, wo, hidden, y, workspace=None, workspace_bytes=0,
+                             stream=None, check=True):
     st = lib().starkv_output_projection(_layer_ptr(layer), batch, _ptr(o), _ptr(wo), hidden,
-                                        _ptr(y), _stream(stream))
+                                        _ptr(y), _ptr(workspace), int(workspace_bytes),
+                                        _stream(stream))
     if check:
         _check(st, "starkv_output_projection")
+    return st
+
+
+def starkv_append_tokens_workspace_bytes(layer, batch, n_new, model_dim) -> int:
+    return int(lib().starkv_append_tokens_workspace_bytes(_layer_ptr(layer), batch, n_new,
+                                                          model_dim))
+
+
+def starkv_append_tokens(layer, cache, pos, n_new, x, model_dim, a_k, a_v, workspace=None,
+                         workspace_bytes=0, stream=None, check=True):
+    st = lib().starkv_append_tokens(_layer_ptr(layer), _cache_ptr(cache), pos, n_new, _ptr(x),
+                                    model_dim, _ptr(a_k), _ptr(a_v), _ptr(workspace),
+                                    int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "starkv_append_tokens")
     return st

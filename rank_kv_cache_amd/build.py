@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libstarkv.so")
 
-SOURCES = ["api.cpp", "latent_decode.hip", "dense_decode.hip", "cache_ops.hip", "quant.hip"]
+SOURCES = ["api.cpp", "latent_decode.hip", "dense_decode.hip", "cache_ops.hip", "quant.hip", "linear.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

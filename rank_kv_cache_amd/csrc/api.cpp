@@ -18,8 +18,8 @@ hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int 
                                 hipStream_t st);
 hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, hipStream_t st);
 int value_tiles_per_wave(int rv);
-int out_projection_max_width();
-hipError_t launch_out_projection(const OutProjParams& p, int elem, hipStream_t st);
+hipError_t launch_linear(const LinearParams& p, int elem, hipStream_t st);
+hipError_t launch_linear_store(const LinearStoreParams& p, int elem, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
@@ -308,6 +308,91 @@ float q_scale_of(const starkv_layer* L, int D) {
 }
 
 inline starkv_status dev(hipError_t e) { return e == hipSuccess ? STARKV_OK : STARKV_ERR_DEVICE; }
+
+// ---- rows x output-major weights (token down-projection, output projection) ----
+constexpr int kLinearTargetWorkgroups = 512;   // two 4-wave workgroups per CU
+constexpr int kLinearMaxRows = 1024;           // rows per launch (32 row tiles)
+
+// Splits of Kd: about two workgroups per CU, every wave of a workgroup with at least one 64-wide
+// K tile.
+int linear_splits(int64_t M, int N, int Kd) {
+    const int64_t tiles = ((N + 31) / 32) * ((M + 31) / 32);
+    const int64_t s = (kLinearTargetWorkgroups + tiles - 1) / tiles;
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, std::max(1, Kd / 64 / 4))));
+}
+
+// Partial-sum bytes of the largest launch over up to `rows` rows (launches never exceed
+// kLinearMaxRows rows; within a 32-row tile count the split count is fixed).
+size_t linear_workspace_bound(int64_t rows, int N, int Kd) {
+    const int64_t mmax = std::min<int64_t>(rows, kLinearMaxRows);
+    size_t best = 0;
+    for (int64_t tm = 1; tm <= (mmax + 31) / 32; ++tm) {
+        const int64_t m = std::min<int64_t>(32 * tm, mmax);
+        best = std::max(best, static_cast<size_t>(linear_splits(m, N, Kd)) * m * N * sizeof(float));
+    }
+    return align_up(best);
+}
+
+struct LinearRun {
+    const float* x = nullptr;
+    int64_t x_tokens = 1;          // rows of x per sequence
+    const void* w0 = nullptr;      // output rows [0, N0)
+    const void* w1 = nullptr;      // output rows [N0, N)
+    int N0 = 0, N = 0, Kd = 0;
+    int elem = kF16;               // weight type
+    float* part = nullptr;         // workspace
+    int kind = 0;                  // store (see LinearStoreParams)
+    int store_elem = kF32;
+    void* dst0 = nullptr;
+    void* dst1 = nullptr;
+    int64_t pos = 0, cap = 0;
+};
+
+// Rows (b, t) for every sequence b < B and tokens t0 <= t < t0 + tl, at most kLinearMaxRows rows
+// per launch pair.
+starkv_status run_linear(const LinearRun& r, int B, int64_t t0, int64_t tl, hipStream_t st) {
+    const int64_t tchunk = std::min<int64_t>(tl, kLinearMaxRows);
+    for (int64_t tc = t0; tc < t0 + tl; tc += tchunk) {
+        const int tn = static_cast<int>(std::min<int64_t>(tchunk, t0 + tl - tc));
+        const int bchunk = std::max(1, kLinearMaxRows / tn);
+        for (int b0 = 0; b0 < B; b0 += bchunk) {
+            const int nb = std::min(bchunk, B - b0);
+            LinearParams p;
+            p.x = r.x;
+            p.w0 = r.w0;
+            p.w1 = r.w1;
+            p.part = r.part;
+            p.M = nb * tn;
+            p.N = r.N;
+            p.N0 = r.N0;
+            p.Kd = r.Kd;
+            p.S = linear_splits(p.M, r.N, r.Kd);
+            p.b0 = b0;
+            p.t0 = static_cast<int>(tc);
+            p.tl = tn;
+            p.x_tokens = static_cast<int>(r.x_tokens);
+            starkv_status s = dev(launch_linear(p, r.elem, st));
+            if (s != STARKV_OK) return s;
+            LinearStoreParams q;
+            q.part = r.part;
+            q.dst0 = r.dst0;
+            q.dst1 = r.dst1;
+            q.M = p.M;
+            q.N = p.N;
+            q.N0 = p.N0;
+            q.S = p.S;
+            q.b0 = p.b0;
+            q.t0 = p.t0;
+            q.tl = p.tl;
+            q.x_tokens = p.x_tokens;
+            q.kind = r.kind;
+            q.pos = r.pos;
+            q.cap = r.cap;
+            if ((s = dev(launch_linear_store(q, r.store_elem, st))) != STARKV_OK) return s;
+        }
+    }
+    return STARKV_OK;
+}
 
 }  // namespace
 
@@ -743,29 +828,123 @@ starkv_status starkv_hadamard_rotate(const starkv_layer* layer, int32_t which, i
     return dev(launch_hadamard_rotate(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t starkv_output_projection_workspace_bytes(const starkv_layer* layer, int32_t batch,
+                                               int32_t hidden) {
+    LayerInfo li;
+    if (check_layer(layer, &li) != STARKV_OK || batch < 1 || hidden < 1) return 0;
+    return linear_workspace_bound(batch, hidden, li.H * li.D);
+}
+
 starkv_status starkv_output_projection(const starkv_layer* layer, int32_t batch, const float* o,
-                                      const void* wo, int32_t hidden, float* y, void* stream) {
+                                      const void* wo, int32_t hidden, float* y, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
     LayerInfo li;
     starkv_status s = check_layer(layer, &li);
     if (s != STARKV_OK) return s;
     if (batch < 0 || hidden < 1) return STARKV_ERR_SHAPE;
-    const int kd = li.H * li.D;
-    if (kd > out_projection_max_width()) return STARKV_ERR_UNSUPPORTED;
     if (batch == 0) return STARKV_OK;
-    if (!o || !wo || !y) return STARKV_ERR_NULL;
-    const int wdt = li.dense ? li.cache_dt : li.factor_dt;    // the layer's weight type
-    const int esz = elem_bytes(wdt);
-    if ((reinterpret_cast<uintptr_t>(o) & 3) || (reinterpret_cast<uintptr_t>(y) & 3) ||
-        (reinterpret_cast<uintptr_t>(wo) & (esz - 1)))
+    if (!o || !wo || !y || !workspace) return STARKV_ERR_NULL;
+    if (!aligned16(o) || !aligned16(wo) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(y) & 3))
         return STARKV_ERR_MISALIGNED;
-    OutProjParams p;
-    p.o = o;
-    p.wo = wo;
-    p.y = y;
-    p.B = batch;
-    p.Kd = kd;
-    p.N = hidden;
-    return dev(launch_out_projection(p, elem_kind(wdt), static_cast<hipStream_t>(stream)));
+    const int kd = li.H * li.D;
+    if (workspace_bytes < linear_workspace_bound(batch, hidden, kd)) return STARKV_ERR_WORKSPACE;
+    const int wdt = li.dense ? li.cache_dt : li.factor_dt;    // the layer's weight type
+    LinearRun r;
+    r.x = o;
+    r.x_tokens = 1;
+    r.w0 = wo;
+    r.w1 = wo;
+    r.N0 = hidden;
+    r.N = hidden;
+    r.Kd = kd;
+    r.elem = elem_kind(wdt);
+    r.kind = 0;
+    r.dst0 = y;
+    r.dst1 = y;
+    r.part = static_cast<float*>(workspace);
+    return run_linear(r, batch, 0, 1, static_cast<hipStream_t>(stream));
+}
+
+size_t starkv_append_tokens_workspace_bytes(const starkv_layer* layer, int32_t batch,
+                                            int64_t n_new, int32_t model_dim) {
+    LayerInfo li;
+    if (check_layer(layer, &li) != STARKV_OK || batch < 1 || n_new < 1 || model_dim < 64) return 0;
+    const int n_out = li.dense ? 2 * li.H * li.D : li.Rk + li.rv;
+    const int64_t rows = li.q43 ? static_cast<int64_t>(batch) * std::min<int64_t>(n_new, kTile)
+                                : static_cast<int64_t>(batch) * n_new;
+    return linear_workspace_bound(rows, n_out, model_dim);
+}
+
+starkv_status starkv_append_tokens(const starkv_layer* layer, const starkv_cache* cache,
+                                   int64_t pos, int64_t n_new, const float* x, int32_t model_dim,
+                                   const void* a_k, const void* a_v, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if ((s = check_cache(cache, li)) != STARKV_OK) return s;
+    if (pos < 0 || n_new < 0 || model_dim < 1) return STARKV_ERR_SHAPE;
+    if (model_dim % 64) return STARKV_ERR_UNSUPPORTED;
+    if (pos + n_new > cache->capacity) return STARKV_ERR_CAPACITY;
+    if (n_new > INT32_MAX) return STARKV_ERR_UNSUPPORTED;
+    if (n_new == 0 || cache->batch == 0) return STARKV_OK;
+    if (!x || !a_k || !a_v || !workspace) return STARKV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(a_k) || !aligned16(a_v) || !aligned16(workspace))
+        return STARKV_ERR_MISALIGNED;
+    const int B = cache->batch;
+    if (workspace_bytes < starkv_append_tokens_workspace_bytes(layer, B, n_new, model_dim))
+        return STARKV_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    LinearRun r;
+    r.x = x;
+    r.x_tokens = n_new;
+    r.w0 = a_k;
+    r.w1 = a_v;
+    r.N0 = li.dense ? li.H * li.D : li.Rk;
+    r.N = li.dense ? 2 * li.H * li.D : li.Rk + li.rv;
+    r.Kd = model_dim;
+    r.elem = elem_kind(li.dense ? li.cache_dt : li.factor_dt);
+    r.part = static_cast<float*>(workspace);
+    r.pos = pos;
+    if (!li.q43) {
+        r.kind = li.dense ? 2 : 1;
+        r.store_elem = elem_kind(li.cache_dt);
+        r.dst0 = cache->zk;
+        r.dst1 = cache->zv;
+        r.cap = li.dense ? cache->capacity : cache->capacity / kTile;
+        return run_linear(r, B, 0, n_new, st);
+    }
+    // mixed 4/3-bit cache: the binary16 rows go to the tail one 64-token group at a time; a group
+    // that this call completes is then quantised from the tail
+    r.kind = 3;
+    r.dst0 = cache->zk_tail;
+    r.dst1 = cache->zv_tail;
+    Q43Layout K, V;
+    q43_layouts(li, &K, &V);
+    for (int64_t t0 = 0; t0 < n_new;) {
+        const int64_t g_end = ((pos + t0) / kTile + 1) * kTile;
+        const int64_t t1 = std::min(n_new, g_end - pos);
+        if ((s = run_linear(r, B, t0, t1 - t0, st)) != STARKV_OK) return s;
+        if (pos + t1 == g_end) {
+            for (int which = 0; which < 2; ++which) {
+                Q43QuantParams q;
+                q.L = which ? V : K;
+                q.src = which ? cache->zv_tail : cache->zk_tail;   // every row comes from the tail
+                q.tail = q.src;
+                q.codes = which ? cache->zv : cache->zk;
+                q.meta = which ? cache->zv_meta : cache->zk_meta;
+                q.B = B;
+                q.nblk_cap = cache->capacity / kTile;
+                q.g_first = static_cast<int>(g_end / kTile) - 1;
+                q.pos = g_end;
+                q.n = 0;
+                if ((s = dev(launch_q43_quantize(q, 1, st))) != STARKV_OK) return s;
+            }
+        }
+        t0 = t1;
+    }
+    return STARKV_OK;
 }
 
 }  // extern "C"

@@ -232,11 +232,32 @@ struct ProjectParams {
     int B, H, D, rv, S;
 };
 
-struct OutProjParams {
-    const float* o;        // [B][Kd] per-head attention outputs, heads concatenated (Kd = H*D)
-    const void* wo;        // [Kd][N] output projection
-    float* y;              // [B][N]
-    int B, Kd, N;
+// Rows times a weight matrix, y[m][n] = sum_k x[m][k] W[n][k] (weights output-major: row n holds
+// output n's Kd weights), split over Kd. Row m of a launch is (sequence b0 + m / tl, token
+// t0 + m % tl) and reads x + (b * x_tokens + t) * Kd. Output rows [0, N0) use w0, [N0, N) use w1.
+struct LinearParams {
+    const float* x;
+    const void* w0;
+    const void* w1;
+    float* part;           // [S][M][N] partial sums, one slice per split of Kd
+    int M, N, N0, Kd, S;
+    int b0, t0, tl, x_tokens;
+};
+
+// Sum of the split partials and the store of row (b, t), output n:
+//   kind 0: fp32 y[(b * x_tokens + t) * N + n]
+//   kind 1: latent cache block layout, key channel n < N0 / value channel n - N0, token pos + t
+//   kind 2: dense cache rows [B][cap][N0] (keys) and [B][cap][N - N0] (values), token pos + t
+//   kind 3: binary16 tail rows [B][64][N0] / [B][64][N - N0], row (pos + t) % 64
+struct LinearStoreParams {
+    const float* part;
+    void* dst0;
+    void* dst1;
+    int M, N, N0, S;
+    int b0, t0, tl, x_tokens;
+    int kind;
+    long long pos;
+    long long cap;         // kind 1: capacity / 64 blocks; kind 2: capacity in tokens
 };
 
 struct DenseDecodeParams {

@@ -843,56 +843,6 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// 6. Output projection of the layer (Alg. 2 step 8): y[b][n] = sum_k o[b][k] W_o[k][n] with o the
-// heads' outputs concatenated (k = h*D + j). Workgroup (64-column tile, chunk of 4 sequences),
-// 16 waves; the chunk's o rows sit in LDS; wave w sums k = w + 16*i with lane = column (coalesced
-// rows of W_o), and the waves' partial sums are reduced through LDS.
-// ------------------------------------------------------------------------------------------------
-constexpr int kOutBatch = 4;
-constexpr int kOutMaxK = 4096;
-
-template <int K>
-__global__ __launch_bounds__(1024) void out_projection(const OutProjParams p) {
-    __shared__ __attribute__((aligned(16))) float s_o[kOutMaxK * kOutBatch];
-    __shared__ float s_red[kProjWaves][kOutBatch][64];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int col = blockIdx.x * 64 + lane;
-    const int b0 = blockIdx.y * kOutBatch;
-    const int nb = min(kOutBatch, p.B - b0);
-    for (int e = tid; e < kOutBatch * p.Kd; e += 1024) {
-        const int bi = e / p.Kd, k = e - bi * p.Kd;
-        s_o[k * kOutBatch + bi] = bi < nb ? p.o[(size_t)(b0 + bi) * p.Kd + k] : 0.0f;
-    }
-    __syncthreads();
-    float acc[kOutBatch];
-#pragma unroll
-    for (int i = 0; i < kOutBatch; ++i) acc[i] = 0.0f;
-    const bool colok = col < p.N;
-    const size_t cidx = colok ? col : 0;
-#pragma unroll 8
-    for (int k = wave; k < p.Kd; k += kProjWaves) {
-        const float w = load_scalar<K>(p.wo, (size_t)k * p.N + cidx);
-        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&s_o[k * kOutBatch]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += a4[e] * w;
-    }
-#pragma unroll
-    for (int i = 0; i < kOutBatch; ++i) s_red[wave][i][lane] = acc[i];
-    __syncthreads();
-    if (tid < kOutBatch * 64) {
-        const int i = tid >> 6, jc = tid & 63;
-        const int c2 = blockIdx.x * 64 + jc;
-        if (i < nb && c2 < p.N) {
-            float v = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kProjWaves; ++w) v += s_red[w][i][jc];
-            p.y[(size_t)(b0 + i) * p.N + c2] = v;
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------------------------
 // Host launchers
 // ------------------------------------------------------------------------------------------------
 template <int D, int K, int MAXKS, bool QK>
@@ -955,19 +905,6 @@ hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int 
     if (ntw == 4) return launch_values_t<4>(p, elem, chunks, st);
     if (ntw == 2) return launch_values_t<2>(p, elem, chunks, st);
     return hipErrorInvalidValue;
-}
-
-int out_projection_max_width() { return kOutMaxK; }
-
-hipError_t launch_out_projection(const OutProjParams& p, int elem, hipStream_t st) {
-    const dim3 grid((p.N + 63) / 64, (p.B + kOutBatch - 1) / kOutBatch);
-    switch (elem) {
-    case kF32: hipLaunchKernelGGL(out_projection<kF32>, grid, dim3(1024), 0, st, p); break;
-    case kF16: hipLaunchKernelGGL(out_projection<kF16>, grid, dim3(1024), 0, st, p); break;
-    case kBF16: hipLaunchKernelGGL(out_projection<kBF16>, grid, dim3(1024), 0, st, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t st) {

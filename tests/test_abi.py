@@ -162,13 +162,42 @@ def test_hadamard_validation():
 
 def test_output_projection_validation():
     L = _latent()
-    op = lambda *a: sk.starkv_output_projection(*a, check=False)
+    op = lambda *a, ws=FAKE, nws=1 << 40: sk.starkv_output_projection(*a, ws, nws, check=False)
     assert op(L, -1, FAKE, FAKE, 8, FAKE) == 2
     assert op(L, 2, FAKE, FAKE, 0, FAKE) == 2
     assert op(L, 2, None, FAKE, 8, FAKE) == 1
-    assert op(L, 2, FAKE, FAKE, 8, 0x10002) == 5
-    assert op(L, 0, None, None, 8, None) == 0               # nothing to project
-    wide = sk.Layer(num_heads=64, head_dim=128, key_ranks=(16,) * 64, value_rank=64,
-                    cache_dtype=sk.F16)
-    assert op(wide, 2, FAKE, FAKE, 8, FAKE) == 8            # H*d = 8192 exceeds the kernel's row
-    assert op(_latent(cache_dtype=sk.F32), 2, FAKE, 0x10002, 8, FAKE) == 5   # fp32 W_o unaligned
+    assert op(L, 2, FAKE, FAKE, 8, FAKE, ws=None) == 1
+    assert op(L, 2, FAKE, FAKE, 8, 0x10002) == 5               # y needs 4-byte alignment
+    assert op(L, 2, FAKE + 4, FAKE, 8, FAKE) == 5              # o needs 16
+    assert op(L, 2, FAKE, FAKE, 8, FAKE, nws=16) == 7
+    assert op(L, 0, None, None, 8, None, ws=None) == 0         # nothing to project
+
+
+def test_linear_workspace_sizes():
+    """Split planning is host arithmetic: about two 4-wave workgroups per CU, each wave at least
+    one 64-wide K tile; the workspace holds one fp32 [rows][outputs] slice per split."""
+    L = sk.Layer(num_heads=32, head_dim=128, key_ranks=(16, 32, 48, 64) * 8, value_rank=1024,
+                 cache_dtype=sk.F16)
+    # 128 output tiles of 32 x 1 row tile -> 4 splits of K = 4096
+    assert sk.starkv_output_projection_workspace_bytes(L, 16, 4096) == 4 * 16 * 4096 * 4
+    # R_k + r_v = 1280 + 1024 outputs (72 tiles) -> 8 splits
+    assert sk.starkv_append_tokens_workspace_bytes(L, 16, 1, 4096) == 8 * 16 * 2304 * 4
+    assert sk.starkv_output_projection_workspace_bytes(L, 0, 4096) == 0
+    assert sk.starkv_append_tokens_workspace_bytes(L, 16, 1, 32) == 0
+    # many rows: launches of at most 1024 rows, one split
+    assert sk.starkv_append_tokens_workspace_bytes(L, 16, 4096, 4096) == 1024 * 2304 * 4
+
+
+def test_append_tokens_validation():
+    L, Cc = _latent(), _cache()
+    at = lambda pos=0, n=1, x=FAKE, D=64, ak=FAKE, av=FAKE, ws=FAKE, nws=1 << 40, L=L, Cc=Cc: \
+        sk.starkv_append_tokens(L, Cc, pos, n, x, D, ak, av, ws, nws, check=False)
+    assert at(pos=-1) == 2 and at(n=-1) == 2 and at(D=0) == 2
+    assert at(D=96) == 8                                       # model_dim not a multiple of 64
+    assert at(pos=250, n=7) == 6                               # past the capacity (256)
+    assert at(n=0, x=None) == 0
+    assert at(x=None) == 1 and at(ak=None) == 1 and at(av=None) == 1 and at(ws=None) == 1
+    assert at(x=FAKE + 8) == 5 and at(ak=FAKE + 2) == 5
+    assert at(nws=0) == 7
+    assert at(L=_latent(cache_dtype=sk.BF16, factor_dtype=sk.F16)) == 4
+    assert at(Cc=_cache(batch=0), x=None) == 0

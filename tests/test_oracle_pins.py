@@ -480,11 +480,64 @@ def test_output_projection_pins():
     o = oracle.decode_latent(zk, zv, bk, bv, q, ranks)
     assert np.array_equal(oracle.output_projection(o, np.eye(H * d)), o.reshape(B, H * d))
     hidden = 5
-    wo = rng.standard_normal((H * d, hidden))
+    wo = rng.standard_normal((H * d, hidden))                # y = o . wo, passed transposed
     zk1, zv1, bk1, bv1, q1 = _rand_layer(rng, B, H, d, 1, ranks, rv)
-    y1 = oracle.output_projection(oracle.decode_latent(zk1, zv1, bk1, bv1, q1, ranks), wo)
+    y1 = oracle.output_projection(oracle.decode_latent(zk1, zv1, bk1, bv1, q1, ranks),
+                                  np.ascontiguousarray(wo.T))
     assert np.allclose(y1, zv1[:, 0, :] @ (bv1 @ wo), rtol=0, atol=1e-12)
     for h in range(H):
-        sel = np.zeros((H * d, d))
-        sel[h * d:(h + 1) * d] = np.eye(d)
+        sel = np.zeros((d, H * d))                           # output j reads head h's element j
+        sel[:, h * d:(h + 1) * d] = np.eye(d)
         assert np.array_equal(oracle.output_projection(o, sel), o[:, h, :])
+    # the transposed layout: output n reads row n of wo_t
+    wo_t = rng.standard_normal((hidden, H * d))
+    y = oracle.output_projection(o, wo_t)
+    for b in range(B):
+        for n in range(hidden):
+            assert np.isclose(y[b, n], sum(o.reshape(B, -1)[b, k] * wo_t[n, k] for k in range(H * d)),
+                              rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_rounding_pins():
+    """Nearest-even rounding of doubles to bfloat16 (8 significant bits, binary32 exponents),
+    from the format's definition; includes a case that rounding through binary32 would get wrong
+    (1 + 2^-8 + 2^-40 lies just above the tie between 1 and 1 + 2^-7)."""
+    r = oracle.f64_to_bf16
+    assert r(1.0) == 0x3F80 and r(-2.0) == 0xC000 and r(0.0) == 0 and r(-0.0) == 0x8000
+    assert r(1.0 + 2.0 ** -8) == 0x3F80                      # tie -> even (1.0)
+    assert r(1.0 + 3 * 2.0 ** -8) == 0x3F82                  # tie -> even (1 + 2^-6)
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81         # just above the tie: up
+    assert r(1.0 + 2.0 ** -8 - 2.0 ** -40) == 0x3F80
+    assert r(3.0e38) == 0x7F62 and r(3.4e38) == 0x7F80      # 3.4e38 is past max + half ulp
+    assert r(2.0 ** -133) == 0x0001 and r(2.0 ** -134) == 0  # smallest subnormal; tie -> 0
+    assert r(2.0 ** -126) == 0x0080                          # smallest normal
+    x = np.array([1.0, 1.0 + 2.0 ** -8 + 2.0 ** -40, -3.5, 2.0 ** -133])
+    assert oracle.round_to_storage(x, "bf16").tolist() == [0x3F80, 0x3F81, 0xC060, 0x0001]
+    assert oracle.round_to_storage(x, "f16").view(np.uint16).tolist() == \
+        [0x3C00, 0x3C04, 0xC300, 0x0000]                      # 1 + 2^-8 is exact in binary16
+    assert oracle.round_to_storage(x, "f32").tolist() == [1.0, 1.0 + 2.0 ** -8, -3.5, 2.0 ** -133]
+
+
+def test_project_tokens_pins():
+    """Alg. 2 steps 1-2: an identity down-projection returns the rounded hidden state; a one-hot
+    weight row copies one input; the key and value products are independent; each output is
+    the fp64 product rounded once (values chosen exactly representable stay exact)."""
+    rng = np.random.default_rng(23)
+    B, n, D = 2, 3, 8
+    x = rng.standard_normal((B, n, D))
+    zk, zv = oracle.project_tokens(x, np.eye(D), np.eye(D)[::-1].copy(), "f32")
+    assert np.array_equal(zk, x.astype(np.float32)) and np.array_equal(zv, x[..., ::-1].astype(np.float32))
+    sel = np.zeros((2, D))
+    sel[0, 5] = 1.0
+    sel[1, 2] = -2.0
+    zk, zv = oracle.project_tokens(x, sel, sel, "f16")
+    assert np.array_equal(zk.astype(np.float64)[..., 0], x[..., 5].astype(np.float16).astype(np.float64))
+    assert np.array_equal(zk, zv)
+    a = rng.standard_normal((5, D))
+    zk, _ = oracle.project_tokens(x, a, a, "bf16")
+    ref = np.einsum("bnd,cd->bnc", x, a)
+    assert zk.tolist() == [[[oracle.f64_to_bf16(v) for v in row] for row in seq] for seq in ref]
+    xi = rng.integers(-4, 5, (B, n, D)) * 0.25                 # exact dyadic products and sums
+    ai = rng.integers(-3, 4, (5, D)).astype(np.float16)
+    zk, _ = oracle.project_tokens(xi, ai, ai, "f16")
+    assert np.array_equal(zk.astype(np.float64), np.einsum("bnd,cd->bnc", xi, ai.astype(np.float64)))
