@@ -15,7 +15,9 @@ streaming kernel's algorithmic bytes (latent bytes it must read: key latents for
 value latent for the value kernel, codes plus scales / zero points for a mixed 4/3-bit cache,
 K and V for an exempt layer) are divided by its duration from HIP events recorded around its
 launch on the launch stream; the kernel with the largest total time is reported (all appear under
-``kernels``). ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
+``kernels``). ``projections`` times, apart from the step, the two dense products around a latent
+layer's attention (the fused token down-projection + append and the output projection) with HIP
+events. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
 pairs of the same workload, scaled to the whole workload.
 """
 from __future__ import annotations
@@ -68,6 +70,12 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def create(self, n):
         out = []
@@ -304,6 +312,64 @@ def setup_model(a, sk, buffers, synth, sample):
     return runs, desc, spec["dtype"], B
 
 
+def measure_projections(sk, buffers, run, B, stream, hip, steps, model_dim=4096, hidden=4096):
+    """The two dense products around one latent layer's attention, timed apart from the step with
+    HIP events on the launch stream: the fused append front-end (the new token's hidden state
+    projected to its key and value latents and stored in the cache at the step's position) and the
+    output projection of the heads' outputs (LLaMA-7B widths: hidden 4096). Weights are random in
+    the layer's factor type (binary16), inputs resident in HBM. Before each timed call a 512 MiB
+    buffer is rewritten so that the weights come from HBM, as in a decode step where the KV cache
+    stream evicts them from the last-level cache. Algorithmic bytes: the weights, the fp32 rows
+    read and the outputs written, each once."""
+    import torch
+    L = run.layer
+    H, d = L.num_heads, L.head_dim
+    Rk, rv = int(sum(L.key_ranks)), L.value_rank
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    a_k = (torch.randn((Rk, model_dim), device="cuda", generator=g) / model_dim ** 0.5).half()
+    a_v = (torch.randn((rv, model_dim), device="cuda", generator=g) / model_dim ** 0.5).half()
+    wo_t = (torch.randn((hidden, H * d), device="cuda", generator=g) / (H * d) ** 0.5).half()
+    x = torch.randn((B, 1, model_dim), device="cuda", generator=g)
+    y = torch.empty((B, hidden), dtype=torch.float32, device="cuda")
+    nws = max(sk.starkv_append_tokens_workspace_bytes(L, B, 1, model_dim),
+              sk.starkv_output_projection_workspace_bytes(L, B, hidden))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    sp = stream.cuda_stream
+    calls = {
+        "append_tokens": (lambda: sk.starkv_append_tokens(L, run.cache, run.T - 1, 1, x, model_dim,
+                                                          a_k, a_v, ws, nws, stream=stream),
+                          (Rk + rv) * model_dim * 2 + B * model_dim * 4 + B * (Rk + rv) * 2,
+                          f"B={B}: x [{B}][{model_dim}] fp32 -> {Rk} key + {rv} value latent "
+                          f"channels, binary16 weights"),
+        "output_projection": (lambda: sk.starkv_output_projection(L, B, run.out, wo_t, hidden, y,
+                                                                  ws, nws, stream=stream),
+                              hidden * H * d * 2 + B * H * d * 4 + B * hidden * 4,
+                              f"B={B}: o [{B}][{H * d}] fp32 -> y [{B}][{hidden}], binary16 W_o"),
+    }
+    res = {}
+    for name, (fn, nbytes, shape) in calls.items():
+        for _ in range(3):
+            fn()
+        ev = hip.create(2 * steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush.bitwise_not_()
+            hip.record(ev[2 * i], sp)
+            fn()
+            hip.record(ev[2 * i + 1], sp)
+        torch.cuda.synchronize()
+        us = statistics.fmean(hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps)) * 1e3
+        hip.destroy(ev)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"avg_us": us, "alg_bytes": nbytes, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                     "shape": shape}
+        log(f"[bench] {name}: {us:.2f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of HBM)")
+    del flush
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +380,8 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's split planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle wall seconds")
+    ap.add_argument("--no-projections", action="store_true",
+                    help="skip timing the token down-projection and the output projection")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, stream this many MiB through one elementwise copy "
                          "kernel (reads and writes that many bytes once): the reference for "
@@ -412,6 +480,11 @@ def main(argv=None):
         if not np.all(np.isfinite(res)):
             raise SystemExit("non-finite attention output")
 
+    projections = None
+    if not a.no_projections:
+        lat = [r for r in runs if not r.dense]
+        projections = measure_projections(sk, buffers, lat[0], B, stream, hip, a.steps)
+
     ms_per_step = elapsed * 1e3 / a.steps
     kernels = {}
     for k in k_ms:
@@ -456,6 +529,8 @@ def main(argv=None):
                      "alg_bytes_per_launch": dk["alg_bytes_per_step"] // dk["launches_per_step"]},
         "kernels": kernels,
     }
+    if projections is not None:
+        rec["projections"] = projections
     if sample is not None and sample.pairs:
         import oracle
         thr = oracle.threads()

@@ -19,6 +19,7 @@ hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int 
 hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, hipStream_t st);
 int value_tiles_per_wave(int rv);
 hipError_t launch_linear(const LinearParams& p, int elem, hipStream_t st);
+int linear_rows_per_workgroup(int elem);
 hipError_t launch_linear_store(const LinearStoreParams& p, int elem, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
@@ -315,20 +316,21 @@ constexpr int kLinearMaxRows = 1024;           // rows per launch (32 row tiles)
 
 // Splits of Kd: about two workgroups per CU, every wave of a workgroup with at least one 64-wide
 // K tile.
-int linear_splits(int64_t M, int N, int Kd) {
-    const int64_t tiles = ((N + 31) / 32) * ((M + 31) / 32);
+int linear_splits(int64_t M, int N, int Kd, int elem) {
+    const int rows = linear_rows_per_workgroup(elem);
+    const int64_t tiles = ((N + rows - 1) / rows) * ((M + 31) / 32);
     const int64_t s = (kLinearTargetWorkgroups + tiles - 1) / tiles;
     return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, std::max(1, Kd / 64 / 4))));
 }
 
 // Partial-sum bytes of the largest launch over up to `rows` rows (launches never exceed
 // kLinearMaxRows rows; within a 32-row tile count the split count is fixed).
-size_t linear_workspace_bound(int64_t rows, int N, int Kd) {
+size_t linear_workspace_bound(int64_t rows, int N, int Kd, int elem) {
     const int64_t mmax = std::min<int64_t>(rows, kLinearMaxRows);
     size_t best = 0;
     for (int64_t tm = 1; tm <= (mmax + 31) / 32; ++tm) {
         const int64_t m = std::min<int64_t>(32 * tm, mmax);
-        best = std::max(best, static_cast<size_t>(linear_splits(m, N, Kd)) * m * N * sizeof(float));
+        best = std::max(best, static_cast<size_t>(linear_splits(m, N, Kd, elem)) * m * N * sizeof(float));
     }
     return align_up(best);
 }
@@ -366,7 +368,7 @@ starkv_status run_linear(const LinearRun& r, int B, int64_t t0, int64_t tl, hipS
             p.N = r.N;
             p.N0 = r.N0;
             p.Kd = r.Kd;
-            p.S = linear_splits(p.M, r.N, r.Kd);
+            p.S = linear_splits(p.M, r.N, r.Kd, r.elem);
             p.b0 = b0;
             p.t0 = static_cast<int>(tc);
             p.tl = tn;
@@ -832,7 +834,8 @@ size_t starkv_output_projection_workspace_bytes(const starkv_layer* layer, int32
                                                int32_t hidden) {
     LayerInfo li;
     if (check_layer(layer, &li) != STARKV_OK || batch < 1 || hidden < 1) return 0;
-    return linear_workspace_bound(batch, hidden, li.H * li.D);
+    return linear_workspace_bound(batch, hidden, li.H * li.D,
+                                  elem_kind(li.dense ? li.cache_dt : li.factor_dt));
 }
 
 starkv_status starkv_output_projection(const starkv_layer* layer, int32_t batch, const float* o,
@@ -848,8 +851,9 @@ starkv_status starkv_output_projection(const starkv_layer* layer, int32_t batch,
         (reinterpret_cast<uintptr_t>(y) & 3))
         return STARKV_ERR_MISALIGNED;
     const int kd = li.H * li.D;
-    if (workspace_bytes < linear_workspace_bound(batch, hidden, kd)) return STARKV_ERR_WORKSPACE;
     const int wdt = li.dense ? li.cache_dt : li.factor_dt;    // the layer's weight type
+    if (workspace_bytes < linear_workspace_bound(batch, hidden, kd, elem_kind(wdt)))
+        return STARKV_ERR_WORKSPACE;
     LinearRun r;
     r.x = o;
     r.x_tokens = 1;
@@ -873,7 +877,8 @@ size_t starkv_append_tokens_workspace_bytes(const starkv_layer* layer, int32_t b
     const int n_out = li.dense ? 2 * li.H * li.D : li.Rk + li.rv;
     const int64_t rows = li.q43 ? static_cast<int64_t>(batch) * std::min<int64_t>(n_new, kTile)
                                 : static_cast<int64_t>(batch) * n_new;
-    return linear_workspace_bound(rows, n_out, model_dim);
+    return linear_workspace_bound(rows, n_out, model_dim,
+                                  elem_kind(li.dense ? li.cache_dt : li.factor_dt));
 }
 
 starkv_status starkv_append_tokens(const starkv_layer* layer, const starkv_cache* cache,
