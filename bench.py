@@ -45,13 +45,13 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 # current kernels, scaled by the factors a plain copy of known size gives (FETCH x 2.0, WRITE x
 # 1.0); the counter summaries are under profiles/. Kernels without an entry report null.
 MEASURED_TRAFFIC = {
-    ("longchat_b16_t32768_f16", "latent_scores"): 1_433_519_099,
-    ("longchat_b16_t32768_f16", "latent_values"): 1_171_252_142,
-    ("longchat_b16_t16384_q43", "latent_scores"): 213_436_701,
-    ("longchat_b16_t16384_q43", "latent_values"): 179_985_037,
-    ("model32_b32_t8192_f16", "dense_attention"): 4_310_993_077,
-    ("model32_b32_t8192_f16", "latent_scores"): 967_187_093,       # mean over the latent layers
-    ("model32_b32_t8192_f16", "latent_values"): 650_069_912,       # mean over the latent layers
+    ("longchat_b16_t32768_f16", "latent_scores"): 1_434_223_473,
+    ("longchat_b16_t32768_f16", "latent_values"): 1_171_038_503,
+    ("longchat_b16_t16384_q43", "latent_scores"): 213_450_100,
+    ("longchat_b16_t16384_q43", "latent_values"): 179_919_237,
+    ("model32_b32_t8192_f16", "dense_attention"): 4_310_875_245,
+    ("model32_b32_t8192_f16", "latent_scores"): 967_172_659,       # mean over the latent layers
+    ("model32_b32_t8192_f16", "latent_values"): 637_290_826,       # mean over the latent layers
 }
 
 
