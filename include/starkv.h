@@ -17,8 +17,14 @@
  *  - Validation runs on the host before anything is enqueued: a non-OK return means nothing was
  *    enqueued and no buffer was touched. A failed launch returns STARKV_ERR_DEVICE. Faults inside
  *    kernels surface at the caller's next synchronisation of the stream.
- *  - Shapes: num_heads in [1, 32]; head_dim 64 or 128; key and value ranks multiples of 16 with
- *    r_k[h] <= head_dim and 16 <= r_v <= 2048 (latent layers); capacity a multiple of 64.
+ *  - Shapes: num_heads in [1, 32]; head_dim 64 or 128; latent layers: 1 <= r_k[h] <= head_dim and
+ *    1 <= r_v <= 2048, multiples of 16 for Q43 caches; capacity a multiple of 64.
+ *  - Ranks and the 16-channel tile (Zhou notes, section 6.2: a kernel that rounds ranks to its
+ *    tile stores more coordinates than the chosen rank): fp caches store each head's key latent
+ *    and the value latent with their ranks rounded up to a multiple of 16; the extra channels are
+ *    written as zeros by every append, and the cache sizes count them. Everything the caller
+ *    passes or reads back (new rows, factors, read-back rows, down-projections) uses the true
+ *    ranks; in the layouts below, R_k and r_v of the cache are the rounded sums.
  *  - Bulk pointers must be 16-byte aligned.
  *  - Calls that write the same buffers must not overlap in time (use one stream per cache).
  *
@@ -69,7 +75,7 @@ typedef enum {
     STARKV_OK = 0,
     STARKV_ERR_NULL = 1,         /* a required pointer is NULL */
     STARKV_ERR_SHAPE = 2,        /* a size is negative, zero where it must not be, or inconsistent */
-    STARKV_ERR_RANK_ALIGN = 3,   /* a rank is not a multiple of 16, or exceeds its bound */
+    STARKV_ERR_RANK_ALIGN = 3,   /* a rank is out of bounds, or not a multiple of 16 for Q43 */
     STARKV_ERR_DTYPE = 4,        /* unknown dtype or unsupported cache/factor combination */
     STARKV_ERR_MISALIGNED = 5,   /* a bulk pointer is not 16-byte aligned */
     STARKV_ERR_CAPACITY = 6,     /* capacity not a multiple of 64, or a range beyond capacity */

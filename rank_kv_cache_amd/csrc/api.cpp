@@ -24,12 +24,14 @@ hipError_t launch_linear_store(const LinearStoreParams& p, int elem, hipStream_t
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
-                            const int16_t* rank, int elem, hipStream_t st);
+                            const int16_t* rank, const int16_t* soff, const int16_t* srank,
+                            int elem, hipStream_t st);
 hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
 hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st);
+hipError_t launch_padded_rows(const PaddedRowsParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t st);
 hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st);
 hipError_t launch_hadamard_rotate(const HadamardParams& p, hipStream_t st);
@@ -56,13 +58,18 @@ inline int elem_kind(int dt) {
     return dt == STARKV_F32 ? kF32 : dt == STARKV_BF16 ? kBF16 : kF16;
 }
 
+// Ranks as stored (rounded up to the 16-channel tile: rv, Rk, koff, rank) and as the caller
+// passes rows and factors (rv_src, Rk_src, soff, srank); `padded` when they differ.
 struct LayerInfo {
     int H = 0, D = 0, rv = 0, Rk = 0;
-    bool dense = false, q43 = false;
+    int rv_src = 0, Rk_src = 0;
+    bool dense = false, q43 = false, padded = false;
     int cache_dt = 0, factor_dt = 0;
     double top_fraction = 0.0;
     int16_t koff[kMaxHeads + 1] = {0};
     int16_t rank[kMaxHeads] = {0};
+    int16_t soff[kMaxHeads + 1] = {0};
+    int16_t srank[kMaxHeads] = {0};
 };
 
 // Validates the layer descriptor (host arithmetic only).
@@ -87,18 +94,29 @@ starkv_status check_layer(const starkv_layer* L, LayerInfo* out) {
     if (!L->key_ranks) return STARKV_ERR_NULL;
     const int want_factor = li.cache_dt == STARKV_Q43 ? STARKV_F16 : li.cache_dt;
     if (li.factor_dt != want_factor) return STARKV_ERR_DTYPE;
-    int off = 0;
+    // fp caches take any rank and store it rounded up to the 16-channel tile (zero channels);
+    // the mixed 4/3-bit layout is built on whole 16-channel groups and needs multiples of 16
+    const bool q43 = li.cache_dt == STARKV_Q43;
+    int off = 0, soff = 0;
     for (int h = 0; h < li.H; ++h) {
         const int r = L->key_ranks[h];
-        if (r < 16 || r > li.D || (r % 16)) return STARKV_ERR_RANK_ALIGN;
+        if (r < 1 || r > li.D || (q43 && r % 16)) return STARKV_ERR_RANK_ALIGN;
+        const int rp = (r + 15) / 16 * 16;
         li.koff[h] = static_cast<int16_t>(off);
-        li.rank[h] = static_cast<int16_t>(r);
-        off += r;
+        li.rank[h] = static_cast<int16_t>(rp);
+        li.soff[h] = static_cast<int16_t>(soff);
+        li.srank[h] = static_cast<int16_t>(r);
+        off += rp;
+        soff += r;
     }
     li.koff[li.H] = static_cast<int16_t>(off);
+    li.soff[li.H] = static_cast<int16_t>(soff);
     li.Rk = off;
-    li.rv = L->value_rank;
-    if (li.rv < 16 || (li.rv % 16) || li.rv > 2048) return STARKV_ERR_RANK_ALIGN;
+    li.Rk_src = soff;
+    li.rv_src = L->value_rank;
+    if (li.rv_src < 1 || li.rv_src > 2048 || (q43 && li.rv_src % 16)) return STARKV_ERR_RANK_ALIGN;
+    li.rv = (li.rv_src + 15) / 16 * 16;
+    li.padded = li.Rk != li.Rk_src || li.rv != li.rv_src;
     if (li.cache_dt == STARKV_Q43) {
         li.q43 = true;
         if (L->q_group != 64) return STARKV_ERR_UNSUPPORTED;
@@ -310,6 +328,46 @@ float q_scale_of(const starkv_layer* L, int D) {
 
 inline starkv_status dev(hipError_t e) { return e == hipSuccess ? STARKV_OK : STARKV_ERR_DEVICE; }
 
+PadMap pad_map(const LayerInfo& li) {
+    PadMap m;
+    std::memset(&m, 0, sizeof(m));
+    m.H = li.H;
+    m.rv = li.rv;
+    m.rv_src = li.rv_src;
+    for (int h = 0; h <= li.H; ++h) {
+        m.koff[h] = li.koff[h];
+        m.soff[h] = li.soff[h];
+    }
+    for (int h = 0; h < li.H; ++h) m.srank[h] = li.srank[h];
+    return m;
+}
+
+// Rows [B][n][C_src] of the key latent (zk_rows) and value latent (zv_rows) to or from cache
+// tokens t0 .. t0 + n - 1 of a layer whose ranks were rounded up (either pointer may be NULL).
+starkv_status copy_padded(const LayerInfo& li, const starkv_cache* cache, const void* zk_rows,
+                          const void* zv_rows, int to_cache, int64_t t0, int64_t n,
+                          hipStream_t st) {
+    for (int which = 0; which < 2; ++which) {
+        const void* rows = which ? zv_rows : zk_rows;
+        if (!rows) continue;
+        PaddedRowsParams p;
+        p.rows = rows;
+        p.cache = which ? cache->zv : cache->zk;
+        p.B = cache->batch;
+        p.nblk_cap = static_cast<int>(cache->capacity / kTile);
+        p.which = which;
+        p.C = which ? li.rv : li.Rk;
+        p.C_src = which ? li.rv_src : li.Rk_src;
+        p.to_cache = to_cache;
+        p.t0 = t0;
+        p.n = n;
+        p.map = pad_map(li);
+        const starkv_status s = dev(launch_padded_rows(p, elem_bytes(li.cache_dt), st));
+        if (s != STARKV_OK) return s;
+    }
+    return STARKV_OK;
+}
+
 // ---- rows x output-major weights (token down-projection, output projection) ----
 constexpr int kLinearTargetWorkgroups = 512;   // two 4-wave workgroups per CU
 constexpr int kLinearMaxRows = 1024;           // rows per launch (32 row tiles)
@@ -348,6 +406,8 @@ struct LinearRun {
     void* dst0 = nullptr;
     void* dst1 = nullptr;
     int64_t pos = 0, cap = 0;
+    bool padded = false;           // kind 1: stored ranks rounded up (see PadMap)
+    PadMap map{};
 };
 
 // Rows (b, t) for every sequence b < B and tokens t0 <= t < t0 + tl, at most kLinearMaxRows rows
@@ -390,6 +450,8 @@ starkv_status run_linear(const LinearRun& r, int B, int64_t t0, int64_t tl, hipS
             q.kind = r.kind;
             q.pos = r.pos;
             q.cap = r.cap;
+            q.padded = r.padded ? 1 : 0;
+            q.map = r.map;
             if ((s = dev(launch_linear_store(q, r.store_elem, st))) != STARKV_OK) return s;
         }
     }
@@ -527,6 +589,7 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
         }
         return STARKV_OK;
     }
+    if (li.padded) return copy_padded(li, cache, zk_new, zv_new, 1, pos, n_new, st);
     if (n_new <= kSmallAppend) {
         AppendSmallParams a;
         a.zk_src = zk_new;
@@ -619,7 +682,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
 
     const int ek = elem_kind(li.cache_dt);
     void* bkt = ws + w.bkt;
-    if ((s = dev(launch_pack_keys(bk, bkt, li.D, li.H, li.koff, li.rank, ek, st))) != STARKV_OK)
+    if ((s = dev(launch_pack_keys(bk, bkt, li.D, li.H, li.koff, li.rank, li.soff, li.srank, ek, st))) != STARKV_OK)
         return s;
     ScoreParams sp;
     std::memset(&sp, 0, sizeof(sp));
@@ -689,6 +752,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     pr.H = li.H;
     pr.D = li.D;
     pr.rv = li.rv;
+    pr.rv_src = li.rv_src;
     return dev(launch_project(pr, ek, st));
 }
 
@@ -762,6 +826,7 @@ starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cach
         }
         return STARKV_OK;
     }
+    if (li.padded) return copy_padded(li, cache, zk_out, zv_out, 0, t0, n, st);
     for (int which = 0; which < 2; ++which) {
         void* outp = which ? zv_out : zk_out;
         if (!outp) continue;
@@ -803,7 +868,7 @@ starkv_status starkv_hadamard_rotate(const starkv_layer* layer, int32_t which, i
     p.dst = static_cast<uint16_t*>(dst);
     p.n = n;
     p.kind = kind;
-    p.C = which == 0 ? li.Rk : li.rv;
+    p.C = which == 0 ? li.Rk_src : li.rv_src;
     // each latent splits into its leading 4-bit channels and the rest; each part of width w is
     // rotated in blocks of b = min(64, largest power of two dividing w)
     auto add = [&](int start, int w) {
@@ -818,14 +883,14 @@ starkv_status starkv_hadamard_rotate(const starkv_layer* layer, int32_t which, i
     };
     if (which == 0) {
         for (int h = 0; h < li.H; ++h) {
-            const int nh = q43_hi_channels(li.rank[h], li.top_fraction);
-            add(li.koff[h], nh);
-            add(li.koff[h] + nh, li.rank[h] - nh);
+            const int nh = q43_hi_channels(li.srank[h], li.top_fraction);
+            add(li.soff[h], nh);
+            add(li.soff[h] + nh, li.srank[h] - nh);
         }
     } else {
-        const int nh = q43_hi_channels(li.rv, li.top_fraction);
+        const int nh = q43_hi_channels(li.rv_src, li.top_fraction);
         add(0, nh);
-        add(nh, li.rv - nh);
+        add(nh, li.rv_src - nh);
     }
     return dev(launch_hadamard_rotate(p, static_cast<hipStream_t>(stream)));
 }
@@ -874,7 +939,7 @@ size_t starkv_append_tokens_workspace_bytes(const starkv_layer* layer, int32_t b
                                             int64_t n_new, int32_t model_dim) {
     LayerInfo li;
     if (check_layer(layer, &li) != STARKV_OK || batch < 1 || n_new < 1 || model_dim < 64) return 0;
-    const int n_out = li.dense ? 2 * li.H * li.D : li.Rk + li.rv;
+    const int n_out = li.dense ? 2 * li.H * li.D : li.Rk_src + li.rv_src;
     const int64_t rows = li.q43 ? static_cast<int64_t>(batch) * std::min<int64_t>(n_new, kTile)
                                 : static_cast<int64_t>(batch) * n_new;
     return linear_workspace_bound(rows, n_out, model_dim,
@@ -906,8 +971,10 @@ starkv_status starkv_append_tokens(const starkv_layer* layer, const starkv_cache
     r.x_tokens = n_new;
     r.w0 = a_k;
     r.w1 = a_v;
-    r.N0 = li.dense ? li.H * li.D : li.Rk;
-    r.N = li.dense ? 2 * li.H * li.D : li.Rk + li.rv;
+    r.N0 = li.dense ? li.H * li.D : li.Rk_src;
+    r.N = li.dense ? 2 * li.H * li.D : li.Rk_src + li.rv_src;
+    r.padded = li.padded;
+    if (li.padded) r.map = pad_map(li);
     r.Kd = model_dim;
     r.elem = elem_kind(li.dense ? li.cache_dt : li.factor_dt);
     r.part = static_cast<float*>(workspace);

@@ -103,6 +103,44 @@ __global__ __launch_bounds__(256) void append_small(const AppendSmallParams p) {
     }
 }
 
+// Latents whose ranks were rounded up to the 16-channel tile. Thread per (sequence, row, channel):
+// channels of the stored width when writing the cache (padding channels get zero, so that the
+// zero factor rows they meet never multiply stale memory), caller channels when reading back.
+template <typename E>
+__global__ __launch_bounds__(256) void padded_rows(const PaddedRowsParams p) {
+    const int C = p.to_cache ? p.C : p.C_src;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.B * p.n * C) return;
+    const int c = (int)(idx % C);
+    const long long bt = idx / C;
+    const long long row = bt % p.n;
+    const int b = (int)(bt / p.n);
+    const long long tok = p.t0 + row;
+    E* cache = static_cast<E*>(p.cache);
+    if (p.to_cache) {
+        const int cs = p.which ? (c < p.C_src ? c : -1) : src_key_channel(p.map, c);
+        const E v = cs >= 0 ? static_cast<const E*>(p.rows)[bt * p.C_src + cs] : E(0);
+        cache[p.which ? zv_block_index(b, p.nblk_cap, p.C, tok, c) : zk_block_index(b, p.nblk_cap, p.C, tok, c)] = v;
+    } else {
+        const int cc = p.which ? c : pad_key_channel(p.map, c);
+        static_cast<E*>(const_cast<void*>(p.rows))[bt * p.C_src + c] =
+            cache[p.which ? zv_block_index(b, p.nblk_cap, p.C, tok, cc) : zk_block_index(b, p.nblk_cap, p.C, tok, cc)];
+    }
+}
+
+hipError_t launch_padded_rows(const PaddedRowsParams& p, int elem_bytes, hipStream_t st) {
+    const long long n = (long long)p.B * p.n * (p.to_cache ? p.C : p.C_src);
+    if (n <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(padded_rows<uint16_t>, grid, dim3(256), 0, st, p);
+    else if (elem_bytes == 4)
+        hipLaunchKernelGGL(padded_rows<uint32_t>, grid, dim3(256), 0, st, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st) {
     const long long n = (long long)p.B * p.n * ((p.Rk + p.rv) / 8);
     const dim3 grid((unsigned)((n + 255) / 256));

@@ -165,6 +165,31 @@ __host__ __device__ inline size_t zv_block_index(size_t b, size_t nblk_cap, int 
            (size_t)((t & 63) >> 4) * 256 + (size_t)(c & 15) * 16 + (size_t)(t & 15);
 }
 
+// Ranks rounded up to the 16-channel tile: the cache stores each head's key latent with
+// rank[h] = 16 * ceil(srank[h] / 16) channels at koff[h] and the value latent with rv channels
+// (rv_src rounded up); the extra channels hold zeros. Callers' rows and factors keep the true
+// ranks srank[h] at soff[h] (and rv_src). For ranks that are already multiples of 16 both views
+// coincide.
+struct PadMap {
+    int H, rv, rv_src;
+    int16_t koff[kMaxHeads + 1];
+    int16_t soff[kMaxHeads + 1];
+    int16_t srank[kMaxHeads];
+};
+// stored key channel of caller channel c
+__device__ inline int pad_key_channel(const PadMap& m, int c) {
+    int h = 0;
+    while (h + 1 < m.H && c >= m.soff[h + 1]) ++h;
+    return m.koff[h] + (c - m.soff[h]);
+}
+// caller key channel of stored channel c, or -1 for a padding channel
+__device__ inline int src_key_channel(const PadMap& m, int c) {
+    int h = 0;
+    while (h + 1 < m.H && c >= m.koff[h + 1]) ++h;
+    const int local = c - m.koff[h];
+    return local < m.srank[h] ? m.soff[h] + local : -1;
+}
+
 // Mixed 4/3-bit code layout of one latent (see quant.hip for the byte layout).
 constexpr int kMaxKeyGroups = 256;          // R_k <= 4096
 struct Q43Layout {
@@ -227,9 +252,9 @@ struct MergeParams {
 struct ProjectParams {
     const float* ws_ml;    // [B][S][H][2] split (max, sum)
     const float* ws_acc;   // [B][S][H][rv] split partial sums, merged while loading
-    const void* bv;        // [rv][H*D]
+    const void* bv;        // [rv_src][H*D] (stored value channels past rv_src are zero)
     float* out;            // [B][H][D]
-    int B, H, D, rv, S;
+    int B, H, D, rv, S, rv_src;
 };
 
 // Rows times a weight matrix, y[m][n] = sum_k x[m][k] W[n][k] (weights output-major: row n holds
@@ -258,6 +283,8 @@ struct LinearStoreParams {
     int kind;
     long long pos;
     long long cap;         // kind 1: capacity / 64 blocks; kind 2: capacity in tokens
+    int padded;            // kind 1 with rounded ranks: outputs map through `map`, pads are zeroed
+    PadMap map;
 };
 
 struct DenseDecodeParams {
@@ -302,6 +329,17 @@ struct AppendSmallParams {
     void* zv;
     int B, Rk, rv, nblk_cap;
     long long pos, n;
+};
+
+// Rows of a latent with rounded ranks between the caller's layout [B][n][C_src] and the cache
+// (token t0 + row): to_cache writes every stored channel (zeros in the padding), otherwise the
+// caller channels are gathered back.
+struct PaddedRowsParams {
+    const void* rows;
+    void* cache;
+    int B, nblk_cap, which, C, C_src, to_cache;
+    long long t0, n;
+    PadMap map;
 };
 
 struct Q43QuantParams {

@@ -33,9 +33,10 @@
 namespace starkv {
 
 // ------------------------------------------------------------------------------------------------
-// 1. Key-factor packing: for head h (rank r, offset ko), fragment f = mt*(r/16) + ks, lane l holds
-// B_k[ko + 16*ks + 8*(l/32) + j][32*mt + l%32], j = 0..7, at element ko*D + (f*64 + l)*8 + j.
-// One thread per 8-element lane run.
+// 1. Key-factor packing: for head h (stored rank r, offset ko), fragment f = mt*(r/16) + ks, lane l
+// holds factor row k = 16*ks + 8*(l/32) + j of the head, column 32*mt + l%32, j = 0..7, at element
+// ko*D + (f*64 + l)*8 + j. The row is B_k[so + k] for k below the head's true rank (caller offset
+// so) and zero in the rounding of the rank up to 16. One thread per 8-element lane run.
 // ------------------------------------------------------------------------------------------------
 struct PackParams {
     const void* bk;
@@ -43,6 +44,8 @@ struct PackParams {
     int D, H, Rk;
     int16_t koff[kMaxHeads + 1];
     int16_t rank[kMaxHeads];
+    int16_t soff[kMaxHeads + 1];
+    int16_t srank[kMaxHeads];
 };
 
 template <int K>
@@ -59,11 +62,12 @@ __global__ __launch_bounds__(256) void pack_key_factors(const PackParams p) {
     const int f = local >> 9;
     const int mt = f / nks, ks = f - mt * nks;
     const int dim = 32 * mt + (l & 31);
-    const int r0 = ko + 16 * ks + 8 * (l >> 5);
+    const int k0 = 16 * ks + 8 * (l >> 5);
     const T* src = static_cast<const T*>(p.bk);
     T v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = src[(size_t)(r0 + j) * p.D + dim];
+    for (int j = 0; j < 8; ++j)
+        v[j] = k0 + j < p.srank[h] ? src[(size_t)(p.soff[h] + k0 + j) * p.D + dim] : T(0);
     T* dst = static_cast<T*>(p.bkt) + e0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) dst[j] = v[j];
@@ -818,7 +822,7 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
     const size_t HD = (size_t)p.H * p.D;
     const size_t cbase = (size_t)h * p.D + (colok ? col : 0);
 #pragma unroll 8
-    for (int c = wave; c < p.rv; c += kProjWaves) {
+    for (int c = wave; c < p.rv_src; c += kProjWaves) {     // stored channels past rv_src are zero
         const float w = load_scalar<K>(p.bv, (size_t)c * HD + cbase);
 #pragma unroll
         for (int k4 = 0; k4 < kProjBatch / 4; ++k4) {
@@ -925,7 +929,8 @@ hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st) {
 }
 
 hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
-                            const int16_t* rank, int elem, hipStream_t st) {
+                            const int16_t* rank, const int16_t* soff, const int16_t* srank,
+                            int elem, hipStream_t st) {
     PackParams p;
     p.bk = bk;
     p.bkt = bkt;
@@ -934,6 +939,8 @@ hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16
     p.Rk = koff[H];
     for (int h = 0; h <= H; ++h) p.koff[h] = koff[h];
     for (int h = 0; h < H; ++h) p.rank[h] = rank[h];
+    for (int h = 0; h <= H; ++h) p.soff[h] = soff[h];
+    for (int h = 0; h < H; ++h) p.srank[h] = srank[h];
     const int runs = p.Rk * D / 8;
     const dim3 grid((runs + 255) / 256);
     switch (elem) {

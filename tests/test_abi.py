@@ -67,10 +67,12 @@ def test_decode_validation():
     assert st_decode(_latent(cache_dtype=7), Cc) == E["DTYPE"]
     assert st_decode(_latent(factor_dtype=sk.F32), Cc) == E["DTYPE"]
     assert st_decode(_latent(cache_dtype=sk.Q43, factor_dtype=sk.BF16), Cc) == E["DTYPE"]
-    assert st_decode(_latent(key_ranks=(16, 32, 40, 64)), Cc) == E["RANK"]
+    # fp caches take any rank in [1, head_dim]; the mixed 4/3-bit layout needs multiples of 16
+    assert st_decode(_latent(cache_dtype=sk.Q43, key_ranks=(16, 32, 40, 64)), Cc) == E["RANK"]
     assert st_decode(_latent(key_ranks=(16, 32, 48, 144)), Cc) == E["RANK"]
     assert st_decode(_latent(key_ranks=(0, 32, 48, 64)), Cc) == E["RANK"]
-    assert st_decode(_latent(value_rank=100), Cc) == E["RANK"]
+    assert st_decode(_latent(cache_dtype=sk.Q43, value_rank=100), Cc) == E["RANK"]
+    assert st_decode(_latent(value_rank=0), Cc) == E["RANK"]
     assert st_decode(_latent(value_rank=4096), Cc) == E["RANK"]
     assert st_decode(_latent(value_rank=2064), Cc) == E["RANK"]
     assert st_decode(_latent(num_heads=40, key_ranks=(16,) * 40), Cc) == E["UNSUP"]
@@ -202,3 +204,20 @@ def test_append_tokens_validation():
     assert at(nws=0) == 7
     assert at(L=_latent(cache_dtype=sk.BF16, factor_dtype=sk.F16)) == 4
     assert at(Cc=_cache(batch=0), x=None) == 0
+
+
+def test_rounded_rank_sizes():
+    """Ranks that are not multiples of 16 are stored rounded up to the 16-channel tile (the extra
+    channels hold zeros): cache and workspace sizes follow the stored widths, while the token
+    append's projection works on the true ones."""
+    L = _latent(key_ranks=(5, 17, 30, 64), value_rank=100)
+    s = sk.starkv_cache_bytes(L, 3, 128)
+    assert s[0] == 3 * 128 * (16 + 32 + 32 + 64) * 2 and s[1] == 3 * 128 * 112 * 2
+    assert s[2:] == [0, 0, 0, 0]
+    L16 = _latent(key_ranks=(16, 32, 32, 64), value_rank=112)
+    assert sk.starkv_decode_workspace_bytes(L, 2, 1000) == sk.starkv_decode_workspace_bytes(L16, 2, 1000)
+    # append projection outputs: 5 + 17 + 30 + 64 = 116 key + 100 value channels in one tile
+    assert sk.starkv_append_tokens_workspace_bytes(L, 2, 1, 64) % 256 == 0
+    assert sk.starkv_append_tokens_workspace_bytes(L, 2, 1, 64) >= 2 * 216 * 4
+    fp32 = _latent(key_ranks=(1, 2, 3, 4), value_rank=1, cache_dtype=sk.F32)
+    assert sk.starkv_cache_bytes(fp32, 1, 64)[0] == 64 * 64 * 4
