@@ -167,6 +167,35 @@ starkv_status starkv_decode_attn(const starkv_layer *layer, const starkv_cache *
                                  size_t workspace_bytes, void *stream);
 
 /*
+ * Ragged batches (serving): every sequence of the batch has its own length. seq_lens is a device
+ * array of batch int32 lengths (4-byte aligned); each is clamped to [0, max_seq_len], and
+ * max_seq_len (host) plans the splits and sizes the workspace exactly as seq_len does for
+ * starkv_decode_attn (use starkv_decode_workspace_bytes with max_seq_len). Sequence b attends to
+ * its first seq_lens[b] cached tokens; splits past its end contribute nothing; a length of 0
+ * gives an all-zero output row. For Q43 caches each length must equal the tokens appended to
+ * that sequence or be a multiple of 64 not above it. Everything else is as starkv_decode_attn.
+ * Errors: those of starkv_decode_attn with seq_len = max_seq_len; NULL (seq_lens), MISALIGNED.
+ */
+starkv_status starkv_decode_attn_ragged(const starkv_layer *layer, const starkv_cache *cache,
+                                        int64_t max_seq_len, const int32_t *seq_lens,
+                                        const float *q, const void *bk, const void *bv,
+                                        float *out, int32_t num_splits, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/*
+ * One new token per sequence at its own position (the append step of a ragged decode batch,
+ * Alg. 2 steps 1-3): positions is a device array of batch int32 positions (4-byte aligned);
+ * sequence b's rows zk_new[b] ([batch][R_k] with the caller's ranks; dense: [batch][H*d]) and
+ * zv_new[b] go to cache token positions[b]. A position outside [0, capacity) skips that sequence
+ * (idle slots of a serving batch). Q43: the row is written to the tail and, when it is the last
+ * token of its 64-token group, the group is quantised; each sequence must be appended in
+ * increasing, gap-free positions. Errors: NULL, DTYPE, MISALIGNED; batch == 0 returns OK.
+ */
+starkv_status starkv_append_latents_ragged(const starkv_layer *layer, const starkv_cache *cache,
+                                           const int32_t *positions, const void *zk_new,
+                                           const void *zv_new, void *stream);
+
+/*
  * starkv_decode_attn with kernel timing for profiling tools: event_begin, event_mid and event_end
  * (hipEvent_t passed as void*, created by the caller, each may be NULL) are recorded on `stream`
  * immediately before the kernel that streams the key latents, between it and the kernel that

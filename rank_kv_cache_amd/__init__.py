@@ -21,7 +21,8 @@ __all__ = [
     "starkv_decode_workspace_bytes", "starkv_decode_attn", "starkv_dequant",
     "starkv_hadamard_rotate", "starkv_decode_attn_timed", "starkv_output_projection",
     "starkv_output_projection_workspace_bytes", "starkv_append_tokens",
-    "starkv_append_tokens_workspace_bytes",
+    "starkv_append_tokens_workspace_bytes", "starkv_decode_attn_ragged",
+    "starkv_append_latents_ragged",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -33,6 +34,7 @@ EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decod
                     "starkv_decode_attn", "starkv_decode_attn_timed", "starkv_dequant", "starkv_hadamard_rotate",
                     "starkv_output_projection", "starkv_output_projection_workspace_bytes",
                     "starkv_append_tokens", "starkv_append_tokens_workspace_bytes",
+                    "starkv_decode_attn_ragged", "starkv_append_latents_ragged",
                     "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +88,10 @@ def lib():
         L.starkv_decode_workspace_bytes.argtypes = [LP, i32, i64, i32]
         L.starkv_decode_attn.restype = C.c_int
         L.starkv_decode_attn.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.starkv_decode_attn_ragged.restype = C.c_int
+        L.starkv_decode_attn_ragged.argtypes = [LP, CP, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.starkv_append_latents_ragged.restype = C.c_int
+        L.starkv_append_latents_ragged.argtypes = [LP, CP, vp, vp, vp, vp]
         L.starkv_decode_attn_timed.restype = C.c_int
         L.starkv_decode_attn_timed.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp, vp, vp, vp]
         L.starkv_dequant.restype = C.c_int
@@ -221,6 +227,25 @@ def starkv_decode_attn(layer, cache, seq_len, q, bk, bv, out, num_splits=0, work
                                   int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "starkv_decode_attn")
+    return st
+
+
+def starkv_decode_attn_ragged(layer, cache, max_seq_len, seq_lens, q, bk, bv, out, num_splits=0,
+                              workspace=None, workspace_bytes=0, stream=None, check=True):
+    st = lib().starkv_decode_attn_ragged(_layer_ptr(layer), _cache_ptr(cache), max_seq_len,
+                                         _ptr(seq_lens), _ptr(q), _ptr(bk), _ptr(bv), _ptr(out),
+                                         num_splits, _ptr(workspace), int(workspace_bytes),
+                                         _stream(stream))
+    if check:
+        _check(st, "starkv_decode_attn_ragged")
+    return st
+
+
+def starkv_append_latents_ragged(layer, cache, positions, zk_new, zv_new, stream=None, check=True):
+    st = lib().starkv_append_latents_ragged(_layer_ptr(layer), _cache_ptr(cache), _ptr(positions),
+                                            _ptr(zk_new), _ptr(zv_new), _stream(stream))
+    if check:
+        _check(st, "starkv_append_latents_ragged")
     return st
 
 

@@ -346,7 +346,7 @@ PadMap pad_map(const LayerInfo& li) {
 // tokens t0 .. t0 + n - 1 of a layer whose ranks were rounded up (either pointer may be NULL).
 starkv_status copy_padded(const LayerInfo& li, const starkv_cache* cache, const void* zk_rows,
                           const void* zv_rows, int to_cache, int64_t t0, int64_t n,
-                          hipStream_t st) {
+                          hipStream_t st, const int32_t* positions = nullptr) {
     for (int which = 0; which < 2; ++which) {
         const void* rows = which ? zv_rows : zk_rows;
         if (!rows) continue;
@@ -361,6 +361,7 @@ starkv_status copy_padded(const LayerInfo& li, const starkv_cache* cache, const 
         p.to_cache = to_cache;
         p.t0 = t0;
         p.n = n;
+        p.positions = positions;
         p.map = pad_map(li);
         const starkv_status s = dev(launch_padded_rows(p, elem_bytes(li.cache_dt), st));
         if (s != STARKV_OK) return s;
@@ -623,11 +624,83 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
     return STARKV_OK;
 }
 
+// seq_lens: NULL (every sequence attends to seq_len tokens) or a device array of per-sequence
+// lengths, each clamped to [0, seq_len] in the kernels; seq_len then plans the splits.
+starkv_status starkv_append_latents_ragged(const starkv_layer* layer, const starkv_cache* cache,
+                                           const int32_t* positions, const void* zk_new,
+                                           const void* zv_new, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if ((s = check_cache(cache, li)) != STARKV_OK) return s;
+    if (cache->batch == 0) return STARKV_OK;
+    if (!positions || !zk_new || !zv_new) return STARKV_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(positions) & 3) || !aligned16(zk_new) || !aligned16(zv_new))
+        return STARKV_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int B = cache->batch;
+    const int es = elem_bytes(li.cache_dt);
+    if (li.q43 || li.dense) {
+        // one row per sequence: dense rows at their position, mixed-cache rows into the tail at
+        // position % 64 (then the groups that these tokens complete are quantised)
+        for (int which = 0; which < 2; ++which) {
+            const long long row = static_cast<long long>(li.dense ? li.H * li.D : which ? li.rv : li.Rk) *
+                                  (li.dense ? es : 2);
+            RowCopyParams p;
+            p.src = static_cast<const char*>(which ? zv_new : zk_new);
+            p.dst = static_cast<char*>(li.dense ? (which ? cache->zv : cache->zk)
+                                                : (which ? cache->zv_tail : cache->zk_tail));
+            p.src_seq_stride = row;
+            p.dst_seq_stride = (li.dense ? cache->capacity : kTile) * row;
+            p.src_off = 0;
+            p.dst_off = 0;
+            p.bytes = row;
+            p.positions = positions;
+            p.pos_mod = li.dense ? 0 : kTile;
+            p.pos_limit = cache->capacity;
+            if ((s = dev(launch_copy_rows(p, B, st))) != STARKV_OK) return s;
+        }
+        if (li.dense) return STARKV_OK;
+        Q43Layout K, V;
+        q43_layouts(li, &K, &V);
+        for (int which = 0; which < 2; ++which) {
+            Q43QuantParams q;
+            q.L = which ? V : K;
+            q.src = which ? cache->zv_tail : cache->zk_tail;
+            q.tail = q.src;
+            q.codes = which ? cache->zv : cache->zk;
+            q.meta = which ? cache->zv_meta : cache->zk_meta;
+            q.B = B;
+            q.nblk_cap = static_cast<int>(cache->capacity / kTile);
+            q.g_first = 0;
+            q.pos = 0;
+            q.n = 0;
+            q.positions = positions;
+            if ((s = dev(launch_q43_quantize(q, 1, st))) != STARKV_OK) return s;
+        }
+        return STARKV_OK;
+    }
+    if (li.padded) return copy_padded(li, cache, zk_new, zv_new, 1, 0, 1, st, positions);
+    AppendSmallParams a;
+    a.zk_src = zk_new;
+    a.zv_src = zv_new;
+    a.zk = cache->zk;
+    a.zv = cache->zv;
+    a.B = B;
+    a.Rk = li.Rk;
+    a.rv = li.rv;
+    a.nblk_cap = static_cast<int>(cache->capacity / kTile);
+    a.pos = 0;
+    a.n = 1;
+    a.positions = positions;
+    return dev(launch_append_small(a, es, st));
+}
+
 static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* cache,
-                                 int64_t seq_len, const float* q, const void* bk, const void* bv,
-                                 float* out, int32_t num_splits, void* workspace,
-                                 size_t workspace_bytes, void* stream, void* ev0, void* evm,
-                                 void* ev1) {
+                                 int64_t seq_len, const int32_t* seq_lens, const float* q,
+                                 const void* bk, const void* bv, float* out, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, void* stream, void* ev0,
+                                 void* evm, void* ev1) {
     LayerInfo li;
     starkv_status s = check_layer(layer, &li);
     if (s != STARKV_OK) return s;
@@ -660,6 +733,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
         p.D = li.D;
         p.cap = cache->capacity;
         p.seq_len = static_cast<int>(seq_len);
+        p.seq_lens = seq_lens;
         p.S = w.S;
         p.tiles_per_split = w.tps;
         p.q_scale = q_scale_of(layer, li.D);
@@ -697,6 +771,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     sp.Rk = li.Rk;
     sp.nblk_cap = cache->capacity / kTile;
     sp.seq_len = static_cast<int>(seq_len);
+    sp.seq_lens = seq_lens;
     sp.nblk = w.nblk;
     sp.Tp = w.nblk * kTile;
     sp.blocks_per_wg = w.sp.bpw;
@@ -730,6 +805,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     vp.rv = li.rv;
     vp.nblk_cap = sp.nblk_cap;
     vp.seq_len = sp.seq_len;
+    vp.seq_lens = seq_lens;
     vp.nblk = w.nblk;
     vp.Tp = sp.Tp;
     vp.S = w.vp.splits;
@@ -760,8 +836,21 @@ starkv_status starkv_decode_attn(const starkv_layer* layer, const starkv_cache* 
                                  int64_t seq_len, const float* q, const void* bk, const void* bv,
                                  float* out, int32_t num_splits, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    return decode_impl(layer, cache, seq_len, q, bk, bv, out, num_splits, workspace,
+    return decode_impl(layer, cache, seq_len, nullptr, q, bk, bv, out, num_splits, workspace,
                        workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+starkv_status starkv_decode_attn_ragged(const starkv_layer* layer, const starkv_cache* cache,
+                                        int64_t max_seq_len, const int32_t* seq_lens,
+                                        const float* q, const void* bk, const void* bv,
+                                        float* out, int32_t num_splits, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    if (cache && cache->batch > 0) {
+        if (!seq_lens) return STARKV_ERR_NULL;
+        if (reinterpret_cast<uintptr_t>(seq_lens) & 3) return STARKV_ERR_MISALIGNED;
+    }
+    return decode_impl(layer, cache, max_seq_len, seq_lens, q, bk, bv, out, num_splits,
+                       workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
 starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_cache* cache,
@@ -769,7 +858,7 @@ starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_c
                                        const void* bv, float* out, int32_t num_splits,
                                        void* workspace, size_t workspace_bytes, void* stream,
                                        void* event_begin, void* event_mid, void* event_end) {
-    return decode_impl(layer, cache, seq_len, q, bk, bv, out, num_splits, workspace,
+    return decode_impl(layer, cache, seq_len, nullptr, q, bk, bv, out, num_splits, workspace,
                        workspace_bytes, stream, event_begin, event_mid, event_end);
 }
 

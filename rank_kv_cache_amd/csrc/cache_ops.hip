@@ -14,8 +14,14 @@ namespace starkv {
 __global__ __launch_bounds__(256) void copy_rows(const RowCopyParams p) {
     const int b = blockIdx.y;
     const long long n16 = p.bytes / 16;
+    long long dst_off = p.dst_off;
+    if (p.positions) {
+        const long long pb = p.positions[b];
+        if (pb < 0 || pb >= p.pos_limit) return;
+        dst_off += (p.pos_mod ? pb % p.pos_mod : pb) * p.bytes;
+    }
     const u32x4* s = reinterpret_cast<const u32x4*>(p.src + b * p.src_seq_stride + p.src_off);
-    u32x4* d = reinterpret_cast<u32x4*>(p.dst + b * p.dst_seq_stride + p.dst_off);
+    u32x4* d = reinterpret_cast<u32x4*>(p.dst + b * p.dst_seq_stride + dst_off);
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n16; i += (long long)gridDim.x * 256)
         d[i] = s[i];
 }
@@ -89,7 +95,8 @@ __global__ __launch_bounds__(256) void append_small(const AppendSmallParams p) {
     const long long bt = idx / per_tok;
     const int t = (int)(bt % p.n);
     const int b = (int)(bt / p.n);
-    const long long tok = p.pos + t;
+    const long long tok = p.positions ? (long long)p.positions[b] : p.pos + t;
+    if (p.positions && (tok < 0 || tok >= (long long)p.nblk_cap * 64)) return;
     if (run < runs_k) {
         const int c = run * 8;
         const Run v = *reinterpret_cast<const Run*>(static_cast<const E*>(p.zk_src) + (bt * p.Rk + c));
@@ -115,7 +122,8 @@ __global__ __launch_bounds__(256) void padded_rows(const PaddedRowsParams p) {
     const long long bt = idx / C;
     const long long row = bt % p.n;
     const int b = (int)(bt / p.n);
-    const long long tok = p.t0 + row;
+    const long long tok = p.positions ? (long long)p.positions[b] : p.t0 + row;
+    if (p.positions && (tok < 0 || tok >= (long long)p.nblk_cap * 64)) return;
     E* cache = static_cast<E*>(p.cache);
     if (p.to_cache) {
         const int cs = p.which ? (c < p.C_src ? c : -1) : src_key_channel(p.map, c);

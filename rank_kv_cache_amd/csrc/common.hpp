@@ -215,6 +215,7 @@ struct ScoreParams {
     void* P;               // [B][H][Tp] probabilities, relative to each block's maximum
     float* stats;          // [B][H][nblk][2] per block: max (log2 units), sum of probabilities
     int B, H, D, Rk, nblk_cap, seq_len, nblk, Tp, blocks_per_wg;
+    const int32_t* seq_lens = nullptr;   // per-sequence lengths (device, clamped to [0, seq_len])
     float q_scale;         // softmax scale * log2(e)
     int8_t order[kMaxHeads];          // heads grouped: group g = order[gstart[g] .. gstart[g+1])
     int8_t gstart[kMaxGroups + 1];
@@ -235,6 +236,7 @@ struct ValueParams {
     float* ws_ml;          // [B][S][H][2]   (max in log2 units, sum)
     float* ws_acc;         // [B][S][H][rv]
     int B, H, rv, nblk_cap, seq_len, nblk, Tp, S, blocks_per_split;
+    const int32_t* seq_lens = nullptr;   // per-sequence lengths (device) or NULL
     // mixed 4/3-bit value cache only
     const void* zv_meta;   // [B][cap/64][2][rv]
     const void* zv_tail;   // [B][64][rv]
@@ -294,9 +296,16 @@ struct DenseDecodeParams {
     float* ws_ml;          // [B][S][H][2]
     float* ws_acc;         // [B][S][H][D]
     int B, H, D, cap, seq_len, S, tiles_per_split;
+    const int32_t* seq_lens = nullptr;   // per-sequence lengths (device) or NULL
     float q_scale;
     double rope_rev[64];
 };
+
+// A sequence's length: its entry of the per-sequence array clamped to [0, the launch's maximum],
+// or the launch's length.
+__device__ inline int seq_length(const int32_t* lens, int b, int max_len) {
+    return lens ? min(max(lens[b], 0), max_len) : max_len;
+}
 
 // Copy one contiguous byte range per sequence: dst[b*dst_seq_stride + dst_off + i] =
 // src[b*src_seq_stride + src_off + i] for i < bytes (a multiple of 16, 16-byte aligned).
@@ -306,6 +315,12 @@ struct RowCopyParams {
     long long src_seq_stride, dst_seq_stride;
     long long src_off, dst_off;
     long long bytes;
+    // one row per sequence at its own position (device array, or NULL): dst_off grows by
+    // (positions[b] % pos_mod, or positions[b] when pos_mod is 0) * bytes; sequences whose
+    // position lies outside [0, pos_limit) are skipped
+    const int32_t* positions = nullptr;
+    int pos_mod = 0;
+    long long pos_limit = 0;
 };
 
 // Token-major rows <-> block layout of a latent (layout 0: key, 1: value). to_blocks = 1:
@@ -329,6 +344,9 @@ struct AppendSmallParams {
     void* zv;
     int B, Rk, rv, nblk_cap;
     long long pos, n;
+    const int32_t* positions = nullptr;   // n == 1: sequence b's token goes to positions[b]
+                                // (device; skipped outside [0, capacity)), or NULL: tokens pos ..
+                                // pos + n - 1
 };
 
 // Rows of a latent with rounded ranks between the caller's layout [B][n][C_src] and the cache
@@ -339,6 +357,7 @@ struct PaddedRowsParams {
     void* cache;
     int B, nblk_cap, which, C, C_src, to_cache;
     long long t0, n;
+    const int32_t* positions = nullptr;   // as in AppendSmallParams (n == 1), or NULL
     PadMap map;
 };
 
@@ -350,6 +369,9 @@ struct Q43QuantParams {
     void* meta;                 // [B][cap/64][2][C] binary16 (scales, then zero points)
     int B, nblk_cap, g_first;
     long long pos, n;
+    // one appended token per sequence (device array, or NULL): the group of sequence b is
+    // quantised from the tail only when positions[b] is its last token
+    const int32_t* positions = nullptr;
 };
 
 // Blockwise Hadamard rotation of binary16 rows (kind 0: latent rows dst = src . H, [n][C]) or

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void dense_decode_split(const DenseDecodeParam
     const int h_raw = wave * HPW + lane / LPH;
     const bool hok = h_raw < H;
     const int h = min(h_raw, H - 1);
-    const int seq_len = p.seq_len;
+    const int seq_len = seq_length(p.seq_lens, b, p.seq_len);   // this sequence's length
     const int t_begin = split * p.tiles_per_split * kTile;
     const int t_end = min(seq_len, t_begin + p.tiles_per_split * kTile);
 

@@ -167,9 +167,11 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     const int hs0 = p.gstart[grp];
     const int ng = p.gstart[grp + 1] - hs0;
     const int H = p.H;
-    const int seq_len = p.seq_len;
+    const int seq_len = seq_length(p.seq_lens, b, p.seq_len);   // this sequence's length
     const int Tp = p.Tp;
-    const int nblk = p.nblk;
+    const int nblk = p.nblk;                                     // stride of the statistics
+    const int my_nblk = (seq_len + 63) >> 6;
+    const int full_blocks = QK ? seq_len >> 6 : my_nblk;         // quantised groups (mixed cache)
     const float q_scale = p.q_scale;
     const T* __restrict__ zk = static_cast<const T*>(p.zk);
     const T* __restrict__ bkt = static_cast<const T*>(p.bkt);
@@ -233,11 +235,11 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     __syncthreads();
 
     const int blk_begin = split * p.blocks_per_wg;
-    const int blk_end = min(nblk, blk_begin + p.blocks_per_wg);
+    const int blk_end = min(my_nblk, blk_begin + p.blocks_per_wg);
     // the pipelined loop covers the blocks stored in the main layout (all blocks for binary16 /
     // bf16 / fp32 caches; the quantised groups for a mixed-precision cache, whose partial last
     // block is read from the binary16 tail afterwards)
-    const int main_end = QK ? min(blk_end, p.full_blocks) : blk_end;
+    const int main_end = QK ? min(blk_end, full_blocks) : blk_end;
     const int my_blocks = blk_begin + wave < main_end ? (main_end - blk_begin - wave + NW - 1) / NW : 0;
     const int nunits = my_blocks * ng;
 
@@ -418,7 +420,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     if constexpr (QK) {
         // the partial last block of a mixed-precision cache: its rows are still binary16 in the
         // tail buffer [B][64][Rk], token-major
-        const int tb = p.full_blocks;
+        const int tb = full_blocks;
         if (tb < blk_end && tb >= blk_begin && (tb - blk_begin) % NW == wave) {
             for (int s = 0; s < ng; ++s) {
                 const T* rowp = qtail + ((size_t)b * 64 + j) * Rk + 16 * s_kgrp[s] + 8 * half;
@@ -549,9 +551,10 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     const int chunk = blockIdx.y;
     const int b = blockIdx.z;
     const int H = p.H;
-    const int seq_len = p.seq_len;
+    const int seq_len = seq_length(p.seq_lens, b, p.seq_len);   // this sequence's length
     const int blk_begin = split * p.blocks_per_split;
-    const int blk_end = min(p.nblk, blk_begin + p.blocks_per_split);
+    // a split past this sequence's end is empty (blk_end == blk_begin): (M, L, Acc) = (-inf, 0, 0)
+    const int blk_end = max(blk_begin, min((seq_len + 63) >> 6, blk_begin + p.blocks_per_split));
     const int nb = blk_end - blk_begin;
 
     // ---- split statistics per head: M = max m_blk, f_blk = 2^(m_blk - M), L = sum f l ----
@@ -607,7 +610,9 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
         hi4[k] = cc < p.n_hi;
         roff[k] = cc < p.n_hi ? 32 * cc : 32 * p.n_hi + 24 * (cc - p.n_hi);
     }
-    const int main_end = QV ? min(blk_end, p.full_blocks) : blk_end;
+    // mixed cache: blocks [blk_begin, main_end) are quantised; a block main_end < blk_end is the
+    // partial last group, read from the binary16 tail
+    const int main_end = QV ? max(blk_begin, min(blk_end, seq_len >> 6)) : blk_end;
 
     auto load_blk = [&](typename PF::Raw (&pr)[4], Buf& z, int blk) __attribute__((always_inline)) {
 #pragma unroll
@@ -726,9 +731,10 @@ __global__ __launch_bounds__(256) void merge_splits(const MergeParams p) {
     const float* ml = p.ws_ml + ((size_t)b * p.S * p.H + h) * 2;
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(size_t)s * p.H * 2]);
+    if (M == -INFINITY) M = 0.0f;                  // every split empty (a length-0 sequence): zeros
     float L = 0.0f;
     for (int s = 0; s < S; ++s) L += __builtin_amdgcn_exp2f(ml[(size_t)s * p.H * 2] - M) * ml[(size_t)s * p.H * 2 + 1];
-    const float inv_l = 1.0f / L;
+    const float inv_l = L > 0.0f ? 1.0f / L : 0.0f;
     const f32x4* acc = reinterpret_cast<const f32x4*>(p.ws_acc + ((size_t)b * p.S * p.H + h) * p.W) + c4;
     const size_t sstride = (size_t)p.H * W4;
     f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -785,10 +791,11 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
         float M = -INFINITY;
         for (int s = lane; s < p.S; s += 64) M = fmaxf(M, ml[s * sstride]);
         M = wave_max(M);
+        if (M == -INFINITY) M = 0.0f;              // every split empty (a length-0 sequence): zeros
         float L = 0.0f;
         for (int s = lane; s < p.S; s += 64) L += __builtin_amdgcn_exp2f(ml[s * sstride] - M) * ml[s * sstride + 1];
         L = wave_sum(L);
-        const float inv_l = 1.0f / L;
+        const float inv_l = L > 0.0f ? 1.0f / L : 0.0f;
         for (int s = lane; s < p.S; s += 64)
             s_w[bi][s] = bi < nb ? __builtin_amdgcn_exp2f(ml[s * sstride] - M) * inv_l : 0.0f;
     }

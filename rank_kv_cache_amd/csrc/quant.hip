@@ -52,9 +52,16 @@ __global__ __launch_bounds__(256) void q43_quantize(const Q43QuantParams p) {
 
     const Q43Layout& L = p.L;
     const int tid = threadIdx.x;
-    const int g = p.g_first + blockIdx.x;
     const int c0 = blockIdx.y * 64;
     const int b = blockIdx.z;
+    int g = p.g_first + blockIdx.x;
+    long long pos = p.pos;
+    if (p.positions) {                 // one token per sequence: quantise only a completed group
+        const long long pb = p.positions[b];
+        if (pb < 0 || pb >= (long long)p.nblk_cap * 64 || (pb & 63) != 63) return;
+        g = (int)(pb >> 6);
+        pos = pb + 1;                  // every row of the group is in the tail
+    }
     const int C = L.C;
     const long long tok0 = (long long)g * 64;
     const _Float16* src = static_cast<const _Float16*>(p.src);
@@ -65,8 +72,8 @@ __global__ __launch_bounds__(256) void q43_quantize(const Q43QuantParams p) {
         const long long tok = tok0 + t;
         _Float16 v = (_Float16)0.0f;
         if (c < C)
-            v = tok < p.pos ? tail[((size_t)b * 64 + t) * C + c]
-                            : src[((size_t)b * p.n + (tok - p.pos)) * C + c];
+            v = tok < pos ? tail[((size_t)b * 64 + t) * C + c]
+                          : src[((size_t)b * p.n + (tok - pos)) * C + c];
         x[t][cc] = v;
     }
     __syncthreads();

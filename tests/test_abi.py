@@ -221,3 +221,21 @@ def test_rounded_rank_sizes():
     assert sk.starkv_append_tokens_workspace_bytes(L, 2, 1, 64) >= 2 * 216 * 4
     fp32 = _latent(key_ranks=(1, 2, 3, 4), value_rank=1, cache_dtype=sk.F32)
     assert sk.starkv_cache_bytes(fp32, 1, 64)[0] == 64 * 64 * 4
+
+
+def test_ragged_validation():
+    L, Cc = _latent(), _cache()
+    rd = lambda lens=FAKE, Cc=Cc: sk.starkv_decode_attn_ragged(L, Cc, 100, lens, FAKE, FAKE, FAKE,
+                                                               FAKE, 0, FAKE, 1 << 40, check=False)
+    assert rd(lens=None) == 1
+    assert rd(lens=FAKE + 2) == 5
+    assert rd(Cc=_cache(batch=0), lens=None) == 0
+    assert sk.starkv_decode_attn_ragged(L, Cc, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40,
+                                        check=False) == 2
+    assert sk.starkv_decode_attn_ragged(L, Cc, 300, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40,
+                                        check=False) == 6
+    ra = lambda pos=FAKE, zk=FAKE, zv=FAKE, Cc=Cc: sk.starkv_append_latents_ragged(L, Cc, pos, zk,
+                                                                                    zv, check=False)
+    assert ra(pos=None) == 1 and ra(zk=None) == 1 and ra(zv=None) == 1
+    assert ra(pos=FAKE + 2) == 5 and ra(zk=FAKE + 8) == 5
+    assert ra(Cc=_cache(batch=0), pos=None) == 0
