@@ -183,6 +183,27 @@ starkv_status starkv_decode_attn_ragged(const starkv_layer *layer, const starkv_
                                         size_t workspace_bytes, void *stream);
 
 /*
+ * Several queries per cached sequence (speculative-decoding verification, a chunk of prefill
+ * queries, parallel samples; Alg. 2 steps 4-7 for each query): query row i (q[i], out[i], both
+ * [num_queries][H][d] fp32) reads cache sequence query_seq[i] and attends to its first
+ * query_len[i] tokens (a causal query at position p uses p + 1). query_seq and query_len are
+ * device int32 arrays of num_queries entries (4-byte aligned); a sequence index is clamped to
+ * [0, batch) and a length to [0, max_len]; a length of 0 gives a zero row. max_len (host) plans
+ * the splits; the workspace is starkv_decode_workspace_bytes(layer, num_queries, max_len,
+ * num_splits). Each query runs the single-query kernels on its own row, so rows that read the
+ * same sequence share no work beyond what the caches return (the latents are streamed once per
+ * query). Q43 lengths follow the starkv_decode_attn_ragged rule. Errors: those of
+ * starkv_decode_attn with seq_len = max_len; SHAPE (num_queries < 0, or queries on a batch-0
+ * cache), NULL, MISALIGNED. num_queries == 0 returns OK.
+ */
+starkv_status starkv_decode_attn_queries(const starkv_layer *layer, const starkv_cache *cache,
+                                         int32_t num_queries, const int32_t *query_seq,
+                                         const int32_t *query_len, int64_t max_len,
+                                         const float *q, const void *bk, const void *bv,
+                                         float *out, int32_t num_splits, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/*
  * One new token per sequence at its own position (the append step of a ragged decode batch,
  * Alg. 2 steps 1-3): positions is a device array of batch int32 positions (4-byte aligned);
  * sequence b's rows zk_new[b] ([batch][R_k] with the caller's ranks; dense: [batch][H*d]) and

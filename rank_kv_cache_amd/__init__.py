@@ -22,7 +22,7 @@ __all__ = [
     "starkv_hadamard_rotate", "starkv_decode_attn_timed", "starkv_output_projection",
     "starkv_output_projection_workspace_bytes", "starkv_append_tokens",
     "starkv_append_tokens_workspace_bytes", "starkv_decode_attn_ragged",
-    "starkv_append_latents_ragged",
+    "starkv_append_latents_ragged", "starkv_decode_attn_queries",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decod
                     "starkv_output_projection", "starkv_output_projection_workspace_bytes",
                     "starkv_append_tokens", "starkv_append_tokens_workspace_bytes",
                     "starkv_decode_attn_ragged", "starkv_append_latents_ragged",
+                    "starkv_decode_attn_queries",
                     "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +91,9 @@ def lib():
         L.starkv_decode_attn.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp]
         L.starkv_decode_attn_ragged.restype = C.c_int
         L.starkv_decode_attn_ragged.argtypes = [LP, CP, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.starkv_decode_attn_queries.restype = C.c_int
+        L.starkv_decode_attn_queries.argtypes = [LP, CP, i32, vp, vp, i64, vp, vp, vp, vp, i32, vp,
+                                                 sz, vp]
         L.starkv_append_latents_ragged.restype = C.c_int
         L.starkv_append_latents_ragged.argtypes = [LP, CP, vp, vp, vp, vp]
         L.starkv_decode_attn_timed.restype = C.c_int
@@ -238,6 +242,18 @@ def starkv_decode_attn_ragged(layer, cache, max_seq_len, seq_lens, q, bk, bv, ou
                                          _stream(stream))
     if check:
         _check(st, "starkv_decode_attn_ragged")
+    return st
+
+
+def starkv_decode_attn_queries(layer, cache, num_queries, query_seq, query_len, max_len, q, bk,
+                               bv, out, num_splits=0, workspace=None, workspace_bytes=0,
+                               stream=None, check=True):
+    st = lib().starkv_decode_attn_queries(_layer_ptr(layer), _cache_ptr(cache), num_queries,
+                                          _ptr(query_seq), _ptr(query_len), max_len, _ptr(q),
+                                          _ptr(bk), _ptr(bv), _ptr(out), num_splits,
+                                          _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "starkv_decode_attn_queries")
     return st
 
 

@@ -624,8 +624,6 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
     return STARKV_OK;
 }
 
-// seq_lens: NULL (every sequence attends to seq_len tokens) or a device array of per-sequence
-// lengths, each clamped to [0, seq_len] in the kernels; seq_len then plans the splits.
 starkv_status starkv_append_latents_ragged(const starkv_layer* layer, const starkv_cache* cache,
                                            const int32_t* positions, const void* zk_new,
                                            const void* zv_new, void* stream) {
@@ -696,11 +694,16 @@ starkv_status starkv_append_latents_ragged(const starkv_layer* layer, const star
     return dev(launch_append_small(a, es, st));
 }
 
+// rows: query rows (q, out and the workspace are per row), -1 for one per cache sequence.
+// seq_map: NULL (row b reads cache sequence b) or a device array of the cache sequence each row
+// reads. seq_lens: NULL (every row attends to seq_len tokens) or a device array of per-row
+// lengths, each clamped to [0, seq_len] in the kernels; seq_len then plans the splits.
 static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* cache,
                                  int64_t seq_len, const int32_t* seq_lens, const float* q,
                                  const void* bk, const void* bv, float* out, int32_t num_splits,
                                  void* workspace, size_t workspace_bytes, void* stream, void* ev0,
-                                 void* evm, void* ev1) {
+                                 void* evm, void* ev1, int rows = -1,
+                                 const int32_t* seq_map = nullptr) {
     LayerInfo li;
     starkv_status s = check_layer(layer, &li);
     if (s != STARKV_OK) return s;
@@ -709,12 +712,13 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     if (seq_len > cache->capacity) return STARKV_ERR_CAPACITY;
     if (seq_len > static_cast<int64_t>(kMaxSplits) * kMaxBlocksPerSplit * kTile)
         return STARKV_ERR_UNSUPPORTED;
-    if (cache->batch == 0) return STARKV_OK;
+    const int B = rows < 0 ? cache->batch : rows;
+    if (B == 0) return STARKV_OK;
+    if (cache->batch == 0) return STARKV_ERR_SHAPE;          // query rows but no cache sequence
     if (!q || !out) return STARKV_ERR_NULL;
     if (!li.dense && (!bk || !bv)) return STARKV_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return STARKV_ERR_MISALIGNED;
     if (!li.dense && (!aligned16(bk) || !aligned16(bv))) return STARKV_ERR_MISALIGNED;
-    const int B = cache->batch;
     const WorkspaceLayout w = workspace_layout(li, B, seq_len, num_splits);
     if (!workspace || workspace_bytes < w.total) return STARKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return STARKV_ERR_MISALIGNED;
@@ -734,6 +738,8 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
         p.cap = cache->capacity;
         p.seq_len = static_cast<int>(seq_len);
         p.seq_lens = seq_lens;
+        p.seq_map = seq_map;
+        p.cache_batch = cache->batch;
         p.S = w.S;
         p.tiles_per_split = w.tps;
         p.q_scale = q_scale_of(layer, li.D);
@@ -772,6 +778,8 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     sp.nblk_cap = cache->capacity / kTile;
     sp.seq_len = static_cast<int>(seq_len);
     sp.seq_lens = seq_lens;
+    sp.seq_map = seq_map;
+    sp.cache_batch = cache->batch;
     sp.nblk = w.nblk;
     sp.Tp = w.nblk * kTile;
     sp.blocks_per_wg = w.sp.bpw;
@@ -806,6 +814,8 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     vp.nblk_cap = sp.nblk_cap;
     vp.seq_len = sp.seq_len;
     vp.seq_lens = seq_lens;
+    vp.seq_map = seq_map;
+    vp.cache_batch = cache->batch;
     vp.nblk = w.nblk;
     vp.Tp = sp.Tp;
     vp.S = w.vp.splits;
@@ -851,6 +861,22 @@ starkv_status starkv_decode_attn_ragged(const starkv_layer* layer, const starkv_
     }
     return decode_impl(layer, cache, max_seq_len, seq_lens, q, bk, bv, out, num_splits,
                        workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
+}
+
+starkv_status starkv_decode_attn_queries(const starkv_layer* layer, const starkv_cache* cache,
+                                         int32_t num_queries, const int32_t* query_seq,
+                                         const int32_t* query_len, int64_t max_len,
+                                         const float* q, const void* bk, const void* bv,
+                                         float* out, int32_t num_splits, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (num_queries < 0) return STARKV_ERR_SHAPE;
+    if (num_queries > 0) {
+        if (!query_seq || !query_len) return STARKV_ERR_NULL;
+        if ((reinterpret_cast<uintptr_t>(query_seq) & 3) || (reinterpret_cast<uintptr_t>(query_len) & 3))
+            return STARKV_ERR_MISALIGNED;
+    }
+    return decode_impl(layer, cache, max_len, query_len, q, bk, bv, out, num_splits, workspace,
+                       workspace_bytes, stream, nullptr, nullptr, nullptr, num_queries, query_seq);
 }
 
 starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_cache* cache,

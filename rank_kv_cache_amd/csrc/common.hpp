@@ -216,6 +216,8 @@ struct ScoreParams {
     float* stats;          // [B][H][nblk][2] per block: max (log2 units), sum of probabilities
     int B, H, D, Rk, nblk_cap, seq_len, nblk, Tp, blocks_per_wg;
     const int32_t* seq_lens = nullptr;   // per-sequence lengths (device, clamped to [0, seq_len])
+    const int32_t* seq_map = nullptr;    // query row b reads cache sequence seq_map[b] (or b)
+    int cache_batch = 0;
     float q_scale;         // softmax scale * log2(e)
     int8_t order[kMaxHeads];          // heads grouped: group g = order[gstart[g] .. gstart[g+1])
     int8_t gstart[kMaxGroups + 1];
@@ -237,6 +239,8 @@ struct ValueParams {
     float* ws_acc;         // [B][S][H][rv]
     int B, H, rv, nblk_cap, seq_len, nblk, Tp, S, blocks_per_split;
     const int32_t* seq_lens = nullptr;   // per-sequence lengths (device) or NULL
+    const int32_t* seq_map = nullptr;    // query row b reads cache sequence seq_map[b] (or b)
+    int cache_batch = 0;
     // mixed 4/3-bit value cache only
     const void* zv_meta;   // [B][cap/64][2][rv]
     const void* zv_tail;   // [B][64][rv]
@@ -297,6 +301,8 @@ struct DenseDecodeParams {
     float* ws_acc;         // [B][S][H][D]
     int B, H, D, cap, seq_len, S, tiles_per_split;
     const int32_t* seq_lens = nullptr;   // per-sequence lengths (device) or NULL
+    const int32_t* seq_map = nullptr;    // query row b reads cache sequence seq_map[b] (or b)
+    int cache_batch = 0;
     float q_scale;
     double rope_rev[64];
 };
@@ -305,6 +311,11 @@ struct DenseDecodeParams {
 // or the launch's length.
 __device__ inline int seq_length(const int32_t* lens, int b, int max_len) {
     return lens ? min(max(lens[b], 0), max_len) : max_len;
+}
+// The cache sequence a query row reads: its entry of the map clamped to [0, cache_batch), or the
+// row itself (one query per sequence).
+__device__ inline int cache_seq(const int32_t* map, int b, int cache_batch) {
+    return map ? min(max(map[b], 0), cache_batch - 1) : b;
 }
 
 // Copy one contiguous byte range per sequence: dst[b*dst_seq_stride + dst_off + i] =

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void dense_decode_split(const DenseDecodeParam
     const bool hok = h_raw < H;
     const int h = min(h_raw, H - 1);
     const int seq_len = seq_length(p.seq_lens, b, p.seq_len);   // this sequence's length
+    const int bc = cache_seq(p.seq_map, b, p.cache_batch);      // the cache sequence read
     const int t_begin = split * p.tiles_per_split * kTile;
     const int t_end = min(seq_len, t_begin + p.tiles_per_split * kTile);
 
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void dense_decode_split(const DenseDecodeParam
                 const int j = j0 + jj;
                 // rows past the sequence end lie inside the 64-token-aligned capacity; their
                 // scores are replaced below, so the loads stay unconditional
-                const size_t row = ((size_t)b * p.cap + t0 + j) * W + col;
+                const size_t row = ((size_t)bc * p.cap + t0 + j) * W + col;
                 float k1[8], k2[8];
                 load8<K>(p.k, row, k1);
                 load8<K>(p.k, row + NF, k2);
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void dense_decode_split(const DenseDecodeParam
                 // this slot: rows past the end may hold anything (0 * NaN is NaN)
                 const int j = j0 + min(jj, nt - 1);
                 const float pj = jj < nt ? sc[jj] : 0.0f;
-                const size_t row = ((size_t)b * p.cap + t0 + j) * W + col;
+                const size_t row = ((size_t)bc * p.cap + t0 + j) * W + col;
                 float v1[8], v2[8];
                 load8<K>(p.v, row, v1);
                 load8<K>(p.v, row + NF, v2);

@@ -180,7 +180,8 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     float* __restrict__ stats = p.stats;
     const int Rk = p.Rk;
     const size_t kgroups = (size_t)(Rk >> 4);
-    const size_t blk_base = (size_t)b * p.nblk_cap;
+    const int bc = cache_seq(p.seq_map, b, p.cache_batch);      // the cache sequence read
+    const size_t blk_base = (size_t)bc * p.nblk_cap;
     const uint32_t* __restrict__ qcodes = static_cast<const uint32_t*>(p.zk);
     const uint16_t* __restrict__ qmeta = static_cast<const uint16_t*>(p.zk_meta);
     const T* __restrict__ qtail = static_cast<const T*>(p.zk_tail);
@@ -423,7 +424,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         const int tb = full_blocks;
         if (tb < blk_end && tb >= blk_begin && (tb - blk_begin) % NW == wave) {
             for (int s = 0; s < ng; ++s) {
-                const T* rowp = qtail + ((size_t)b * 64 + j) * Rk + 16 * s_kgrp[s] + 8 * half;
+                const T* rowp = qtail + ((size_t)bc * 64 + j) * Rk + 16 * s_kgrp[s] + 8 * half;
                 unit(tb, s, [&](int nt, int ks) __attribute__((always_inline)) {
                     return load_frag<K>(rowp, (size_t)(32 * nt) * Rk + 16 * ks);
                 });
@@ -552,6 +553,7 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     const int b = blockIdx.z;
     const int H = p.H;
     const int seq_len = seq_length(p.seq_lens, b, p.seq_len);   // this sequence's length
+    const int bc = cache_seq(p.seq_map, b, p.cache_batch);      // the cache sequence read
     const int blk_begin = split * p.blocks_per_split;
     // a split past this sequence's end is empty (blk_end == blk_begin): (M, L, Acc) = (-inf, 0, 0)
     const int blk_end = max(blk_begin, min((seq_len + 63) >> 6, blk_begin + p.blocks_per_split));
@@ -618,13 +620,13 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
         if constexpr (!QV) {
-            const size_t bbase = ((size_t)b * p.nblk_cap + blk) * cgroups * 1024;
+            const size_t bbase = ((size_t)bc * p.nblk_cap + blk) * cgroups * 1024;
 #pragma unroll
             for (int k = 0; k < NTW; ++k)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) z.z[k][ks] = load_frag<K>(p.zv, bbase + zoff[k] + ks * 256);
         } else {
-            const size_t bb = ((size_t)b * p.nblk_cap + blk);
+            const size_t bb = ((size_t)bc * p.nblk_cap + blk);
             const uint8_t* blkp = qcodes + bb * p.block_bytes;
             const uint16_t* meta = qmeta + bb * 2 * p.rv;
 #pragma unroll
@@ -688,7 +690,7 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
             typename PF::Raw pr[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
-            const _Float16* tail = static_cast<const _Float16*>(p.zv_tail) + (size_t)b * 64 * p.rv;
+            const _Float16* tail = static_cast<const _Float16*>(p.zv_tail) + (size_t)bc * 64 * p.rv;
             accumulate(pr, blk, [&](int k, int ks) __attribute__((always_inline)) {
                 const int cc = min(ch[k], p.rv - 1);
                 Fr zf;

@@ -239,3 +239,15 @@ def test_ragged_validation():
     assert ra(pos=None) == 1 and ra(zk=None) == 1 and ra(zv=None) == 1
     assert ra(pos=FAKE + 2) == 5 and ra(zk=FAKE + 8) == 5
     assert ra(Cc=_cache(batch=0), pos=None) == 0
+
+
+def test_queries_validation():
+    L, Cc = _latent(), _cache()
+    dq = lambda n=3, qs=FAKE, ql=FAKE, Cc=Cc, mx=100: sk.starkv_decode_attn_queries(
+        L, Cc, n, qs, ql, mx, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, check=False)
+    assert dq(n=-1) == 2
+    assert dq(qs=None) == 1 and dq(ql=None) == 1
+    assert dq(qs=FAKE + 2) == 5 and dq(ql=FAKE + 1) == 5
+    assert dq(n=0, qs=None, ql=None) == 0
+    assert dq(Cc=_cache(batch=0)) == 2                      # queries but no cache sequence
+    assert dq(mx=0) == 2 and dq(mx=300) == 6
