@@ -17,7 +17,8 @@ K and V for an exempt layer) are divided by its duration from HIP events recorde
 launch on the launch stream; the kernel with the largest total time is reported (all appear under
 ``kernels``). ``projections`` times, apart from the step, the two dense products around a latent
 layer's attention (the fused token down-projection + append and the output projection) with HIP
-events. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
+events; ``queries`` times four queries per sequence (speculative-decoding verification) through
+the multi-query entry point. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
 pairs of the same workload, scaled to the whole workload.
 """
 from __future__ import annotations
@@ -370,6 +371,53 @@ def measure_projections(sk, buffers, run, B, stream, hip, steps, model_dim=4096,
     return res
 
 
+def measure_queries(sk, run, B, stream, hip, steps, per_seq=4):
+    """Several queries per sequence through starkv_decode_attn_queries, timed with HIP events on
+    the launch stream: per_seq causal queries at the last per_seq positions of every sequence
+    (speculative-decoding verification; for a mixed 4/3-bit cache, whose partial group fixes the
+    length, per_seq samples at the full length). Each query row streams its sequence's latents;
+    rows of one sequence that run close together find them in the caches."""
+    import torch
+    L, T = run.layer, run.T
+    q43 = L.cache_dtype == sk.Q43
+    seqs = [b for b in range(B) for _ in range(per_seq)]
+    lens = [T if q43 else T - per_seq + 1 + i for _ in range(B) for i in range(per_seq)]
+    n = len(seqs)
+    H, d = L.num_heads, L.head_dim
+    qs = torch.tensor(np.asarray(seqs, np.int32), device="cuda")
+    ql = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    q = torch.randn((n, H, d), device="cuda", generator=g)
+    out = torch.empty((n, H, d), dtype=torch.float32, device="cuda")
+    nws = sk.starkv_decode_workspace_bytes(L, n, T, 0)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    sp = stream.cuda_stream
+
+    def call():
+        sk.starkv_decode_attn_queries(L, run.cache, n, qs, ql, T, q, run.bk, run.bv, out, 0, ws,
+                                      nws, stream=stream)
+
+    for _ in range(2):
+        call()
+    ev = hip.create(2)
+    torch.cuda.synchronize()
+    hip.record(ev[0], sp)
+    for _ in range(steps):
+        call()
+    hip.record(ev[1], sp)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+    hip.destroy(ev)
+    if not bool(torch.isfinite(out).all()):
+        raise SystemExit("non-finite multi-query output")
+    res = {"queries_per_sequence": per_seq, "query_rows": n, "causal": not q43,
+           "avg_us": us, "us_per_query_row": us / n}
+    log(f"[bench] queries: {n} rows ({per_seq} per sequence) in {us:.1f} us")
+    del ws
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,10 +528,12 @@ def main(argv=None):
         if not np.all(np.isfinite(res)):
             raise SystemExit("non-finite attention output")
 
-    projections = None
+    projections = queries = None
     if not a.no_projections:
         lat = [r for r in runs if not r.dense]
         projections = measure_projections(sk, buffers, lat[0], B, stream, hip, a.steps)
+        if len(runs) == 1:
+            queries = measure_queries(sk, lat[0], B, stream, hip, min(a.steps, 10))
 
     ms_per_step = elapsed * 1e3 / a.steps
     kernels = {}
@@ -531,6 +581,9 @@ def main(argv=None):
     }
     if projections is not None:
         rec["projections"] = projections
+    if queries is not None:
+        queries["vs_single_query_step"] = queries["avg_us"] / (ms_per_step * 1e3)
+        rec["queries"] = queries
     if sample is not None and sample.pairs:
         import oracle
         thr = oracle.threads()
