@@ -104,13 +104,25 @@ typedef struct {
     int32_t q_group;             /* Q43: tokens per quantisation group; must be 64 */
 } starkv_layer;
 
-/* Caller-owned device buffers of one layer's cache (see layouts above). */
+/*
+ * Caller-owned device buffers of one layer's cache (see layouts above).
+ * Paged caches (block_table != NULL): every 64-token block of a sequence lives in a page of a
+ * shared pool, as in paged KV caches for serving. Block blk of sequence b is page
+ * block_table[b * table_stride + blk] (device int32, 4-byte aligned, table_stride >=
+ * capacity / 64) of zk, zv, zk_meta and zv_meta, which then hold num_pages pages each: size them
+ * with starkv_cache_bytes(layer, num_pages, 64) (fields 0-3). The tails stay per sequence
+ * ([batch][64][C], fields 4-5 of starkv_cache_bytes(layer, batch, capacity)). capacity is the
+ * per-sequence capacity in tokens. Page indices are read on the device and are not checked: each
+ * must address a page of the pool, and two live blocks must not share a page.
+ */
 typedef struct {
     int32_t batch;               /* B */
     int32_t capacity;            /* tokens per sequence the buffers hold; multiple of 64 */
     void *zk, *zv;
     void *zk_meta, *zv_meta;     /* Q43 only */
     void *zk_tail, *zv_tail;     /* Q43 only */
+    const int32_t *block_table;  /* NULL: contiguous per sequence; else [batch][table_stride] */
+    int32_t table_stride;
 } starkv_cache;
 
 /* Byte sizes of the six cache buffers {zk, zv, zk_meta, zv_meta, zk_tail, zv_tail} for a layer,

@@ -62,7 +62,8 @@ class _Layer(C.Structure):
 class _Cache(C.Structure):
     _fields_ = [("batch", C.c_int32), ("capacity", C.c_int32),
                 ("zk", C.c_void_p), ("zv", C.c_void_p), ("zk_meta", C.c_void_p),
-                ("zv_meta", C.c_void_p), ("zk_tail", C.c_void_p), ("zv_tail", C.c_void_p)]
+                ("zv_meta", C.c_void_p), ("zk_tail", C.c_void_p), ("zv_tail", C.c_void_p),
+                ("block_table", C.c_void_p), ("table_stride", C.c_int32)]
 
 
 def library_path() -> str:
@@ -175,10 +176,13 @@ class Cache:
     zv_meta: object = None
     zk_tail: object = None
     zv_tail: object = None
+    block_table: object = None        # paged cache: [batch][table_stride] int32 page indices
+    table_stride: int = 0
 
     def c(self):
         return _Cache(self.batch, self.capacity, _ptr(self.zk), _ptr(self.zv), _ptr(self.zk_meta),
-                      _ptr(self.zv_meta), _ptr(self.zk_tail), _ptr(self.zv_tail))
+                      _ptr(self.zv_meta), _ptr(self.zk_tail), _ptr(self.zv_tail),
+                      _ptr(self.block_table), self.table_stride)
 
 
 def _layer_ptr(layer):

@@ -32,6 +32,7 @@ hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
 hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_padded_rows(const PaddedRowsParams& p, int elem_bytes, hipStream_t st);
+hipError_t launch_paged_rows(const PagedRowsParams& p, hipStream_t st);
 hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t st);
 hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st);
 hipError_t launch_hadamard_rotate(const HadamardParams& p, hipStream_t st);
@@ -136,6 +137,10 @@ starkv_status check_cache(const starkv_cache* c, const LayerInfo& li) {
     if (c->batch == 0) return STARKV_OK;
     if (!c->zk || !c->zv) return STARKV_ERR_NULL;
     if (!aligned16(c->zk) || !aligned16(c->zv)) return STARKV_ERR_MISALIGNED;
+    if (c->block_table) {
+        if (c->table_stride < c->capacity / kTile) return STARKV_ERR_CAPACITY;
+        if (reinterpret_cast<uintptr_t>(c->block_table) & 3) return STARKV_ERR_MISALIGNED;
+    }
     if (li.q43) {
         if (!c->zk_meta || !c->zv_meta || !c->zk_tail || !c->zv_tail) return STARKV_ERR_NULL;
         if (!aligned16(c->zk_meta) || !aligned16(c->zv_meta) || !aligned16(c->zk_tail) ||
@@ -328,6 +333,37 @@ float q_scale_of(const starkv_layer* L, int D) {
 
 inline starkv_status dev(hipError_t e) { return e == hipSuccess ? STARKV_OK : STARKV_ERR_DEVICE; }
 
+BlockMap pages_of(const starkv_cache* c) {
+    BlockMap m;
+    m.table = c->block_table;
+    m.stride = c->table_stride;
+    return m;
+}
+
+// Dense rows of a paged cache: rows [B][n][H*d] <-> tokens t0 .. t0 + n - 1 (or positions[b])
+starkv_status dense_paged(const LayerInfo& li, const starkv_cache* cache, const void* k_rows,
+                          const void* v_rows, int to_cache, int64_t t0, int64_t n,
+                          hipStream_t st, const int32_t* positions = nullptr) {
+    for (int which = 0; which < 2; ++which) {
+        const void* rows = which ? v_rows : k_rows;
+        if (!rows) continue;
+        PagedRowsParams p;
+        p.rows = static_cast<const char*>(rows);
+        p.cache = static_cast<char*>(which ? cache->zv : cache->zk);
+        p.row_bytes = static_cast<long long>(li.H) * li.D * elem_bytes(li.cache_dt);
+        p.t0 = t0;
+        p.n = n;
+        p.B = cache->batch;
+        p.nblk_cap = static_cast<int>(cache->capacity / kTile);
+        p.to_cache = to_cache;
+        p.positions = positions;
+        p.pages = pages_of(cache);
+        const starkv_status s = dev(launch_paged_rows(p, st));
+        if (s != STARKV_OK) return s;
+    }
+    return STARKV_OK;
+}
+
 PadMap pad_map(const LayerInfo& li) {
     PadMap m;
     std::memset(&m, 0, sizeof(m));
@@ -362,6 +398,7 @@ starkv_status copy_padded(const LayerInfo& li, const starkv_cache* cache, const 
         p.t0 = t0;
         p.n = n;
         p.positions = positions;
+        p.pages = pages_of(cache);
         p.map = pad_map(li);
         const starkv_status s = dev(launch_padded_rows(p, elem_bytes(li.cache_dt), st));
         if (s != STARKV_OK) return s;
@@ -409,6 +446,7 @@ struct LinearRun {
     int64_t pos = 0, cap = 0;
     bool padded = false;           // kind 1: stored ranks rounded up (see PadMap)
     PadMap map{};
+    BlockMap pages;                // kinds 1 and 2: the cache's block table
 };
 
 // Rows (b, t) for every sequence b < B and tokens t0 <= t < t0 + tl, at most kLinearMaxRows rows
@@ -453,6 +491,7 @@ starkv_status run_linear(const LinearRun& r, int B, int64_t t0, int64_t tl, hipS
             q.cap = r.cap;
             q.padded = r.padded ? 1 : 0;
             q.map = r.map;
+            q.pages = r.pages;
             if ((s = dev(launch_linear_store(q, r.store_elem, st))) != STARKV_OK) return s;
         }
     }
@@ -544,6 +583,7 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
         const int ngroups = static_cast<int>((pos + n_new) / kTile) - g_first;
         for (int which = 0; which < 2; ++which) {
             Q43QuantParams q;
+            q.pages = pages_of(cache);
             q.L = which ? V : K;
             q.src = which ? zv_new : zk_new;
             q.tail = which ? cache->zv_tail : cache->zk_tail;
@@ -574,6 +614,7 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
         }
         return STARKV_OK;
     }
+    if (li.dense && cache->block_table) return dense_paged(li, cache, zk_new, zv_new, 1, pos, n_new, st);
     if (li.dense) {
         const long long cap = cache->capacity;
         const long long row = static_cast<long long>(li.H) * li.D * es;
@@ -593,6 +634,7 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
     if (li.padded) return copy_padded(li, cache, zk_new, zv_new, 1, pos, n_new, st);
     if (n_new <= kSmallAppend) {
         AppendSmallParams a;
+        a.pages = pages_of(cache);
         a.zk_src = zk_new;
         a.zv_src = zv_new;
         a.zk = cache->zk;
@@ -607,6 +649,7 @@ starkv_status starkv_append_latents(const starkv_layer* layer, const starkv_cach
     }
     for (int which = 0; which < 2; ++which) {
         BlockXposeParams x;
+        x.pages = pages_of(cache);
         x.src = which ? zv_new : zk_new;
         x.dst = which ? cache->zv : cache->zk;
         x.B = B;
@@ -638,6 +681,8 @@ starkv_status starkv_append_latents_ragged(const starkv_layer* layer, const star
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int B = cache->batch;
     const int es = elem_bytes(li.cache_dt);
+    if (li.dense && cache->block_table)
+        return dense_paged(li, cache, zk_new, zv_new, 1, 0, 1, st, positions);
     if (li.q43 || li.dense) {
         // one row per sequence: dense rows at their position, mixed-cache rows into the tail at
         // position % 64 (then the groups that these tokens complete are quantised)
@@ -663,6 +708,7 @@ starkv_status starkv_append_latents_ragged(const starkv_layer* layer, const star
         q43_layouts(li, &K, &V);
         for (int which = 0; which < 2; ++which) {
             Q43QuantParams q;
+            q.pages = pages_of(cache);
             q.L = which ? V : K;
             q.src = which ? cache->zv_tail : cache->zk_tail;
             q.tail = q.src;
@@ -680,6 +726,7 @@ starkv_status starkv_append_latents_ragged(const starkv_layer* layer, const star
     }
     if (li.padded) return copy_padded(li, cache, zk_new, zv_new, 1, 0, 1, st, positions);
     AppendSmallParams a;
+    a.pages = pages_of(cache);
     a.zk_src = zk_new;
     a.zv_src = zv_new;
     a.zk = cache->zk;
@@ -727,6 +774,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     if (li.dense) {
         const int active = (w.nblk + w.tps - 1) / w.tps;
         DenseDecodeParams p;
+        p.pages = pages_of(cache);
         p.k = cache->zk;
         p.v = cache->zv;
         p.q = q;
@@ -766,6 +814,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
         return s;
     ScoreParams sp;
     std::memset(&sp, 0, sizeof(sp));
+    sp.pages = pages_of(cache);
     sp.zk = cache->zk;
     sp.bkt = bkt;
     sp.q = q;
@@ -803,6 +852,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
         return s;
     if (evm && (s = dev(hipEventRecord(static_cast<hipEvent_t>(evm), st))) != STARKV_OK) return s;
     ValueParams vp;
+    vp.pages = pages_of(cache);
     vp.zv = cache->zv;
     vp.P = sp.P;
     vp.stats = sp.stats;
@@ -910,6 +960,7 @@ starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cach
             void* outp = which ? zv_out : zk_out;
             if (!outp) continue;
             Q43ReadParams r;
+            r.pages = pages_of(cache);
             r.L = which ? V : K;
             r.codes = which ? cache->zv : cache->zk;
             r.meta = which ? cache->zv_meta : cache->zk_meta;
@@ -924,6 +975,7 @@ starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cach
         }
         return STARKV_OK;
     }
+    if (li.dense && cache->block_table) return dense_paged(li, cache, zk_out, zv_out, 0, t0, n, st);
     if (li.dense) {
         const long long row = static_cast<long long>(li.H) * li.D * es;
         for (int which = 0; which < 2; ++which) {
@@ -946,6 +998,7 @@ starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cach
         void* outp = which ? zv_out : zk_out;
         if (!outp) continue;
         BlockXposeParams x;
+        x.pages = pages_of(cache);
         x.src = which ? cache->zv : cache->zk;
         x.dst = outp;
         x.B = B;
@@ -1090,6 +1143,7 @@ starkv_status starkv_append_tokens(const starkv_layer* layer, const starkv_cache
     r.N = li.dense ? 2 * li.H * li.D : li.Rk_src + li.rv_src;
     r.padded = li.padded;
     if (li.padded) r.map = pad_map(li);
+    r.pages = pages_of(cache);
     r.Kd = model_dim;
     r.elem = elem_kind(li.dense ? li.cache_dt : li.factor_dt);
     r.part = static_cast<float*>(workspace);
@@ -1116,6 +1170,7 @@ starkv_status starkv_append_tokens(const starkv_layer* layer, const starkv_cache
         if (pos + t1 == g_end) {
             for (int which = 0; which < 2; ++which) {
                 Q43QuantParams q;
+                q.pages = pages_of(cache);
                 q.L = which ? V : K;
                 q.src = which ? cache->zv_tail : cache->zk_tail;   // every row comes from the tail
                 q.tail = q.src;

@@ -3,7 +3,7 @@
 //
 // Layouts: token-major rows [B][cap][H*d] for dense K/V; 64-token blocks of 16-channel groups for
 // the latents (key: token-major inside a group, value: 16-token runs per channel inside a group;
-// see zk_block_index / zv_block_index). The block transposes go through LDS so that both the row
+// see zk_block_at / zv_block_at). The block transposes go through LDS so that both the row
 // side and the block side are accessed in order.
 
 #include "common.hpp"
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void block_transpose(const BlockXposeParams p)
     const E* src = static_cast<const E*>(p.src);
     E* dst = static_cast<E*>(p.dst);
     const int ncg = min(64, p.C - c0) >> 4;            // 16-channel groups in this chunk
-    const size_t gbase = ((size_t)b * p.nblk_cap + blk) * (size_t)(p.C >> 4) + (size_t)(c0 >> 4);
+    const size_t gbase = block_id(p.pages, p.nblk_cap, b, blk) * (size_t)(p.C >> 4) + (size_t)(c0 >> 4);
     // element e of the chunk's contiguous block-layout range -> (token, channel)
     auto decode = [&](int e, int* tok, int* ch) {
         const int gl = e >> 10, w = e & 1023;
@@ -100,13 +100,14 @@ __global__ __launch_bounds__(256) void append_small(const AppendSmallParams p) {
     if (run < runs_k) {
         const int c = run * 8;
         const Run v = *reinterpret_cast<const Run*>(static_cast<const E*>(p.zk_src) + (bt * p.Rk + c));
-        *reinterpret_cast<Run*>(static_cast<E*>(p.zk) + zk_block_index(b, p.nblk_cap, p.Rk, tok, c)) = v;
+        *reinterpret_cast<Run*>(static_cast<E*>(p.zk) + zk_block_at(block_id(p.pages, p.nblk_cap, b, tok >> 6), p.Rk, tok, c)) = v;
     } else {
         const int c = (run - runs_k) * 8;
         const Run v = *reinterpret_cast<const Run*>(static_cast<const E*>(p.zv_src) + (bt * p.rv + c));
         E* dst = static_cast<E*>(p.zv);
+        const size_t id = block_id(p.pages, p.nblk_cap, b, tok >> 6);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[zv_block_index(b, p.nblk_cap, p.rv, tok, c + e)] = v.v[e];
+        for (int e = 0; e < 8; ++e) dst[zv_block_at(id, p.rv, tok, c + e)] = v.v[e];
     }
 }
 
@@ -128,11 +129,13 @@ __global__ __launch_bounds__(256) void padded_rows(const PaddedRowsParams p) {
     if (p.to_cache) {
         const int cs = p.which ? (c < p.C_src ? c : -1) : src_key_channel(p.map, c);
         const E v = cs >= 0 ? static_cast<const E*>(p.rows)[bt * p.C_src + cs] : E(0);
-        cache[p.which ? zv_block_index(b, p.nblk_cap, p.C, tok, c) : zk_block_index(b, p.nblk_cap, p.C, tok, c)] = v;
+        const size_t id = block_id(p.pages, p.nblk_cap, b, tok >> 6);
+        cache[p.which ? zv_block_at(id, p.C, tok, c) : zk_block_at(id, p.C, tok, c)] = v;
     } else {
         const int cc = p.which ? c : pad_key_channel(p.map, c);
         static_cast<E*>(const_cast<void*>(p.rows))[bt * p.C_src + c] =
-            cache[p.which ? zv_block_index(b, p.nblk_cap, p.C, tok, cc) : zk_block_index(b, p.nblk_cap, p.C, tok, cc)];
+            cache[p.which ? zv_block_at(block_id(p.pages, p.nblk_cap, b, tok >> 6), p.C, tok, cc)
+                          : zk_block_at(block_id(p.pages, p.nblk_cap, b, tok >> 6), p.C, tok, cc)];
     }
 }
 
@@ -146,6 +149,33 @@ hipError_t launch_padded_rows(const PaddedRowsParams& p, int elem_bytes, hipStre
         hipLaunchKernelGGL(padded_rows<uint32_t>, grid, dim3(256), 0, st, p);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Rows of a paged dense cache: thread per 16 bytes of a (sequence, row); each token's row lives in
+// its block's page.
+__global__ __launch_bounds__(256) void paged_rows(const PagedRowsParams p) {
+    const long long per_row = p.row_bytes / 16;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)p.B * p.n * per_row) return;
+    const long long chunk = idx % per_row;
+    const long long br = idx / per_row;
+    const long long row = br % p.n;
+    const int b = (int)(br / p.n);
+    const long long tok = p.positions ? (long long)p.positions[b] : p.t0 + row;
+    if (p.positions && (tok < 0 || tok >= (long long)p.nblk_cap * 64)) return;
+    u32x4* c = reinterpret_cast<u32x4*>(p.cache + (block_id(p.pages, p.nblk_cap, b, tok >> 6) * 64 + (tok & 63)) * p.row_bytes) + chunk;
+    u32x4* r = reinterpret_cast<u32x4*>(const_cast<char*>(p.rows) + br * p.row_bytes) + chunk;
+    if (p.to_cache)
+        *c = *r;
+    else
+        *r = *c;
+}
+
+hipError_t launch_paged_rows(const PagedRowsParams& p, hipStream_t st) {
+    const long long n = (long long)p.B * p.n * (p.row_bytes / 16);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(paged_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -156,13 +156,22 @@ constexpr int kMaxBlocksPerSplit = 256;
 //   value latent zv[b][blk][g][u][k][v]   u < 4, v < 16: token 16u + v, k < 16 channel in group
 // so that one 16-byte lane load of eight consecutive elements feeds an MFMA operand fragment and
 // the 64 lanes of a wave read 1 KB (key) or two 512-byte runs (value) of contiguous memory.
-__host__ __device__ inline size_t zk_block_index(size_t b, size_t nblk_cap, int C, long long t, int c) {
-    return ((b * nblk_cap + (size_t)(t >> 6)) * (size_t)(C >> 4) + (size_t)(c >> 4)) * 1024 +
-           (size_t)(t & 63) * 16 + (size_t)(c & 15);
+// Where 64-token block blk of sequence b lives: block b * nblk_cap + blk of the buffer, or, for a
+// paged cache, page table[b * stride + blk] of the buffer's pool (the caller's block table).
+struct BlockMap {
+    const int32_t* table = nullptr;
+    int stride = 0;
+};
+__device__ inline size_t block_id(const BlockMap& m, int nblk_cap, size_t b, long long blk) {
+    return m.table ? (size_t)m.table[b * (size_t)m.stride + (size_t)blk] : b * (size_t)nblk_cap + (size_t)blk;
 }
-__host__ __device__ inline size_t zv_block_index(size_t b, size_t nblk_cap, int C, long long t, int c) {
-    return ((b * nblk_cap + (size_t)(t >> 6)) * (size_t)(C >> 4) + (size_t)(c >> 4)) * 1024 +
-           (size_t)((t & 63) >> 4) * 256 + (size_t)(c & 15) * 16 + (size_t)(t & 15);
+// element (token t, channel c) of a latent of C channels whose token t lies in block `id`
+__host__ __device__ inline size_t zk_block_at(size_t id, int C, long long t, int c) {
+    return (id * (size_t)(C >> 4) + (size_t)(c >> 4)) * 1024 + (size_t)(t & 63) * 16 + (size_t)(c & 15);
+}
+__host__ __device__ inline size_t zv_block_at(size_t id, int C, long long t, int c) {
+    return (id * (size_t)(C >> 4) + (size_t)(c >> 4)) * 1024 + (size_t)((t & 63) >> 4) * 256 +
+           (size_t)(c & 15) * 16 + (size_t)(t & 15);
 }
 
 // Ranks rounded up to the 16-channel tile: the cache stores each head's key latent with
@@ -218,6 +227,7 @@ struct ScoreParams {
     const int32_t* seq_lens = nullptr;   // per-sequence lengths (device, clamped to [0, seq_len])
     const int32_t* seq_map = nullptr;    // query row b reads cache sequence seq_map[b] (or b)
     int cache_batch = 0;
+    BlockMap pages;
     float q_scale;         // softmax scale * log2(e)
     int8_t order[kMaxHeads];          // heads grouped: group g = order[gstart[g] .. gstart[g+1])
     int8_t gstart[kMaxGroups + 1];
@@ -241,6 +251,7 @@ struct ValueParams {
     const int32_t* seq_lens = nullptr;   // per-sequence lengths (device) or NULL
     const int32_t* seq_map = nullptr;    // query row b reads cache sequence seq_map[b] (or b)
     int cache_batch = 0;
+    BlockMap pages;
     // mixed 4/3-bit value cache only
     const void* zv_meta;   // [B][cap/64][2][rv]
     const void* zv_tail;   // [B][64][rv]
@@ -291,6 +302,7 @@ struct LinearStoreParams {
     long long cap;         // kind 1: capacity / 64 blocks; kind 2: capacity in tokens
     int padded;            // kind 1 with rounded ranks: outputs map through `map`, pads are zeroed
     PadMap map;
+    BlockMap pages;        // kinds 1 and 2
 };
 
 struct DenseDecodeParams {
@@ -303,6 +315,7 @@ struct DenseDecodeParams {
     const int32_t* seq_lens = nullptr;   // per-sequence lengths (device) or NULL
     const int32_t* seq_map = nullptr;    // query row b reads cache sequence seq_map[b] (or b)
     int cache_batch = 0;
+    BlockMap pages;
     float q_scale;
     double rope_rev[64];
 };
@@ -346,6 +359,7 @@ struct BlockXposeParams {
     int blk_first;              // first 64-token block touched
     int to_blocks;
     int layout;
+    BlockMap pages;
 };
 
 struct AppendSmallParams {
@@ -358,6 +372,7 @@ struct AppendSmallParams {
     const int32_t* positions = nullptr;   // n == 1: sequence b's token goes to positions[b]
                                 // (device; skipped outside [0, capacity)), or NULL: tokens pos ..
                                 // pos + n - 1
+    BlockMap pages;
 };
 
 // Rows of a latent with rounded ranks between the caller's layout [B][n][C_src] and the cache
@@ -369,7 +384,19 @@ struct PaddedRowsParams {
     int B, nblk_cap, which, C, C_src, to_cache;
     long long t0, n;
     const int32_t* positions = nullptr;   // as in AppendSmallParams (n == 1), or NULL
+    BlockMap pages;
     PadMap map;
+};
+
+// Token rows of a paged dense cache: rows [B][n][row_bytes] <-> tokens t0 + i of sequence b (or
+// positions[b] when n == 1 and positions is set; positions outside [0, capacity) are skipped).
+struct PagedRowsParams {
+    const char* rows;
+    char* cache;
+    long long row_bytes, t0, n;
+    int B, nblk_cap, to_cache;
+    const int32_t* positions = nullptr;
+    BlockMap pages;
 };
 
 struct Q43QuantParams {
@@ -383,6 +410,7 @@ struct Q43QuantParams {
     // one appended token per sequence (device array, or NULL): the group of sequence b is
     // quantised from the tail only when positions[b] is its last token
     const int32_t* positions = nullptr;
+    BlockMap pages;
 };
 
 // Blockwise Hadamard rotation of binary16 rows (kind 0: latent rows dst = src . H, [n][C]) or
@@ -410,6 +438,7 @@ struct Q43ReadParams {
     void* out;                  // [B][t1 - t0][C] binary16
     int B, nblk_cap;
     long long t0, t1, full_tokens;   // tokens below full_tokens sit in complete groups
+    BlockMap pages;
 };
 
 }  // namespace starkv

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void dense_decode_split(const DenseDecodeParam
                 const int j = j0 + jj;
                 // rows past the sequence end lie inside the 64-token-aligned capacity; their
                 // scores are replaced below, so the loads stay unconditional
-                const size_t row = ((size_t)bc * p.cap + t0 + j) * W + col;
+                const size_t row = (block_id(p.pages, p.cap >> 6, bc, (t0 + j) >> 6) * 64 + ((t0 + j) & 63)) * W + col;
                 float k1[8], k2[8];
                 load8<K>(p.k, row, k1);
                 load8<K>(p.k, row + NF, k2);
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void dense_decode_split(const DenseDecodeParam
                 // this slot: rows past the end may hold anything (0 * NaN is NaN)
                 const int j = j0 + min(jj, nt - 1);
                 const float pj = jj < nt ? sc[jj] : 0.0f;
-                const size_t row = ((size_t)bc * p.cap + t0 + j) * W + col;
+                const size_t row = (block_id(p.pages, p.cap >> 6, bc, (t0 + j) >> 6) * 64 + ((t0 + j) & 63)) * W + col;
                 float v1[8], v2[8];
                 load8<K>(p.v, row, v1);
                 load8<K>(p.v, row + NF, v2);

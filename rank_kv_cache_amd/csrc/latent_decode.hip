@@ -181,7 +181,6 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     const int Rk = p.Rk;
     const size_t kgroups = (size_t)(Rk >> 4);
     const int bc = cache_seq(p.seq_map, b, p.cache_batch);      // the cache sequence read
-    const size_t blk_base = (size_t)bc * p.nblk_cap;
     const uint32_t* __restrict__ qcodes = static_cast<const uint32_t*>(p.zk);
     const uint16_t* __restrict__ qmeta = static_cast<const uint16_t*>(p.zk_meta);
     const T* __restrict__ qtail = static_cast<const T*>(p.zk_tail);
@@ -251,7 +250,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         // Every slot is loaded (steps past the head's rank repeat its last step, a cache hit), so
         // the number of loads in flight is static and the compiler's wait counts stay exact:
         // loads are retired in order, and a data-dependent count would force a full drain.
-        const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
+        const size_t base = (block_id(p.pages, p.nblk_cap, bc, blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -374,7 +373,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         for (int u = 0; u < nunits; ++u) {
             const int blk = blk_begin + wave + NW * (u / ng);
             const int s = u - (u / ng) * ng;
-            const size_t base = ((blk_base + blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
+            const size_t base = (block_id(p.pages, p.nblk_cap, bc, blk) * kgroups + s_kgrp[s]) * 1024 + (size_t)j * 16 + 8 * half;
             unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
                 return load_frag<K>(zk, base + (size_t)ks * 1024 + nt * 512);
             });
@@ -385,8 +384,9 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         for (int u = 0; u < nunits; ++u) {
             const int blk = blk_begin + wave + NW * (u / ng);
             const int s = u - (u / ng) * ng;
-            const uint32_t* blkw = qcodes + (blk_base + blk) * qblock_words;
-            const uint16_t* meta = qmeta + (blk_base + blk) * 2 * (size_t)Rk;
+            const size_t bid = block_id(p.pages, p.nblk_cap, bc, blk);
+            const uint32_t* blkw = qcodes + bid * qblock_words;
+            const uint16_t* meta = qmeta + bid * 2 * (size_t)Rk;
             unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
                 const int n = s_gn[s][ks];
                 const int c0 = 16 * (s_kgrp[s] + ks) + 8 * half;
@@ -620,13 +620,13 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
         if constexpr (!QV) {
-            const size_t bbase = ((size_t)bc * p.nblk_cap + blk) * cgroups * 1024;
+            const size_t bbase = block_id(p.pages, p.nblk_cap, bc, blk) * cgroups * 1024;
 #pragma unroll
             for (int k = 0; k < NTW; ++k)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) z.z[k][ks] = load_frag<K>(p.zv, bbase + zoff[k] + ks * 256);
         } else {
-            const size_t bb = ((size_t)bc * p.nblk_cap + blk);
+            const size_t bb = block_id(p.pages, p.nblk_cap, bc, blk);
             const uint8_t* blkp = qcodes + bb * p.block_bytes;
             const uint16_t* meta = qmeta + bb * 2 * p.rv;
 #pragma unroll

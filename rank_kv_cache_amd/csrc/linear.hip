@@ -217,7 +217,8 @@ __device__ __forceinline__ void store_one(const LinearStoreParams& p, int m, int
         break;
     case 1:
         if (!p.padded) {
-            store_elem<E>(dst, key ? zk_block_index(b, p.cap, C, tok, c) : zv_block_index(b, p.cap, C, tok, c), v);
+            const size_t id = block_id(p.pages, (int)p.cap, b, tok >> 6);
+            store_elem<E>(dst, key ? zk_block_at(id, C, tok, c) : zv_block_at(id, C, tok, c), v);
         } else if (key) {
             // caller channel c of head h goes to stored channel koff[h] + (c - soff[h]); the
             // head's last channel also zeroes the head's padding channels of this token
@@ -225,18 +226,20 @@ __device__ __forceinline__ void store_one(const LinearStoreParams& p, int m, int
             int h = 0;
             while (h + 1 < m.H && c >= m.soff[h + 1]) ++h;
             const int Cs = m.koff[m.H], cs = m.koff[h] + (c - m.soff[h]);
-            store_elem<E>(dst, zk_block_index(b, p.cap, Cs, tok, cs), v);
+            const size_t id = block_id(p.pages, (int)p.cap, b, tok >> 6);
+            store_elem<E>(dst, zk_block_at(id, Cs, tok, cs), v);
             if (c + 1 == m.soff[h + 1])
-                for (int z = cs + 1; z < m.koff[h + 1]; ++z) store_elem<E>(dst, zk_block_index(b, p.cap, Cs, tok, z), 0.0f);
+                for (int z = cs + 1; z < m.koff[h + 1]; ++z) store_elem<E>(dst, zk_block_at(id, Cs, tok, z), 0.0f);
         } else {
             const int Cs = p.map.rv;
-            store_elem<E>(dst, zv_block_index(b, p.cap, Cs, tok, c), v);
+            const size_t id = block_id(p.pages, (int)p.cap, b, tok >> 6);
+            store_elem<E>(dst, zv_block_at(id, Cs, tok, c), v);
             if (c + 1 == p.map.rv_src)
-                for (int z = c + 1; z < Cs; ++z) store_elem<E>(dst, zv_block_index(b, p.cap, Cs, tok, z), 0.0f);
+                for (int z = c + 1; z < Cs; ++z) store_elem<E>(dst, zv_block_at(id, Cs, tok, z), 0.0f);
         }
         break;
     case 2:
-        store_elem<E>(dst, ((size_t)b * p.cap + tok) * C + c, v);
+        store_elem<E>(dst, (block_id(p.pages, (int)(p.cap >> 6), b, tok >> 6) * 64 + (tok & 63)) * C + c, v);
         break;
     default:
         store_elem<kF16>(dst, ((size_t)b * 64 + (tok & 63)) * C + c, v);

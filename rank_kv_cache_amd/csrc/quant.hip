@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void q43_quantize(const Q43QuantParams p) {
         if (z16 == 0x8000u) z16 = 0;
         s_s[tid] = s16;
         s_z[tid] = z16;
-        uint16_t* meta = static_cast<uint16_t*>(p.meta) + ((size_t)b * p.nblk_cap + g) * 2 * C + c;
+        uint16_t* meta = static_cast<uint16_t*>(p.meta) + block_id(p.pages, p.nblk_cap, b, g) * 2 * C + c;
         meta[0] = s16;
         meta[C] = z16;
     }
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void q43_quantize(const Q43QuantParams p) {
     }
     __syncthreads();
 
-    uint8_t* blk = static_cast<uint8_t*>(p.codes) + ((size_t)b * p.nblk_cap + g) * L.block_bytes;
+    uint8_t* blk = static_cast<uint8_t*>(p.codes) + block_id(p.pages, p.nblk_cap, b, g) * L.block_bytes;
     if (!L.is_key) {
         // value latent: thread per channel writes its whole run
         if (tid < 64 && c0 + tid < C) {
@@ -208,8 +208,9 @@ __global__ __launch_bounds__(256) void q43_readback(const Q43ReadParams p) {
     _Float16 v[8];
     if (tok < p.full_tokens) {
         const int g = (int)(tok >> 6), t = (int)(tok & 63);
-        const uint8_t* blk = static_cast<const uint8_t*>(p.codes) + ((size_t)b * p.nblk_cap + g) * L.block_bytes;
-        const uint16_t* meta = static_cast<const uint16_t*>(p.meta) + ((size_t)b * p.nblk_cap + g) * 2 * L.C + c;
+        const size_t bid = block_id(p.pages, p.nblk_cap, b, g);
+        const uint8_t* blk = static_cast<const uint8_t*>(p.codes) + bid * L.block_bytes;
+        const uint16_t* meta = static_cast<const uint16_t*>(p.meta) + bid * 2 * L.C + c;
         for (int e = 0; e < 8; ++e) {
             const int q = L.is_key ? q43_key_code(blk, L, c + e, t) : q43_value_code(blk, L, c + e, t);
             v[e] = q43_dequant(q, meta[e], meta[L.C + e]);

@@ -251,3 +251,13 @@ def test_queries_validation():
     assert dq(n=0, qs=None, ql=None) == 0
     assert dq(Cc=_cache(batch=0)) == 2                      # queries but no cache sequence
     assert dq(mx=0) == 2 and dq(mx=300) == 6
+
+
+def test_paged_cache_validation():
+    L = _latent()
+    paged = lambda stride=4, table=FAKE: _cache(block_table=table, table_stride=stride)
+    # capacity 256 tokens = 4 blocks per sequence: the table needs at least 4 columns
+    assert st_decode(L, paged(stride=3)) == 6
+    assert st_decode(L, paged(table=FAKE + 2)) == 5
+    import ctypes
+    assert ctypes.sizeof(sk._Cache) == 72                    # matches the C struct
