@@ -38,6 +38,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, AMD datasheet
+# fp32 vector peak without packed fp32 (disabled in this build): 256 CUs x 4 SIMDs x 16 lanes x
+# 2 flop (FMA) x 2.4 GHz; AMD's 157.3 TFLOP/s counts the packed forms
+VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 DEFAULT_WORKLOAD = "longchat_b16_t32768_f16"
 MODEL_WORKLOAD = "model32_b32_t8192_f16"
 METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=16 T=32K"
@@ -557,6 +560,17 @@ def main(argv=None):
                  "kv_gbs_stream_kernels": round(total_bytes / (stream_ms * 1e-3) / 1e9, 1),
                  "cached_tokens_per_s": B * runs[0].T / (ms_per_step * 1e-3)})
     dk = kernels[dom]
+    alu = None
+    if dom == "latent_scores":
+        # the score kernel's own bound is VALU issue: per (cached token, sequence, head) rotate-half
+        # RoPE of the rebuilt key (d/2 rotations, 6 flop each) + the dot (2d) + softmax (~5)
+        lat = [r for r in runs if not r.dense]
+        H, d = lat[0].layer.num_heads, lat[0].layer.head_dim
+        flop = sum(B * r.T * H * (5 * d + 5) for r in lat) / len(lat)
+        tf = flop / (dk["avg_us_per_launch"] * 1e-6) / 1e12
+        alu = {"achieved": tf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / VALU_PEAK_TFLOPS,
+               "flop_per_launch": flop,
+               "peak_note": "fp32 vector without packed fp32 (157.3 with it)"}
     rec = {
         "metric": METRIC,
         "value": B / (ms_per_step * 1e-3),
@@ -576,7 +590,8 @@ def main(argv=None):
                      "frac": dk["gbs"] / HBM_PEAK_GBS,
                      "traffic": MEASURED_TRAFFIC.get((desc["workload"], dom)),
                      "kernel_avg_us": dk["avg_us_per_launch"],
-                     "alg_bytes_per_launch": dk["alg_bytes_per_step"] // dk["launches_per_step"]},
+                     "alg_bytes_per_launch": dk["alg_bytes_per_step"] // dk["launches_per_step"],
+                     "alu": alu},
         "kernels": kernels,
     }
     if projections is not None:
