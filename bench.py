@@ -18,7 +18,8 @@ launch on the launch stream; the kernel with the largest total time is reported 
 ``kernels``). ``projections`` times, apart from the step, the two dense products around a latent
 layer's attention (the fused token down-projection + append and the output projection) with HIP
 events; ``queries`` times four queries per sequence (speculative-decoding verification) through
-the multi-query entry point. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
+the per-row multi-query entry point and through the one that shares each key and latent stream
+between a sequence's queries. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
 pairs of the same workload, scaled to the whole workload.
 """
 from __future__ import annotations
@@ -397,27 +398,42 @@ def measure_queries(sk, run, B, stream, hip, steps, per_seq=4):
     ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
     sp = stream.cuda_stream
 
-    def call():
+    nws_m = sk.starkv_decode_multi_workspace_bytes(L, B, per_seq, T, 0)
+    ws_m = torch.empty(nws_m, dtype=torch.uint8, device="cuda")
+    out_m = torch.empty_like(out)
+
+    def per_row():        # each row streams its sequence's latents on its own
         sk.starkv_decode_attn_queries(L, run.cache, n, qs, ql, T, q, run.bk, run.bv, out, 0, ws,
                                       nws, stream=stream)
 
-    for _ in range(2):
-        call()
-    ev = hip.create(2)
-    torch.cuda.synchronize()
-    hip.record(ev[0], sp)
-    for _ in range(steps):
-        call()
-    hip.record(ev[1], sp)
-    torch.cuda.synchronize()
-    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
-    hip.destroy(ev)
-    if not bool(torch.isfinite(out).all()):
+    def shared():         # one key rebuild and one latent stream for a sequence's rows
+        sk.starkv_decode_attn_multi(L, run.cache, per_seq, T, ql, q, run.bk, run.bv, out_m, 0,
+                                    ws_m, nws_m, stream=stream)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = hip.create(2)
+        torch.cuda.synchronize()
+        hip.record(ev[0], sp)
+        for _ in range(steps):
+            fn()
+        hip.record(ev[1], sp)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+        hip.destroy(ev)
+        return us
+
+    us = timed(per_row)
+    us_m = timed(shared)
+    if not (bool(torch.isfinite(out).all()) and bool(torch.isfinite(out_m).all())):
         raise SystemExit("non-finite multi-query output")
     res = {"queries_per_sequence": per_seq, "query_rows": n, "causal": not q43,
-           "avg_us": us, "us_per_query_row": us / n}
-    log(f"[bench] queries: {n} rows ({per_seq} per sequence) in {us:.1f} us")
-    del ws
+           "avg_us": us, "us_per_query_row": us / n, "shared_avg_us": us_m,
+           "shared_us_per_query_row": us_m / n}
+    log(f"[bench] queries: {n} rows ({per_seq} per sequence) in {us:.1f} us per row, "
+        f"{us_m:.1f} us shared")
+    del ws, ws_m
     return res
 
 
@@ -598,6 +614,7 @@ def main(argv=None):
         rec["projections"] = projections
     if queries is not None:
         queries["vs_single_query_step"] = queries["avg_us"] / (ms_per_step * 1e3)
+        queries["shared_vs_single_query_step"] = queries["shared_avg_us"] / (ms_per_step * 1e3)
         rec["queries"] = queries
     if sample is not None and sample.pairs:
         import oracle

@@ -216,6 +216,27 @@ starkv_status starkv_decode_attn_queries(const starkv_layer *layer, const starkv
                                          size_t workspace_bytes, void *stream);
 
 /*
+ * nq queries per cached sequence with one key rebuild and one latent stream for all of them
+ * (speculative-decoding verification of nq drafted tokens, nq parallel samples; Alg. 2 steps 4-7
+ * for each query): row b*nq + i of q and out ([batch*nq][H][d] fp32) is query i of sequence b.
+ * The score kernel rotates each rebuilt key once and dots it with the nq queries; the value
+ * kernel feeds each latent fragment to the nq rows' probability operands. q_lens: NULL (every row
+ * attends to max_len tokens) or a device int32 array of batch*nq lengths (4-byte aligned,
+ * clamped to [0, max_len]; a causal query at position p uses p + 1; 0 gives a zero row). The
+ * workspace is starkv_decode_multi_workspace_bytes(layer, batch, nq, max_len, num_splits).
+ * nq is 1, 2 or 4; latent layers with F16, BF16 or Q43 caches (nq = 1 also F32). Q43 lengths
+ * follow the starkv_decode_attn_ragged rule. Errors: those of starkv_decode_attn with seq_len =
+ * max_len; SHAPE (nq < 1), UNSUPPORTED (other nq, dense layers, F32 with nq > 1), MISALIGNED.
+ */
+size_t starkv_decode_multi_workspace_bytes(const starkv_layer *layer, int32_t batch, int32_t nq,
+                                           int64_t max_len, int32_t num_splits);
+starkv_status starkv_decode_attn_multi(const starkv_layer *layer, const starkv_cache *cache,
+                                       int32_t nq, int64_t max_len, const int32_t *q_lens,
+                                       const float *q, const void *bk, const void *bv, float *out,
+                                       int32_t num_splits, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/*
  * One new token per sequence at its own position (the append step of a ragged decode batch,
  * Alg. 2 steps 1-3): positions is a device array of batch int32 positions (4-byte aligned);
  * sequence b's rows zk_new[b] ([batch][R_k] with the caller's ranks; dense: [batch][H*d]) and

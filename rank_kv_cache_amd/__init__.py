@@ -22,7 +22,8 @@ __all__ = [
     "starkv_hadamard_rotate", "starkv_decode_attn_timed", "starkv_output_projection",
     "starkv_output_projection_workspace_bytes", "starkv_append_tokens",
     "starkv_append_tokens_workspace_bytes", "starkv_decode_attn_ragged",
-    "starkv_append_latents_ragged", "starkv_decode_attn_queries",
+    "starkv_append_latents_ragged", "starkv_decode_attn_queries", "starkv_decode_attn_multi",
+    "starkv_decode_multi_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -35,7 +36,8 @@ EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decod
                     "starkv_output_projection", "starkv_output_projection_workspace_bytes",
                     "starkv_append_tokens", "starkv_append_tokens_workspace_bytes",
                     "starkv_decode_attn_ragged", "starkv_append_latents_ragged",
-                    "starkv_decode_attn_queries",
+                    "starkv_decode_attn_queries", "starkv_decode_attn_multi",
+                    "starkv_decode_multi_workspace_bytes",
                     "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +97,10 @@ def lib():
         L.starkv_decode_attn_queries.restype = C.c_int
         L.starkv_decode_attn_queries.argtypes = [LP, CP, i32, vp, vp, i64, vp, vp, vp, vp, i32, vp,
                                                  sz, vp]
+        L.starkv_decode_multi_workspace_bytes.restype = sz
+        L.starkv_decode_multi_workspace_bytes.argtypes = [LP, i32, i32, i64, i32]
+        L.starkv_decode_attn_multi.restype = C.c_int
+        L.starkv_decode_attn_multi.argtypes = [LP, CP, i32, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         L.starkv_append_latents_ragged.restype = C.c_int
         L.starkv_append_latents_ragged.argtypes = [LP, CP, vp, vp, vp, vp]
         L.starkv_decode_attn_timed.restype = C.c_int
@@ -258,6 +264,22 @@ def starkv_decode_attn_queries(layer, cache, num_queries, query_seq, query_len, 
                                           _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "starkv_decode_attn_queries")
+    return st
+
+
+def starkv_decode_multi_workspace_bytes(layer, batch, nq, max_len, num_splits=0) -> int:
+    return int(lib().starkv_decode_multi_workspace_bytes(_layer_ptr(layer), batch, nq, max_len,
+                                                         num_splits))
+
+
+def starkv_decode_attn_multi(layer, cache, nq, max_len, q_lens, q, bk, bv, out, num_splits=0,
+                             workspace=None, workspace_bytes=0, stream=None, check=True):
+    st = lib().starkv_decode_attn_multi(_layer_ptr(layer), _cache_ptr(cache), nq, max_len,
+                                        _ptr(q_lens), _ptr(q), _ptr(bk), _ptr(bv), _ptr(out),
+                                        num_splits, _ptr(workspace), int(workspace_bytes),
+                                        _stream(stream))
+    if check:
+        _check(st, "starkv_decode_attn_multi")
     return st
 
 

@@ -15,8 +15,9 @@
 
 namespace starkv {
 hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
+                                int nq, hipStream_t st);
+hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, int nq,
                                 hipStream_t st);
-hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, hipStream_t st);
 int value_tiles_per_wave(int rv);
 hipError_t launch_linear(const LinearParams& p, int elem, hipStream_t st);
 int linear_rows_per_workgroup(int elem);
@@ -192,7 +193,9 @@ struct ScorePlan {
     int8_t gstart[kMaxGroups + 1] = {0};
 };
 
-bool plan_groups(const LayerInfo& li, int G, ScorePlan* sp) {
+// nq query rows per sequence share the score workgroup: more than one leaves a smaller factor
+// budget and at most kMaxGroupHeadsMQ heads per group
+bool plan_groups(const LayerInfo& li, int G, ScorePlan* sp, int nq = 1) {
     std::vector<int> order(li.H);
     for (int h = 0; h < li.H; ++h) order[h] = h;
     std::stable_sort(order.begin(), order.end(),
@@ -208,8 +211,10 @@ bool plan_groups(const LayerInfo& li, int G, ScorePlan* sp) {
     }
     const int esz = elem_bytes(li.factor_dt);
     int pos = 0;
+    const size_t budget = static_cast<size_t>(nq > 1 ? kFragLdsBytesMQ : kFragLdsBytes);
     for (int g = 0; g < G; ++g) {
-        if (static_cast<size_t>(load[g]) * li.D * esz > static_cast<size_t>(kFragLdsBytes)) return false;
+        if (static_cast<size_t>(load[g]) * li.D * esz > budget) return false;
+        if (nq > 1 && groups[g].size() > static_cast<size_t>(kMaxGroupHeadsMQ)) return false;
         sp->gstart[g] = static_cast<int8_t>(pos);
         for (int h : groups[g]) sp->order[pos++] = static_cast<int8_t>(h);
     }
@@ -218,12 +223,13 @@ bool plan_groups(const LayerInfo& li, int G, ScorePlan* sp) {
     return true;
 }
 
-ScorePlan plan_scores(const LayerInfo& li, int B, int nblk) {
+// B: cache sequences (one workgroup each per group and split), whatever their query rows
+ScorePlan plan_scores(const LayerInfo& li, int B, int nblk, int nq = 1) {
     ScorePlan sp;
     // one head per group always fits (a rank-d head needs at most d * d * 4 bytes of fragments)
     int G = 1;
-    while (G < li.H && !plan_groups(li, G, &sp)) ++G;
-    if (G == li.H) plan_groups(li, G, &sp);
+    while (G < li.H && !plan_groups(li, G, &sp, nq)) ++G;
+    if (G == li.H) plan_groups(li, G, &sp, nq);
     int maxr = 0;
     for (int h = 0; h < li.H; ++h) maxr = std::max(maxr, static_cast<int>(li.rank[h]));
     sp.maxks = maxr / 16;
@@ -251,14 +257,18 @@ struct ValuePlan {
     int chunks = 1, splits = 1, bps = 1, ntw = 4;
 };
 
-ValuePlan plan_values(const LayerInfo& li, int B, int nblk, int requested) {
+// B: cache sequences; nq query rows each share a workgroup (four channel tiles' accumulators in
+// all: 4 / nq tiles per wave) and splits of at most kMaxBlocksPerSplit / nq blocks
+ValuePlan plan_values(const LayerInfo& li, int B, int nblk, int requested, int nq = 1) {
     ValuePlan vp;
-    vp.ntw = li.cache_dt == STARKV_F32 ? 2 : value_tiles_per_wave(li.rv);   // fp32 operands: 2 tiles fit
+    vp.ntw = nq > 1 ? 4 / nq
+                    : li.cache_dt == STARKV_F32 ? 2 : value_tiles_per_wave(li.rv);   // fp32 operands: 2 tiles fit
     const int chunk_channels = kValueWaves * vp.ntw * 32;
     vp.chunks = (li.rv + chunk_channels - 1) / chunk_channels;
     const int per = std::max(1, B) * vp.chunks;
+    const int max_bps = kMaxBlocksPerSplit / nq;
     int S = requested > 0 ? requested : (kValueTargetWorkgroups + per - 1) / per;
-    S = std::max({1, std::min(S, nblk), (nblk + kMaxBlocksPerSplit - 1) / kMaxBlocksPerSplit});
+    S = std::max({1, std::min(S, nblk), (nblk + max_bps - 1) / max_bps});
     S = std::min(S, kMaxSplits);
     vp.bps = (nblk + S - 1) / S;
     vp.splits = (nblk + vp.bps - 1) / vp.bps;
@@ -286,7 +296,8 @@ struct WorkspaceLayout {
     ValuePlan vp;
 };
 
-WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, int requested) {
+// B: query rows (nq per cache sequence)
+WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, int requested, int nq = 1) {
     WorkspaceLayout w;
     const int nblk = static_cast<int>((seq_len + kTile - 1) / kTile);
     w.nblk = nblk;
@@ -301,8 +312,8 @@ WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, in
         w.total = off;
         return w;
     }
-    w.sp = plan_scores(li, B, nblk);
-    w.vp = plan_values(li, B, nblk, requested);
+    w.sp = plan_scores(li, B / nq, nblk, nq);
+    w.vp = plan_values(li, B / nq, nblk, requested, nq);
     w.S = w.vp.splits;
     w.tps = w.vp.bps;
     const size_t Tp = static_cast<size_t>(nblk) * kTile;
@@ -750,7 +761,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
                                  const void* bk, const void* bv, float* out, int32_t num_splits,
                                  void* workspace, size_t workspace_bytes, void* stream, void* ev0,
                                  void* evm, void* ev1, int rows = -1,
-                                 const int32_t* seq_map = nullptr) {
+                                 const int32_t* seq_map = nullptr, int nq = 1) {
     LayerInfo li;
     starkv_status s = check_layer(layer, &li);
     if (s != STARKV_OK) return s;
@@ -766,7 +777,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     if (!li.dense && (!bk || !bv)) return STARKV_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return STARKV_ERR_MISALIGNED;
     if (!li.dense && (!aligned16(bk) || !aligned16(bv))) return STARKV_ERR_MISALIGNED;
-    const WorkspaceLayout w = workspace_layout(li, B, seq_len, num_splits);
+    const WorkspaceLayout w = workspace_layout(li, B, seq_len, num_splits, nq);
     if (!workspace || workspace_bytes < w.total) return STARKV_ERR_WORKSPACE;
     if (!aligned16(workspace)) return STARKV_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -848,7 +859,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     }
     const int stream_kind = li.q43 ? -1 : ek;     // -1: mixed 4/3-bit codes, dequantised in-kernel
     if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
-    if ((s = dev(launch_latent_scores(sp, stream_kind, w.sp.G, w.sp.splits, w.sp.maxks, st))) != STARKV_OK)
+    if ((s = dev(launch_latent_scores(sp, stream_kind, w.sp.G, w.sp.splits, w.sp.maxks, nq, st))) != STARKV_OK)
         return s;
     if (evm && (s = dev(hipEventRecord(static_cast<hipEvent_t>(evm), st))) != STARKV_OK) return s;
     ValueParams vp;
@@ -875,7 +886,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     vp.full_blocks = static_cast<int>(seq_len / kTile);
     vp.block_bytes = li.q43 ? qv.block_bytes : 0;
     vp.n_hi = li.q43 ? qv.n_hi : 0;
-    if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, st))) != STARKV_OK) return s;
+    if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, nq, st))) != STARKV_OK) return s;
     if (ev1 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev1), st))) != STARKV_OK) return s;
     // the split merge happens inside the projection kernel, while it loads its inputs
     ProjectParams pr;
@@ -927,6 +938,33 @@ starkv_status starkv_decode_attn_queries(const starkv_layer* layer, const starkv
     }
     return decode_impl(layer, cache, max_len, query_len, q, bk, bv, out, num_splits, workspace,
                        workspace_bytes, stream, nullptr, nullptr, nullptr, num_queries, query_seq);
+}
+
+size_t starkv_decode_multi_workspace_bytes(const starkv_layer* layer, int32_t batch, int32_t nq,
+                                           int64_t max_len, int32_t num_splits) {
+    LayerInfo li;
+    if (check_layer(layer, &li) != STARKV_OK || li.dense || batch < 0 || max_len < 1 || num_splits < 0)
+        return 0;
+    if (nq != 1 && nq != 2 && nq != 4) return 0;
+    return workspace_layout(li, batch * nq, max_len, num_splits, nq).total;
+}
+
+starkv_status starkv_decode_attn_multi(const starkv_layer* layer, const starkv_cache* cache,
+                                       int32_t nq, int64_t max_len, const int32_t* q_lens,
+                                       const float* q, const void* bk, const void* bv, float* out,
+                                       int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if (nq < 1) return STARKV_ERR_SHAPE;
+    if (li.dense || (nq != 1 && nq != 2 && nq != 4) || (nq > 1 && li.cache_dt == STARKV_F32))
+        return STARKV_ERR_UNSUPPORTED;
+    if (q_lens && (reinterpret_cast<uintptr_t>(q_lens) & 3)) return STARKV_ERR_MISALIGNED;
+    if (!cache) return STARKV_ERR_NULL;
+    return decode_impl(layer, cache, max_len, q_lens, q, bk, bv, out, num_splits, workspace,
+                       workspace_bytes, stream, nullptr, nullptr, nullptr, cache->batch * nq,
+                       nullptr, nq);
 }
 
 starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_cache* cache,

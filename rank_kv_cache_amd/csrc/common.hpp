@@ -147,6 +147,10 @@ __device__ __forceinline__ void sincos_rev(float x, float* c, float* s) {
 constexpr int kMaxHeads = 32;
 constexpr int kTile = 64;              // tokens per cache block
 constexpr int kFragLdsBytes = 96 * 1024;   // key-factor fragments of one head group in LDS
+// several queries per sequence: a smaller factor budget (the rotated queries take the room) and
+// at most this many heads per group
+constexpr int kFragLdsBytesMQ = 64 * 1024;
+constexpr int kMaxGroupHeadsMQ = 16;
 constexpr int kMaxGroups = 32;
 constexpr int kValueWaves = 4;         // waves per value workgroup
 constexpr int kMaxBlocksPerSplit = 256;

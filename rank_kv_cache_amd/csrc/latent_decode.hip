@@ -134,10 +134,21 @@ constexpr int score_waves() { return K == kF32 ? 8 : 12; }
 // fragments are loaded once the first tile's MFMAs have consumed theirs.
 template <int K, int MAXKS, bool QK>
 constexpr bool score_split_loads() { return score_waves<K, MAXKS, QK>() == 12 && (QK || MAXKS > 4); }
+// NQ queries of one sequence share each rebuilt, rotated key: eight waves (the per-query sums and
+// query tiles need the larger register budget), a smaller factor budget in LDS to make room for
+// NQ rotated queries per wave, and head groups of at most kMaxGroupHeadsMQ heads.
+template <int K, int MAXKS, bool QK, int NQ>
+constexpr int score_waves_q() { return NQ > 1 ? 8 : score_waves<K, MAXKS, QK>(); }
+// (mixed 4/3-bit codes are only ever read by the per-fragment loads of the split path)
+template <int K, int MAXKS, bool QK, int NQ>
+constexpr bool score_split_q() { return NQ == 1 ? score_split_loads<K, MAXKS, QK>() : QK; }
+static_assert(score_split_q<kF16, 4, true, 1>() && score_split_q<kF16, 8, true, 1>() &&
+              score_split_q<kF16, 4, true, 2>() && score_split_q<kF16, 8, true, 4>(),
+              "mixed 4/3-bit caches must take the per-fragment load path");
 
-template <int D, int K, int MAXKS, bool QK>
-__global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_scores(const ScoreParams p) {
-    constexpr int NW = score_waves<K, MAXKS, QK>();
+template <int D, int K, int MAXKS, bool QK, int NQ>
+__global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void latent_scores(const ScoreParams p) {
+    constexpr int NW = score_waves_q<K, MAXKS, QK, NQ>();
     constexpr int NF = D / 2;           // RoPE frequencies
     constexpr int HMT = D / 64;         // m-tile pairs (mt, mt + HMT)
     using Fr = typename Elem<K>::frag;
@@ -145,9 +156,9 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     using PT = typename PStore<K>::T;
     using Buf = KeyBuf<K, MAXKS>;
 
-    __shared__ __attribute__((aligned(32))) T s_bk[kFragLdsBytes / sizeof(T)];
-    __shared__ __attribute__((aligned(16))) float s_q[kMaxHeads * D];
-    __shared__ __attribute__((aligned(16))) float s_qr[NW][2][D];
+    __shared__ __attribute__((aligned(32))) T s_bk[(NQ > 1 ? kFragLdsBytesMQ : kFragLdsBytes) / sizeof(T)];
+    __shared__ __attribute__((aligned(16))) float s_q[(NQ > 1 ? kMaxGroupHeadsMQ : kMaxHeads) * NQ * D];
+    __shared__ __attribute__((aligned(16))) float s_qr[NW][NQ][2][D];
     __shared__ int s_slot[kMaxHeads + 1];
 
     // small per-layer tables, copied out of the kernel arguments so that every dynamic index
@@ -167,7 +178,14 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
     const int hs0 = p.gstart[grp];
     const int ng = p.gstart[grp + 1] - hs0;
     const int H = p.H;
-    const int seq_len = seq_length(p.seq_lens, b, p.seq_len);   // this sequence's length
+    // query rows row0 .. row0 + NQ - 1 read cache sequence b; the blocks cover the longest
+    int qlen[NQ];
+    const int row0 = b * NQ;
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi) qlen[qi] = seq_length(p.seq_lens, row0 + qi, p.seq_len);
+    int seq_len = qlen[0];
+#pragma unroll
+    for (int qi = 1; qi < NQ; ++qi) seq_len = max(seq_len, qlen[qi]);
     const int Tp = p.Tp;
     const int nblk = p.nblk;                                     // stride of the statistics
     const int my_nblk = (seq_len + 63) >> 6;
@@ -216,7 +234,10 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         const Fr* src = reinterpret_cast<const Fr*>(bkt + (size_t)s_kgrp[s] * 16 * D);
         Fr* dst = reinterpret_cast<Fr*>(&s_bk[s_slot[s]]);
         for (int i = tid; i < n8; i += 64 * NW) dst[i] = src[i];
-        for (int i = tid; i < D; i += 64 * NW) s_q[s * D + i] = qg[((size_t)b * H + h) * D + i] * q_scale;
+        for (int i = tid; i < NQ * D; i += 64 * NW) {
+            const int qi = i / D, e = i - qi * D;
+            s_q[(s * NQ + qi) * D + e] = qg[((size_t)(row0 + qi) * H + h) * D + e] * q_scale;
+        }
     }
 
     // ---- constant rotation by j*theta_i for this lane's column j and its frequencies ----
@@ -271,24 +292,29 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
                 sincos_rev((float)(rev - floor(rev)), &cb[nt], &sb[nt]);
             }
         }
-        // q' = R_{n0}^T q for both column tiles, wave-private LDS
+        // q' = R_{n0}^T q for both column tiles and every query, wave-private LDS
         if (lane < NF) {
-            const float q1 = s_q[s * D + lane], q2 = s_q[s * D + lane + NF];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                s_qr[wave][nt][lane] = q1 * cb[nt] + q2 * sb[nt];
-                s_qr[wave][nt][lane + NF] = q2 * cb[nt] - q1 * sb[nt];
+            for (int qi = 0; qi < NQ; ++qi) {
+                const float q1 = s_q[(s * NQ + qi) * D + lane], q2 = s_q[(s * NQ + qi) * D + lane + NF];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    s_qr[wave][qi][nt][lane] = q1 * cb[nt] + q2 * sb[nt];
+                    s_qr[wave][qi][nt][lane + NF] = q2 * cb[nt] - q1 * sb[nt];
+                }
             }
         }
         wave_sync_lds();
         const T* fr = &s_bk[s_slot[s]];
-        float sc[2] = {0.0f, 0.0f};
+        float sc[NQ][2];
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) sc[qi][0] = sc[qi][1] = 0.0f;
         // Key rebuild + RoPE + dot for a head of NKS rank steps, as straight-line code: the rank
         // is dispatched once per unit, so no branch separates the MFMA chains from the RoPE
         // arithmetic and the scheduler can overlap one pass's MFMAs with another's VALU work.
         auto core = [&](auto nks_c) __attribute__((always_inline)) {
             constexpr int NKS = decltype(nks_c)::value;
-            constexpr bool SPLIT = score_split_loads<K, MAXKS, QK>();
+            constexpr bool SPLIT = score_split_q<K, MAXKS, QK, NQ>();
             Fr z[2][NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) z[0][ks] = frag(0, ks);
@@ -321,19 +347,29 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int i0 = 32 * pp + 8 * g + 4 * half;
-                        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0]);
-                        const f32x4 q2 = *reinterpret_cast<const f32x4*>(&s_qr[wave][nt][i0 + NF]);
+                        f32x4 q1[NQ], q2[NQ];
+#pragma unroll
+                        for (int qi = 0; qi < NQ; ++qi) {
+                            q1[qi] = *reinterpret_cast<const f32x4*>(&s_qr[wave][qi][nt][i0]);
+                            q2[qi] = *reinterpret_cast<const f32x4*>(&s_qr[wave][qi][nt][i0 + NF]);
+                        }
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const float a = acc0[4 * g + r], bb = acc1[4 * g + r];
                             const float c = cj[pp][g][r], sn = sj[pp][g][r];
-                            sc[nt] = fmaf(q1[r], fmaf(-bb, sn, a * c), sc[nt]);
-                            sc[nt] = fmaf(q2[r], fmaf(a, sn, bb * c), sc[nt]);
+                            // the key rotated by j*theta, then its dot with each query
+                            const float ra = fmaf(-bb, sn, a * c), rb = fmaf(a, sn, bb * c);
+#pragma unroll
+                            for (int qi = 0; qi < NQ; ++qi) {
+                                sc[qi][nt] = fmaf(q1[qi][r], ra, sc[qi][nt]);
+                                sc[qi][nt] = fmaf(q2[qi][r], rb, sc[qi][nt]);
+                            }
                         }
                     }
                     // consume the dot here, so the compiler cannot sink every pass's RoPE
                     // arithmetic past all the MFMA chains (all accumulators would stay live)
-                    asm volatile("" : "+v"(sc[nt]));
+#pragma unroll
+                    for (int qi = 0; qi < NQ; ++qi) asm volatile("" : "+v"(sc[qi][nt]));
                 }
             }
         };
@@ -347,18 +383,23 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         case 7: core(std::integral_constant<int, (MAXKS >= 7 ? 7 : 1)>{}); break;
         default: core(std::integral_constant<int, MAXKS>{}); break;
         }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) sc[nt] = add_xor32(sc[nt]);
         const int tok = blk * 64 + lane;
-        float my = half ? sc[1] : sc[0];
-        if (tok >= seq_len) my = -INFINITY;
-        const float m = wave_max(my);
-        const float pr = __builtin_amdgcn_exp2f(my - m);
-        const float l = wave_sum(pr);
-        Pout[((size_t)b * H + h) * Tp + tok] = (PT)pr;
-        // every lane stores (even lanes m, odd lanes l, to the same two words): no branch, so
-        // the count of memory operations in flight stays static
-        stats[(((size_t)b * H + h) * nblk + blk) * 2 + (lane & 1)] = (lane & 1) ? l : m;
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) sc[qi][nt] = add_xor32(sc[qi][nt]);
+            float my = half ? sc[qi][1] : sc[qi][0];
+            if (tok >= qlen[qi]) my = -INFINITY;
+            const float m = wave_max(my);
+            // a query shorter than the block range sees whole blocks past its end: p = 0, l = 0
+            const float pr = (NQ == 1 || m != -INFINITY) ? __builtin_amdgcn_exp2f(my - m) : 0.0f;
+            const float l = wave_sum(pr);
+            const size_t row = (size_t)(row0 + qi) * H + h;
+            Pout[row * Tp + tok] = (PT)pr;
+            // every lane stores (even lanes m, odd lanes l, to the same two words): no branch, so
+            // the count of memory operations in flight stays static
+            stats[(row * nblk + blk) * 2 + (lane & 1)] = (lane & 1) ? l : m;
+        }
         wave_sync_lds();
     };
 
@@ -368,7 +409,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
         unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) { return z.z[nt][ks]; });
     };
 
-    if constexpr (score_split_loads<K, MAXKS, QK>() && !QK) {
+    if constexpr (score_split_q<K, MAXKS, QK, NQ>() && !QK) {
         // One unit at a time, latent fragments loaded inside the unit, per column tile.
         for (int u = 0; u < nunits; ++u) {
             const int blk = blk_begin + wave + NW * (u / ng);
@@ -378,7 +419,7 @@ __global__ __launch_bounds__((64 * score_waves<K, MAXKS, QK>()), 1) void latent_
                 return load_frag<K>(zk, base + (size_t)ks * 1024 + nt * 512);
             });
         }
-    } else if constexpr (score_split_loads<K, MAXKS, QK>()) {
+    } else if constexpr (score_split_q<K, MAXKS, QK, NQ>()) {
         // Mixed 4/3-bit codes: the code window, scales and zero points of each fragment are
         // loaded inside the unit, per column tile, and dequantised in registers.
         for (int u = 0; u < nunits; ++u) {
@@ -536,13 +577,16 @@ template <int K, int NTW> struct ValBuf<K, NTW, true> {
     uint32_t s2[NTW], z2[NTW];
 };
 
-template <int K, int NTW, bool QV>
+// NQ query rows of one cache sequence (row0 = b * NQ ...): each latent fragment feeds NQ stacked
+// 32-row operands (one per query row's heads), so the value latent is streamed once for all.
+template <int K, int NTW, bool QV, int NQ>
 __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     using Fr = typename Elem<K>::frag;
     using Buf = ValBuf<K, NTW, QV>;
     using PF = ProbFrag<K>;
-    __shared__ float s_f[kMaxHeads][kMaxBlocksPerSplit];
-    __shared__ float s_M[kMaxHeads], s_L[kMaxHeads];
+    constexpr int BPS = kMaxBlocksPerSplit / NQ;      // the planner caps splits at this many blocks
+    __shared__ float s_f[NQ][kMaxHeads][BPS];
+    __shared__ float s_M[NQ][kMaxHeads], s_L[NQ][kMaxHeads];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -552,27 +596,33 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     const int chunk = blockIdx.y;
     const int b = blockIdx.z;
     const int H = p.H;
-    const int seq_len = seq_length(p.seq_lens, b, p.seq_len);   // this sequence's length
+    const int row0 = b * NQ;                                     // this workgroup's query rows
+    int seq_len = seq_length(p.seq_lens, row0, p.seq_len);      // the longest of their lengths
+#pragma unroll
+    for (int qi = 1; qi < NQ; ++qi) seq_len = max(seq_len, seq_length(p.seq_lens, row0 + qi, p.seq_len));
     const int bc = cache_seq(p.seq_map, b, p.cache_batch);      // the cache sequence read
     const int blk_begin = split * p.blocks_per_split;
     // a split past this sequence's end is empty (blk_end == blk_begin): (M, L, Acc) = (-inf, 0, 0)
     const int blk_end = max(blk_begin, min((seq_len + 63) >> 6, blk_begin + p.blocks_per_split));
     const int nb = blk_end - blk_begin;
 
-    // ---- split statistics per head: M = max m_blk, f_blk = 2^(m_blk - M), L = sum f l ----
-    for (int h = wave; h < H; h += kValueWaves) {
-        const float* st = p.stats + (((size_t)b * H + h) * p.nblk + blk_begin) * 2;
+    // ---- split statistics per (query row, head): M = max m_blk, f_blk = 2^(m_blk - M), L = sum f l
+    for (int hq = wave; hq < NQ * H; hq += kValueWaves) {
+        const int qi = hq / H, h = hq - qi * H;
+        const float* st = p.stats + (((size_t)(row0 + qi) * H + h) * p.nblk + blk_begin) * 2;
         float M = -INFINITY;
         for (int i = lane; i < nb; i += 64) M = fmaxf(M, st[2 * i]);
         M = wave_max(M);
+        // a row whose blocks here all lie past its own end: every f is 0 (no -inf - -inf)
+        const float Mc = (NQ == 1 || M != -INFINITY) ? M : 0.0f;
         float L = 0.0f;
         for (int i = lane; i < nb; i += 64) {
-            const float f = __builtin_amdgcn_exp2f(st[2 * i] - M);
-            s_f[h][i] = f;
+            const float f = __builtin_amdgcn_exp2f(st[2 * i] - Mc);
+            s_f[qi][h][i] = f;
             L += f * st[2 * i + 1];
         }
         L = wave_sum(L);
-        if (lane == 0) { s_M[h] = M; s_L[h] = L; }
+        if (lane == 0) { s_M[qi][h] = M; s_L[qi][h] = L; }
     }
     __syncthreads();
 
@@ -592,15 +642,19 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
         const int cc = min(ch[k], p.rv - 1);
         zoff[k] = (size_t)(cc >> 4) * 1024 + (cc & 15) * 16 + 8 * half;
     }
-    f32x16 acc[NTW];
+    f32x16 acc[NQ][NTW];
 #pragma unroll
-    for (int k = 0; k < NTW; ++k)
+    for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
+        for (int k = 0; k < NTW; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qi][k][r] = 0.0f;
 
-    typename PF::Raw pA[4], pB[4];
+    typename PF::Raw pA[NQ][4], pB[NQ][4];
     Buf zA, zB;
-    const size_t prow = ((size_t)b * H + min(hrow, H - 1)) * p.Tp + 8 * half;
+    // probability row of this lane's head for query row qi: prow + qi * qstride
+    const size_t prow = ((size_t)row0 * H + min(hrow, H - 1)) * p.Tp + 8 * half;
+    const size_t qstride = (size_t)H * p.Tp;
     // mixed 4/3-bit cache: per lane, the channel's run offset and width are fixed
     const uint8_t* __restrict__ qcodes = static_cast<const uint8_t*>(p.zv);
     const uint16_t* __restrict__ qmeta = static_cast<const uint16_t*>(p.zv_meta);
@@ -616,9 +670,11 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     // partial last group, read from the binary16 tail
     const int main_end = QV ? max(blk_begin, min(blk_end, seq_len >> 6)) : blk_end;
 
-    auto load_blk = [&](typename PF::Raw (&pr)[4], Buf& z, int blk) __attribute__((always_inline)) {
+    auto load_blk = [&](typename PF::Raw (&pr)[NQ][4], Buf& z, int blk) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
+        for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) pr[qi][ks] = PF::load(p.P, prow + qi * qstride + (size_t)blk * 64 + 16 * ks);
         if constexpr (!QV) {
             const size_t bbase = block_id(p.pages, p.nblk_cap, bc, blk) * cgroups * 1024;
 #pragma unroll
@@ -648,12 +704,16 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
         }
     };
     // Fr frag(k, ks) of the block's latent operand; zero past the sequence end
-    auto accumulate = [&](const typename PF::Raw (&pr)[4], int blk, auto&& frag) __attribute__((always_inline)) {
-        const float f = hvalid ? s_f[hrow][blk - blk_begin] : 0.0f;
+    auto accumulate = [&](const typename PF::Raw (&pr)[NQ][4], int blk, auto&& frag) __attribute__((always_inline)) {
+        float f[NQ];
+#pragma unroll
+        for (int qi = 0; qi < NQ; ++qi) f[qi] = hvalid ? s_f[qi][hrow][blk - blk_begin] : 0.0f;
         const bool ragged = (blk + 1) * 64 > seq_len;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const typename PF::Op a = PF::scale(pr[ks], f);
+            typename PF::Op a[NQ];
+#pragma unroll
+            for (int qi = 0; qi < NQ; ++qi) a[qi] = PF::scale(pr[qi][ks], f[qi]);
 #pragma unroll
             for (int k = 0; k < NTW; ++k) {
                 Fr zf = frag(k, ks);
@@ -662,11 +722,12 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
                     for (int e = 0; e < 8; ++e)
                         if (blk * 64 + 16 * ks + 8 * half + e >= seq_len) zf[e] = 0;
                 }
-                acc[k] = PF::mma(a, zf, acc[k]);
+#pragma unroll
+                for (int qi = 0; qi < NQ; ++qi) acc[qi][k] = PF::mma(a[qi], zf, acc[qi][k]);
             }
         }
     };
-    auto compute_blk = [&](const typename PF::Raw (&pr)[4], const Buf& z, int blk) __attribute__((always_inline)) {
+    auto compute_blk = [&](const typename PF::Raw (&pr)[NQ][4], const Buf& z, int blk) __attribute__((always_inline)) {
         if constexpr (!QV) {
             accumulate(pr, blk, [&](int k, int ks) __attribute__((always_inline)) { return z.z[k][ks]; });
         } else {
@@ -687,9 +748,11 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
         // the partial last block of a mixed-precision cache: binary16 rows in the tail [B][64][rv]
         if (main_end < blk_end) {
             const int blk = main_end;
-            typename PF::Raw pr[4];
+            typename PF::Raw pr[NQ][4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) pr[ks] = PF::load(p.P, prow + (size_t)blk * 64 + 16 * ks);
+            for (int qi = 0; qi < NQ; ++qi)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) pr[qi][ks] = PF::load(p.P, prow + qi * qstride + (size_t)blk * 64 + 16 * ks);
             const _Float16* tail = static_cast<const _Float16*>(p.zv_tail) + (size_t)bc * 64 * p.rv;
             accumulate(pr, blk, [&](int k, int ks) __attribute__((always_inline)) {
                 const int cc = min(ch[k], p.rv - 1);
@@ -701,19 +764,24 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
         }
     }
 
-    const size_t part = (size_t)b * p.S + split;
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-        if (!chok[k]) continue;
+    for (int qi = 0; qi < NQ; ++qi) {
+        const size_t part = (size_t)(row0 + qi) * p.S + split;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int h = acc_row(r, lane);
-            if (h < H) p.ws_acc[(part * H + h) * p.rv + ch[k]] = acc[k][r];
+        for (int k = 0; k < NTW; ++k) {
+            if (!chok[k]) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int h = acc_row(r, lane);
+                if (h < H) p.ws_acc[(part * H + h) * p.rv + ch[k]] = acc[qi][k][r];
+            }
         }
     }
-    if (chunk == 0 && tid < H) {
-        p.ws_ml[(part * H + tid) * 2 + 0] = s_M[tid];
-        p.ws_ml[(part * H + tid) * 2 + 1] = s_L[tid];
+    if (chunk == 0 && tid < NQ * H) {
+        const int qi = tid / H, h = tid - qi * H;
+        const size_t part = (size_t)(row0 + qi) * p.S + split;
+        p.ws_ml[(part * H + h) * 2 + 0] = s_M[qi][h];
+        p.ws_ml[(part * H + h) * 2 + 1] = s_L[qi][h];
     }
 }
 
@@ -858,37 +926,49 @@ __global__ __launch_bounds__(1024) void project_heads(const ProjectParams p) {
 // ------------------------------------------------------------------------------------------------
 // Host launchers
 // ------------------------------------------------------------------------------------------------
-template <int D, int K, int MAXKS, bool QK>
+// grid.z = cache sequences (each workgroup serves its sequence's NQ query rows)
+template <int D, int K, int MAXKS, bool QK, int NQ>
 static hipError_t launch_scores_t(const ScoreParams& p, int groups, int splits, hipStream_t st) {
-    hipLaunchKernelGGL((latent_scores<D, K, MAXKS, QK>), dim3(splits, groups, p.B),
-                       dim3(64 * score_waves<K, MAXKS, QK>()), 0, st, p);
+    hipLaunchKernelGGL((latent_scores<D, K, MAXKS, QK, NQ>), dim3(splits, groups, p.B / NQ),
+                       dim3(64 * score_waves_q<K, MAXKS, QK, NQ>()), 0, st, p);
     return hipGetLastError();
 }
 
-template <int D, int K, bool QK>
+template <int D, int K, bool QK, int NQ>
 static hipError_t launch_scores_d(const ScoreParams& p, int groups, int splits, int maxks, hipStream_t st) {
-    if (maxks <= 4) return launch_scores_t<D, K, 4, QK>(p, groups, splits, st);
-    if (D == 128 && maxks <= 8) return launch_scores_t<D, K, (D == 128 ? 8 : 4), QK>(p, groups, splits, st);
+    if (maxks <= 4) return launch_scores_t<D, K, 4, QK, NQ>(p, groups, splits, st);
+    if (D == 128 && maxks <= 8) return launch_scores_t<D, K, (D == 128 ? 8 : 4), QK, NQ>(p, groups, splits, st);
     return hipErrorInvalidValue;
 }
 
-template <int K, bool QK>
+template <int K, bool QK, int NQ>
 static hipError_t launch_scores_k(const ScoreParams& p, int groups, int splits, int maxks, hipStream_t st) {
-    if (p.D == 128) return launch_scores_d<128, K, QK>(p, groups, splits, maxks, st);
-    if (p.D == 64) return launch_scores_d<64, K, QK>(p, groups, splits, maxks, st);
+    if (p.D == 128) return launch_scores_d<128, K, QK, NQ>(p, groups, splits, maxks, st);
+    if (p.D == 64) return launch_scores_d<64, K, QK, NQ>(p, groups, splits, maxks, st);
     return hipErrorInvalidValue;
 }
 
-// elem: kF32 / kF16 / kBF16, or -1 for a mixed 4/3-bit key cache (binary16 factors)
-hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
-                                hipStream_t st) {
+template <int NQ>
+static hipError_t launch_scores_q(const ScoreParams& p, int elem, int groups, int splits, int maxks,
+                                  hipStream_t st) {
     switch (elem) {
-    case kF32: return launch_scores_k<kF32, false>(p, groups, splits, maxks, st);
-    case kF16: return launch_scores_k<kF16, false>(p, groups, splits, maxks, st);
-    case kBF16: return launch_scores_k<kBF16, false>(p, groups, splits, maxks, st);
-    case -1: return launch_scores_k<kF16, true>(p, groups, splits, maxks, st);
+    case kF16: return launch_scores_k<kF16, false, NQ>(p, groups, splits, maxks, st);
+    case kBF16: return launch_scores_k<kBF16, false, NQ>(p, groups, splits, maxks, st);
+    case -1: return launch_scores_k<kF16, true, NQ>(p, groups, splits, maxks, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+// elem: kF32 / kF16 / kBF16, or -1 for a mixed 4/3-bit key cache (binary16 factors). nq: query
+// rows per cache sequence (p.B rows in all); 2 and 4 share each key between the rows (16-bit and
+// mixed caches).
+hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
+                                int nq, hipStream_t st) {
+    if (nq == 2) return launch_scores_q<2>(p, elem, groups, splits, maxks, st);
+    if (nq == 4) return launch_scores_q<4>(p, elem, groups, splits, maxks, st);
+    if (nq != 1) return hipErrorInvalidValue;
+    if (elem == kF32) return launch_scores_k<kF32, false, 1>(p, groups, splits, maxks, st);
+    return launch_scores_q<1>(p, elem, groups, splits, maxks, st);
 }
 
 // 32-channel tiles per value wave: four where r_v fills whole 512-channel chunks (each probability
@@ -901,22 +981,32 @@ int value_tiles_per_wave(int rv) {
     return waste2 < waste4 ? 2 : 4;
 }
 
-template <int NTW>
+// grid.z = cache sequences; NQ query rows each (p.B rows in all)
+template <int NTW, int NQ>
 static hipError_t launch_values_t(const ValueParams& p, int elem, int chunks, hipStream_t st) {
-    const dim3 grid(p.S, chunks, p.B);
+    const dim3 grid(p.S, chunks, p.B / NQ);
     switch (elem) {
-    case kF32: hipLaunchKernelGGL((latent_values<kF32, NTW, false>), grid, dim3(256), 0, st, p); break;
-    case kF16: hipLaunchKernelGGL((latent_values<kF16, NTW, false>), grid, dim3(256), 0, st, p); break;
-    case kBF16: hipLaunchKernelGGL((latent_values<kBF16, NTW, false>), grid, dim3(256), 0, st, p); break;
-    case -1: hipLaunchKernelGGL((latent_values<kF16, NTW, true>), grid, dim3(256), 0, st, p); break;
+    case kF16: hipLaunchKernelGGL((latent_values<kF16, NTW, false, NQ>), grid, dim3(256), 0, st, p); break;
+    case kBF16: hipLaunchKernelGGL((latent_values<kBF16, NTW, false, NQ>), grid, dim3(256), 0, st, p); break;
+    case -1: hipLaunchKernelGGL((latent_values<kF16, NTW, true, NQ>), grid, dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, hipStream_t st) {
-    if (ntw == 4) return launch_values_t<4>(p, elem, chunks, st);
-    if (ntw == 2) return launch_values_t<2>(p, elem, chunks, st);
+// ntw channel tiles per wave (nq query rows per sequence: 2 and 4 use ntw = 4 / nq, so the
+// accumulators stay at four tiles' worth)
+hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, int nq, hipStream_t st) {
+    if (nq == 2 && ntw == 2) return launch_values_t<2, 2>(p, elem, chunks, st);
+    if (nq == 4 && ntw == 1) return launch_values_t<1, 4>(p, elem, chunks, st);
+    if (nq != 1) return hipErrorInvalidValue;
+    if (elem == kF32) {
+        if (ntw != 2) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((latent_values<kF32, 2, false, 1>), dim3(p.S, chunks, p.B), dim3(256), 0, st, p);
+        return hipGetLastError();
+    }
+    if (ntw == 4) return launch_values_t<4, 1>(p, elem, chunks, st);
+    if (ntw == 2) return launch_values_t<2, 1>(p, elem, chunks, st);
     return hipErrorInvalidValue;
 }
 

@@ -261,3 +261,17 @@ def test_paged_cache_validation():
     assert st_decode(L, paged(table=FAKE + 2)) == 5
     import ctypes
     assert ctypes.sizeof(sk._Cache) == 72                    # matches the C struct
+
+
+def test_multi_validation():
+    L, Cc = _latent(), _cache()
+    mu = lambda nq=2, lens=None, L=L, Cc=Cc: sk.starkv_decode_attn_multi(
+        L, Cc, nq, 100, lens, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 40, check=False)
+    assert mu(nq=0) == 2 and mu(nq=3) == 8 and mu(nq=8) == 8
+    assert mu(L=_latent(cache_dtype=sk.F32)) == 8           # fp32 shares keys only with nq = 1
+    assert mu(L=sk.Layer(num_heads=4, head_dim=128, dense=True, cache_dtype=sk.F16)) == 8
+    assert mu(lens=FAKE + 2) == 5
+    assert mu(Cc=_cache(batch=0)) == 0
+    assert sk.starkv_decode_multi_workspace_bytes(L, 2, 3, 100) == 0
+    a = sk.starkv_decode_multi_workspace_bytes(L, 2, 4, 1000)
+    assert a > sk.starkv_decode_workspace_bytes(L, 2, 1000) and a % 256 == 0
