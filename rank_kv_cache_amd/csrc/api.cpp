@@ -24,9 +24,6 @@ int linear_rows_per_workgroup(int elem);
 hipError_t launch_linear_store(const LinearStoreParams& p, int elem, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
-hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
-                            const int16_t* rank, const int16_t* soff, const int16_t* srank,
-                            int elem, hipStream_t st);
 hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
@@ -290,7 +287,7 @@ int plan_splits(int B, int64_t seq_len, int requested) {
 }
 
 struct WorkspaceLayout {
-    size_t bkt = 0, P = 0, stats = 0, ml = 0, acc = 0, total = 0;
+    size_t P = 0, stats = 0, ml = 0, acc = 0, total = 0;
     int S = 1, tps = 1, nblk = 1;
     ScorePlan sp;
     ValuePlan vp;
@@ -318,8 +315,6 @@ WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, in
     w.tps = w.vp.bps;
     const size_t Tp = static_cast<size_t>(nblk) * kTile;
     const size_t pesz = li.cache_dt == STARKV_F32 ? 4 : 2;
-    w.bkt = off;
-    off += align_up(static_cast<size_t>(li.Rk) * li.D * elem_bytes(li.factor_dt));
     w.P = off;
     off += align_up(static_cast<size_t>(B) * li.H * Tp * pesz);
     w.stats = off;
@@ -820,14 +815,11 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     }
 
     const int ek = elem_kind(li.cache_dt);
-    void* bkt = ws + w.bkt;
-    if ((s = dev(launch_pack_keys(bk, bkt, li.D, li.H, li.koff, li.rank, li.soff, li.srank, ek, st))) != STARKV_OK)
-        return s;
     ScoreParams sp;
     std::memset(&sp, 0, sizeof(sp));
     sp.pages = pages_of(cache);
     sp.zk = cache->zk;
-    sp.bkt = bkt;
+    sp.bk = bk;
     sp.q = q;
     sp.P = ws + w.P;
     sp.stats = reinterpret_cast<float*>(ws + w.stats);
@@ -848,6 +840,8 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     for (int g = 0; g <= w.sp.G; ++g) sp.gstart[g] = w.sp.gstart[g];
     for (int h = 0; h <= li.H; ++h) sp.koff[h] = li.koff[h];
     for (int h = 0; h < li.H; ++h) sp.rank[h] = li.rank[h];
+    for (int h = 0; h <= li.H; ++h) sp.soff[h] = li.soff[h];
+    for (int h = 0; h < li.H; ++h) sp.srank[h] = li.srank[h];
     fill_rope(layer->rope_base, li.D, sp.rope_rev);
     Q43Layout qk, qv;
     if (li.q43) {

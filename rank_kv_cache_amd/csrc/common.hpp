@@ -223,7 +223,7 @@ __host__ __device__ inline int q43_value_run_offset(const Q43Layout& L, int c) {
 
 struct ScoreParams {
     const void* zk;        // key latent, block layout
-    const void* bkt;       // key factors in MFMA fragment order (head h at koff[h] * D)
+    const void* bk;        // key factors [R_k caller rows][D], head h's rows at soff[h]
     const float* q;        // [B][H][D]
     void* P;               // [B][H][Tp] probabilities, relative to each block's maximum
     float* stats;          // [B][H][nblk][2] per block: max (log2 units), sum of probabilities
@@ -237,6 +237,8 @@ struct ScoreParams {
     int8_t gstart[kMaxGroups + 1];
     int16_t koff[kMaxHeads + 1];
     int16_t rank[kMaxHeads];
+    int16_t soff[kMaxHeads + 1];   // caller rows of head h's factor (true rank srank[h] <= rank[h])
+    int16_t srank[kMaxHeads];
     double rope_rev[64];   // theta_i / (2 pi): RoPE frequency in revolutions per position
     // mixed 4/3-bit key cache only: codes in zk, scales / zero points, binary16 tail rows
     const void* zk_meta;   // [B][cap/64][2][Rk]

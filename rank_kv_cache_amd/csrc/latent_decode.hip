@@ -7,10 +7,10 @@
 //   out_h = (sum_n p_n Z_v[n]) B_v[:, h*d:(h+1)*d]        values summed in latent space
 // No full-width K or V is ever written to memory.
 //
-// Four kernels per call:
-//  1. pack_key_factors: B_k into MFMA A-operand fragment order (one 16-byte run per lane).
-//  2. latent_scores: one workgroup per (split of the sequence, head group, sequence). The group's
-//     factor fragments are staged once in LDS; each wave walks 64-token blocks and, per head,
+// Three kernels per call:
+//  1. latent_scores: one workgroup per (split of the sequence, head group, sequence). The group's
+//     B_k rows are staged once in LDS in MFMA fragment order (zero rows where a rank was rounded
+//     up to 16); each wave walks 64-token blocks and, per head,
 //     rebuilds K~^T (d x 64 tokens) = B_k^T Z_k^T on MFMA 32x32x16 (A = factor fragments from
 //     LDS, B = latent fragments streamed from HBM one unit ahead in registers), applies RoPE and
 //     the dot with q in registers, and writes the block's probabilities p = exp2(s - m_blk)
@@ -18,11 +18,11 @@
 //     token of a 32-token MFMA column tile, j = lane's column) is split as R_{n0+j} = R_{n0} R_j:
 //     the query is rotated back by n0 once per (head, tile) and the constant rotation by j*theta
 //     is kept in registers, so no per-token trigonometry runs in the hot loop.
-//  3. latent_values: one workgroup per (split, channel chunk, sequence): per-head split maximum
+//  2. latent_values: one workgroup per (split, channel chunk, sequence): per-head split maximum
 //     M and sum L from the block statistics, then Acc[H x r_v] += (p * 2^(m_blk - M)) Z_v on MFMA
 //     with all heads stacked into one 32-row operand (notes, section 5.3), Z_v fragments
 //     streamed one block ahead in registers. Writes (M, L, Acc) per split.
-//  4. project_heads: merges the splits per (b, h) (log-sum-exp weights, normalised) while it
+//  3. project_heads: merges the splits per (b, h) (log-sum-exp weights, normalised) while it
 //     loads them, then out[b][h] = a[b][h] . B_v[:, h*d:(h+1)*d] for a batch of sequences.
 //  merge_splits (the same merge as a kernel of its own) finishes the exempt-layer path.
 
@@ -31,47 +31,6 @@
 #include "common.hpp"
 
 namespace starkv {
-
-// ------------------------------------------------------------------------------------------------
-// 1. Key-factor packing: for head h (stored rank r, offset ko), fragment f = mt*(r/16) + ks, lane l
-// holds factor row k = 16*ks + 8*(l/32) + j of the head, column 32*mt + l%32, j = 0..7, at element
-// ko*D + (f*64 + l)*8 + j. The row is B_k[so + k] for k below the head's true rank (caller offset
-// so) and zero in the rounding of the rank up to 16. One thread per 8-element lane run.
-// ------------------------------------------------------------------------------------------------
-struct PackParams {
-    const void* bk;
-    void* bkt;
-    int D, H, Rk;
-    int16_t koff[kMaxHeads + 1];
-    int16_t rank[kMaxHeads];
-    int16_t soff[kMaxHeads + 1];
-    int16_t srank[kMaxHeads];
-};
-
-template <int K>
-__global__ __launch_bounds__(256) void pack_key_factors(const PackParams p) {
-    using T = typename Elem<K>::storage;
-    const int run = blockIdx.x * 256 + threadIdx.x;        // run index over Rk*D/8
-    if (run >= p.Rk * p.D / 8) return;
-    const int e0 = run * 8;
-    int h = 0;
-    while (h + 1 < p.H && e0 >= p.koff[h + 1] * p.D) ++h;
-    const int ko = p.koff[h], nks = p.rank[h] >> 4;
-    const int local = e0 - ko * p.D;                         // element inside the head's block
-    const int l = (local >> 3) & 63;
-    const int f = local >> 9;
-    const int mt = f / nks, ks = f - mt * nks;
-    const int dim = 32 * mt + (l & 31);
-    const int k0 = 16 * ks + 8 * (l >> 5);
-    const T* src = static_cast<const T*>(p.bk);
-    T v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        v[j] = k0 + j < p.srank[h] ? src[(size_t)(p.soff[h] + k0 + j) * p.D + dim] : T(0);
-    T* dst = static_cast<T*>(p.bkt) + e0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = v[j];
-}
 
 // ------------------------------------------------------------------------------------------------
 // 2. Scores.
@@ -165,6 +124,7 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
     // reads LDS (indexing the by-value argument block would make the compiler copy it to scratch)
     __shared__ double s_rev[64];
     __shared__ int s_head[kMaxHeads], s_rank[kMaxHeads], s_kgrp[kMaxHeads];
+    __shared__ int s_srank[kMaxHeads], s_soff[kMaxHeads];
     __shared__ int s_goff[QK ? kMaxHeads : 1][8], s_gn[QK ? kMaxHeads : 1][8];
 
     const int tid = threadIdx.x;
@@ -192,7 +152,7 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
     const int full_blocks = QK ? seq_len >> 6 : my_nblk;         // quantised groups (mixed cache)
     const float q_scale = p.q_scale;
     const T* __restrict__ zk = static_cast<const T*>(p.zk);
-    const T* __restrict__ bkt = static_cast<const T*>(p.bkt);
+    const T* __restrict__ bkg = static_cast<const T*>(p.bk);
     const float* __restrict__ qg = p.q;
     PT* __restrict__ Pout = static_cast<PT*>(p.P);
     float* __restrict__ stats = p.stats;
@@ -210,6 +170,8 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
         s_head[tid] = h;
         s_rank[tid] = p.rank[h];
         s_kgrp[tid] = p.koff[h] >> 4;
+        s_srank[tid] = p.srank[h];
+        s_soff[tid] = p.soff[h];
     }
     if (QK && tid < 8 * ng) {
         const int sl = tid >> 3, k = tid & 7;
@@ -230,10 +192,24 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
     __syncthreads();
     for (int s = 0; s < ng; ++s) {
         const int h = s_head[s];
-        const int n8 = s_rank[s] * D / 8;
-        const Fr* src = reinterpret_cast<const Fr*>(bkt + (size_t)s_kgrp[s] * 16 * D);
-        Fr* dst = reinterpret_cast<Fr*>(&s_bk[s_slot[s]]);
-        for (int i = tid; i < n8; i += 64 * NW) dst[i] = src[i];
+        // B_k rows of the head into MFMA A-operand fragment order: fragment f = mt*(rank/16) + ks,
+        // lane l holds rows 16*ks + 8*(l/32) + jj (jj < 8) at column 32*mt + l%32, elements
+        // (f*64 + l)*8 + jj of the head's slot. Rows past the head's true rank (the rounding of
+        // its rank up to 16) are zero. Thread per (8 rows, column): the eight row reads are
+        // coalesced across the wave's consecutive columns, and the eight values are one
+        // contiguous LDS store (consecutive columns write consecutive 16-byte runs).
+        const int rk = s_rank[s], sr = s_srank[s], so = s_soff[s], nks = rk >> 4;
+        T* dst = &s_bk[s_slot[s]];
+        for (int i = tid; i < (rk >> 3) * D; i += 64 * NW) {
+            const int k8 = i / D, dim = i - k8 * D;
+            struct __attribute__((aligned(16))) Run { T v[8]; } run;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int k = 8 * k8 + jj;
+                run.v[jj] = k < sr ? bkg[(size_t)(so + k) * D + dim] : T(0);
+            }
+            *reinterpret_cast<Run*>(dst + (((dim >> 5) * nks + (k8 >> 1)) * 64 + (k8 & 1) * 32 + (dim & 31)) * 8) = run;
+        }
         for (int i = tid; i < NQ * D; i += 64 * NW) {
             const int qi = i / D, e = i - qi * D;
             s_q[(s * NQ + qi) * D + e] = qg[((size_t)(row0 + qi) * H + h) * D + e] * q_scale;
@@ -1027,28 +1003,5 @@ hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_pack_keys(const void* bk, void* bkt, int D, int H, const int16_t* koff,
-                            const int16_t* rank, const int16_t* soff, const int16_t* srank,
-                            int elem, hipStream_t st) {
-    PackParams p;
-    p.bk = bk;
-    p.bkt = bkt;
-    p.D = D;
-    p.H = H;
-    p.Rk = koff[H];
-    for (int h = 0; h <= H; ++h) p.koff[h] = koff[h];
-    for (int h = 0; h < H; ++h) p.rank[h] = rank[h];
-    for (int h = 0; h <= H; ++h) p.soff[h] = soff[h];
-    for (int h = 0; h < H; ++h) p.srank[h] = srank[h];
-    const int runs = p.Rk * D / 8;
-    const dim3 grid((runs + 255) / 256);
-    switch (elem) {
-    case kF32: hipLaunchKernelGGL(pack_key_factors<kF32>, grid, dim3(256), 0, st, p); break;
-    case kF16: hipLaunchKernelGGL(pack_key_factors<kF16>, grid, dim3(256), 0, st, p); break;
-    case kBF16: hipLaunchKernelGGL(pack_key_factors<kBF16>, grid, dim3(256), 0, st, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
 
 }  // namespace starkv
