@@ -134,6 +134,24 @@ __device__ __forceinline__ float wave_sum(float v) {
     p = swap32(v);
     return p.a + p.b;
 }
+// Reductions over each 32-lane half of the wave (the first five steps of the wave-wide ones):
+// every lane gets the result of its own half.
+__device__ __forceinline__ float half_max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    const LanePair p = swap16(v);
+    return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float half_sum(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    const LanePair p = swap16(v);
+    return p.a + p.b;
+}
 
 // cos and sin of 2*pi*x for x in [0, 1) (hardware v_cos_f32 / v_sin_f32 take revolutions).
 __device__ __forceinline__ void sincos_rev(float x, float* c, float* s) {
@@ -154,6 +172,7 @@ constexpr int kMaxGroupHeadsMQ = 16;
 constexpr int kMaxGroups = 32;
 constexpr int kValueWaves = 4;         // waves per value workgroup
 constexpr int kMaxBlocksPerSplit = 256;
+constexpr int kFoldMaxMeanRank = 48;     // layers below this mean key rank use the folded scores
 
 // Latent cache block layouts (64-token blocks, 16-channel groups of 1024 elements):
 //   key latent   zk[b][blk][g][t][k]      t < 64 token in block, k < 16 channel in group

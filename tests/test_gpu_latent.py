@@ -149,6 +149,29 @@ def test_peaked_attention_and_custom_scale():
     assert e2 <= TOL
 
 
+# Binary16 layers whose mean key rank is below 48 take the query-folded score kernel, the others
+# the rebuilt-key kernel; a folded layer splits heads of rank above 64 into two rank chunks.
+@pytest.mark.parametrize("name,ranks", [
+    ("folded", [16, 32, 48, 64, 32, 16]),
+    ("folded_chunked", [16, 96, 16, 16, 128, 16, 16, 64]),
+    ("rebuilt", [64, 80, 96, 64, 48, 128]),
+])
+def test_score_kernel_paths(name, ranks):
+    H, B, d, rv = len(ranks), 2, 128, 160
+    for T in (1000, 4161):
+        w = synth.Workload("k", batch=B, heads=H, head_dim=d, seq_len=T, dtype="f16",
+                           layer_seed=41, cache_seed=42 + T, value_rank=rv, power=0.5)
+        ld = synth.draw_layer(w, key_ranks=ranks)
+        zk, zv = synth.draw_latent_cache(w, ld)
+        q = synth.draw_queries(43 + T, 0, B, H, d)
+        dl = DeviceLayer(latent_layer(H, d, ranks, rv, "f16"), zk, zv, ld.bk, ld.bv)
+        for S in (0, 3):
+            got = dl.decode(q, num_splits=S)
+            e = rel_err(got, _oracle(ld, zk, zv, q, "f16"))
+            say(f"[paths] {name} mean rank {np.mean(ranks):.1f} T={T} splits={S} rel err {e:.3e}")
+            assert np.all(np.isfinite(got)) and e <= TOL
+
+
 def test_append_chunks_and_readback():
     """Cache built by many appends (prefill, then one token at a time) is byte-identical to the
     input rows, and attends identically."""

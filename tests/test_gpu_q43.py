@@ -274,6 +274,30 @@ def test_q43_decode_short_lengths(T):
         assert np.all(np.isfinite(got)) and e <= 2e-3
 
 
+@pytest.mark.parametrize("ranks", [[64, 80, 96, 64, 48, 128], [16, 96, 16, 16, 112, 16]])
+def test_q43_decode_both_score_kernels(ranks):
+    """Mean key rank 80 takes the rebuilt-key score kernel, mean 45 the query-folded one (with two
+    heads split into rank chunks); both against the oracle on the same dequantised values."""
+    from rank_kv_cache_amd import buffers
+    from gpu_support import rel_err
+    H, d, B, T, rv = len(ranks), 128, 2, 700, 208
+    cap = 768
+    w = synth.Workload("qk", batch=B, heads=H, head_dim=d, seq_len=T, dtype="f16", layer_seed=91,
+                       cache_seed=92, value_rank=rv, power=0.5)
+    ld = synth.draw_layer(w, key_ranks=ranks)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = synth.draw_queries(93, 0, B, H, d)
+    L = q43_layer(H, d, ranks, rv)
+    cache = buffers.alloc_cache(L, B, cap, fill=0xFF)
+    _append(L, cache, zk, zv, [T])
+    ref = _q43_reference(ld, zk, zv, q, ranks, rv, T, cap)
+    for S in (0, 2):
+        got = _gpu_decode(L, cache, T, q, ld.bk, ld.bv, S)
+        e = rel_err(got, ref)
+        say(f"[q43 kernels] mean rank {np.mean(ranks):.1f} splits={S} rel err {e:.3e}")
+        assert np.all(np.isfinite(got)) and e <= 2e-3
+
+
 @pytest.mark.parametrize("frac,d", [(0.2, 128), (1.0, 128), (0.0, 128), (0.25, 64)])
 def test_q43_fractions_and_head_dim(frac, d):
     """Quantisation variants the pages measure: the paper's 20 % at 4 bits (3.2 bits per value),
