@@ -13,13 +13,17 @@
 //     up to 16); each wave walks 64-token blocks and, per head,
 //     rebuilds K~^T (d x 64 tokens) = B_k^T Z_k^T on MFMA 32x32x16 (A = factor fragments from
 //     LDS, B = latent fragments streamed from HBM one unit ahead in registers), applies RoPE and
-//     the dot with q in registers, and writes the block's probabilities p = exp2(s - m_blk)
-//     (relative to the block maximum) plus (m_blk, sum p). RoPE at position n0 + j (n0 = first
-//     token of a 32-token MFMA column tile, j = lane's column) is split as R_{n0+j} = R_{n0} R_j:
-//     the query is rotated back by n0 once per (head, tile) and the constant rotation by j*theta
-//     is kept in registers, so no per-token trigonometry runs in the hot loop.
+//     the dot with q in registers, and writes the probabilities p = exp2(s - m_t) of each
+//     32-token tile (relative to the tile maximum) plus (m_t, sum p). RoPE at position n0 + j
+//     (n0 = first token of a 32-token MFMA column tile, j = lane's column) is split as
+//     R_{n0+j} = R_{n0} R_j: the query is rotated back by n0 once per (head, tile) and the
+//     constant rotation by j*theta is kept in registers, so no per-token trigonometry runs in
+//     the hot loop.
+//     latent_scores_folded (section 2b) computes the same scores for binary16 and mixed 4/3-bit
+//     layers of low mean key rank with the query folded into the factor: MFMA yields
+//     [u | v] = Z_k W and the rotation reduces to two FMAs per rotary pair.
 //  2. latent_values: one workgroup per (split, channel chunk, sequence): per-head split maximum
-//     M and sum L from the block statistics, then Acc[H x r_v] += (p * 2^(m_blk - M)) Z_v on MFMA
+//     M and sum L from the tile statistics, then Acc[H x r_v] += (p * 2^(m_t - M)) Z_v on MFMA
 //     with all heads stacked into one 32-row operand (notes, section 5.3), Z_v fragments
 //     streamed one block ahead in registers. Writes (M, L, Acc) per split.
 //  3. project_heads: merges the splits per (b, h) (log-sum-exp weights, normalised) while it
