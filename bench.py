@@ -50,7 +50,13 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 # current kernels, scaled by the factors a plain copy of known size gives (FETCH x 2.0, WRITE x
 # 1.0); the counter summaries are under profiles/. Kernels without an entry report null.
 MEASURED_TRAFFIC = {
-    ("model32_b32_t8192_f16", "dense_attention"): 4_310_875_245,
+    ("longchat_b16_t32768_f16", "latent_scores"): 1_438_578_638,
+    ("longchat_b16_t32768_f16", "latent_values"): 1_173_501_804,
+    ("longchat_b16_t16384_q43", "latent_scores"): 257_207_498,
+    ("longchat_b16_t16384_q43", "latent_values"): 180_596_418,
+    ("model32_b32_t8192_f16", "dense_attention"): 4_310_900_125,
+    ("model32_b32_t8192_f16", "latent_scores"): 967_505_820,       # mean over the latent layers
+    ("model32_b32_t8192_f16", "latent_values"): 639_198_239,       # mean over the latent layers
 }
 # Binary16 and mixed 4/3-bit layers whose mean key rank is below this take the library's
 # query-folded score kernel (the library applies the same rule); the others rebuild each key.
