@@ -50,17 +50,14 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 # current kernels, scaled by the factors a plain copy of known size gives (FETCH x 2.0, WRITE x
 # 1.0); the counter summaries are under profiles/. Kernels without an entry report null.
 MEASURED_TRAFFIC = {
-    ("longchat_b16_t32768_f16", "latent_scores"): 1_438_578_638,
-    ("longchat_b16_t32768_f16", "latent_values"): 1_173_501_804,
-    ("longchat_b16_t16384_q43", "latent_scores"): 257_207_498,
-    ("longchat_b16_t16384_q43", "latent_values"): 180_596_418,
+    ("longchat_b16_t32768_f16", "latent_scores"): 1_435_767_564,
+    ("longchat_b16_t32768_f16", "latent_values"): 1_173_500_204,
+    ("longchat_b16_t16384_q43", "latent_scores"): 217_578_566,
+    ("longchat_b16_t16384_q43", "latent_values"): 180_752_571,
     ("model32_b32_t8192_f16", "dense_attention"): 4_310_900_125,
     ("model32_b32_t8192_f16", "latent_scores"): 967_505_820,       # mean over the latent layers
     ("model32_b32_t8192_f16", "latent_values"): 639_198_239,       # mean over the latent layers
 }
-# Binary16 and mixed 4/3-bit layers whose mean key rank is below this take the library's
-# query-folded score kernel (the library applies the same rule); the others rebuild each key.
-FOLD_MAX_MEAN_RANK = 48
 
 
 def log(*a):
@@ -581,23 +578,14 @@ def main(argv=None):
     dk = kernels[dom]
     alu = None
     if dom == "latent_scores":
-        # fp32 vector work per (cached token, sequence, head). Rebuilt keys: rotate-half RoPE of
-        # the key (d/2 rotations, 6 flop each) + the dot (2d) + softmax (~5). Query folded into
-        # the factor: two FMAs per rotary pair on the MFMA output (2d) + softmax (~5); the
-        # per-tile cos / sin, shared by a head group, is left out.
+        # the score kernel's own bound is VALU issue: per (cached token, sequence, head) rotate-half
+        # RoPE of the rebuilt key (d/2 rotations, 6 flop each) + the dot (2d) + softmax (~5)
         lat = [r for r in runs if not r.dense]
         H, d = lat[0].layer.num_heads, lat[0].layer.head_dim
-
-        def folded(r):
-            return (r.layer.cache_dtype in (sk.F16, sk.Q43)
-                    and sum(r.layer.key_ranks) < FOLD_MAX_MEAN_RANK * len(r.layer.key_ranks))
-
-        flop = sum(B * r.T * H * ((2 if folded(r) else 5) * d + 5) for r in lat) / len(lat)
+        flop = sum(B * r.T * H * (5 * d + 5) for r in lat) / len(lat)
         tf = flop / (dk["avg_us_per_launch"] * 1e-6) / 1e12
         alu = {"achieved": tf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / VALU_PEAK_TFLOPS,
                "flop_per_launch": flop,
-               "score_kernel": "query-folded" if all(folded(r) for r in lat) else
-                               "rebuilt-key" if not any(folded(r) for r in lat) else "mixed",
                "peak_note": "fp32 vector without packed fp32 (157.3 with it)"}
     rec = {
         "metric": METRIC,

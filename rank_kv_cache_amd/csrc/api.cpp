@@ -15,7 +15,7 @@
 
 namespace starkv {
 hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
-                                int nq, bool fold, hipStream_t st);
+                                int nq, hipStream_t st);
 hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int ntw, int nq,
                                 hipStream_t st);
 int value_tiles_per_wave(int rv);
@@ -284,18 +284,6 @@ int plan_splits(int B, int64_t seq_len, int requested) {
     S = std::max(1, std::min({S, ntiles, kMaxSplits}));
     const int tps = (ntiles + S - 1) / S;
     return (ntiles + tps - 1) / tps;
-}
-
-// The query-folded score kernel (binary16 and mixed 4/3-bit caches, one query row per sequence)
-// spends two FMAs per rotary pair where the rebuilt-key kernel spends six, but its partial dot is
-// formed per rank chunk and its work items are half as large; the rebuilt-key kernel's cost grows
-// more slowly with rank. Measured on MI355X (32 heads, d = 128): the folded kernel is 13 % faster
-// at mean key rank 40 (ranks 16..64) and 0-13 % slower at mean ranks 48.5-62 (ranks 16..96).
-bool use_folded_scores(const LayerInfo& li, int stream_kind, int nq) {
-    if (nq != 1 || (stream_kind != kF16 && stream_kind != -1)) return false;
-    int sum = 0;
-    for (int h = 0; h < li.H; ++h) sum += li.rank[h];
-    return sum < kFoldMaxMeanRank * li.H;
 }
 
 struct WorkspaceLayout {
@@ -864,9 +852,8 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
         sp.ql = qk;
     }
     const int stream_kind = li.q43 ? -1 : ek;     // -1: mixed 4/3-bit codes, dequantised in-kernel
-    const bool fold = use_folded_scores(li, stream_kind, nq);
     if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
-    if ((s = dev(launch_latent_scores(sp, stream_kind, w.sp.G, w.sp.splits, w.sp.maxks, nq, fold, st))) != STARKV_OK)
+    if ((s = dev(launch_latent_scores(sp, stream_kind, w.sp.G, w.sp.splits, w.sp.maxks, nq, st))) != STARKV_OK)
         return s;
     if (evm && (s = dev(hipEventRecord(static_cast<hipEvent_t>(evm), st))) != STARKV_OK) return s;
     ValueParams vp;

@@ -172,7 +172,6 @@ constexpr int kMaxGroupHeadsMQ = 16;
 constexpr int kMaxGroups = 32;
 constexpr int kValueWaves = 4;         // waves per value workgroup
 constexpr int kMaxBlocksPerSplit = 256;
-constexpr int kFoldMaxMeanRank = 48;     // layers below this mean key rank use the folded scores
 
 // Latent cache block layouts (64-token blocks, 16-channel groups of 1024 elements):
 //   key latent   zk[b][blk][g][t][k]      t < 64 token in block, k < 16 channel in group

@@ -19,9 +19,6 @@
 //     R_{n0+j} = R_{n0} R_j: the query is rotated back by n0 once per (head, tile) and the
 //     constant rotation by j*theta is kept in registers, so no per-token trigonometry runs in
 //     the hot loop.
-//     latent_scores_folded (section 2b) computes the same scores for binary16 and mixed 4/3-bit
-//     layers of low mean key rank with the query folded into the factor: MFMA yields
-//     [u | v] = Z_k W and the rotation reduces to two FMAs per rotary pair.
 //  2. latent_values: one workgroup per (split, channel chunk, sequence): per-head split maximum
 //     M and sum L from the tile statistics, then Acc[H x r_v] += (p * 2^(m_t - M)) Z_v on MFMA
 //     with all heads stacked into one 32-row operand (notes, section 5.3), Z_v fragments
@@ -451,383 +448,6 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
                     return load_frag<K>(rowp, (size_t)(32 * nt) * Rk + 16 * ks);
                 });
             }
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------------------------
-// 2b. Scores with the query folded into the key factor (binary16 latents and mixed 4/3-bit codes
-// dequantised to binary16; one query row per cache sequence).
-//
-// With RoPE pairing dimension i with i + d/2 (LLaMA convention) and c, s the cosine and sine of
-// the angle of token n at frequency i, the score of the rebuilt key k = Z_k[n] B_k is
-//   q . RoPE_n(k) = sum_i c (q_i k_i + q_{i+d/2} k_{i+d/2}) + s (q_{i+d/2} k_i - q_i k_{i+d/2})
-//                 = sum_i c u_i + s v_i,   [u | v] = Z_k[n] W,
-//   W[:, i] = q_i B_k[:, i] + q_{i+d/2} B_k[:, i+d/2],  W[:, i+d/2] = q_{i+d/2} B_k[:, i] - q_i B_k[:, i+d/2].
-// W depends on the query only, so it is formed once per workgroup (rounded to binary16 after a
-// per-head power-of-two scaling of the query, undone on the score) and takes the place of B_k
-// as the MFMA operand; the cosines and sines of a 32-token tile depend on the position only, so
-// they are formed once per tile (in fp32) and serve every head of the group. Per rank-16 step
-// and 32 tokens the rotation costs two FMAs per frequency instead of six.
-//
-// Work items ("sub-units") are (64-token block, 32-token tile, chunk): a chunk is a head, or half
-// of a head whose rank exceeds 64 (partial scores carried from the first half to the second), so
-// every sub-unit reads at most four 16-channel groups and the latents stream through a two-deep
-// register ring. Statistics (m, l) are written per 32-token tile.
-// ------------------------------------------------------------------------------------------------
-constexpr int kFoldWaves = 12;
-constexpr int kFoldSteps = 4;                 // rank-16 steps of a chunk, at most
-constexpr int kMaxChunks = 2 * kMaxHeads;
-
-template <int D, bool QK>
-__global__ __launch_bounds__((64 * kFoldWaves), 1) void latent_scores_folded(const ScoreParams p) {
-    constexpr int NW = kFoldWaves;
-    constexpr int NF = D / 2;           // RoPE frequencies
-    constexpr int HMT = D / 64;         // m-tile pairs (mt, mt + HMT)
-    constexpr int TS = NF + 4;          // padded row of the in-tile rotation table
-    constexpr int MS = kFoldSteps;
-    using Fr = f16x8;
-    using T = _Float16;
-
-    __shared__ __attribute__((aligned(32))) T s_w[kFragLdsBytes / sizeof(T)];
-    __shared__ __attribute__((aligned(16))) float s_q[kMaxHeads * D];
-    __shared__ __attribute__((aligned(16))) float s_cj[32 * TS], s_sj[32 * TS];
-    __shared__ __attribute__((aligned(16))) float s_cs0[NW][2][D];
-    __shared__ int s_slot[kMaxHeads + 1];
-    __shared__ float s_scl[kMaxHeads], s_inv[kMaxHeads];
-    __shared__ double s_rev[64];
-    __shared__ int s_head[kMaxHeads], s_rank[kMaxHeads], s_kgrp[kMaxHeads];
-    __shared__ int s_srank[kMaxHeads], s_soff[kMaxHeads];
-    __shared__ int s_goff[QK ? kMaxHeads : 1][8], s_gn[QK ? kMaxHeads : 1][8];
-    __shared__ int s_cmeta[kMaxChunks], s_cw[kMaxChunks], s_ck[kMaxChunks];
-    __shared__ int s_nc;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int half = lane >> 5;
-    const int j = lane & 31;
-    const int split = blockIdx.x;
-    const int grp = blockIdx.y;
-    const int b = blockIdx.z;
-    const int hs0 = p.gstart[grp];
-    const int ng = p.gstart[grp + 1] - hs0;
-    const int H = p.H;
-    const int qlen = seq_length(p.seq_lens, b, p.seq_len);
-    const int Tp = p.Tp;
-    const int nblk = p.nblk;
-    const int my_nblk = (qlen + 63) >> 6;
-    const int full_blocks = QK ? qlen >> 6 : my_nblk;
-    const T* __restrict__ zk = static_cast<const T*>(p.zk);
-    const T* __restrict__ bkg = static_cast<const T*>(p.bk);
-    _Float16* __restrict__ Pout = static_cast<_Float16*>(p.P);
-    float* __restrict__ stats = p.stats;
-    const int Rk = p.Rk;
-    const size_t kgroups = (size_t)(Rk >> 4);
-    const int bc = cache_seq(p.seq_map, b, p.cache_batch);
-    const uint32_t* __restrict__ qcodes = static_cast<const uint32_t*>(p.zk);
-    const uint16_t* __restrict__ qmeta = static_cast<const uint16_t*>(p.zk_meta);
-    const T* __restrict__ qtail = static_cast<const T*>(p.zk_tail);
-    const size_t qblock_words = (size_t)(p.ql.block_bytes >> 2);
-
-    // ---- per-layer tables ----
-    if (tid < 64) s_rev[tid] = tid < NF ? p.rope_rev[tid] : 0.0;
-    if (tid < ng) {
-        const int h = p.order[hs0 + tid];
-        s_head[tid] = h;
-        s_rank[tid] = p.rank[h];
-        s_kgrp[tid] = p.koff[h] >> 4;
-        s_srank[tid] = p.srank[h];
-        s_soff[tid] = p.soff[h];
-    }
-    if (QK && tid < 8 * ng) {
-        const int sl = tid >> 3, k = tid & 7;
-        const int h = p.order[hs0 + sl];
-        const int g16 = min((p.koff[h] >> 4) + k, (int)kgroups - 1);
-        s_goff[sl][k] = p.ql.goff[g16];
-        s_gn[sl][k] = p.ql.gn[g16];
-    }
-    if (tid == 0) {
-        // factor slots, and the chunks: (steps n, first step k0, head steps nkt, head slot s,
-        // first / last chunk of the head), the chunk's first W element and first latent group
-        int off = 0, c = 0;
-        for (int s = 0; s < ng; ++s) {
-            const int h = p.order[hs0 + s];
-            const int nkt = p.rank[h] >> 4;
-            s_slot[s] = off;
-            const int parts = nkt > MS ? 2 : 1;
-            int k0 = 0;
-            for (int q = 0; q < parts; ++q) {
-                const int n = parts == 1 ? nkt : (q == 0 ? (nkt + 1) / 2 : nkt / 2);
-                s_cmeta[c] = n | (k0 << 4) | (nkt << 8) | ((q == 0) << 12) | ((q == parts - 1) << 13) | (s << 16);
-                s_cw[c] = off + k0 * 512;
-                s_ck[c] = ((p.koff[h] >> 4) + k0) * 1024;
-                k0 += n;
-                ++c;
-            }
-            off += p.rank[h] * D;
-        }
-        s_slot[ng] = off;
-        s_nc = c;
-    }
-    __syncthreads();
-    // scaled queries of the group, and cos / sin of j * theta_i for the 32 in-tile offsets j
-    for (int i = tid; i < ng * D; i += 64 * NW) {
-        const int s = i / D, e = i - s * D;
-        s_q[i] = p.q[((size_t)b * H + s_head[s]) * D + e] * p.q_scale;
-    }
-    for (int i = tid; i < 32 * NF; i += 64 * NW) {
-        const int jj = i / NF, f = i - jj * NF;
-        const double rev = (double)jj * s_rev[f];
-        float c, sn;
-        sincos_rev((float)(rev - floor(rev)), &c, &sn);
-        s_cj[jj * TS + f] = c;
-        s_sj[jj * TS + f] = sn;
-    }
-    // per head a power of two that brings the query's largest magnitude into [0.5, 1), so that W
-    // sits well inside the binary16 range (read from the query itself, beside its staging)
-    for (int s = wave; s < ng; s += NW) {
-        float mx = 0.0f;
-        for (int e = lane; e < D; e += 64) mx = fmaxf(mx, fabsf(p.q[((size_t)b * H + s_head[s]) * D + e] * p.q_scale));
-        mx = wave_max(mx);
-        int ex = 0;
-        if (mx > 0.0f && mx <= 3.0e38f) (void)frexpf(mx, &ex);
-        if (lane == 0) {
-            s_scl[s] = ldexpf(1.0f, -ex);
-            s_inv[s] = ldexpf(1.0f, ex);
-        }
-    }
-    __syncthreads();
-    // W of each head into MFMA A-operand fragment order (the layout B_k rows take in the unfolded
-    // kernel): fragment f = mt*(rank/16) + ks, lane l holds rows 16*ks + 8*(l/32) + jj (jj < 8) at
-    // column 32*mt + l%32, elements (f*64 + l)*8 + jj of the head's slot; rows past the head's
-    // true rank are zero. Thread per (head, 8 rows, frequency) over the whole group in one loop,
-    // so that all factor reads are in flight together: both columns i and i + d/2 of the eight
-    // rows, one 16-byte LDS store each. Head s owns items [slot_s / 16, slot_{s+1} / 16).
-    {
-        int s = 0;
-        for (int i = tid; i < s_slot[ng] >> 4; i += 64 * NW) {
-            while (i >= s_slot[s + 1] >> 4) ++s;
-            const int rk = s_rank[s], sr = s_srank[s], so = s_soff[s], nks = rk >> 4;
-            const int il = i - (s_slot[s] >> 4);
-            const int k8 = il / NF, dim = il - k8 * NF;
-            const float scl = s_scl[s];
-            const float q1 = s_q[s * D + dim] * scl, q2 = s_q[s * D + dim + NF] * scl;
-            struct __attribute__((aligned(16))) Run { T v[8]; } ru, rv;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int k = 8 * k8 + jj;
-                const float b1 = k < sr ? (float)bkg[(size_t)(so + k) * D + dim] : 0.0f;
-                const float b2 = k < sr ? (float)bkg[(size_t)(so + k) * D + dim + NF] : 0.0f;
-                ru.v[jj] = (T)fmaf(q2, b2, q1 * b1);
-                rv.v[jj] = (T)fmaf(-q1, b2, q2 * b1);
-            }
-            T* dst = &s_w[s_slot[s]];
-            const int d2 = dim + NF;
-            *reinterpret_cast<Run*>(dst + (((dim >> 5) * nks + (k8 >> 1)) * 64 + (k8 & 1) * 32 + (dim & 31)) * 8) = ru;
-            *reinterpret_cast<Run*>(dst + (((d2 >> 5) * nks + (k8 >> 1)) * 64 + (k8 & 1) * 32 + (d2 & 31)) * 8) = rv;
-        }
-    }
-    __syncthreads();
-
-    const int nc = s_nc;
-    const int blk_begin = split * p.blocks_per_wg;
-    const int blk_end = min(my_nblk, blk_begin + p.blocks_per_wg);
-    const int main_end = QK ? min(blk_end, full_blocks) : blk_end;
-    const int my_blocks = blk_begin + wave < main_end ? (main_end - blk_begin - wave + NW - 1) / NW : 0;
-    const int nsub = my_blocks * 2 * nc;          // sub-units (block, tile, chunk), chunk fastest
-
-    // Per-chunk values in lane c of one register each (c < nc <= 64), read with a wave-uniform
-    // lane index: nothing on the way from a sub-unit to its load addresses touches memory.
-    const int cl = lane < nc ? lane : 0;
-    const int v_meta = s_cmeta[cl];
-    const int v_w = s_cw[cl];
-    const int v_k = s_ck[cl];
-    const int v_hd = s_head[(v_meta >> 16) & 31];
-    const int v_inv = __float_as_int(s_inv[(v_meta >> 16) & 31]);
-    auto rd = [](int v, int c) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(v, c); };
-    const int lane_off = j * 16 + 8 * half;       // the lane's fragment inside a 16-channel group
-    auto block_base = [&](int ib) __attribute__((always_inline)) {
-        return block_id(p.pages, p.nblk_cap, bc, blk_begin + wave + NW * ib) * kgroups * 1024;
-    };
-
-    // cos / sin of the tile's tokens at the lane's frequencies i = 32*pp + 8*g + 4*half + r
-    float tc[HMT][4][4], ts[HMT][4][4];
-    float carry = 0.0f;                           // partial score of a head's first chunk
-
-    // One sub-unit: chunk c over the 32-token tile nt of block blk; frag(kk) supplies the latent
-    // operand of the chunk's step kk (token 32*nt + lane%32, rank rows 16*kk + 8*half .. +7).
-    auto sub = [&](int blk, int nt, int c, auto&& frag) __attribute__((always_inline)) {
-        if (c == 0) {
-            if (nt == 0) {
-                // cos / sin of n0 * theta_i for both tiles of the block (n0 = first token)
-                wave_sync_lds();
-                if (lane < NF) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const double rev = (double)(blk * 64 + 32 * t) * s_rev[lane];
-                        float cc, sn;
-                        sincos_rev((float)(rev - floor(rev)), &cc, &sn);
-                        s_cs0[wave][t][lane] = cc;
-                        s_cs0[wave][t][NF + lane] = sn;
-                    }
-                }
-                wave_sync_lds();
-            }
-            // angle n0 + j: rotate (cos, sin)(j theta) by n0 theta
-#pragma unroll
-            for (int pp = 0; pp < HMT; ++pp)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int i0 = 32 * pp + 8 * g + 4 * half;
-                    const f32x4 c0 = *reinterpret_cast<const f32x4*>(&s_cs0[wave][nt][i0]);
-                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(&s_cs0[wave][nt][NF + i0]);
-                    const f32x4 cj = *reinterpret_cast<const f32x4*>(&s_cj[j * TS + i0]);
-                    const f32x4 sj = *reinterpret_cast<const f32x4*>(&s_sj[j * TS + i0]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        tc[pp][g][r] = fmaf(-s0[r], sj[r], c0[r] * cj[r]);
-                        ts[pp][g][r] = fmaf(c0[r], sj[r], s0[r] * cj[r]);
-                    }
-                }
-        }
-        const int meta = rd(v_meta, c);
-        const int n = meta & 15, nkt = (meta >> 8) & 15;
-        const bool first = (meta >> 12) & 1, last = (meta >> 13) & 1;
-        const T* fr = &s_w[rd(v_w, c)];
-        float sc = first ? 0.0f : carry;
-        auto core = [&](auto n_c) __attribute__((always_inline)) {
-            constexpr int NKS = decltype(n_c)::value;
-            Fr z[NKS];
-#pragma unroll
-            for (int kk = 0; kk < NKS; ++kk) z[kk] = frag(kk);
-#pragma unroll
-            for (int pp = 0; pp < HMT; ++pp) {
-                f32x16 acc0, acc1;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) { acc0[r] = 0.0f; acc1[r] = 0.0f; }
-#pragma unroll
-                for (int kk = 0; kk < NKS; ++kk) {
-                    const Fr a0 = *reinterpret_cast<const Fr*>(fr + ((pp * nkt + kk) * 64 + lane) * 8);
-                    const Fr a1 = *reinterpret_cast<const Fr*>(fr + (((pp + HMT) * nkt + kk) * 64 + lane) * 8);
-                    acc0 = mma32<kF16>(a0, z[kk], acc0);
-                    acc1 = mma32<kF16>(a1, z[kk], acc1);
-                }
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        sc = fmaf(tc[pp][g][r], acc0[4 * g + r], sc);
-                        sc = fmaf(ts[pp][g][r], acc1[4 * g + r], sc);
-                    }
-                // consume the partial sum here, so the compiler cannot sink every m-tile's
-                // rotation arithmetic past all the MFMA chains
-                asm volatile("" : "+v"(sc));
-            }
-        };
-        switch (n) {
-        case 1: core(std::integral_constant<int, 1>{}); break;
-        case 2: core(std::integral_constant<int, 2>{}); break;
-        case 3: core(std::integral_constant<int, 3>{}); break;
-        default: core(std::integral_constant<int, 4>{}); break;
-        }
-        if (!last) {
-            carry = sc;
-            return;
-        }
-        // both halves now hold the score of token 32*nt + j
-        const int tok = blk * 64 + 32 * nt + j;
-        float my = add_xor32(sc) * __int_as_float(rd(v_inv, c));
-        if (tok >= qlen) my = -INFINITY;
-        const float m = half_max(my);
-        const float pr = m != -INFINITY ? __builtin_amdgcn_exp2f(my - m) : 0.0f;
-        const float l = half_sum(pr);
-        const size_t row = (size_t)b * H + rd(v_hd, c);
-        // both halves store the same value to the same address, and every lane stores its
-        // tile's (m, l) word: no branch, so the count of memory operations stays static
-        Pout[row * Tp + tok] = (_Float16)pr;
-        stats[(row * 2 * nblk + 2 * blk + nt) * 2 + (lane & 1)] = (lane & 1) ? l : m;
-    };
-
-    // A cursor over the sub-units (block ib of the wave, tile nt, chunk c), advanced in place.
-    struct Cursor { int ib, nt, c; };
-    auto advance = [&](Cursor& cu) __attribute__((always_inline)) {
-        if (++cu.c == nc) {
-            cu.c = 0;
-            if (++cu.nt == 2) {
-                cu.nt = 0;
-                ++cu.ib;
-            }
-        }
-    };
-
-    if constexpr (!QK) {
-        // Software pipeline over sub-units through a two-deep register ring. Every slot is loaded
-        // (steps past the chunk's own repeat its last step, a cache hit, and the load after the
-        // last sub-unit reloads it), so the number of loads in flight is static and the wait
-        // counts stay exact.
-        struct Buf { Fr z[MS]; };
-        Cursor lc{0, 0, 0}, cc{0, 0, 0};
-        int lu = 0;                                   // sub-unit of the next load
-        size_t lbase = nsub > 0 ? block_base(0) : 0;  // first element of the load cursor's block
-        auto issue = [&](Buf& z) __attribute__((always_inline)) {
-            const int n = rd(v_meta, lc.c) & 15;
-            const size_t base = lbase + rd(v_k, lc.c) + lane_off + lc.nt * 512;
-#pragma unroll
-            for (int kk = 0; kk < MS; ++kk) z.z[kk] = load_frag<kF16>(zk, base + (size_t)min(kk, n - 1) * 1024);
-            if (lu + 1 < nsub) {
-                ++lu;
-                const int ib = lc.ib;
-                advance(lc);
-                if (lc.ib != ib) lbase = block_base(lc.ib);
-            }
-        };
-        Buf zA, zB;
-        if (nsub > 0) issue(zA);
-        for (int u = 0; u < nsub; u += 2) {
-            issue(zB);
-            sub(blk_begin + wave + NW * cc.ib, cc.nt, cc.c, [&](int kk) __attribute__((always_inline)) { return zA.z[kk]; });
-            advance(cc);
-            issue(zA);
-            if (u + 1 < nsub) {
-                sub(blk_begin + wave + NW * cc.ib, cc.nt, cc.c, [&](int kk) __attribute__((always_inline)) { return zB.z[kk]; });
-                advance(cc);
-            }
-        }
-    } else {
-        // mixed 4/3-bit codes: code window, scales and zero points per fragment, loaded inside the
-        // sub-unit and dequantised in registers
-        Cursor cc{0, 0, 0};
-        for (int u = 0; u < nsub; ++u) {
-            const int blk = blk_begin + wave + NW * cc.ib;
-            const int c = cc.c, nt = cc.nt;
-            const int meta = rd(v_meta, c);
-            const int s = (meta >> 16) & 31, k0 = (meta >> 4) & 15;
-            const int kg = rd(v_k, c) >> 10;              // first 16-channel group of the chunk
-            const size_t bid = block_id(p.pages, p.nblk_cap, bc, blk);
-            const uint32_t* blkw = qcodes + bid * qblock_words;
-            const uint16_t* meta16 = qmeta + bid * 2 * (size_t)Rk;
-            sub(blk, nt, c, [&](int kk) __attribute__((always_inline)) {
-                const int nb = s_gn[s][k0 + kk];
-                const int c0 = 16 * (kg + kk) + 8 * half;
-                const u32x4 sc4 = *reinterpret_cast<const u32x4*>(meta16 + c0);
-                const u32x4 zc4 = *reinterpret_cast<const u32x4*>(meta16 + Rk + c0);
-                const int rb = 8 * s_goff[s][k0 + kk] + (32 * nt + j) * (48 + nb);
-                const uint32_t* wp = blkw + (rb >> 5);
-                return q43_key_frag(wp[0], wp[1], wp[2], rb & 31, nb, half, sc4, zc4);
-            });
-            advance(cc);
-        }
-        // the partial last block: its rows are still binary16 in the tail buffer [B][64][Rk]
-        const int tb = full_blocks;
-        if (tb < blk_end && tb >= blk_begin && (tb - blk_begin) % NW == wave) {
-            for (int nt = 0; nt < 2; ++nt)
-                for (int c = 0; c < nc; ++c) {
-                    const T* rowp = qtail + ((size_t)bc * 64 + 32 * nt + j) * Rk + (rd(v_k, c) >> 6) + 8 * half;
-                    sub(tb, nt, c, [&](int kk) __attribute__((always_inline)) {
-                        return load_frag<kF16>(rowp, (size_t)(16 * kk));
-                    });
-                }
         }
     }
 }
@@ -1320,33 +940,15 @@ static hipError_t launch_scores_q(const ScoreParams& p, int elem, int groups, in
     }
 }
 
-template <int D, bool QK>
-static hipError_t launch_fold_t(const ScoreParams& p, int groups, int splits, hipStream_t st) {
-    hipLaunchKernelGGL((latent_scores_folded<D, QK>), dim3(splits, groups, p.B), dim3(64 * kFoldWaves), 0, st, p);
-    return hipGetLastError();
-}
-
-// heads of up to 2 * kFoldSteps rank steps (rank <= d for d = 64 and 128)
-template <bool QK>
-static hipError_t launch_scores_fold(const ScoreParams& p, int groups, int splits, int maxks, hipStream_t st) {
-    if (maxks > 2 * kFoldSteps || maxks > p.D / 16) return hipErrorInvalidValue;
-    if (p.D == 128) return launch_fold_t<128, QK>(p, groups, splits, st);
-    if (p.D == 64) return launch_fold_t<64, QK>(p, groups, splits, st);
-    return hipErrorInvalidValue;
-}
-
 // elem: kF32 / kF16 / kBF16, or -1 for a mixed 4/3-bit key cache (binary16 factors). nq: query
 // rows per cache sequence (p.B rows in all); 2 and 4 share each key between the rows (16-bit and
-// mixed caches). fold: the query-folded kernel (binary16 and mixed caches, one query row each).
+// mixed caches).
 hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,
-                                int nq, bool fold, hipStream_t st) {
+                                int nq, hipStream_t st) {
     if (nq == 2) return launch_scores_q<2>(p, elem, groups, splits, maxks, st);
     if (nq == 4) return launch_scores_q<4>(p, elem, groups, splits, maxks, st);
     if (nq != 1) return hipErrorInvalidValue;
     if (elem == kF32) return launch_scores_k<kF32, false, 1>(p, groups, splits, maxks, st);
-    if (fold && elem == kF16) return launch_scores_fold<false>(p, groups, splits, maxks, st);
-    if (fold && elem == -1) return launch_scores_fold<true>(p, groups, splits, maxks, st);
-    if (fold) return hipErrorInvalidValue;
     return launch_scores_q<1>(p, elem, groups, splits, maxks, st);
 }
 
