@@ -472,6 +472,30 @@ template <> struct ProbFrag<kF16> {
     __device__ static f32x16 mma(const Op& a, const f16x8& z, f32x16 acc) { return mma32<kF16>(a.v, z, acc); }
 };
 
+// One query row per sequence (binary16 and mixed caches): the rescaled probability
+// p * 2^(m_t - M) as a binary16 hi + lo pair, so that the rescaling adds no second rounding to the
+// stored binary16 probability (the multi-query forms keep one operand: their registers are full).
+struct ProbFragF16Pair {
+    using Raw = f16x8;
+    __device__ static Raw load(const void* P, size_t i) { return ProbFrag<kF16>::load(P, i); }
+    __device__ static Raw zero() { return ProbFrag<kF16>::zero(); }
+    struct Op { f16x8 hi, lo; };
+    __device__ static Op scale(const Raw& r, float f) {
+        Op o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = (float)r[e] * f;
+            o.hi[e] = (_Float16)v;
+            o.lo[e] = (_Float16)(v - (float)o.hi[e]);
+        }
+        return o;
+    }
+    __device__ static f32x16 mma(const Op& a, const f16x8& z, f32x16 acc) {
+        acc = mma32<kF16>(a.hi, z, acc);
+        return mma32<kF16>(a.lo, z, acc);
+    }
+};
+
 template <> struct ProbFrag<kBF16> {
     // probabilities are stored as fp16; the bf16 operand is split into hi + lo so that the pair
     // keeps the ~16 significant bits of the scaled probability.
@@ -561,7 +585,7 @@ template <int K, int NTW, bool QV, int NQ>
 __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     using Fr = typename Elem<K>::frag;
     using Buf = ValBuf<K, NTW, QV>;
-    using PF = ProbFrag<K>;
+    using PF = std::conditional_t<K == kF16 && NQ == 1, ProbFragF16Pair, ProbFrag<K>>;
     constexpr int BPS = kMaxBlocksPerSplit / NQ;      // the planner caps splits at this many blocks
     __shared__ float s_f[NQ][kMaxHeads][2 * BPS];       // per 32-token tile
     __shared__ float s_M[NQ][kMaxHeads], s_L[NQ][kMaxHeads];
