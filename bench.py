@@ -50,10 +50,10 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 # current kernels, scaled by the factors a plain copy of known size gives (FETCH x 2.0, WRITE x
 # 1.0); the counter summaries are under profiles/. Kernels without an entry report null.
 MEASURED_TRAFFIC = {
-    ("longchat_b16_t32768_f16", "latent_scores"): 1_435_767_564,
-    ("longchat_b16_t32768_f16", "latent_values"): 1_173_500_204,
-    ("longchat_b16_t16384_q43", "latent_scores"): 217_578_566,
-    ("longchat_b16_t16384_q43", "latent_values"): 180_752_571,
+    ("longchat_b16_t32768_f16", "latent_scores"): 1_435_443_680,
+    ("longchat_b16_t32768_f16", "latent_values"): 1_173_964_774,
+    ("longchat_b16_t16384_q43", "latent_scores"): 217_632_198,
+    ("longchat_b16_t16384_q43", "latent_values"): 180_330_193,
     ("model32_b32_t8192_f16", "dense_attention"): 4_310_900_125,
     ("model32_b32_t8192_f16", "latent_scores"): 967_505_820,       # mean over the latent layers
     ("model32_b32_t8192_f16", "latent_values"): 639_198_239,       # mean over the latent layers
