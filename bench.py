@@ -15,11 +15,11 @@ streaming kernel's algorithmic bytes (latent bytes it must read: key latents for
 value latent for the value kernel, codes plus scales / zero points for a mixed 4/3-bit cache,
 K and V for an exempt layer) are divided by its duration from HIP events recorded around its
 launch on the launch stream; the kernel with the largest total time is reported (all appear under
-``kernels``). ``projections`` times, apart from the step, the two dense products around a latent
-layer's attention (the fused token down-projection + append and the output projection) with HIP
-events; ``queries`` times four queries per sequence (speculative-decoding verification) through
-the per-row multi-query entry point and through the one that shares each key and latent stream
-between a sequence's queries. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
+``kernels``). With ``--extras``, ``projections`` times, apart from the step, the two dense products
+around a latent layer's attention (the fused token down-projection + append and the output
+projection) with HIP events, and ``queries`` times four queries per sequence (speculative-decoding
+verification) through the per-row multi-query entry point and through the one that shares each
+key and latent stream between a sequence's queries. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
 pairs of the same workload, scaled to the whole workload.
 """
 from __future__ import annotations
@@ -447,8 +447,11 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's split planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle wall seconds")
-    ap.add_argument("--no-projections", action="store_true",
-                    help="skip timing the token down-projection and the output projection")
+    ap.add_argument("--extras", action="store_true",
+                    help="after the steps, also time the token down-projection, the output "
+                         "projection and several queries per sequence (outside the step; they call "
+                         "the decode kernels with other shapes, so a kernel trace of such a run "
+                         "mixes those calls with the step's)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, stream this many MiB through one elementwise copy "
                          "kernel (reads and writes that many bytes once): the reference for "
@@ -548,7 +551,7 @@ def main(argv=None):
             raise SystemExit("non-finite attention output")
 
     projections = queries = None
-    if not a.no_projections:
+    if a.extras:
         lat = [r for r in runs if not r.dense]
         projections = measure_projections(sk, buffers, lat[0], B, stream, hip, a.steps)
         if len(runs) == 1:
