@@ -243,8 +243,8 @@ struct ScoreParams {
     const void* zk;        // key latent, block layout
     const void* bk;        // key factors [R_k caller rows][D], head h's rows at soff[h]
     const float* q;        // [B][H][D]
-    void* P;               // [B][H][Tp] probabilities, relative to each block's maximum
-    float* stats;          // [B][H][nblk][2] per block: max (log2 units), sum of probabilities
+    void* P;               // [B][H][Tp] probabilities, relative to each 32-token tile's maximum
+    float* stats;          // [B][H][2 * nblk][2] per 32-token tile: max (log2 units), sum of probabilities
     int B, H, D, Rk, nblk_cap, seq_len, nblk, Tp, blocks_per_wg;
     const int32_t* seq_lens = nullptr;   // per-sequence lengths (device, clamped to [0, seq_len])
     const int32_t* seq_map = nullptr;    // query row b reads cache sequence seq_map[b] (or b)
@@ -268,7 +268,7 @@ struct ScoreParams {
 struct ValueParams {
     const void* zv;        // value latent, block layout
     const void* P;         // [B][H][Tp]
-    const float* stats;    // [B][H][nblk][2]
+    const float* stats;    // [B][H][2 * nblk][2] per 32-token tile
     float* ws_ml;          // [B][S][H][2]   (max in log2 units, sum)
     float* ws_acc;         // [B][S][H][rv]
     int B, H, rv, nblk_cap, seq_len, nblk, Tp, S, blocks_per_split;
