@@ -291,7 +291,9 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
         // arithmetic and the scheduler can overlap one pass's MFMAs with another's VALU work.
         auto core = [&](auto nks_c) __attribute__((always_inline)) {
             constexpr int NKS = decltype(nks_c)::value;
-            constexpr bool SPLIT = score_split_q<K, MAXKS, QK, NQ>();
+            // heads of at most four rank steps load both column tiles up front even where the
+            // instantiation's larger ranks need the split (their fragments fit the same registers)
+            constexpr bool SPLIT = score_split_q<K, MAXKS, QK, NQ>() && (QK || NKS > 4);
             Fr z[2][NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) z[0][ks] = frag(0, ks);
