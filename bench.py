@@ -52,8 +52,8 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 MEASURED_TRAFFIC = {
     ("longchat_b16_t32768_f16", "latent_scores"): 1_433_219_328,
     ("longchat_b16_t32768_f16", "latent_values"): 1_143_322_261,
-    ("longchat_b16_t16384_q43", "latent_scores"): 217_647_097,
-    ("longchat_b16_t16384_q43", "latent_values"): 180_392_184,
+    ("longchat_b16_t16384_q43", "latent_scores"): 217_559_664,
+    ("longchat_b16_t16384_q43", "latent_values"): 178_939_971,
     ("model32_b32_t8192_f16", "dense_attention"): 4_310_896_887,
     ("model32_b32_t8192_f16", "latent_scores"): 967_531_371,       # mean over the latent layers
     ("model32_b32_t8192_f16", "latent_values"): 635_010_231,       # mean over the latent layers

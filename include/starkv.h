@@ -51,9 +51,11 @@
  *           the low three bits of channel e of the group, bit 48+e the fourth bit of channel
  *           e < n_g. key_block_bytes = 24*R_k + 8*(number of 4-bit key channels).
  *      zv:  [B][capacity/64][value_block_bytes]: channel c's 64 codes at byte 32c when 4-bit,
- *           32*n_hi + 24*(c - n_hi) when 3-bit. 4-bit: token t in byte t/2, low nibble for even
- *           t. 3-bit: bytes 0..15 hold the low two bits (token t in byte t/4 at bit 2*(t%4)),
- *           bytes 16..23 the third bit (token t in byte 16 + t/8, bit t%8).
+ *           32*n_hi + 24*(c - n_hi) when 3-bit, as 32-bit words whose low 16 bits hold the
+ *           even tokens of the word's span and whose high 16 bits the odd tokens. 4-bit: token t
+ *           in word t/8 at bit 16*(t%2) + 4*((t/2)%4). 3-bit: words 0..3 the low two bits (token
+ *           t in word t/16 at bit 16*(t%2) + 2*((t/2)%8)), words 4..5 the third bit (word
+ *           4 + t/32, bit 16*(t%2) + (t/2)%16).
  *      Bits are little-endian in little-endian bytes; both code buffers carry 32 bytes of
  *      padding at the end (readers load aligned windows).
  *      zk_meta / zv_meta: [B][capacity/64][2][C] fp16: per block the scales of all channels,

@@ -552,13 +552,38 @@ int orc_rotate_factor_f16(int C, int ncols, int nseg, const int *seg, const uint
 /*              binary16 is an integer multiple of 2^-24 and |code * s + z| < 2^21, so the     */
 /*              exact value is an integer times 2^-24 below 2^45 and fp64 holds it exactly.    */
 /*                                                                                              */
-/* Packed layout of one channel's 64 codes (little-endian bytes):                               */
-/*   4 bits: 32 bytes; token t sits in byte t/2, low nibble for even t.                         */
-/*   3 bits: 24 bytes; bytes 0..15 hold the low two bits (token t in byte t/4 at bit 2*(t%4)),  */
-/*           bytes 16..23 the third bit (token t in byte 16 + t/8 at bit t%8).                  */
+/* Packed layout of one channel's 64 codes (little-endian 32-bit words; in every word the even */
+/* tokens of its span fill the low 16 bits and the odd tokens the high 16 bits, so that tokens   */
+/* 2i and 2i+1 sit 16 bits apart):                                                              */
+/*   4 bits: 8 words; word t/8 holds tokens 8*(t/8) .. +7; token t at bit 16*(t%2) + 4*((t/2)%4). */
+/*   3 bits: 6 words; words 0..3 the low two bits (word t/16, bit 16*(t%2) + 2*((t/2)%8)),      */
+/*           words 4..5 the third bit (word 4 + t/32, bit 16*(t%2) + (t/2)%16).                 */
 /* ------------------------------------------------------------------------------------------ */
 
 static float f16_to_f32(uint16_t h) { return (float)orc_f16_to_f64(h); }
+
+/* Bit offset of token t's w-bit field inside its 32-bit word: even tokens from bit 0, odd tokens
+ * from bit 16, in token order (one field per token pair). */
+static int code_bit(int t, int w)
+{
+    int per_half = 16 / w;                      /* fields in one 16-bit half */
+    return 16 * (t & 1) + w * ((t / 2) % per_half);
+}
+
+/* Bit-addressed access to a little-endian byte string (bit i = bit i%8 of byte i/8). */
+static void set_code_bits(uint8_t *bytes, int bit, int value, int w)
+{
+    for (int i = 0; i < w; ++i)
+        bytes[(bit + i) / 8] |= (uint8_t)(((value >> i) & 1) << ((bit + i) % 8));
+}
+
+static int get_code_bits(const uint8_t *bytes, int bit, int w)
+{
+    int v = 0;
+    for (int i = 0; i < w; ++i)
+        v |= ((bytes[(bit + i) / 8] >> ((bit + i) % 8)) & 1) << i;
+    return v;
+}
 
 void orc_quantize_group(const uint16_t *x, long stride, int bits, uint8_t *codes_out,
                         uint16_t *scale_out, uint16_t *zero_out)
@@ -593,15 +618,13 @@ void orc_quantize_group(const uint16_t *x, long stride, int bits, uint8_t *codes
             r = (float)qmax;
         code[t] = (uint8_t)r;
     }
-    if (bits == 4) {
-        memset(codes_out, 0, 32);
-        for (int t = 0; t < 64; ++t)
-            codes_out[t / 2] |= (uint8_t)((code[t] & 0xf) << (4 * (t & 1)));
-    } else {
-        memset(codes_out, 0, 24);
-        for (int t = 0; t < 64; ++t) {
-            codes_out[t / 4] |= (uint8_t)((code[t] & 3) << (2 * (t & 3)));
-            codes_out[16 + t / 8] |= (uint8_t)(((code[t] >> 2) & 1) << (t & 7));
+    memset(codes_out, 0, (size_t)8 * bits);
+    for (int t = 0; t < 64; ++t) {
+        if (bits == 4) {
+            set_code_bits(codes_out, 32 * (t / 8) + code_bit(t, 4), code[t] & 0xf, 4);
+        } else {
+            set_code_bits(codes_out, 32 * (t / 16) + code_bit(t, 2), code[t] & 3, 2);
+            set_code_bits(codes_out, 128 + 32 * (t / 32) + code_bit(t, 1), (code[t] >> 2) & 1, 1);
         }
     }
     *scale_out = s16;
@@ -611,8 +634,9 @@ void orc_quantize_group(const uint16_t *x, long stride, int bits, uint8_t *codes
 int orc_unpack_code(const uint8_t *codes, int bits, int t)
 {
     if (bits == 4)
-        return (codes[t / 2] >> (4 * (t & 1))) & 0xf;
-    return ((codes[t / 4] >> (2 * (t & 3))) & 3) | (((codes[16 + t / 8] >> (t & 7)) & 1) << 2);
+        return get_code_bits(codes, 32 * (t / 8) + code_bit(t, 4), 4);
+    return get_code_bits(codes, 32 * (t / 16) + code_bit(t, 2), 2) |
+           (get_code_bits(codes, 128 + 32 * (t / 32) + code_bit(t, 1), 1) << 2);
 }
 
 uint16_t orc_dequant_value(int code, uint16_t s16, uint16_t z16)

@@ -544,27 +544,30 @@ template <> struct ProbFrag<kF32> {
 };
 
 // Eight mixed 4/3-bit value codes (tokens 16*ks + 8*half .. +7 of one channel) to an fp16 MFMA
-// operand fragment. run: the channel's 64 codes as eight words (4-bit: a nibble per token; 3-bit:
-// words 0..3 the low two bits, words 4..5 the third bit); s2 / z2: the channel's scale and zero
-// point in both halves. Each value is binary16(q*s + z) rounded once.
+// operand fragment. run: the channel's 64 codes as eight words (4-bit: eight tokens per word;
+// 3-bit: words 0..3 the low two bits of sixteen tokens each, words 4..5 the third bit of 32), each
+// word holding the even tokens of its span in its low 16 bits and the odd tokens in its high 16
+// bits, so that one shift and mask leave tokens 2k and 2k+1 of the fragment in the two halves of
+// a word; s2 / z2: the channel's scale and zero point in both halves. Each value is
+// binary16(q*s + z) rounded once; q is formed exactly as binary16(1024 + q) - 1024.
 __device__ __forceinline__ f16x8 q43_value_frag(const uint32_t (&run)[8], bool hi4, int ks, int half,
                                                uint32_t s2, uint32_t z2) {
-    uint32_t q[8];
+    uint32_t bits[4];
     if (hi4) {
         const uint32_t w = half ? run[2 * ks + 1] : run[2 * ks];   // static register indices
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = (w >> (4 * e)) & 15u;
+        for (int k = 0; k < 4; ++k) bits[k] = ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
     } else {
-        const uint32_t w2 = run[ks] >> (16 * half);
-        const uint32_t w1 = run[4 + (ks >> 1)] >> (16 * (ks & 1) + 8 * half);
+        const uint32_t w2 = run[ks] >> (8 * half);
+        const uint32_t w1 = run[4 + (ks >> 1)] >> (8 * (ks & 1) + 4 * half);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = ((w2 >> (2 * e)) & 3u) | (((w1 >> e) & 1u) << 2);
+        for (int k = 0; k < 4; ++k)
+            bits[k] = ((w2 >> (2 * k)) & 0x00030003u) | (((w1 >> k) & 0x00010001u) << 2) | 0x64006400u;
     }
     f16x8 out;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t bits = 0x64006400u | q[2 * k] | (q[2 * k + 1] << 16);
-        const f16x2 qv = __builtin_bit_cast(f16x2, bits) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+        const f16x2 qv = __builtin_bit_cast(f16x2, bits[k]) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
         const f16x2 r = __builtin_elementwise_fma(qv, __builtin_bit_cast(f16x2, s2), __builtin_bit_cast(f16x2, z2));
         out[2 * k] = r[0];
         out[2 * k + 1] = r[1];

@@ -16,9 +16,12 @@
 //    3e .. 3e+2 are the low three bits of channel e, and bit 48 + e the fourth bit of channel
 //    e < n. Bits are little-endian in little-endian 32-bit words.
 //  * value latent (channel-major, consumed as operands of eight tokens of one channel): channel c
-//    at byte 32c (4-bit, c < n_hi) or 32 n_hi + 24 (c - n_hi) (3-bit); 4-bit run: token t in
-//    byte t/2, low nibble for even t; 3-bit run: bytes 0..15 hold the low two bits (token t at
-//    bits 2(t%4) of byte t/4), bytes 16..23 the third bit (token t at bit t%8 of byte 16 + t/8).
+//    at byte 32c (4-bit, c < n_hi) or 32 n_hi + 24 (c - n_hi) (3-bit), in 32-bit words whose low
+//    16 bits hold the even tokens of the word's span and whose high 16 bits hold the odd tokens,
+//    so that tokens 2i and 2i+1 sit 16 bits apart (one AND-OR then yields both halves of a packed
+//    binary16 pair). 4-bit run: word t/8, bit 16(t%2) + 4((t/2)%4); 3-bit run: words 0..3 the low
+//    two bits (word t/16, bit 16(t%2) + 2((t/2)%8)), words 4..5 the third bit (word 4 + t/32,
+//    bit 16(t%2) + (t/2)%16).
 //  * meta [B][cap/64][2][C] binary16: per block a row of scales, then a row of zero points (so
 //    that the scales, and the zero points, of neighbouring channels pair up in one word);
 //    tail [B][64][C] binary16 holds the rows of the unfinished group.
@@ -120,21 +123,24 @@ __global__ __launch_bounds__(256) void q43_quantize(const Q43QuantParams p) {
         if (tid < 64 && c0 + tid < C) {
             const int c = c0 + tid;
             uint32_t* run = reinterpret_cast<uint32_t*>(blk + q43_value_run_offset(L, c));
+            // token k of a word's span: bit 16 * (k & 1) + width * (k >> 1)
             if (q43_is_hi(L, c)) {
                 for (int w = 0; w < 8; ++w) {
                     uint32_t v = 0;
-                    for (int k = 0; k < 8; ++k) v |= (uint32_t)code[8 * w + k][tid] << (4 * k);
+                    for (int k = 0; k < 8; ++k) v |= (uint32_t)code[8 * w + k][tid] << (16 * (k & 1) + 4 * (k >> 1));
                     run[w] = v;
                 }
             } else {
                 for (int w = 0; w < 4; ++w) {
                     uint32_t v = 0;
-                    for (int k = 0; k < 16; ++k) v |= (uint32_t)(code[16 * w + k][tid] & 3u) << (2 * k);
+                    for (int k = 0; k < 16; ++k)
+                        v |= (uint32_t)(code[16 * w + k][tid] & 3u) << (16 * (k & 1) + 2 * (k >> 1));
                     run[w] = v;
                 }
                 for (int w = 0; w < 2; ++w) {
                     uint32_t v = 0;
-                    for (int k = 0; k < 32; ++k) v |= (uint32_t)((code[32 * w + k][tid] >> 2) & 1u) << k;
+                    for (int k = 0; k < 32; ++k)
+                        v |= (uint32_t)((code[32 * w + k][tid] >> 2) & 1u) << (16 * (k & 1) + (k >> 1));
                     run[4 + w] = v;
                 }
             }
@@ -185,9 +191,10 @@ __device__ __forceinline__ int q43_key_code(const uint8_t* blk, const Q43Layout&
 }
 
 __device__ __forceinline__ int q43_value_code(const uint8_t* blk, const Q43Layout& L, int c, int t) {
-    const uint8_t* run = blk + q43_value_run_offset(L, c);
-    if (q43_is_hi(L, c)) return (run[t >> 1] >> (4 * (t & 1))) & 15;
-    return ((run[t >> 2] >> (2 * (t & 3))) & 3) | (((run[16 + (t >> 3)] >> (t & 7)) & 1) << 2);
+    const uint32_t* run = reinterpret_cast<const uint32_t*>(blk + q43_value_run_offset(L, c));
+    const int odd = 16 * (t & 1);
+    if (q43_is_hi(L, c)) return (run[t >> 3] >> (odd + 4 * ((t >> 1) & 3))) & 15;
+    return ((run[t >> 4] >> (odd + 2 * ((t >> 1) & 7))) & 3) | (((run[4 + (t >> 5)] >> (odd + ((t >> 1) & 15))) & 1) << 2);
 }
 
 __device__ __forceinline__ _Float16 q43_dequant(int q, uint16_t s16, uint16_t z16) {
