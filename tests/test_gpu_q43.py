@@ -183,8 +183,8 @@ def test_q43_decode_parity_rotated():
             got = _gpu_decode(L, cache, Tq, q, ld.bk, ld.bv, S)
             e = rel_err(got, ref)
             say(f"[q43 decode] T={Tq} splits={S} rel err {e:.3e}")
-            assert np.all(np.isfinite(got)) and e <= 1e-2
-            assert e <= 2e-3          # same dequantised values: only fp32 vs fp64 arithmetic differs
+            # same dequantised values on both sides: only fp32 vs fp64 arithmetic differs
+            assert np.all(np.isfinite(got)) and e <= 2e-3
 
 
 def test_q43_decode_full_size_sampled():
@@ -210,7 +210,7 @@ def test_q43_decode_full_size_sampled():
     sub = np.stack([got[sel_b[b], h] for b, h in pairs])
     e = rel_err(sub, ref)
     say(f"[q43 full] sampled {len(pairs)} pairs rel err {e:.3e}")
-    assert np.all(np.isfinite(got)) and e <= 1e-2
+    assert np.all(np.isfinite(got)) and e <= 2e-3
 
 
 @pytest.mark.parametrize("which,kind", [(0, 0), (1, 0), (0, 1), (1, 1)])
