@@ -91,6 +91,8 @@ def lib():
                                      C.c_long, C.c_long, vp]
         L.orc_threads.restype = C.c_int
         L.orc_threads.argtypes = []
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [C.c_int]
         _lib = L
     return _lib
 
@@ -128,6 +130,11 @@ def to_f64(a: np.ndarray, bf16: bool = False) -> np.ndarray:
 
 def threads() -> int:
     return int(lib().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls (timing only: results do not depend on it)."""
+    lib().orc_set_threads(int(n))
 
 
 # ----------------------------------------------------------------------------------------------

@@ -500,6 +500,7 @@ int orc_rotate_rows_f16(long rows, int ld, int nseg, const int *seg, const uint1
         int s0 = seg[2 * g], w = seg[2 * g + 1];
         int bsz = orc_hadamard_block(w);
         double inv = 1.0 / sqrt((double)bsz);
+#pragma omp parallel for schedule(static)
         for (long t = 0; t < rows; ++t) {
             const uint16_t *xr = x + (size_t)t * ld;
             uint16_t *orow = out + (size_t)t * ld;
@@ -525,6 +526,7 @@ int orc_rotate_factor_f16(int C, int ncols, int nseg, const int *seg, const uint
         int s0 = seg[2 * g], w = seg[2 * g + 1];
         int bsz = orc_hadamard_block(w);
         double inv = 1.0 / sqrt((double)bsz);
+#pragma omp parallel for collapse(2) schedule(static)
         for (int j0 = s0; j0 < s0 + w; j0 += bsz)
             for (int i = 0; i < bsz; ++i)
                 for (int col = 0; col < ncols; ++col) {
@@ -723,6 +725,17 @@ int orc_q43_unpack(int B, long seq_len, long T_cap, int C, const uint8_t *bits,
 #include <omp.h>
 #endif
 /* Threads the attention loops use (OpenMP over independent (b, h) pairs). */
+/* Thread count for later parallel regions (timing only; results do not depend on it). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_threads(void)
 {
 #ifdef _OPENMP

@@ -312,26 +312,98 @@ def test_rotation_absorbs_exactly():
     assert np.allclose(Br, Hfull.T @ Bm, atol=1e-13, rtol=0)
 
 
-def test_rotation_fp16_storage_rule():
-    rng = np.random.default_rng(10)
-    ranks = [16, 32, 48, 64]
-    segs = oracle.latent_segments(ranks, 0.25)
-    Z16 = (rng.standard_normal((40, sum(ranks))) * 3).astype(np.float16)
-    got = oracle.rotate_rows(Z16, segs)
-    exact = oracle.rotate_rows(Z16.astype(np.float64), segs)
-    # blocks of 1, 4, 16 and 64 have power-of-two scales: one rounding of the exact value
-    blocks = np.zeros(sum(ranks), int)
+def _rot_rule_bits(S, b):
+    """The binary16 storage rule of a rotated value, from the exact signed sum S (a Fraction):
+    multiply by the binary64 value of 1/sqrt(b) (IEEE division of 1 by the IEEE square root), round
+    that product to binary64 (Python's float() of a Fraction rounds correctly), then to binary16
+    with numpy's nearest-even conversion from binary64."""
+    from fractions import Fraction
+    inv = Fraction(float(np.float64(1.0) / np.sqrt(np.float64(b))))
+    return int(np.array([float(S * inv)], np.float64).astype(np.float16).view(np.uint16)[0])
+
+
+def _rot_exact_rows(x16, segs):
+    """Rotated rows by the rule above, element by element, with the Sylvester signs taken from
+    scipy.linalg.hadamard (the textbook Kronecker construction) and exact rational sums."""
+    from fractions import Fraction
+    import scipy.linalg
+    out = x16.view(np.uint16).copy()
     for s0, w in segs:
-        blocks[s0:s0 + w] = oracle.hadamard_block(int(w))
-    one_round = np.isin(blocks, (1, 4, 16, 64))
-    assert np.array_equal(got[:, one_round].view(np.uint16),
-                          exact[:, one_round].astype(np.float16).view(np.uint16))
-    # blocks of 2, 8, 32: exact sum times fp64(1/sqrt(b)), then one more rounding to fp16
-    assert np.all(np.abs(got.astype(np.float64) - exact) <= 2.0 ** -10 * np.abs(exact) + 2.0 ** -24)
-    B16 = (rng.standard_normal((sum(ranks), 64)) / 4).astype(np.float16)
-    gotb = oracle.rotate_factor(B16, segs)
-    exb = oracle.rotate_factor(B16.astype(np.float64), segs)
-    assert np.array_equal(gotb[one_round].view(np.uint16), exb[one_round].astype(np.float16).view(np.uint16))
+        b = oracle.hadamard_block(int(w))
+        Hs = scipy.linalg.hadamard(b)
+        for t in range(x16.shape[0]):
+            for j0 in range(s0, s0 + w, b):
+                xs = [Fraction(float(v)) for v in x16[t, j0:j0 + b]]
+                for i in range(b):
+                    S = sum((int(Hs[j, i]) * xs[j] for j in range(b)), Fraction(0))
+                    out[t, j0 + i] = _rot_rule_bits(S, b)
+    return out
+
+
+# block widths 1, 2, 4, 8, 16, 32 and 64 (a segment's block is the largest power of two dividing
+# its width, at most 64)
+_ROT_SEGS = np.array([[0, 3], [3, 2], [5, 6], [11, 12], [23, 8], [31, 24], [55, 16], [71, 32],
+                      [103, 96], [199, 64]], np.int32)
+
+
+def test_rotation_fp16_storage_rule():
+    """orc_rotate_rows_f16 / orc_rotate_factor_f16 (Zhou notes, section 6.1 and Fig. 5: the latents
+    are rotated blockwise before they are quantised; the stored binary16 rule is a reading of
+    this build): every element is the exact signed sum times binary64(1/sqrt(b)), rounded to
+    binary64 and then to binary16, bit for bit, for every block size 1 ... 64 — in particular
+    2, 8 and 32, whose scale is not a power of two. A wrong sign or index of the Sylvester
+    matrix, a transposed block, a binary32 intermediate or a binary32 1/sqrt(b) fails here."""
+    rng = np.random.default_rng(10)
+    C = int(_ROT_SEGS[-1].sum())
+    blocks = {oracle.hadamard_block(int(w)) for _, w in _ROT_SEGS}
+    assert blocks == {1, 2, 4, 8, 16, 32, 64}
+    Z16 = (rng.standard_normal((6, C)) * 3).astype(np.float16)
+    Z16[0, :8] = [65504, 65504, -65504, 1.0, 2.0 ** -24, -2.0 ** -24, 6e-5, -6e-5]   # range ends
+    got = oracle.rotate_rows(Z16, _ROT_SEGS)
+    assert np.array_equal(got.view(np.uint16), _rot_exact_rows(Z16, _ROT_SEGS))
+    # factor rows: the same rule on columns (B' = blockdiag(H)^T B)
+    B16 = (rng.standard_normal((C, 5)) / 4).astype(np.float16)
+    gotb = oracle.rotate_factor(B16, _ROT_SEGS)
+    assert np.array_equal(gotb.T.view(np.uint16), _rot_exact_rows(np.ascontiguousarray(B16.T), _ROT_SEGS))
+
+
+def _double_rounding_cases(b, n_want, seed):
+    """Pairs of inputs (a block of b binary16 values) whose rotated first element differs between
+    the rule and (1) a product rounded through binary32, (2) a binary32 value of 1/sqrt(b). Found
+    by a seeded search in binary64 and confirmed with exact arithmetic."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    inv64 = np.float64(1.0) / np.sqrt(np.float64(b))
+    inv32 = np.float32(1.0) / np.sqrt(np.float32(b))
+    found = {"f32_product": [], "f32_scale": []}
+    for _ in range(50):
+        x = (rng.standard_normal((20000, b)) * 2.0 ** rng.integers(-8, 8, (20000, 1))).astype(np.float16)
+        S = x.astype(np.float64).sum(axis=1)                            # first output: all signs +
+        rule = (S * inv64).astype(np.float16)
+        via32 = (S * inv64).astype(np.float32).astype(np.float16)
+        scale32 = (S * np.float64(inv32)).astype(np.float16)
+        for key, alt in (("f32_product", via32), ("f32_scale", scale32)):
+            for r in np.nonzero(rule.view(np.uint16) != alt.view(np.uint16))[0][:n_want]:
+                Sx = sum((Fraction(float(v)) for v in x[r]), Fraction(0))
+                if _rot_rule_bits(Sx, b) != int(alt[r:r + 1].view(np.uint16)[0]):
+                    found[key].append(x[r])
+        if all(len(v) >= n_want for v in found.values()):
+            break
+    return found
+
+
+@pytest.mark.parametrize("b", [2, 8, 32])
+def test_rotation_fp16_rule_against_binary32_shortcuts(b):
+    """Blocks where a binary32 shortcut gives another binary16 than the rule: the oracle must give
+    the rule's value on each (and so differs from the shortcut)."""
+    found = _double_rounding_cases(b, 3, seed=100 + b)
+    segs = np.array([[0, b]], np.int32)
+    for key, rows in found.items():
+        assert len(rows) >= 1, f"no {key} case found for b={b}"
+        x16 = np.ascontiguousarray(np.stack(rows))
+        got = oracle.rotate_rows(x16, segs)
+        want = _rot_exact_rows(x16, segs)
+        assert np.array_equal(got.view(np.uint16), want), key
 
 
 # ------------------------------------------------------------------------------------------------
