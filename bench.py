@@ -11,18 +11,20 @@ already resident in HBM when timing starts.
 
 Prints one JSON line. ``value`` is decode tokens per second (one new token per sequence per step,
 B / step time). ``roofline`` prices the dominant kernel (the one with the largest total time; all
-appear under ``kernels``) against the limit that binds it. Every kernel's algorithmic bytes (latent
-bytes it must read: key latents for the score kernel, value latent for the value kernel, codes
-plus scales / zero points for a mixed 4/3-bit cache, K and V for an exempt layer) are divided by
-its duration from HIP events recorded around its launch on the launch stream and compared with
-MI355X's 8 TB/s HBM. The score kernel is bound by VALU issue, not by its bytes: when it dominates,
-``roofline`` reports its algorithmic fp32 work per launch over its duration against the fp32
-vector peak (``bound``: ``alu``), with the HBM figures under ``roofline.hbm``. With ``--extras``, ``projections`` times, apart from the step, the two dense products
-around a latent layer's attention (the fused token down-projection + append and the output
-projection) with HIP events, and ``queries`` times four queries per sequence (speculative-decoding
-verification) through the per-row multi-query entry point and through the one that shares each
-key and latent stream between a sequence's queries. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head)
-pairs of the same workload, scaled to the whole workload.
+appear under ``kernels``) on HBM: its algorithmic bytes (latent bytes it must read: key latents
+for the score kernel, value latent for the value kernel, codes plus scales / zero points for a
+mixed 4/3-bit cache, K and V for an exempt layer) over its duration from HIP events recorded
+around its launch on the launch stream, against MI355X's 8 TB/s, and against a device-copy
+ceiling measured in the same run. Beside it: the kernel's algorithmic vector and matrix work over
+the same duration against the published fp32 vector and fp16 matrix peaks, and the counter
+figures (HBM traffic, MfmaUtil, VALUBusy) of the rocprofv3 summary taken on the same kernel
+sources (null when the sources have changed since). With ``--extras``, ``projections`` times,
+apart from the step, the two dense products around a latent layer's attention (the fused token
+down-projection + append and the output projection) with HIP events, and ``queries`` times four
+queries per sequence (speculative-decoding verification) through the per-row multi-query entry
+point and through the one that shares each key and latent stream between a sequence's queries.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of (sequence, head) pairs of the
+same workload, scaled to the whole workload, on all host threads and on one.
 """
 from __future__ import annotations
 
@@ -41,25 +43,33 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, AMD datasheet
-# fp32 vector peak without packed fp32 (disabled in this build): 256 CUs x 4 SIMDs x 16 lanes x
-# 2 flop (FMA) x 2.4 GHz; AMD's 157.3 TFLOP/s counts the packed forms
-VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# MI355X published peaks: fp32 vector 157.3 TFLOP/s (counts the packed fp32 forms, which this
+# build does not emit: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz = 78.6 without them);
+# dense fp16 / bf16 matrix 2.5 PFLOP/s
+VALU_PEAK_TFLOPS = 157.3
+VALU_PEAK_NONPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+MFMA_F16_PEAK_TFLOPS = 2500.0
 DEFAULT_WORKLOAD = "longchat_b16_t32768_f16"
 MODEL_WORKLOAD = "model32_b32_t8192_f16"
 METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=16 T=32K"
 
-# HBM bytes per launch (read + written) measured with rocprofv3 FETCH_SIZE / WRITE_SIZE for the
-# current kernels, scaled by the factors a plain copy of known size gives (FETCH x 2.0, WRITE x
-# 1.0); the counter summaries are under profiles/. Kernels without an entry report null.
-MEASURED_TRAFFIC = {
-    ("longchat_b16_t32768_f16", "latent_scores"): 1_433_219_328,
-    ("longchat_b16_t32768_f16", "latent_values"): 1_143_322_261,
-    ("longchat_b16_t16384_q43", "latent_scores"): 217_559_664,
-    ("longchat_b16_t16384_q43", "latent_values"): 178_939_971,
-    ("model32_b32_t8192_f16", "dense_attention"): 4_310_896_887,
-    ("model32_b32_t8192_f16", "latent_scores"): 967_531_371,       # mean over the latent layers
-    ("model32_b32_t8192_f16", "latent_values"): 635_010_231,       # mean over the latent layers
+# Hardware-counter figures per launch from rocprofv3 runs of this bench's default command (the
+# summaries, with their commands, are the files named here): HBM bytes read + written
+# (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a plain copy of known size gives), MfmaUtil
+# and VALUBusy (percent, rocprofv3's derived counters). Each entry carries the digest of the
+# kernel sources it was measured on; when the sources differ the figures are reported as null.
+KERNEL_SOURCES = ("latent_decode.hip", "dense_decode.hip", "common.hpp")
+MEASURED = {
 }
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rank_kv_cache_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -121,10 +131,16 @@ class OracleSample:
     """Accumulates oracle wall time on sampled (sequence, head) pairs, scaled per layer."""
 
     def __init__(self):
+        import oracle
+        self.threads = oracle.threads()
         self.full_s = 0.0
         self.spent = 0.0
         self.pairs = 0
         self.total_pairs = 0
+        # the same oracle on one host thread, on a smaller sample (a quarter of the budget)
+        self.one_thread_s = 0.0
+        self.one_thread_spent = 0.0
+        self.one_thread_pairs = 0
 
     def time_pairs(self, fn, B, H, budget_s, seed, extra_per_seq=None):
         """fn(pairs) runs the oracle on a list of (b, h); extra_per_seq(b) times per-sequence
@@ -156,7 +172,49 @@ class OracleSample:
         self.spent += spent
         self.pairs += done
         self.total_pairs += B * H
+        # one thread: pairs one at a time until a quarter of the budget is spent
+        oracle.set_threads(1)
+        try:
+            spent1, done1 = 0.0, 0
+            while done1 < B * H and spent1 < budget_s / 4:
+                i = int(order[done1])
+                t0 = time.perf_counter()
+                fn([(i // H, i % H)])
+                spent1 += time.perf_counter() - t0
+                done1 += 1
+            full1 = spent1 * (B * H) / done1
+            if extra_per_seq is not None:
+                t0 = time.perf_counter()
+                extra_per_seq(0)
+                e1 = time.perf_counter() - t0
+                spent1 += e1
+                full1 += e1 * B
+        finally:
+            oracle.set_threads(thr)
+        self.one_thread_s += full1
+        self.one_thread_spent += spent1
+        self.one_thread_pairs += done1
         return full
+
+
+def measure_copy_ceiling(hip, stream, mib=1024, reps=5):
+    """Device-copy ceiling of this GPU: one elementwise copy kernel reading and writing `mib` MiB,
+    timed with HIP events on the launch stream; returns (bytes read + written) / median time."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ev = hip.create(2 * reps)
+    dst.copy_(src)
+    for i in range(reps):
+        hip.record(ev[2 * i], stream.cuda_stream)
+        dst.copy_(src)
+        hip.record(ev[2 * i + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    ms = [hip.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(reps)]
+    hip.destroy(ev)
+    del src, dst
+    return 2 * n * 4 / (statistics.median(ms) * 1e-3) / 1e9
 
 
 def cache_capacity(T):
@@ -186,17 +244,28 @@ def build_latent_run(sk, buffers, layer, zk, zv, bk_h, bv_h, q_h, T, bf16, quant
     cache = buffers.alloc_cache(layer, B, cap)
     dzk = buffers.to_device(zk, bf16=bf16)
     dzv = buffers.to_device(zv, bf16=bf16)
+    dbk = buffers.to_device(bk_h, bf16=bf16)
+    dbv = buffers.to_device(bv_h, bf16=bf16)
+    H, d = q_h.shape[1], q_h.shape[2]
+    if quantized:
+        # the quantised layer stores blockwise-Hadamard-rotated latents (Zhou notes, section 6.1:
+        # rotate, then quantise); the rotation is absorbed into the factors. It is offline
+        # preparation, done here on the device before the cache is built, outside the timed steps.
+        def rot(x, which, kind, n):
+            y = torch.empty_like(x)
+            sk.starkv_hadamard_rotate(layer, which, kind, n, x, y)
+            return y
+        dzk, dzv = rot(dzk, 0, 0, B * T), rot(dzv, 1, 0, B * T)
+        dbk, dbv = rot(dbk, 0, 1, d), rot(dbv, 1, 1, H * d)
     sk.starkv_append_latents(layer, cache, 0, T - 1, dzk[:, :T - 1].contiguous(),
                              dzv[:, :T - 1].contiguous())
     new_k = dzk[:, T - 1:].contiguous()
     new_v = dzv[:, T - 1:].contiguous()
     del dzk, dzv
-    H, d = q_h.shape[1], q_h.shape[2]
     out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
     esz = zk.dtype.itemsize
     kb, vb = latent_kernel_bytes(sk, layer, B, T, zk.shape[2], zv.shape[2], esz, quantized)
-    return LayerRun(layer, cache, new_k, new_v, buffers.to_device(bk_h, bf16=bf16),
-                    buffers.to_device(bv_h, bf16=bf16), buffers.to_device(q_h), out, T, False,
+    return LayerRun(layer, cache, new_k, new_v, dbk, dbv, buffers.to_device(q_h), out, T, False,
                     kb, vb)
 
 
@@ -230,10 +299,11 @@ def setup_single(a, sk, buffers, synth, sample):
         f"{' mixed 4/3-bit cache' if w.quantized else ''}; generated "
         f"{(zk.nbytes + zv.nbytes) / 1e9:.2f} GB in {time.perf_counter() - t_gen:.1f} s")
     if w.quantized:
-        # Latents enter the cache already in the rotated basis (the rotation is folded into the
-        # down-projection ahead of the cache); rows of the synthetic generator stand in for them.
+        # the generator's rows are rotated on the device before they enter the cache (see
+        # build_latent_run)
         layer = sk.Layer(num_heads=H, head_dim=d, key_ranks=tuple(int(r) for r in ld.key_ranks),
-                         value_rank=rv, cache_dtype=sk.Q43, rope_base=w.rope_base)
+                         value_rank=rv, cache_dtype=sk.Q43, rope_base=w.rope_base,
+                         q_top_fraction=w.q_top_fraction)
     else:
         dt_code = {"f32": sk.F32, "f16": sk.F16, "bf16": sk.BF16}[w.dtype]
         layer = sk.Layer(num_heads=H, head_dim=d, key_ranks=tuple(int(r) for r in ld.key_ranks),
@@ -244,7 +314,10 @@ def setup_single(a, sk, buffers, synth, sample):
         sample_latent_layer(sample, w, ld, zk, zv, q, a.cpu_budget, w.quantized, seed=2024)
     desc = {"workload": w.name, "batch": B, "heads": H, "head_dim": d, "seq_len": T,
             "key_rank_sum": Rk, "value_rank": rv,
-            "latent_dtype": "q43" if w.quantized else w.dtype, "layers": 1}
+            "latent_dtype": ("q43" if w.q_top_fraction < 1 else "q4") if w.quantized else w.dtype,
+            "layers": 1}
+    if w.quantized:
+        desc["q_top_fraction"] = w.q_top_fraction
     return [run], desc, "f16" if w.quantized else w.dtype, B
 
 
@@ -257,11 +330,13 @@ def sample_latent_layer(sample, w, ld, zk, zv, q, budget, quantized, seed):
                           w.batch, w.heads, budget, seed)
         return
     # the oracle's mixed 4/3-bit path: the cache is quantised once when it is built (not timed);
-    # a step dequantises every sequence (timed once, scaled by B) and attends on the result
+    # a step dequantises every sequence (timed once, scaled by B) and attends on the result. The
+    # oracle's work does not depend on the values, so it runs on the generator's rows without the
+    # offline rotation (which is not part of a step on either side).
     T = zk.shape[1]
     cap = cache_capacity(T)
-    bits_k = oracle.channel_bits(ld.key_ranks, 0.25)
-    bits_v = oracle.channel_bits([ld.value_rank], 0.25)
+    bits_k = oracle.channel_bits(ld.key_ranks, w.q_top_fraction)
+    bits_v = oracle.channel_bits([ld.value_rank], w.q_top_fraction)
     pk = oracle.q43_pack(zk, bits_k, cap)
     pv = oracle.q43_pack(zv, bits_v, cap)
     dk = oracle.q43_unpack(*pk, bits_k, T, cap)
@@ -448,6 +523,8 @@ def main(argv=None):
                     help="a single-layer workload name, or " + MODEL_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's split planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip the device-copy ceiling measurement after the steps")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle wall seconds")
     ap.add_argument("--extras", action="store_true",
                     help="after the steps, also time the token down-projection, the output "
@@ -551,6 +628,7 @@ def main(argv=None):
         res = r.out.cpu().numpy()
         if not np.all(np.isfinite(res)):
             raise SystemExit("non-finite attention output")
+    copy_gbs = None if a.no_copy_ceiling else measure_copy_ceiling(hip, stream)
 
     projections = queries = None
     if a.extras:
@@ -581,24 +659,39 @@ def main(argv=None):
                  "kv_gbs_stream_kernels": round(total_bytes / (stream_ms * 1e-3) / 1e9, 1),
                  "cached_tokens_per_s": B * runs[0].T / (ms_per_step * 1e-3)})
     dk = kernels[dom]
-    hbm = {"achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["gbs"] / HBM_PEAK_GBS}
-    common = {"kernel": dom, "traffic": MEASURED_TRAFFIC.get((desc["workload"], dom)),
-              "kernel_avg_us": dk["avg_us_per_launch"],
-              "alg_bytes_per_launch": dk["alg_bytes_per_step"] // dk["launches_per_step"]}
-    if dom == "latent_scores":
-        # the score kernel is bound by VALU issue (its counters: ~80 % of the VALU instructions are
-        # the RoPE arithmetic), so it is priced against the fp32 vector peak; its algorithmic work
-        # per (cached token, sequence, head): rotate-half RoPE of the rebuilt key (d/2 rotations,
-        # 6 flop each) + the dot with the query (2d) + softmax (~5). The HBM view is kept beside it.
-        lat = [r for r in runs if not r.dense]
-        H, d = lat[0].layer.num_heads, lat[0].layer.head_dim
-        flop = sum(B * r.T * H * (5 * d + 5) for r in lat) / len(lat)
-        tf = flop / (dk["avg_us_per_launch"] * 1e-6) / 1e12
-        roofline = {"bound": "alu", "achieved": tf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": tf / VALU_PEAK_TFLOPS, **common, "flop_per_launch": flop,
-                    "peak_note": "fp32 vector without packed fp32 (157.3 with it)", "hbm": hbm}
+    roofline = {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                "kernel_avg_us": dk["avg_us_per_launch"],
+                "alg_bytes_per_launch": dk["alg_bytes_per_step"] // dk["launches_per_step"]}
+    if copy_gbs:
+        roofline["copy_ceiling_gbs"] = copy_gbs
+        roofline["frac_of_copy_ceiling"] = dk["gbs"] / copy_gbs
+    # algorithmic work per (cached token, sequence) of a latent layer: score kernel 2*d*R_k MFMA
+    # flop (key rebuild) and 6*H*d + 5*H vector flop (RoPE and the dot with the query: 3 flop per
+    # element, softmax: ~5 per head); value kernel 2*H*r_v MFMA flop (probabilities times latents)
+    lat = [r for r in runs if not r.dense]
+    if dom in ("latent_scores", "latent_values") and lat:
+        t_s = dk["avg_us_per_step"] * 1e-6
+        if dom == "latent_scores":
+            mf = sum(B * r.T * 2 * r.layer.head_dim * sum(r.layer.key_ranks) for r in lat)
+            vf = sum(B * r.T * r.layer.num_heads * (6 * r.layer.head_dim + 5) for r in lat)
+            roofline["valu"] = {"achieved": vf / t_s / 1e12, "peak": VALU_PEAK_TFLOPS,
+                                "unit": "TFLOP/s", "frac": vf / t_s / 1e12 / VALU_PEAK_TFLOPS,
+                                "frac_of_nonpacked_peak": vf / t_s / 1e12 / VALU_PEAK_NONPACKED_TFLOPS,
+                                "flop_per_step": vf}
+        else:
+            mf = sum(B * r.T * 2 * r.layer.num_heads * r.layer.value_rank for r in lat)
+        roofline["mfma"] = {"achieved": mf / t_s / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": mf / t_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                            "flop_per_step": mf}
+    meas = MEASURED.get((desc["workload"], dom))
+    digest = kernel_source_digest()
+    if meas is not None and meas["digest"] == digest:
+        roofline["traffic"] = meas["traffic"]
+        roofline["counters"] = {k: meas[k] for k in ("source", "mfma_util_pct", "valu_busy_pct")}
     else:
-        roofline = {"bound": "hbm", **hbm, **common}
+        roofline["counters"] = {"source": None, "note": "no counter run on these kernel sources "
+                                                        f"(digest {digest})"}
     rec = {
         "metric": METRIC,
         "value": B / (ms_per_step * 1e-3),
@@ -624,12 +717,17 @@ def main(argv=None):
         rec["queries"] = queries
     if sample is not None and sample.pairs:
         import oracle
-        thr = oracle.threads()
+        thr = sample.threads
         rec["cpu_baseline"] = {
             "value": B / sample.full_s, "unit": "tokens/s", "cores": thr, "kind": "oracle",
             "sample": f"{sample.pairs} of {sample.total_pairs} (sequence, head, layer) pairs of the "
                       f"same workload, full T, fp64, {sample.spent:.1f} s wall on {thr} threads; "
                       f"scaled per layer to all pairs ({sample.full_s:.1f} s per step)"}
+        if sample.one_thread_s:
+            rec["cpu_baseline"]["value_1thread"] = B / sample.one_thread_s
+            rec["cpu_baseline"]["sample_1thread"] = (
+                f"{sample.one_thread_pairs} pairs on 1 thread, {sample.one_thread_spent:.1f} s wall; "
+                f"scaled the same way ({sample.one_thread_s:.1f} s per step)")
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -173,7 +173,8 @@ size_t starkv_decode_workspace_bytes(const starkv_layer *layer, int32_t batch, i
  * For Q43 caches seq_len must equal the number of tokens appended so far (the unfinished group is
  * read from the tail), or be a multiple of 64 not above it. out and workspace must not alias any input.
  * Errors: NULL, SHAPE (seq_len < 1), CAPACITY (seq_len > capacity), DTYPE, MISALIGNED, WORKSPACE,
- * UNSUPPORTED. batch == 0 returns OK without enqueuing.
+ * UNSUPPORTED (among others: seq_len above 256 splits of 256 blocks, 4,194,304 tokens; the
+ * workspace size is then 0). batch == 0 returns OK without enqueuing.
  */
 starkv_status starkv_decode_attn(const starkv_layer *layer, const starkv_cache *cache,
                                  int64_t seq_len, const float *q, const void *bk, const void *bv,
@@ -206,7 +207,10 @@ starkv_status starkv_decode_attn_ragged(const starkv_layer *layer, const starkv_
  * the splits; the workspace is starkv_decode_workspace_bytes(layer, num_queries, max_len,
  * num_splits). Each query runs the single-query kernels on its own row, so rows that read the
  * same sequence share no work beyond what the caches return (the latents are streamed once per
- * query). Q43 lengths follow the starkv_decode_attn_ragged rule. Errors: those of
+ * query). Q43: for each cache sequence, the longest length among the rows that read it must
+ * equal the tokens appended to that sequence or be a multiple of 64 not above it; the groups
+ * below that length are read from the codes by every row of the sequence, so shorter causal rows
+ * may end anywhere (speculative verification across a group boundary). Errors: those of
  * starkv_decode_attn with seq_len = max_len; SHAPE (num_queries < 0, or queries on a batch-0
  * cache), NULL, MISALIGNED. num_queries == 0 returns OK.
  */
@@ -226,9 +230,11 @@ starkv_status starkv_decode_attn_queries(const starkv_layer *layer, const starkv
  * attends to max_len tokens) or a device int32 array of batch*nq lengths (4-byte aligned,
  * clamped to [0, max_len]; a causal query at position p uses p + 1; 0 gives a zero row). The
  * workspace is starkv_decode_multi_workspace_bytes(layer, batch, nq, max_len, num_splits).
- * nq is 1, 2 or 4; latent layers with F16, BF16 or Q43 caches (nq = 1 also F32). Q43 lengths
- * follow the starkv_decode_attn_ragged rule. Errors: those of starkv_decode_attn with seq_len =
- * max_len; SHAPE (nq < 1), UNSUPPORTED (other nq, dense layers, F32 with nq > 1), MISALIGNED.
+ * nq is 1, 2 or 4; latent layers with F16, BF16 or Q43 caches (nq = 1 also F32). Q43: the
+ * longest of a sequence's nq lengths follows the starkv_decode_attn_queries rule. max_len is at
+ * most 4,194,304 / nq tokens (256 splits of 256 / nq blocks; the workspace size is 0 above it).
+ * Errors: those of starkv_decode_attn with seq_len = max_len; SHAPE (nq < 1), UNSUPPORTED (other
+ * nq, dense layers, F32 with nq > 1, max_len above the limit), MISALIGNED.
  */
 size_t starkv_decode_multi_workspace_bytes(const starkv_layer *layer, int32_t batch, int32_t nq,
                                            int64_t max_len, int32_t num_splits);
@@ -267,11 +273,16 @@ starkv_status starkv_decode_attn_timed(const starkv_layer *layer, const starkv_c
                                        void *event_begin, void *event_mid, void *event_end);
 
 /*
- * Read cached tokens [t0, t1) back in token-major order: zk_out [B][t1-t0][R_k] (dense: H*d) and
- * zv_out [B][t1-t0][r_v] (dense: H*d). Element type: fp16 for Q43 (codes of complete groups are
- * dequantised as binary16(code * scale + zero), the exact value rounded once to nearest-even;
- * rows of the unfinished group come from the tail), otherwise the cache element type (a plain gather). seq_len is the number of tokens
- * appended so far (Q43: decides which groups are complete). Either output may be NULL to skip it.
+ * Read cached tokens [t0, t1) back in token-major order (the dequantisation step of the decode
+ * path: Zhou notes, section 6.1, which stores the cache as per-channel asymmetric 4/3-bit codes
+ * with fp16 scales and zero points per group of 64 tokens, and Algorithm 2 step 4a, which
+ * dequantises the latent tile before the keys are rebuilt): zk_out [B][t1-t0][R_k] (dense: H*d)
+ * and zv_out [B][t1-t0][r_v] (dense: H*d). Element type: fp16 for Q43 (codes of complete groups
+ * are dequantised as binary16(code * scale + zero), the exact value rounded once to
+ * nearest-even; rows of the unfinished group come from the tail), otherwise the cache element
+ * type (a plain gather). The decode kernels dequantise the same way in registers; this call
+ * materialises the rows for inspection and tests. seq_len is the number of tokens appended so
+ * far (Q43: decides which groups are complete). Either output may be NULL to skip it.
  * Errors: NULL (cache buffers), SHAPE (t0 < 0 or t0 > t1), CAPACITY (t1 > seq_len or seq_len >
  * capacity), DTYPE, MISALIGNED.
  */

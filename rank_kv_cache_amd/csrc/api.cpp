@@ -24,6 +24,7 @@ int linear_rows_per_workgroup(int elem);
 hipError_t launch_linear_store(const LinearStoreParams& p, int elem, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
+hipError_t launch_row_fill(const RowFillParams& p, hipStream_t st);
 hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
@@ -292,8 +293,16 @@ int plan_splits(int B, int64_t seq_len, int requested) {
     return (ntiles + tps - 1) / tps;
 }
 
+// Longest sequence a decode call takes: at most kMaxSplits splits, and for latent layers at most
+// kMaxBlocksPerSplit / nq blocks per split (the value kernel keeps a per-split table of that many
+// 32-token tile factors per query row and head in LDS).
+int64_t max_decode_len(const LayerInfo& li, int nq) {
+    const int64_t bps = li.dense ? kMaxBlocksPerSplit : kMaxBlocksPerSplit / std::max(1, nq);
+    return static_cast<int64_t>(kMaxSplits) * bps * kTile;
+}
+
 struct WorkspaceLayout {
-    size_t P = 0, stats = 0, ml = 0, acc = 0, total = 0;
+    size_t P = 0, stats = 0, ml = 0, acc = 0, fill = 0, total = 0;
     int S = 1, tps = 1, nblk = 1;
     ScorePlan sp;
     ValuePlan vp;
@@ -329,6 +338,8 @@ WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, in
     off += align_up(static_cast<size_t>(B) * w.S * li.H * 2 * sizeof(float));
     w.acc = off;
     off += align_up(static_cast<size_t>(B) * w.S * li.H * li.rv * sizeof(float));
+    w.fill = off;                       // per query row: its cache sequence's fill (mixed caches)
+    off += align_up(static_cast<size_t>(B) * sizeof(int32_t));
     w.total = off;
     return w;
 }
@@ -568,6 +579,7 @@ size_t starkv_decode_workspace_bytes(const starkv_layer* layer, int32_t batch, i
     LayerInfo li;
     if (check_layer(layer, &li) != STARKV_OK || batch < 0 || seq_len < 1 || num_splits < 0)
         return 0;
+    if (seq_len > max_decode_len(li, 1)) return 0;
     return workspace_layout(li, batch, seq_len, num_splits).total;
 }
 
@@ -769,8 +781,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     if ((s = check_cache(cache, li)) != STARKV_OK) return s;
     if (seq_len < 1 || num_splits < 0) return STARKV_ERR_SHAPE;
     if (seq_len > cache->capacity) return STARKV_ERR_CAPACITY;
-    if (seq_len > static_cast<int64_t>(kMaxSplits) * kMaxBlocksPerSplit * kTile)
-        return STARKV_ERR_UNSUPPORTED;
+    if (seq_len > max_decode_len(li, nq)) return STARKV_ERR_UNSUPPORTED;
     const int B = rows < 0 ? cache->batch : rows;
     if (B == 0) return STARKV_OK;
     if (cache->batch == 0) return STARKV_ERR_SHAPE;          // query rows but no cache sequence
@@ -854,10 +865,22 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
         q43_layouts(li, &qk, &qv);
         sp.zk_meta = cache->zk_meta;
         sp.zk_tail = cache->zk_tail;
-        sp.full_blocks = static_cast<int>(seq_len / kTile);
         sp.ql = qk;
     }
     const int stream_kind = li.q43 ? -1 : ek;     // -1: mixed 4/3-bit codes, dequantised in-kernel
+    if (li.q43 && seq_map) {
+        // rows mapped to one cache sequence may stop short of its fill: which of its groups are
+        // quantised follows from the longest of them
+        RowFillParams rf;
+        rf.seq_map = seq_map;
+        rf.seq_lens = seq_lens;
+        rf.row_fill = reinterpret_cast<int32_t*>(ws + w.fill);
+        rf.rows = B;
+        rf.cache_batch = cache->batch;
+        rf.max_len = static_cast<int>(seq_len);
+        if ((s = dev(launch_row_fill(rf, st))) != STARKV_OK) return s;
+        sp.row_fill = rf.row_fill;
+    }
     if (ev0 && (s = dev(hipEventRecord(static_cast<hipEvent_t>(ev0), st))) != STARKV_OK) return s;
     if ((s = dev(launch_latent_scores(sp, stream_kind, w.sp.G, w.sp.splits, w.sp.maxks, nq, st))) != STARKV_OK)
         return s;
@@ -883,7 +906,7 @@ static starkv_status decode_impl(const starkv_layer* layer, const starkv_cache* 
     vp.blocks_per_split = w.vp.bps;
     vp.zv_meta = cache->zv_meta;
     vp.zv_tail = cache->zv_tail;
-    vp.full_blocks = static_cast<int>(seq_len / kTile);
+    vp.row_fill = sp.row_fill;
     vp.block_bytes = li.q43 ? qv.block_bytes : 0;
     vp.n_hi = li.q43 ? qv.n_hi : 0;
     if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, nq, st))) != STARKV_OK) return s;
@@ -946,6 +969,7 @@ size_t starkv_decode_multi_workspace_bytes(const starkv_layer* layer, int32_t ba
     if (check_layer(layer, &li) != STARKV_OK || li.dense || batch < 0 || max_len < 1 || num_splits < 0)
         return 0;
     if (nq != 1 && nq != 2 && nq != 4) return 0;
+    if (max_len > max_decode_len(li, nq)) return 0;
     return workspace_layout(li, batch * nq, max_len, num_splits, nq).total;
 }
 
@@ -975,6 +999,7 @@ starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_c
     return decode_impl(layer, cache, seq_len, nullptr, q, bk, bv, out, num_splits, workspace,
                        workspace_bytes, stream, event_begin, event_mid, event_end);
 }
+
 
 starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cache,
                              int64_t seq_len, int64_t t0, int64_t t1, void* zk_out, void* zv_out,

@@ -261,7 +261,10 @@ struct ScoreParams {
     // mixed 4/3-bit key cache only: codes in zk, scales / zero points, binary16 tail rows
     const void* zk_meta;   // [B][cap/64][2][Rk]
     const void* zk_tail;   // [B][64][Rk]
-    int full_blocks;       // blocks [0, full_blocks) are quantised, block full_blocks is the tail
+    // Per query row (or NULL: the row's own length): the longest length among the call's rows
+    // that read the same cache sequence. For a mixed 4/3-bit cache, the sequence's complete
+    // 64-token groups below it are quantised and its partial last group is in the tail buffer.
+    const int32_t* row_fill = nullptr;
     Q43Layout ql;
 };
 
@@ -279,8 +282,16 @@ struct ValueParams {
     // mixed 4/3-bit value cache only
     const void* zv_meta;   // [B][cap/64][2][rv]
     const void* zv_tail;   // [B][64][rv]
-    int full_blocks;
+    const int32_t* row_fill = nullptr;   // as in ScoreParams
     int block_bytes, n_hi;
+};
+
+// row_fill[i] = the largest clamped length among rows that read the same cache sequence as row i
+struct RowFillParams {
+    const int32_t* seq_map;
+    const int32_t* seq_lens;
+    int32_t* row_fill;
+    int rows, cache_batch, max_len;
 };
 
 struct MergeParams {

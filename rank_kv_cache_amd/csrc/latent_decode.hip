@@ -150,7 +150,10 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
     const int Tp = p.Tp;
     const int nblk = p.nblk;                                     // stride of the statistics
     const int my_nblk = (seq_len + 63) >> 6;
-    const int full_blocks = QK ? seq_len >> 6 : my_nblk;         // quantised groups (mixed cache)
+    // quantised groups of a mixed cache: the complete groups below the sequence's fill (the
+    // longest length of the rows that read it; the rows of this workgroup, else row_fill)
+    const int fill = (QK && p.row_fill) ? max(seq_len, p.row_fill[row0]) : seq_len;
+    const int full_blocks = QK ? fill >> 6 : my_nblk;
     const float q_scale = p.q_scale;
     const T* __restrict__ zk = static_cast<const T*>(p.zk);
     const T* __restrict__ bkg = static_cast<const T*>(p.bk);
@@ -676,7 +679,8 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     }
     // mixed cache: blocks [blk_begin, main_end) are quantised; a block main_end < blk_end is the
     // partial last group, read from the binary16 tail
-    const int main_end = QV ? max(blk_begin, min(blk_end, seq_len >> 6)) : blk_end;
+    const int fill = (QV && p.row_fill) ? max(seq_len, p.row_fill[row0]) : seq_len;
+    const int main_end = QV ? max(blk_begin, min(blk_end, fill >> 6)) : blk_end;
 
     auto load_blk = [&](typename PF::Raw (&pr)[NQ][4], Buf& z, int blk) __attribute__((always_inline)) {
 #pragma unroll
@@ -1023,6 +1027,24 @@ hipError_t launch_latent_values(const ValueParams& p, int elem, int chunks, int 
 hipError_t launch_merge(const MergeParams& p, hipStream_t st) {
     const long long n = (long long)p.B * p.H * (p.W / 4);
     hipLaunchKernelGGL(merge_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// One thread per query row: the largest clamped length among the rows that read its cache
+// sequence (rows <= a few thousand, so the quadratic scan is a few microseconds at most).
+__global__ __launch_bounds__(256) void row_fill_max(const RowFillParams p) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= p.rows) return;
+    const int mine = cache_seq(p.seq_map, i, p.cache_batch);
+    int m = 0;
+    for (int r = 0; r < p.rows; ++r)
+        if (cache_seq(p.seq_map, r, p.cache_batch) == mine) m = max(m, seq_length(p.seq_lens, r, p.max_len));
+    p.row_fill[i] = m;
+}
+
+hipError_t launch_row_fill(const RowFillParams& p, hipStream_t st) {
+    if (p.rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(row_fill_max, dim3((p.rows + 255) / 256), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -81,6 +81,7 @@ class Workload:
     fixed_key_rank: int = 0          # ... or all heads use this rank
     power: float = 0.0               # column std exponent (0 -> i.i.d.)
     quantized: bool = False          # cache stored as mixed 4/3-bit codes after rotation
+    q_top_fraction: float = 0.25     # quantised caches: leading channels stored at 4 bits
     rope_base: float = 10000.0
     description: str = ""
 
@@ -105,6 +106,29 @@ WORKLOADS = {
         layer_seed=1, cache_seed=3, value_rank=1024, key_rank_choices=(16, 32, 48, 64), power=0.5,
         quantized=True,
         description="same layer, T=16384, latents rotated + mixed 4/3-bit (top 25% at 4 bits)"),
+    # the same layer at the context lengths where the pages compare cache formats (8K, 16K):
+    # binary16 latents, the mixed 4/3-bit cache and a uniform 4-bit cache (top fraction 1)
+    "longchat_b16_t8192_f16": Workload(
+        "longchat_b16_t8192_f16", batch=16, heads=32, head_dim=128, seq_len=8192, dtype="f16",
+        layer_seed=1, cache_seed=5, value_rank=1024, key_rank_choices=(16, 32, 48, 64), power=0.5,
+        description="same layer, T=8192, binary16 latents"),
+    "longchat_b16_t16384_f16": Workload(
+        "longchat_b16_t16384_f16", batch=16, heads=32, head_dim=128, seq_len=16384, dtype="f16",
+        layer_seed=1, cache_seed=3, value_rank=1024, key_rank_choices=(16, 32, 48, 64), power=0.5,
+        description="same layer and latents as the T=16384 quantised workload, binary16 latents"),
+    "longchat_b16_t8192_q43": Workload(
+        "longchat_b16_t8192_q43", batch=16, heads=32, head_dim=128, seq_len=8192, dtype="f16",
+        layer_seed=1, cache_seed=5, value_rank=1024, key_rank_choices=(16, 32, 48, 64), power=0.5,
+        quantized=True, description="same layer, T=8192, rotated, mixed 4/3-bit"),
+    "longchat_b16_t8192_q4": Workload(
+        "longchat_b16_t8192_q4", batch=16, heads=32, head_dim=128, seq_len=8192, dtype="f16",
+        layer_seed=1, cache_seed=5, value_rank=1024, key_rank_choices=(16, 32, 48, 64), power=0.5,
+        quantized=True, q_top_fraction=1.0, description="same layer, T=8192, rotated, uniform 4-bit"),
+    "longchat_b16_t16384_q4": Workload(
+        "longchat_b16_t16384_q4", batch=16, heads=32, head_dim=128, seq_len=16384, dtype="f16",
+        layer_seed=1, cache_seed=3, value_rank=1024, key_rank_choices=(16, 32, 48, 64), power=0.5,
+        quantized=True, q_top_fraction=1.0,
+        description="same layer and latents as the T=16384 quantised workload, uniform 4-bit"),
 }
 
 # The 32-layer model step: batch 32, T 8192, layers 0, 1 and 31 dense fp16.

@@ -275,3 +275,25 @@ def test_multi_validation():
     assert sk.starkv_decode_multi_workspace_bytes(L, 2, 3, 100) == 0
     a = sk.starkv_decode_multi_workspace_bytes(L, 2, 4, 1000)
     assert a > sk.starkv_decode_workspace_bytes(L, 2, 1000) and a % 256 == 0
+
+
+def test_decode_length_limits():
+    """At most 256 splits of at most 256 / nq blocks of 64 tokens (the value kernel's per-split
+    table holds 2 * 256 / nq tile factors per query row and head): longer requests are
+    UNSUPPORTED and their workspace size is 0, before anything is enqueued."""
+    L = _latent()
+    big = _cache(capacity=1 << 23)
+    full = 256 * 256 * 64                                    # 4,194,304 tokens
+    mu = lambda nq, mx: sk.starkv_decode_attn_multi(L, big, nq, mx, None, FAKE, FAKE, FAKE, FAKE, 0,
+                                                    FAKE, 1 << 50, check=False)
+    for nq in (1, 2, 4):
+        lim = full // nq
+        assert sk.starkv_decode_multi_workspace_bytes(L, 2, nq, lim) > 0
+        assert sk.starkv_decode_multi_workspace_bytes(L, 2, nq, lim + 1) == 0
+        assert mu(nq, lim + 1) == 8
+    assert st_decode(L, big, seq_len=full + 1, nws=1 << 50) == 8
+    assert sk.starkv_decode_workspace_bytes(L, 2, full) > 0
+    assert sk.starkv_decode_workspace_bytes(L, 2, full + 1) == 0
+    dense = sk.Layer(num_heads=4, head_dim=128, dense=True, cache_dtype=sk.F16)
+    assert st_decode(dense, big, seq_len=full + 1, nws=1 << 50) == 8
+

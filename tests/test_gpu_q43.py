@@ -187,11 +187,25 @@ def test_q43_decode_parity_rotated():
             assert np.all(np.isfinite(got)) and e <= 2e-3
 
 
+def _device_rotate(L, which, kind, n, x16):
+    import torch
+    from rank_kv_cache_amd import buffers
+    src = buffers.to_device(x16)
+    dst = torch.empty(src.shape, dtype=torch.float16, device="cuda")
+    sk.starkv_hadamard_rotate(L, which, kind, n, src, dst)
+    del src
+    return dst
+
+
 def test_q43_decode_full_size_sampled():
     """The quantised LongChat-shaped workload at full size (B=16, T=16384) in the library's
-    default launch configuration; the oracle evaluates sampled (sequence, head) pairs on its own
-    dequantisation of the same rows. (Latents are not rotated here: the rotation is absorbed into
-    the factors offline and does not reach the kernels.)"""
+    default launch configuration, on blockwise-Hadamard-rotated latents and factors as the
+    quantised configuration specifies (Zhou notes, section 6.1 and Fig. 5: rotate, then quantise).
+    The GPU side rotates every row with the device rotation; the oracle rotates the sampled
+    sequences itself, and the two rotations must agree bit for bit on them. The oracle then
+    evaluates sampled (sequence, head) pairs on its own quantisation and dequantisation of its
+    own rotated rows."""
+    import torch
     from rank_kv_cache_amd import buffers
     from gpu_support import rel_err
     w = synth.WORKLOADS["longchat_b16_t16384_q43"]
@@ -199,17 +213,38 @@ def test_q43_decode_full_size_sampled():
     zk, zv = synth.draw_latent_cache(w, ld)
     q = synth.draw_queries(w.cache_seed, 0, w.batch, w.heads, w.head_dim)
     ranks, rv = ld.key_ranks, ld.value_rank
-    L = q43_layer(w.heads, w.head_dim, ranks, rv)
-    cache = buffers.alloc_cache(L, w.batch, w.seq_len)
-    _append(L, cache, zk, zv, [w.seq_len])
-    got = _gpu_decode(L, cache, w.seq_len, q, ld.bk, ld.bv)
+    B, T, H, d = w.batch, w.seq_len, w.heads, w.head_dim
+    L = q43_layer(H, d, ranks, rv)
+    seg_k = oracle.latent_segments(ranks, FRAC)
+    seg_v = oracle.latent_segments([rv], FRAC)
+    dzk = _device_rotate(L, 0, 0, B * T, zk)
+    dzv = _device_rotate(L, 1, 0, B * T, zv)
+    dbk = _device_rotate(L, 0, 1, d, ld.bk)
+    dbv = _device_rotate(L, 1, 1, H * d, ld.bv)
+    cache = buffers.alloc_cache(L, B, T)
+    sk.starkv_append_latents(L, cache, 0, T, dzk, dzv)
+    out = torch.full((B, H, d), float("nan"), dtype=torch.float32, device="cuda")
+    ws, nws = buffers.alloc_workspace(L, B, T, 0)
+    sk.starkv_decode_attn(L, cache, T, buffers.to_device(q), dbk, dbv, out, 0, ws, nws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    sel_b = [0, B - 1]
+    zk_r = oracle.rotate_rows(zk[sel_b], seg_k)
+    zv_r = oracle.rotate_rows(zv[sel_b], seg_v)
+    bk_r = oracle.rotate_factor(ld.bk, seg_k)
+    bv_r = oracle.rotate_factor(ld.bv, seg_v)
+    for dev, host in ((dzk, zk_r), (dzv, zv_r)):
+        assert np.array_equal(buffers.to_host(dev[sel_b]).view(np.uint16), host.view(np.uint16))
+    assert np.array_equal(buffers.to_host(dbk).view(np.uint16), bk_r.view(np.uint16))
+    assert np.array_equal(buffers.to_host(dbv).view(np.uint16), bv_r.view(np.uint16))
+    del dzk, dzv
     rng = np.random.default_rng(7)
-    sel_b = [0, w.batch - 1]
-    pairs = [(0, 0), (1, w.heads - 1)] + [(int(rng.integers(0, 2)), int(h)) for h in rng.integers(0, w.heads, 6)]
-    ref = _q43_reference(ld, zk[sel_b], zv[sel_b], q[sel_b], ranks, rv, w.seq_len, w.seq_len, pairs=pairs)
+    pairs = [(0, 0), (1, H - 1)] + [(int(rng.integers(0, 2)), int(h)) for h in rng.integers(0, H, 6)]
+    ld.bk, ld.bv = bk_r, bv_r
+    ref = _q43_reference(ld, zk_r, zv_r, q[sel_b], ranks, rv, T, T, pairs=pairs)
     sub = np.stack([got[sel_b[b], h] for b, h in pairs])
     e = rel_err(sub, ref)
-    say(f"[q43 full] sampled {len(pairs)} pairs rel err {e:.3e}")
+    say(f"[q43 full, rotated] sampled {len(pairs)} pairs rel err {e:.3e}")
     assert np.all(np.isfinite(got)) and e <= 2e-3
 
 
