@@ -121,3 +121,42 @@ def test_queries_q43():
         return oracle.decode_latent(dk, dv, ld.bk, ld.bv, q[i:i + 1], ranks)[0]
 
     _check(qseq, qlen, got, ref, "q43")
+
+
+def test_queries_q43_causal_across_group():
+    """Speculative verification on a mixed 4/3-bit cache with causal lengths that cross a 64-token
+    group boundary: rows shorter than their sequence's fill end inside a group that is already
+    quantised (the longest row of the sequence reaches the fill, whose partial last group is in
+    the tail). The oracle quantises the sequence up to its fill and truncates to each row."""
+    from test_gpu_q43 import _append, q43_layer
+    from rank_kv_cache_amd import buffers
+    H, d, B, T, cap = 3, 128, 2, 150, 192
+    ranks, rv = [16, 64, 32], 96
+    w = synth.Workload("mqx", batch=B, heads=H, head_dim=d, seq_len=T, dtype="f16", layer_seed=241,
+                       cache_seed=242, value_rank=rv, power=0.5)
+    ld = synth.draw_layer(w, key_ranks=ranks)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    L = q43_layer(H, d, ranks, rv)
+    cache = buffers.alloc_cache(L, B, cap, fill=0xFF)
+    _append(L, cache, zk, zv, [T])
+    bits_k, bits_v = oracle.channel_bits(ranks, FRAC), oracle.channel_bits([rv], FRAC)
+    qseq, qlen = [], []
+    for n in (150, 131, 129, 128, 127, 126, 100, 65, 63):
+        for b in range(B):
+            qseq.append(b)
+            qlen.append(n)
+    order = np.random.default_rng(243).permutation(len(qseq))
+    qseq, qlen = [qseq[i] for i in order], [qlen[i] for i in order]
+    q = np.random.default_rng(244).standard_normal((len(qseq), H, d)).astype(np.float32)
+    full = {}
+    for b in range(B):
+        ck, mk, tk = oracle.q43_pack(zk[b:b + 1], bits_k, cap)
+        cv, mv, tv = oracle.q43_pack(zv[b:b + 1], bits_v, cap)
+        full[b] = (oracle.q43_unpack(ck, mk, tk, bits_k, T, cap),
+                   oracle.q43_unpack(cv, mv, tv, bits_v, T, cap))
+    for S in (0, 2):
+        got = _queries(L, cache, qseq, qlen, q, ld.bk, ld.bv, S)
+        _check(qseq, qlen, got,
+               lambda i, b, n: oracle.decode_latent(full[b][0][:, :n], full[b][1][:, :n], ld.bk,
+                                                    ld.bv, q[i:i + 1], ranks)[0],
+               f"q43 across group, splits={S}")
