@@ -273,6 +273,26 @@ starkv_status starkv_decode_attn_timed(const starkv_layer *layer, const starkv_c
                                        void *event_begin, void *event_mid, void *event_end);
 
 /*
+ * starkv_decode_attn without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). Same
+ * arguments, validation, kernels and results as starkv_decode_attn with the same num_splits; the
+ * workspace is a fixed device array of starkv_decode_attn_noalloc_max_bytes() bytes (64 MiB)
+ * inside the library, one per GPU, looked up on the device current at the call (make the
+ * stream's device current), and held until the process ends. Nothing is allocated or freed and
+ * nothing needs to start at zero. Every call on a GPU shares that GPU's array, which keeps the
+ * last call's contents: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.
+ * Errors: those of starkv_decode_attn; WORKSPACE when starkv_decode_workspace_bytes(layer, batch,
+ * seq_len, num_splits) exceeds the maximum (e.g. batch 16, 32 heads, r_v 1024 fits up to about
+ * 43,000 tokens); DEVICE if the array's device address cannot be found.
+ */
+size_t starkv_decode_attn_noalloc_max_bytes(void);
+starkv_status starkv_decode_attn_noalloc(const starkv_layer *layer, const starkv_cache *cache,
+                                         int64_t seq_len, const float *q, const void *bk,
+                                         const void *bv, float *out, int32_t num_splits,
+                                         void *stream);
+
+/*
  * Read cached tokens [t0, t1) back in token-major order (the dequantisation step of the decode
  * path: Zhou notes, section 6.1, which stores the cache as per-channel asymmetric 4/3-bit codes
  * with fp16 scales and zero points per group of 64 tokens, and Algorithm 2 step 4a, which

@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decod
                     "starkv_decode_attn_ragged", "starkv_append_latents_ragged",
                     "starkv_decode_attn_queries", "starkv_decode_attn_multi",
                     "starkv_decode_multi_workspace_bytes",
+                    "starkv_decode_attn_noalloc", "starkv_decode_attn_noalloc_max_bytes",
                     "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +93,10 @@ def lib():
         L.starkv_decode_workspace_bytes.argtypes = [LP, i32, i64, i32]
         L.starkv_decode_attn.restype = C.c_int
         L.starkv_decode_attn.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.starkv_decode_attn_noalloc.restype = C.c_int
+        L.starkv_decode_attn_noalloc.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp]
+        L.starkv_decode_attn_noalloc_max_bytes.restype = sz
+        L.starkv_decode_attn_noalloc_max_bytes.argtypes = []
         L.starkv_decode_attn_ragged.restype = C.c_int
         L.starkv_decode_attn_ragged.argtypes = [LP, CP, i64, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         L.starkv_decode_attn_queries.restype = C.c_int
@@ -241,6 +246,20 @@ def starkv_decode_attn(layer, cache, seq_len, q, bk, bv, out, num_splits=0, work
                                   int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "starkv_decode_attn")
+    return st
+
+
+def starkv_decode_attn_noalloc_max_bytes() -> int:
+    return int(lib().starkv_decode_attn_noalloc_max_bytes())
+
+
+def starkv_decode_attn_noalloc(layer, cache, seq_len, q, bk, bv, out, num_splits=0, stream=None,
+                               check=True):
+    st = lib().starkv_decode_attn_noalloc(_layer_ptr(layer), _cache_ptr(cache), seq_len, _ptr(q),
+                                          _ptr(bk), _ptr(bv), _ptr(out), num_splits,
+                                          _stream(stream))
+    if check:
+        _check(st, "starkv_decode_attn_noalloc")
     return st
 
 

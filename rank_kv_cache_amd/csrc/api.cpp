@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "common.hpp"
@@ -1000,6 +1001,60 @@ starkv_status starkv_decode_attn_timed(const starkv_layer* layer, const starkv_c
                        workspace_bytes, stream, event_begin, event_mid, event_end);
 }
 
+// ------------------------------------------------------------------------------------------------
+// Decode without a caller workspace: for callers that cannot allocate device memory (code under
+// graph capture, tight serving loops). The workspace is a fixed array in device memory, one per
+// GPU, held until the process ends; calls on one GPU share it.
+// ------------------------------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device. (In host code
+// the array's name is only a stand-in for the symbol; its device address comes from the runtime.)
+starkv_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return STARKV_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return STARKV_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return STARKV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t starkv_decode_attn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+starkv_status starkv_decode_attn_noalloc(const starkv_layer* layer, const starkv_cache* cache,
+                                         int64_t seq_len, const float* q, const void* bk,
+                                         const void* bv, float* out, int32_t num_splits,
+                                         void* stream) {
+    // a request whose workspace would not fit is refused before anything else is touched;
+    // requests sized 0 (invalid, beyond the planner's limits, or an empty batch) get their status
+    // from the shared validation without the array
+    const int32_t batch = cache ? cache->batch : 0;
+    const size_t need = layer ? starkv_decode_workspace_bytes(layer, batch, seq_len, num_splits) : 0;
+    if (need > kScratchBytes) return STARKV_ERR_WORKSPACE;
+    if (need == 0)
+        return decode_impl(layer, cache, seq_len, nullptr, q, bk, bv, out, num_splits, nullptr, 0,
+                           stream, nullptr, nullptr, nullptr);
+    void* ws = nullptr;
+    const starkv_status s = scratch_of_current_device(&ws);
+    if (s != STARKV_OK) return s;
+    return decode_impl(layer, cache, seq_len, nullptr, q, bk, bv, out, num_splits, ws,
+                       kScratchBytes, stream, nullptr, nullptr, nullptr);
+}
 
 starkv_status starkv_dequant(const starkv_layer* layer, const starkv_cache* cache,
                              int64_t seq_len, int64_t t0, int64_t t1, void* zk_out, void* zv_out,

@@ -297,3 +297,18 @@ def test_decode_length_limits():
     dense = sk.Layer(num_heads=4, head_dim=128, dense=True, cache_dtype=sk.F16)
     assert st_decode(dense, big, seq_len=full + 1, nws=1 << 50) == 8
 
+
+def test_noalloc_validation():
+    """The no-allocation decode refuses requests whose workspace exceeds its fixed array, and
+    invalid ones with the shared validation's status, before any device work (and before it
+    looks up the array's device address)."""
+    L = _latent(num_heads=32, key_ranks=(64,) * 32, value_rank=2048)
+    big = _cache(batch=64, capacity=1 << 16)
+    assert sk.starkv_decode_attn_noalloc_max_bytes() == 64 << 20
+    assert sk.starkv_decode_workspace_bytes(L, 64, 1 << 16, 0) > 64 << 20
+    na = lambda L=L, Cc=big, T=1 << 16: sk.starkv_decode_attn_noalloc(L, Cc, T, FAKE, FAKE, FAKE,
+                                                                      FAKE, 0, check=False)
+    assert na() == 7
+    assert na(Cc=_cache(batch=64, capacity=1 << 23), T=(1 << 22) + 64) == 8   # beyond the planner
+    assert na(L=None) == 1 and na(Cc=None) == 1 and na(T=0) == 2
+    assert na(Cc=_cache(batch=0), T=100) == 0                                    # nothing to do
