@@ -273,6 +273,55 @@ starkv_status starkv_decode_attn_timed(const starkv_layer *layer, const starkv_c
                                        void *event_begin, void *event_mid, void *event_end);
 
 /*
+ * Decode attention followed by the output projection, in one call (Zhou notes, Algorithm 2 steps
+ * 4-8; section 5.3 applies W_o after the latent value sum): y[b] = concat_h(out[b][h]) . W_o with
+ * out as starkv_decode_attn computes it. wo, hidden: as starkv_output_projection (output-major
+ * [hidden][H*d], the layer's factor type). y: [batch][hidden] fp32. The heads' outputs stay in the
+ * workspace (starkv_decode_attn_project_workspace_bytes(layer, batch, seq_len, num_splits,
+ * hidden)); W_o is read once per call. Results are bit for bit those of starkv_decode_attn
+ * followed by starkv_output_projection. Errors: those of both calls, checked before anything is
+ * enqueued.
+ */
+size_t starkv_decode_attn_project_workspace_bytes(const starkv_layer *layer, int32_t batch,
+                                                  int64_t seq_len, int32_t num_splits,
+                                                  int32_t hidden);
+starkv_status starkv_decode_attn_project(const starkv_layer *layer, const starkv_cache *cache,
+                                         int64_t seq_len, const float *q, const void *bk,
+                                         const void *bv, const void *wo, int32_t hidden, float *y,
+                                         int32_t num_splits, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/*
+ * Prefill: a chunk of causal queries per sequence attends to the latent cache (a prompt chunk or
+ * a long speculative draft; Zhou notes, Algorithm 2 steps 4-7 for every query of the chunk,
+ * section 5.3 for the latent values; the model card times such a prefill kernel beside its decode
+ * kernel). Query l of sequence b sits at position pos0 + l and attends to cached tokens
+ * [0, pos0 + l] (its own token included): the chunk's latents must already be appended.
+ *   chunk_lens: NULL (every sequence has `chunk` queries) or a device int32 array of batch chunk
+ *     lengths (4-byte aligned, clamped to [0, chunk]); rows l >= chunk_lens[b] are empty (zero
+ *     output).
+ *   q:   [B][chunk][H][d] fp32, each query already rotated to its own position.
+ *   bk, bv: as starkv_decode_attn.
+ *   out: [B][chunk][H][d] fp32, per-head outputs before the output projection.
+ * The key side runs query tiles on the matrix cores (keys rebuilt per 32-token tile, rotated in
+ * fp32, query-key products as binary16 hi/lo parts); the value side sums probabilities times the
+ * value latent for all heads of up to four queries at once, then applies B_v per head. Latent
+ * layers with F16, BF16 or Q43 caches (Q43: sequence b must hold pos0 + chunk_lens[b] appended
+ * tokens, or a multiple of 64 not above that). The workspace is
+ * starkv_prefill_workspace_bytes(layer, batch, pos0, chunk) (0 for invalid or unsupported
+ * requests); contents on entry are ignored.
+ * Errors: NULL, SHAPE (pos0 < 0, chunk < 1), CAPACITY (pos0 + chunk > capacity), DTYPE,
+ * MISALIGNED, WORKSPACE, UNSUPPORTED (dense or F32 layers; pos0 + chunk above the decode length
+ * limit for the query grouping). batch == 0 returns OK without enqueuing.
+ */
+size_t starkv_prefill_workspace_bytes(const starkv_layer *layer, int32_t batch, int64_t pos0,
+                                      int32_t chunk);
+starkv_status starkv_prefill_attn(const starkv_layer *layer, const starkv_cache *cache, int64_t pos0,
+                                  int32_t chunk, const int32_t *chunk_lens, const float *q,
+                                  const void *bk, const void *bv, float *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * starkv_decode_attn without a caller workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). Same
  * arguments, validation, kernels and results as starkv_decode_attn with the same num_splits; the

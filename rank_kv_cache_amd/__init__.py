@@ -39,6 +39,8 @@ EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decod
                     "starkv_decode_attn_queries", "starkv_decode_attn_multi",
                     "starkv_decode_multi_workspace_bytes",
                     "starkv_decode_attn_noalloc", "starkv_decode_attn_noalloc_max_bytes",
+                    "starkv_prefill_attn", "starkv_prefill_workspace_bytes",
+                    "starkv_decode_attn_project", "starkv_decode_attn_project_workspace_bytes",
                     "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +95,14 @@ def lib():
         L.starkv_decode_workspace_bytes.argtypes = [LP, i32, i64, i32]
         L.starkv_decode_attn.restype = C.c_int
         L.starkv_decode_attn.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.starkv_decode_attn_project_workspace_bytes.restype = sz
+        L.starkv_decode_attn_project_workspace_bytes.argtypes = [LP, i32, i64, i32, i32]
+        L.starkv_decode_attn_project.restype = C.c_int
+        L.starkv_decode_attn_project.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp, i32, vp, sz, vp]
+        L.starkv_prefill_workspace_bytes.restype = sz
+        L.starkv_prefill_workspace_bytes.argtypes = [LP, i32, i64, i32]
+        L.starkv_prefill_attn.restype = C.c_int
+        L.starkv_prefill_attn.argtypes = [LP, CP, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.starkv_decode_attn_noalloc.restype = C.c_int
         L.starkv_decode_attn_noalloc.argtypes = [LP, CP, i64, vp, vp, vp, vp, i32, vp]
         L.starkv_decode_attn_noalloc_max_bytes.restype = sz
@@ -246,6 +256,35 @@ def starkv_decode_attn(layer, cache, seq_len, q, bk, bv, out, num_splits=0, work
                                   int(workspace_bytes), _stream(stream))
     if check:
         _check(st, "starkv_decode_attn")
+    return st
+
+
+def starkv_decode_attn_project_workspace_bytes(layer, batch, seq_len, num_splits, hidden) -> int:
+    return int(lib().starkv_decode_attn_project_workspace_bytes(_layer_ptr(layer), batch, seq_len,
+                                                                num_splits, hidden))
+
+
+def starkv_decode_attn_project(layer, cache, seq_len, q, bk, bv, wo, hidden, y, num_splits=0,
+                               workspace=None, workspace_bytes=0, stream=None, check=True):
+    st = lib().starkv_decode_attn_project(_layer_ptr(layer), _cache_ptr(cache), seq_len, _ptr(q),
+                                          _ptr(bk), _ptr(bv), _ptr(wo), hidden, _ptr(y), num_splits,
+                                          _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "starkv_decode_attn_project")
+    return st
+
+
+def starkv_prefill_workspace_bytes(layer, batch, pos0, chunk) -> int:
+    return int(lib().starkv_prefill_workspace_bytes(_layer_ptr(layer), batch, pos0, chunk))
+
+
+def starkv_prefill_attn(layer, cache, pos0, chunk, chunk_lens, q, bk, bv, out, workspace=None,
+                        workspace_bytes=0, stream=None, check=True):
+    st = lib().starkv_prefill_attn(_layer_ptr(layer), _cache_ptr(cache), pos0, chunk,
+                                   _ptr(chunk_lens), _ptr(q), _ptr(bk), _ptr(bv), _ptr(out),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check:
+        _check(st, "starkv_prefill_attn")
     return st
 
 

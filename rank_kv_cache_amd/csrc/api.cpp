@@ -26,6 +26,8 @@ hipError_t launch_linear_store(const LinearStoreParams& p, int elem, hipStream_t
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_row_fill(const RowFillParams& p, hipStream_t st);
+hipError_t launch_prefill_scores(const PrefillParams& p, int elem, hipStream_t st);
+hipError_t launch_prefill_rows(const PrefillRowsParams& p, hipStream_t st);
 hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
@@ -343,6 +345,31 @@ WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, in
     off += align_up(static_cast<size_t>(B) * sizeof(int32_t));
     w.total = off;
     return w;
+}
+
+// Prefill: query rows b * chunk + l, grouped nq at a time for the value kernel (4, 2 or 1: the
+// largest that divides the chunk, so that no group straddles two sequences); the decode workspace
+// of those rows plus per-row lengths, per-row fills and the group-to-sequence map.
+struct PrefillLayout {
+    WorkspaceLayout w;
+    int nq = 1, rows = 0;
+    size_t row_len = 0, row_fill = 0, group_seq = 0, total = 0;
+};
+
+PrefillLayout prefill_layout(const LayerInfo& li, int B, int64_t pos0, int chunk) {
+    PrefillLayout pl;
+    pl.nq = chunk % 4 == 0 ? 4 : chunk % 2 == 0 ? 2 : 1;
+    pl.rows = B * chunk;
+    pl.w = workspace_layout(li, pl.rows, pos0 + chunk, 0, pl.nq);
+    size_t off = pl.w.total;
+    pl.row_len = off;
+    off += align_up(static_cast<size_t>(pl.rows) * sizeof(int32_t));
+    pl.row_fill = off;
+    off += align_up(static_cast<size_t>(pl.rows) * sizeof(int32_t));
+    pl.group_seq = off;
+    off += align_up(static_cast<size_t>(pl.rows / pl.nq) * sizeof(int32_t));
+    pl.total = off;
+    return pl;
 }
 
 void fill_rope(double base, int D, double* rev) {
@@ -964,6 +991,136 @@ starkv_status starkv_decode_attn_queries(const starkv_layer* layer, const starkv
                        workspace_bytes, stream, nullptr, nullptr, nullptr, num_queries, query_seq);
 }
 
+// ------------------------------------------------------------------------------------------------
+// Prefill: a chunk of causal queries per sequence.
+// ------------------------------------------------------------------------------------------------
+static starkv_status prefill_check(const starkv_layer* layer, int32_t batch, int64_t pos0,
+                                   int32_t chunk, LayerInfo* li) {
+    starkv_status s = check_layer(layer, li);
+    if (s != STARKV_OK) return s;
+    if (batch < 0 || pos0 < 0 || chunk < 1) return STARKV_ERR_SHAPE;
+    if (li->dense || li->cache_dt == STARKV_F32) return STARKV_ERR_UNSUPPORTED;
+    const PrefillLayout pl = prefill_layout(*li, batch, pos0, chunk);
+    if (pos0 + chunk > max_decode_len(*li, pl.nq)) return STARKV_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(batch) * chunk > (int64_t{1} << 30)) return STARKV_ERR_UNSUPPORTED;
+    return STARKV_OK;
+}
+
+size_t starkv_prefill_workspace_bytes(const starkv_layer* layer, int32_t batch, int64_t pos0,
+                                      int32_t chunk) {
+    LayerInfo li;
+    if (prefill_check(layer, batch, pos0, chunk, &li) != STARKV_OK) return 0;
+    return prefill_layout(li, batch, pos0, chunk).total;
+}
+
+starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache* cache, int64_t pos0,
+                                  int32_t chunk, const int32_t* chunk_lens, const float* q,
+                                  const void* bk, const void* bv, float* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    LayerInfo li;
+    if (!cache) return STARKV_ERR_NULL;
+    starkv_status s = prefill_check(layer, cache->batch, pos0, chunk, &li);
+    if (s != STARKV_OK) return s;
+    if ((s = check_cache(cache, li)) != STARKV_OK) return s;
+    if (pos0 + chunk > cache->capacity) return STARKV_ERR_CAPACITY;
+    const int B = cache->batch;
+    if (B == 0) return STARKV_OK;
+    if (!q || !out || !bk || !bv) return STARKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(bk) || !aligned16(bv)) return STARKV_ERR_MISALIGNED;
+    if (chunk_lens && (reinterpret_cast<uintptr_t>(chunk_lens) & 3)) return STARKV_ERR_MISALIGNED;
+    const PrefillLayout pl = prefill_layout(li, B, pos0, chunk);
+    if (!workspace || workspace_bytes < pl.total) return STARKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return STARKV_ERR_MISALIGNED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const WorkspaceLayout& w = pl.w;
+    const int ek = elem_kind(li.cache_dt);
+    const int stream_kind = li.q43 ? -1 : ek;
+
+    PrefillRowsParams rp;
+    rp.chunk_lens = chunk_lens;
+    rp.row_len = reinterpret_cast<int32_t*>(ws + pl.row_len);
+    rp.row_fill = reinterpret_cast<int32_t*>(ws + pl.row_fill);
+    rp.group_seq = reinterpret_cast<int32_t*>(ws + pl.group_seq);
+    rp.B = B;
+    rp.chunk = chunk;
+    rp.pos0 = static_cast<int>(pos0);
+    rp.nq = pl.nq;
+    if ((s = dev(launch_prefill_rows(rp, st))) != STARKV_OK) return s;
+
+    PrefillParams pp;
+    std::memset(&pp, 0, sizeof(pp));
+    pp.zk = cache->zk;
+    pp.bk = bk;
+    pp.q = q;
+    pp.P = ws + w.P;
+    pp.stats = reinterpret_cast<float*>(ws + w.stats);
+    pp.chunk_lens = chunk_lens;
+    pp.B = B;
+    pp.H = li.H;
+    pp.D = li.D;
+    pp.Rk = li.Rk;
+    pp.nblk_cap = cache->capacity / kTile;
+    pp.chunk = chunk;
+    pp.pos0 = static_cast<int>(pos0);
+    pp.nblk = w.nblk;
+    pp.Tp = w.nblk * kTile;
+    pp.pages = pages_of(cache);
+    pp.q_scale = q_scale_of(layer, li.D);
+    for (int h = 0; h <= li.H; ++h) pp.koff[h] = li.koff[h];
+    for (int h = 0; h < li.H; ++h) pp.rank[h] = li.rank[h];
+    for (int h = 0; h <= li.H; ++h) pp.soff[h] = li.soff[h];
+    for (int h = 0; h < li.H; ++h) pp.srank[h] = li.srank[h];
+    fill_rope(layer->rope_base, li.D, pp.rope_rev);
+    Q43Layout qk, qv;
+    if (li.q43) {
+        q43_layouts(li, &qk, &qv);
+        pp.zk_meta = cache->zk_meta;
+        pp.zk_tail = cache->zk_tail;
+        pp.ql = qk;
+    }
+    if ((s = dev(launch_prefill_scores(pp, stream_kind, st))) != STARKV_OK) return s;
+
+    ValueParams vp;
+    vp.pages = pages_of(cache);
+    vp.zv = cache->zv;
+    vp.P = pp.P;
+    vp.stats = pp.stats;
+    vp.ws_ml = reinterpret_cast<float*>(ws + w.ml);
+    vp.ws_acc = reinterpret_cast<float*>(ws + w.acc);
+    vp.B = pl.rows;
+    vp.H = li.H;
+    vp.rv = li.rv;
+    vp.nblk_cap = pp.nblk_cap;
+    vp.seq_len = static_cast<int>(pos0 + chunk);
+    vp.seq_lens = rp.row_len;
+    vp.seq_map = rp.group_seq;
+    vp.cache_batch = B;
+    vp.nblk = w.nblk;
+    vp.Tp = pp.Tp;
+    vp.S = w.vp.splits;
+    vp.blocks_per_split = w.vp.bps;
+    vp.zv_meta = cache->zv_meta;
+    vp.zv_tail = cache->zv_tail;
+    vp.row_fill = li.q43 ? rp.row_fill : nullptr;
+    vp.block_bytes = li.q43 ? qv.block_bytes : 0;
+    vp.n_hi = li.q43 ? qv.n_hi : 0;
+    if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, pl.nq, st))) != STARKV_OK)
+        return s;
+    ProjectParams pr;
+    pr.ws_ml = vp.ws_ml;
+    pr.ws_acc = vp.ws_acc;
+    pr.S = w.vp.splits;
+    pr.bv = bv;
+    pr.out = out;
+    pr.B = pl.rows;
+    pr.H = li.H;
+    pr.D = li.D;
+    pr.rv = li.rv;
+    pr.rv_src = li.rv_src;
+    return dev(launch_project(pr, ek, st));
+}
+
 size_t starkv_decode_multi_workspace_bytes(const starkv_layer* layer, int32_t batch, int32_t nq,
                                            int64_t max_len, int32_t num_splits) {
     LayerInfo li;
@@ -1219,6 +1376,62 @@ starkv_status starkv_output_projection(const starkv_layer* layer, int32_t batch,
     r.dst1 = y;
     r.part = static_cast<float*>(workspace);
     return run_linear(r, batch, 0, 1, static_cast<hipStream_t>(stream));
+}
+
+// Decode attention and the output projection in one call (Algorithm 2 steps 4-8): the heads'
+// outputs stay in the workspace between the two.
+static size_t decode_project_layout(const starkv_layer* layer, int32_t batch, int64_t seq_len,
+                                    int32_t num_splits, int32_t hidden, size_t* o_off,
+                                    size_t* part_off) {
+    LayerInfo li;
+    if (check_layer(layer, &li) != STARKV_OK || batch < 1 || hidden < 1) return 0;
+    const size_t dec = starkv_decode_workspace_bytes(layer, batch, seq_len, num_splits);
+    if (dec == 0) return 0;
+    const size_t o_bytes = align_up(static_cast<size_t>(batch) * li.H * li.D * sizeof(float));
+    const size_t part = starkv_output_projection_workspace_bytes(layer, batch, hidden);
+    if (part == 0) return 0;
+    *o_off = align_up(dec);
+    *part_off = *o_off + o_bytes;
+    return *part_off + part;
+}
+
+size_t starkv_decode_attn_project_workspace_bytes(const starkv_layer* layer, int32_t batch,
+                                                  int64_t seq_len, int32_t num_splits,
+                                                  int32_t hidden) {
+    size_t o_off = 0, part_off = 0;
+    return decode_project_layout(layer, batch, seq_len, num_splits, hidden, &o_off, &part_off);
+}
+
+starkv_status starkv_decode_attn_project(const starkv_layer* layer, const starkv_cache* cache,
+                                         int64_t seq_len, const float* q, const void* bk,
+                                         const void* bv, const void* wo, int32_t hidden, float* y,
+                                         int32_t num_splits, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    LayerInfo li;
+    starkv_status s = check_layer(layer, &li);
+    if (s != STARKV_OK) return s;
+    if (!cache) return STARKV_ERR_NULL;
+    if (hidden < 1) return STARKV_ERR_SHAPE;
+    if (cache->batch == 0) return STARKV_OK;
+    if (!wo || !y) return STARKV_ERR_NULL;
+    if (!aligned16(wo) || (reinterpret_cast<uintptr_t>(y) & 3)) return STARKV_ERR_MISALIGNED;
+    size_t o_off = 0, part_off = 0;
+    const size_t need = decode_project_layout(layer, cache->batch, seq_len, num_splits, hidden,
+                                              &o_off, &part_off);
+    if (need == 0) {
+        // an invalid decode request: its own validation names the problem
+        return decode_impl(layer, cache, seq_len, nullptr, q, bk, bv, nullptr, num_splits, nullptr, 0,
+                           stream, nullptr, nullptr, nullptr);
+    }
+    if (!workspace || workspace_bytes < need) return STARKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return STARKV_ERR_MISALIGNED;
+    char* ws = static_cast<char*>(workspace);
+    float* o = reinterpret_cast<float*>(ws + o_off);
+    if ((s = decode_impl(layer, cache, seq_len, nullptr, q, bk, bv, o, num_splits, ws, o_off,
+                         stream, nullptr, nullptr, nullptr)) != STARKV_OK)
+        return s;
+    return starkv_output_projection(layer, cache->batch, o, wo, hidden, y, ws + part_off,
+                                    need - part_off, stream);
 }
 
 size_t starkv_append_tokens_workspace_bytes(const starkv_layer* layer, int32_t batch,

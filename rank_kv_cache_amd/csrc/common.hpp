@@ -159,6 +159,39 @@ __device__ __forceinline__ void sincos_rev(float x, float* c, float* s) {
     *s = __builtin_amdgcn_sinf(x);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Eight mixed 4/3-bit key codes of one token (one 16-channel group, channels 8*half .. +7) to an
+// fp16 MFMA operand fragment. w0..w2: the aligned 96-bit window holding the token's row, sh: the
+// row's first bit in the window, n: 4-bit channels at the start of the group; sc / zc: the scales
+// and zero points of the eight channels, two per word. Each value is binary16(q*s + z) rounded
+// once (one fp16 FMA per pair); q is formed exactly as binary16(1024 + q) - 1024.
+__device__ __forceinline__ f16x8 q43_key_frag(uint32_t w0, uint32_t w1, uint32_t w2, int sh, int n,
+                                             int half, const u32x4& sc, const u32x4& zc) {
+    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
+    const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
+    const uint32_t low24 = (half ? __builtin_amdgcn_alignbit(hi, lo, 24) : lo) & 0xffffffu;
+    const int m = min(max(n - 8 * half, 0), 8);
+    const uint32_t ext = (hi >> (16 + 8 * half)) & ((1u << m) - 1u);
+    f16x8 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = 2 * k;
+        const uint32_t q0 = ((low24 >> (3 * e)) & 7u) | (((ext >> e) & 1u) << 3);
+        const uint32_t q1 = ((low24 >> (3 * e + 3)) & 7u) | (((ext >> (e + 1)) & 1u) << 3);
+        const uint32_t bits = 0x64006400u | q0 | (q1 << 16);
+        const f16x2 qv = __builtin_bit_cast(f16x2, bits) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+        // vector elements are copied to scalars first: a bit cast applied directly to an
+        // element of an ext_vector value has been compiled as a cast of element 0
+        const uint32_t sk = sc[k], zk = zc[k];
+        const f16x2 r = __builtin_elementwise_fma(qv, __builtin_bit_cast(f16x2, sk),
+                                                  __builtin_bit_cast(f16x2, zk));
+        out[e] = r[0];
+        out[e + 1] = r[1];
+    }
+    return out;
+}
+
 // ------------------------------------------------------------------------------------------------
 // Parameter blocks (passed by value; each stays well under the 4 KB kernel-argument limit).
 // ------------------------------------------------------------------------------------------------
@@ -284,6 +317,40 @@ struct ValueParams {
     const void* zv_tail;   // [B][64][rv]
     const int32_t* row_fill = nullptr;   // as in ScoreParams
     int block_bytes, n_hi;
+};
+
+// Prefill (a chunk of queries per sequence, causal): the key side. Query l of sequence b is
+// query row b * chunk + l at position pos0 + l and attends to tokens [0, pos0 + l] when
+// l < chunk_len(b) (else it is an empty row). Writes probabilities and 32-token tile statistics
+// in the layout of ScoreParams::P / stats for those rows.
+struct PrefillParams {
+    const void* zk;        // key latent, block layout (or mixed 4/3-bit codes)
+    const void* bk;        // key factors [R_k caller rows][D]
+    const float* q;        // [B][chunk][H][D], rotated to each query's position
+    void* P;               // [B*chunk][H][Tp] binary16
+    float* stats;          // [B*chunk][H][2 * nblk][2]
+    const int32_t* chunk_lens = nullptr;  // per-sequence chunk lengths (device) or NULL
+    int B, H, D, Rk, nblk_cap, chunk, pos0, nblk, Tp;
+    BlockMap pages;
+    float q_scale;         // softmax scale * log2(e)
+    int16_t koff[kMaxHeads + 1];
+    int16_t rank[kMaxHeads];
+    int16_t soff[kMaxHeads + 1];
+    int16_t srank[kMaxHeads];
+    double rope_rev[64];   // theta_i / (2 pi)
+    // mixed 4/3-bit key cache only
+    const void* zk_meta;
+    const void* zk_tail;
+    Q43Layout ql;
+};
+
+// Per-row lengths, row fills and group-to-sequence map of a prefill call (rows b * chunk + l).
+struct PrefillRowsParams {
+    const int32_t* chunk_lens;
+    int32_t* row_len;      // [B*chunk]: pos0 + l + 1 for l < chunk_len(b), else 0
+    int32_t* row_fill;     // [B*chunk]: pos0 + chunk_len(b)
+    int32_t* group_seq;    // [B*chunk / nq]: the sequence of each group of nq rows
+    int B, chunk, pos0, nq;
 };
 
 // row_fill[i] = the largest clamped length among rows that read the same cache sequence as row i

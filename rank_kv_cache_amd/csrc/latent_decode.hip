@@ -47,39 +47,6 @@ __device__ __forceinline__ void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// Eight mixed 4/3-bit key codes of one token (one 16-channel group, channels 8*half .. +7) to an
-// fp16 MFMA operand fragment. w0..w2: the aligned 96-bit window holding the token's row, sh: the
-// row's first bit in the window, n: 4-bit channels at the start of the group; sc / zc: the scales
-// and zero points of the eight channels, two per word. Each value is binary16(q*s + z) rounded
-// once (one fp16 FMA per pair); q is formed exactly as binary16(1024 + q) - 1024.
-__device__ __forceinline__ f16x8 q43_key_frag(uint32_t w0, uint32_t w1, uint32_t w2, int sh, int n,
-                                             int half, const u32x4& sc, const u32x4& zc) {
-    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
-    const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
-    const uint32_t low24 = (half ? __builtin_amdgcn_alignbit(hi, lo, 24) : lo) & 0xffffffu;
-    const int m = min(max(n - 8 * half, 0), 8);
-    const uint32_t ext = (hi >> (16 + 8 * half)) & ((1u << m) - 1u);
-    f16x8 out;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int e = 2 * k;
-        const uint32_t q0 = ((low24 >> (3 * e)) & 7u) | (((ext >> e) & 1u) << 3);
-        const uint32_t q1 = ((low24 >> (3 * e + 3)) & 7u) | (((ext >> (e + 1)) & 1u) << 3);
-        const uint32_t bits = 0x64006400u | q0 | (q1 << 16);
-        const f16x2 qv = __builtin_bit_cast(f16x2, bits) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
-        // vector elements are copied to scalars first: a bit cast applied directly to an
-        // element of an ext_vector value has been compiled as a cast of element 0
-        const uint32_t sk = sc[k], zk = zc[k];
-        const f16x2 r = __builtin_elementwise_fma(qv, __builtin_bit_cast(f16x2, sk),
-                                                  __builtin_bit_cast(f16x2, zk));
-        out[e] = r[0];
-        out[e + 1] = r[1];
-    }
-    return out;
-}
-
 // Latent fragments of one unit held in registers (the paths that load a whole unit at once).
 template <int K, int MAXKS> struct KeyBuf {
     typename Elem<K>::frag z[2][MAXKS];

@@ -312,3 +312,32 @@ def test_noalloc_validation():
     assert na(Cc=_cache(batch=64, capacity=1 << 23), T=(1 << 22) + 64) == 8   # beyond the planner
     assert na(L=None) == 1 and na(Cc=None) == 1 and na(T=0) == 2
     assert na(Cc=_cache(batch=0), T=100) == 0                                    # nothing to do
+
+
+def test_prefill_validation():
+    L, Cc = _latent(), _cache()
+    pf = lambda L=L, Cc=Cc, pos0=10, chunk=20, lens=None, q=FAKE, ws=FAKE, nws=1 << 40: \
+        sk.starkv_prefill_attn(L, Cc, pos0, chunk, lens, q, FAKE, FAKE, FAKE, ws, nws, check=False)
+    assert sk.starkv_prefill_workspace_bytes(L, 2, 10, 20) > 0
+    assert pf(pos0=-1) == 2 and pf(chunk=0) == 2
+    assert pf(pos0=200, chunk=100) == 6                      # beyond the capacity of 256
+    assert pf(L=sk.Layer(num_heads=4, head_dim=128, dense=True, cache_dtype=sk.F16)) == 8
+    assert pf(L=_latent(cache_dtype=sk.F32, factor_dtype=sk.F32)) == 8
+    assert pf(q=None) == 1 and pf(q=MISAL) == 5 and pf(lens=FAKE + 2) == 5
+    assert pf(ws=None) == 7 and pf(nws=16) == 7
+    assert pf(Cc=_cache(batch=0)) == 0
+    assert sk.starkv_prefill_workspace_bytes(L, 2, -1, 20) == 0
+    assert sk.starkv_prefill_workspace_bytes(L, 2, 0, 0) == 0
+
+
+def test_decode_project_validation():
+    L, Cc = _latent(), _cache()
+    dp = lambda Cc=Cc, hidden=300, wo=FAKE, y=FAKE, T=100, ws=FAKE, nws=1 << 40: \
+        sk.starkv_decode_attn_project(L, Cc, T, FAKE, FAKE, FAKE, wo, hidden, y, 0, ws, nws, check=False)
+    assert sk.starkv_decode_attn_project_workspace_bytes(L, 2, 100, 0, 300) > \
+        sk.starkv_decode_workspace_bytes(L, 2, 100, 0)
+    assert dp(hidden=0) == 2 and dp(wo=None) == 1 and dp(y=None) == 1
+    assert dp(wo=MISAL) == 5 and dp(y=FAKE + 2) == 5
+    assert dp(T=300) == 6 and dp(T=0) == 2                   # the decode's own validation
+    assert dp(ws=None) == 7 and dp(nws=64) == 7
+    assert dp(Cc=_cache(batch=0)) == 0

@@ -1,0 +1,170 @@
+"""GPU parity of chunked causal (prefill) attention over the latent cache: query l of sequence b at
+position pos0 + l attends to cached tokens [0, pos0 + l]. Every checked row is compared with the
+oracle's decode of that row's causal prefix (the plain definition, fp64), to the same 2e-3 bar as
+decode. Covers binary16, bfloat16 and mixed 4/3-bit caches, head dims 64 and 128, chunk lengths
+that take every query grouping (multiples of 4, of 2 only, odd), per-sequence ragged chunks, a
+peaked-attention case for the query-key product, and a 2048-query chunk on the LongChat layer."""
+import numpy as np
+import pytest
+
+import oracle
+import rank_kv_cache_amd as sk
+from rank_kv_cache_amd import synth
+
+from gpu_support import DeviceLayer, latent_layer, rel_err, say
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+FRAC = 0.25
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    sk.lib()
+
+
+def _prefill(L, cache, pos0, chunk, q, bk, bv, chunk_lens=None, bf16=False):
+    import torch
+    from rank_kv_cache_amd import buffers
+    B = cache.batch
+    H, d = L.num_heads, L.head_dim
+    out = torch.full((B, chunk, H, d), float("nan"), dtype=torch.float32, device="cuda")
+    nws = sk.starkv_prefill_workspace_bytes(L, B, pos0, chunk)
+    assert nws > 0
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")
+    dl = None if chunk_lens is None else torch.tensor(np.asarray(chunk_lens, np.int32), device="cuda")
+    dbk = bk if hasattr(bk, "data_ptr") else buffers.to_device(bk, bf16=bf16)
+    dbv = bv if hasattr(bv, "data_ptr") else buffers.to_device(bv, bf16=bf16)
+    sk.starkv_prefill_attn(L, cache, pos0, chunk, dl, buffers.to_device(np.ascontiguousarray(q, np.float32)),
+                           dbk, dbv, out, ws, nws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check_rows(got, pos0, chunk_lens, ref_row, rows, what):
+    worst = 0.0
+    for b, l in rows:
+        if l >= chunk_lens[b]:
+            assert np.all(got[b, l] == 0), (what, b, l)
+            continue
+        want = ref_row(b, l, pos0 + l + 1)
+        e = rel_err(got[b, l], want)
+        worst = max(worst, e)
+        assert np.all(np.isfinite(got[b, l])) and e <= TOL, (what, b, l, e)
+    say(f"[prefill] {what}: {len(rows)} rows, worst {worst:.3e}")
+    return worst
+
+
+def _latent_case(dtype, d, ranks, rv, B, pos0, chunk, seed, scale_q=1.0):
+    H = len(ranks)
+    T = pos0 + chunk
+    w = synth.Workload(f"pf{seed}", batch=B, heads=H, head_dim=d, seq_len=T, dtype=dtype,
+                       layer_seed=seed, cache_seed=seed + 1, value_rank=rv, power=0.5)
+    ld = synth.draw_layer(w, key_ranks=ranks)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = np.random.default_rng(seed + 2).standard_normal((B, chunk, H, d)).astype(np.float32) * scale_q
+    return ld, zk, zv, q
+
+
+@pytest.mark.parametrize("dtype,d,chunk,pos0", [("f16", 128, 64, 0), ("f16", 128, 70, 37),
+                                                ("bf16", 128, 33, 130), ("f16", 64, 100, 5),
+                                                ("bf16", 64, 97, 64)])
+def test_prefill_latent_every_row(dtype, d, chunk, pos0):
+    """Every row of small chunks: the first tokens of a prompt (pos0 0), a chunk after a cached
+    prefix, chunk lengths whose query grouping is 4 (64, 100), 2 (70) and 1 (33, 97)."""
+    ranks = [16, 48, 32, 64] if d == 128 else [16, 32, 48, 64]
+    rv = 160
+    B = 2
+    ld, zk, zv, q = _latent_case(dtype, d, ranks, rv, B, pos0, chunk, 500 + chunk + pos0)
+    L = latent_layer(len(ranks), d, ranks, rv, dtype)
+    dev = DeviceLayer(L, zk, zv, ld.bk, ld.bv)
+    bf16 = dtype == "bf16"
+    got = _prefill(L, dev.cache, pos0, chunk, q, dev.bk, dev.bv, bf16=bf16)
+    rows = [(b, l) for b in range(B) for l in range(chunk)]
+    _check_rows(got, pos0, [chunk] * B,
+                lambda b, l, n: oracle.decode_latent(zk[b:b + 1, :n], zv[b:b + 1, :n], ld.bk, ld.bv,
+                                                     q[b:b + 1, l], ranks, bf16=bf16)[0],
+                rows, f"{dtype} d={d} chunk={chunk} pos0={pos0}")
+
+
+def test_prefill_ragged_chunks():
+    """Per-sequence chunk lengths (0, 1, 31, 64 of a 64-query call): rows past a sequence's chunk
+    are empty and give zeros."""
+    ranks, rv, d, B, pos0, chunk = [32, 16, 64], 96, 128, 4, 50, 64
+    ld, zk, zv, q = _latent_case("f16", d, ranks, rv, B, pos0, chunk, 610)
+    L = latent_layer(len(ranks), d, ranks, rv, "f16")
+    dev = DeviceLayer(L, zk, zv, ld.bk, ld.bv)
+    lens = [0, 1, 31, 64]
+    got = _prefill(L, dev.cache, pos0, chunk, q, dev.bk, dev.bv, chunk_lens=lens)
+    rows = [(b, l) for b in range(B) for l in range(chunk)]
+    _check_rows(got, pos0, lens,
+                lambda b, l, n: oracle.decode_latent(zk[b:b + 1, :n], zv[b:b + 1, :n], ld.bk, ld.bv,
+                                                     q[b:b + 1, l], ranks)[0],
+                rows, "ragged chunks")
+
+
+def test_prefill_peaked_attention():
+    """Queries eight times larger: sharp attention, where the error of the query-key product
+    shows up directly in the probabilities."""
+    ranks, rv, d, B, pos0, chunk = [64, 48, 16, 32], 128, 128, 1, 90, 40
+    ld, zk, zv, q = _latent_case("f16", d, ranks, rv, B, pos0, chunk, 620, scale_q=8.0)
+    L = latent_layer(len(ranks), d, ranks, rv, "f16")
+    dev = DeviceLayer(L, zk, zv, ld.bk, ld.bv)
+    got = _prefill(L, dev.cache, pos0, chunk, q, dev.bk, dev.bv)
+    rows = [(0, l) for l in range(chunk)]
+    _check_rows(got, pos0, [chunk],
+                lambda b, l, n: oracle.decode_latent(zk[b:b + 1, :n], zv[b:b + 1, :n], ld.bk, ld.bv,
+                                                     q[b:b + 1, l], ranks)[0],
+                rows, "peaked (q x 8)")
+
+
+@pytest.mark.parametrize("pos0,chunk", [(0, 128), (100, 92), (64, 64)])
+def test_prefill_q43(pos0, chunk):
+    """Mixed 4/3-bit cache holding exactly the prefix plus the chunk (so its partial last group is
+    in the tail): every row against the oracle's quantise / dequantise of the same rows."""
+    from test_gpu_q43 import _append, q43_layer
+    from rank_kv_cache_amd import buffers
+    ranks, rv, d, B = [16, 64, 32, 48], 96, 128, 2
+    T = pos0 + chunk
+    cap = ((T + 63) // 64) * 64 + 64
+    ld, zk, zv, q = _latent_case("f16", d, ranks, rv, B, pos0, chunk, 630 + pos0)
+    L = q43_layer(len(ranks), d, ranks, rv)
+    cache = buffers.alloc_cache(L, B, cap, fill=0xFF)
+    _append(L, cache, zk, zv, [T])
+    got = _prefill(L, cache, pos0, chunk, q, ld.bk, ld.bv)
+    bits_k, bits_v = oracle.channel_bits(ranks, FRAC), oracle.channel_bits([rv], FRAC)
+    deq = []
+    for b in range(B):
+        ck, mk, tk = oracle.q43_pack(zk[b:b + 1], bits_k, cap)
+        cv, mv, tv = oracle.q43_pack(zv[b:b + 1], bits_v, cap)
+        deq.append((oracle.q43_unpack(ck, mk, tk, bits_k, T, cap), oracle.q43_unpack(cv, mv, tv, bits_v, T, cap)))
+    rows = [(b, l) for b in range(B) for l in range(chunk)]
+    _check_rows(got, pos0, [chunk] * B,
+                lambda b, l, n: oracle.decode_latent(deq[b][0][:, :n], deq[b][1][:, :n], ld.bk, ld.bv,
+                                                     q[b:b + 1, l], ranks)[0],
+                rows, f"q43 pos0={pos0} chunk={chunk}")
+
+
+def test_prefill_longchat_chunk_2048_sampled():
+    """A 2048-query chunk on the LongChat-shaped layer (32 heads, key ranks U{16..64}, r_v 1024,
+    binary16), sampled rows including the first and the last, in the library's default
+    configuration."""
+    w = synth.WORKLOADS["longchat_b16_t4096_f16"]
+    chunk, pos0 = 2048, 0
+    ld = synth.draw_layer(w)
+    zk, zv = synth.draw_latent_cache(w, ld, batches=[0], seq_len=chunk)
+    ranks, rv = ld.key_ranks, ld.value_rank
+    H, d = w.heads, w.head_dim
+    q = np.random.default_rng(640).standard_normal((1, chunk, H, d)).astype(np.float32)
+    L = latent_layer(H, d, ranks, rv, "f16")
+    dev = DeviceLayer(L, zk, zv, ld.bk, ld.bv)
+    got = _prefill(L, dev.cache, pos0, chunk, q, dev.bk, dev.bv)
+    rng = np.random.default_rng(641)
+    rows = [(0, 0), (0, 1), (0, 31), (0, 32), (0, 1023), (0, chunk - 1)] + \
+           [(0, int(l)) for l in rng.integers(0, chunk, 6)]
+    _check_rows(got, pos0, [chunk],
+                lambda b, l, n: oracle.decode_latent(zk[:, :n], zv[:, :n], ld.bk, ld.bv, q[:, l], ranks)[0],
+                rows, "longchat chunk 2048")
