@@ -113,3 +113,40 @@ def test_projection_exact_arithmetic(dtype):
     y = _project(L, o, wo_t, hidden, bf16=dtype == "bf16")
     ref = oracle.output_projection(o, wo_t, bf16=dtype == "bf16")
     assert np.array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("dtype,splits", [("f16", 0), ("bf16", 3)])
+def test_decode_attn_project_one_call(dtype, splits):
+    """Decode attention and the output projection in one call: bit for bit the two-call path
+    (the same kernels with the heads' outputs kept in the workspace), and the oracle's attention
+    followed by its fp64 product within the decode bar."""
+    import torch
+    from rank_kv_cache_amd import buffers
+    H, d, B, T, hidden = 6, 128, 7, 333, 260
+    ranks, rv = [16, 64, 32, 48, 16, 80], 224
+    w = synth.Workload("op1", batch=B, heads=H, head_dim=d, seq_len=T, dtype=dtype, layer_seed=111,
+                       cache_seed=112, value_rank=rv, power=0.5)
+    ld = synth.draw_layer(w, key_ranks=ranks)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = synth.draw_queries(113, 0, B, H, d)
+    bf16 = dtype == "bf16"
+    wo_t = _weights(np.random.default_rng(114), hidden, H * d, dtype)
+    L = latent_layer(H, d, ranks, rv, dtype)
+    dl = DeviceLayer(L, zk, zv, ld.bk, ld.bv)
+    dq = buffers.to_device(np.ascontiguousarray(q, np.float32))
+    dwo = buffers.to_device(wo_t, bf16=bf16)
+    nws = sk.starkv_decode_attn_project_workspace_bytes(L, B, T, splits, hidden)
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")
+    y1 = torch.full((B, hidden), float("nan"), dtype=torch.float32, device="cuda")
+    sk.starkv_decode_attn_project(L, dl.cache, T, dq, dl.bk, dl.bv, dwo, hidden, y1, splits, ws, nws)
+    torch.cuda.synchronize()
+    # two calls
+    o = dl.decode(q, num_splits=splits)
+    y2 = _project(L, o, wo_t, hidden, bf16=bf16)
+    got = y1.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), y2.view(np.uint32))
+    ref = oracle.output_projection(
+        oracle.decode_latent(zk, zv, ld.bk, ld.bv, q, ranks, bf16=bf16), wo_t, bf16=bf16)
+    e = rel_err(got, ref)
+    say(f"[outproj] one call {dtype} splits={splits}: bit-equal to two calls, rel err {e:.3e}")
+    assert np.all(np.isfinite(got)) and e <= TOL
