@@ -452,6 +452,108 @@ def measure_projections(sk, buffers, run, B, stream, hip, steps, model_dim=4096,
     return res
 
 
+def measure_prefill(sk, buffers, synth, stream, hip, steps, batch=4, chunk=2048):
+    """Prompt prefill through starkv_prefill_attn on the LongChat-shaped layer: `batch` sequences
+    of `chunk` queries each at positions 0 .. chunk-1 over their own latents (binary16), timed with
+    HIP events on the launch stream. Algorithmic work (the plain definition of latent attention,
+    causal): per (query, key, head) 2*d flop for the score and 2*r_v for the latent value sum,
+    per 32-query tile and key the key rebuild 2*d*R_k, per query the per-head output 2*H*r_v*d."""
+    import torch
+    w = synth.WORKLOADS["longchat_b16_t4096_f16"]
+    ld = synth.draw_layer(w)
+    zk, zv = synth.draw_latent_cache(w, ld, batches=list(range(batch)), seq_len=chunk)
+    H, d, rv = w.heads, w.head_dim, ld.value_rank
+    Rk = int(ld.key_ranks.sum())
+    L = sk.Layer(num_heads=H, head_dim=d, key_ranks=tuple(int(r) for r in ld.key_ranks),
+                 value_rank=rv, cache_dtype=sk.F16)
+    cache = buffers.alloc_cache(L, batch, cache_capacity(chunk))
+    sk.starkv_append_latents(L, cache, 0, chunk, buffers.to_device(zk), buffers.to_device(zv))
+    del zk, zv
+    bk, bv = buffers.to_device(ld.bk), buffers.to_device(ld.bv)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    q = torch.randn((batch, chunk, H, d), device="cuda", generator=g)
+    out = torch.empty_like(q)
+    nws = sk.starkv_prefill_workspace_bytes(L, batch, 0, chunk)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    sp = stream.cuda_stream
+
+    def call():
+        sk.starkv_prefill_attn(L, cache, 0, chunk, None, q, bk, bv, out, ws, nws, stream=stream)
+
+    for _ in range(2):
+        call()
+    ev = hip.create(2)
+    torch.cuda.synchronize()
+    hip.record(ev[0], sp)
+    for _ in range(steps):
+        call()
+    hip.record(ev[1], sp)
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+    hip.destroy(ev)
+    if not bool(torch.isfinite(out).all()):
+        raise SystemExit("non-finite prefill output")
+    pairs = batch * chunk * (chunk + 1) // 2                  # causal (query, key) pairs
+    flop = (pairs * H * (2 * d + 2 * rv) + batch * ((chunk + 31) // 32) * chunk * 2 * d * Rk
+            + batch * chunk * 2 * H * rv * d)
+    tf = flop / (us * 1e-6) / 1e12
+    res = {"batch": batch, "chunk": chunk, "pos0": 0, "avg_us": us, "query_tokens_per_s": batch * chunk / (us * 1e-6),
+           "alg_flop": flop, "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_F16_PEAK_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": tf / MFMA_F16_PEAK_TFLOPS}}
+    log(f"[bench] prefill: {batch} x {chunk} queries in {us:.1f} us ({tf:.1f} TFLOP/s algorithmic)")
+    del ws, cache
+    return res
+
+
+def measure_decode_project(sk, buffers, run, B, stream, hip, steps, hidden=4096):
+    """Decode attention followed by the output projection (LongChat-7B width, binary16 W_o): two
+    calls (starkv_decode_attn, starkv_output_projection) against the one call that keeps the heads'
+    outputs in its workspace (starkv_decode_attn_project), HIP events on the launch stream."""
+    import torch
+    L, T = run.layer, run.T
+    H, d = L.num_heads, L.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    wo = (torch.randn((hidden, H * d), device="cuda", generator=g) / (H * d) ** 0.5).to(torch.float16)
+    y = torch.empty((B, hidden), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    nws_d = sk.starkv_decode_workspace_bytes(L, B, T, 0)
+    nws_p = sk.starkv_output_projection_workspace_bytes(L, B, hidden)
+    nws_1 = sk.starkv_decode_attn_project_workspace_bytes(L, B, T, 0, hidden)
+    ws_d = torch.empty(nws_d, dtype=torch.uint8, device="cuda")
+    ws_p = torch.empty(nws_p, dtype=torch.uint8, device="cuda")
+    ws_1 = torch.empty(nws_1, dtype=torch.uint8, device="cuda")
+    sp = stream.cuda_stream
+
+    def two():
+        sk.starkv_decode_attn(L, run.cache, T, run.q, run.bk, run.bv, o, 0, ws_d, nws_d, stream=stream)
+        sk.starkv_output_projection(L, B, o, wo, hidden, y, ws_p, nws_p, stream=stream)
+
+    def one():
+        sk.starkv_decode_attn_project(L, run.cache, T, run.q, run.bk, run.bv, wo, hidden, y, 0, ws_1,
+                                      nws_1, stream=stream)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = hip.create(2)
+        torch.cuda.synchronize()
+        hip.record(ev[0], sp)
+        for _ in range(steps):
+            fn()
+        hip.record(ev[1], sp)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+        hip.destroy(ev)
+        return us
+
+    res = {"hidden": hidden, "two_calls_avg_us": timed(two), "one_call_avg_us": timed(one)}
+    log(f"[bench] decode + output projection: {res['two_calls_avg_us']:.1f} us in two calls, "
+        f"{res['one_call_avg_us']:.1f} us in one")
+    return res
+
+
 def measure_queries(sk, run, B, stream, hip, steps, per_seq=4):
     """Several queries per sequence through starkv_decode_attn_queries, timed with HIP events on
     the launch stream: per_seq causal queries at the last per_seq positions of every sequence
@@ -630,12 +732,16 @@ def main(argv=None):
             raise SystemExit("non-finite attention output")
     copy_gbs = None if a.no_copy_ceiling else measure_copy_ceiling(hip, stream)
 
-    projections = queries = None
+    projections = queries = prefill = decode_project = None
     if a.extras:
         lat = [r for r in runs if not r.dense]
         projections = measure_projections(sk, buffers, lat[0], B, stream, hip, a.steps)
         if len(runs) == 1:
             queries = measure_queries(sk, lat[0], B, stream, hip, min(a.steps, 10))
+            if lat[0].layer.cache_dtype != sk.Q43:
+                decode_project = measure_decode_project(sk, buffers, lat[0], B, stream, hip,
+                                                        min(a.steps, 10))
+        prefill = measure_prefill(sk, buffers, synth, stream, hip, min(a.steps, 5))
 
     ms_per_step = elapsed * 1e3 / a.steps
     kernels = {}
@@ -711,6 +817,10 @@ def main(argv=None):
     }
     if projections is not None:
         rec["projections"] = projections
+    if decode_project is not None:
+        rec["decode_project"] = decode_project
+    if prefill is not None:
+        rec["prefill"] = prefill
     if queries is not None:
         queries["vs_single_query_step"] = queries["avg_us"] / (ms_per_step * 1e3)
         queries["shared_vs_single_query_step"] = queries["shared_avg_us"] / (ms_per_step * 1e3)
