@@ -625,6 +625,9 @@ def main(argv=None):
                     help="a single-layer workload name, or " + MODEL_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's split planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill of 4 x 2048 queries (for kernel profiles) and print "
+                         "its JSON object")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip the device-copy ceiling measurement after the steps")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="oracle wall seconds")
@@ -651,6 +654,12 @@ def main(argv=None):
     import rank_kv_cache_amd as sk
     from rank_kv_cache_amd import buffers, synth
     sk.lib()                                              # fails loudly if the library is missing
+
+    if a.prefill_only:
+        stream = torch.cuda.current_stream()
+        res = measure_prefill(sk, buffers, synth, stream, HipEvents(), a.steps)
+        print(json.dumps({"prefill": res}), flush=True)
+        return 0
 
     sample = None if a.no_cpu_baseline else OracleSample()
     if a.workload == MODEL_WORKLOAD:

@@ -28,6 +28,8 @@ hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_row_fill(const RowFillParams& p, hipStream_t st);
 hipError_t launch_prefill_scores(const PrefillParams& p, int elem, hipStream_t st);
 hipError_t launch_prefill_rows(const PrefillRowsParams& p, hipStream_t st);
+hipError_t launch_prefill_project(const ProjectParams& p, int elem, hipStream_t st);
+hipError_t launch_prefill_values(const ValueParams& p, int elem, hipStream_t st);
 hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
@@ -1105,8 +1107,12 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
     vp.row_fill = li.q43 ? rp.row_fill : nullptr;
     vp.block_bytes = li.q43 ? qv.block_bytes : 0;
     vp.n_hi = li.q43 ? qv.n_hi : 0;
-    if ((s = dev(launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, pl.nq, st))) != STARKV_OK)
-        return s;
+    // four rows per group on 16-bit latents: the prefill value kernel (probabilities rescaled once
+    // per block and shared by eight channel tiles); otherwise the multi-row decode value kernel
+    const hipError_t ve = (pl.nq == 4 && !li.q43)
+                              ? launch_prefill_values(vp, ek, st)
+                              : launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, pl.nq, st);
+    if ((s = dev(ve)) != STARKV_OK) return s;
     ProjectParams pr;
     pr.ws_ml = vp.ws_ml;
     pr.ws_acc = vp.ws_acc;
@@ -1118,6 +1124,9 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
     pr.D = li.D;
     pr.rv = li.rv;
     pr.rv_src = li.rv_src;
+    // many rows: the matrix-core output step (B_v read once per 128 rows); few rows, or more
+    // splits than its weight table holds: the decode output step
+    if (pl.rows >= 128 && w.vp.splits <= 64) return dev(launch_prefill_project(pr, ek, st));
     return dev(launch_project(pr, ek, st));
 }
 

@@ -321,6 +321,300 @@ hipError_t launch_prefill_scores(const PrefillParams& p, int elem, hipStream_t s
     return hipErrorInvalidValue;
 }
 
+// Value side for query rows stacked four at a time (Zhou notes, Algorithm 2 step 6 per query;
+// section 5.3: all heads in one operand): Acc[row][h][c] = sum_n p_{row,h,n} 2^(m_t - M) Z_v[n][c]
+// over the split's blocks. One workgroup takes four query rows of one sequence and 512 value
+// channels; its eight waves own 64 channels each. Per 64-token block the probabilities of the four
+// rows (all heads) are rescaled by 2^(m_t - M) once, split into binary16 hi + lo parts and staged
+// in LDS in MFMA operand order (double-buffered), so every wave feeds them to its own channel
+// tile (two MFMAs per fragment) without repeating the rescaling. Writes (M, L, Acc) per split in
+// the decode workspace layout, read by the output step.
+constexpr int kPvWaves = 8;
+constexpr int kPvRows = 4;
+constexpr int kPvTiles = 2;                            // 32-channel tiles per wave
+constexpr int kPvChannels = 32 * kPvTiles * kPvWaves;
+
+template <int K>
+__global__ __launch_bounds__(64 * kPvWaves, 1) void prefill_values(const ValueParams p) {
+    using Fr = typename Elem<K>::frag;
+    using T = typename Elem<K>::storage;
+    // [buffer][row][ks][lane][8]: lane l holds head l % 32, tokens 16*ks + 8*(l/32) + 0..7
+    __shared__ __attribute__((aligned(16))) T s_ph[2][kPvRows * 4 * 64 * 8], s_pl[2][kPvRows * 4 * 64 * 8];
+    __shared__ float s_M[kPvRows][kMaxHeads], s_L[kPvRows][kMaxHeads];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int split = blockIdx.x;
+    const int chunk = blockIdx.y;
+    const int grp = blockIdx.z;
+    const int H = p.H;
+    const int row0 = grp * kPvRows;
+    int seq_len = 0;
+#pragma unroll
+    for (int qi = 0; qi < kPvRows; ++qi) seq_len = max(seq_len, seq_length(p.seq_lens, row0 + qi, p.seq_len));
+    const int bc = cache_seq(p.seq_map, grp, p.cache_batch);
+    const int blk_begin = split * p.blocks_per_split;
+    const int blk_end = max(blk_begin, min((seq_len + 63) >> 6, blk_begin + p.blocks_per_split));
+    const int nb = blk_end - blk_begin;
+
+    // split statistics per (row, head) from the 32-token tile statistics
+    for (int hq = wave; hq < kPvRows * H; hq += kPvWaves) {
+        const int qi = hq / H, h = hq - qi * H;
+        const float* st = p.stats + (((size_t)(row0 + qi) * H + h) * 2 * p.nblk + 2 * blk_begin) * 2;
+        float M = -INFINITY;
+        for (int i = lane; i < 2 * nb; i += 64) M = fmaxf(M, st[2 * i]);
+        M = wave_max(M);
+        const float Mc = M != -INFINITY ? M : 0.0f;
+        float L = 0.0f;
+        for (int i = lane; i < 2 * nb; i += 64) L += __builtin_amdgcn_exp2f(st[2 * i] - Mc) * st[2 * i + 1];
+        L = wave_sum(L);
+        if (lane == 0) { s_M[qi][h] = M; s_L[qi][h] = L; }
+    }
+    __syncthreads();
+
+    // staging of one block's operands: 512 threads, two 8-token runs each (row, head, run)
+    auto stage = [&](int buf, int blk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int e = tid + it * 64 * kPvWaves;             // (qi, h, u) with u < 8 runs
+            const int u = e & 7, h = (e >> 3) & 31, qi = e >> 8;
+            const int hh = min(h, H - 1);
+            const size_t prow = ((size_t)(row0 + qi) * H + hh) * p.Tp + (size_t)blk * 64 + 8 * u;
+            const f16x8 pv = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(p.P) + prow);
+            const float m = p.stats[(((size_t)(row0 + qi) * H + hh) * 2 * p.nblk + 2 * blk + (u >> 2)) * 2];
+            const float M = s_M[qi][hh];
+            const float f = (h < H && m != -INFINITY && M != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+            struct __attribute__((aligned(16))) Run { T v[8]; } rh, rl;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float v = (float)pv[k] * f;
+                if constexpr (K == kBF16) {
+                    const uint16_t hb = float_to_bf16_bits(v);
+                    rh.v[k] = hb;
+                    rl.v[k] = float_to_bf16_bits(v - bf16_bits_to_float(hb));
+                } else {
+                    rh.v[k] = (_Float16)v;
+                    rl.v[k] = (_Float16)(v - (float)rh.v[k]);
+                }
+            }
+            const int ks = u >> 1, l = h + 32 * (u & 1);
+            const int at = ((qi * 4 + ks) * 64 + l) * 8;
+            *reinterpret_cast<Run*>(&s_ph[buf][at]) = rh;
+            *reinterpret_cast<Run*>(&s_pl[buf][at]) = rl;
+        }
+    };
+
+    // this wave's channels (channels past r_v read a clamped channel and are never stored)
+    int ch[kPvTiles];
+    size_t zoff[kPvTiles];
+    const int cgroups = p.rv >> 4;
+#pragma unroll
+    for (int k = 0; k < kPvTiles; ++k) {
+        ch[k] = ((chunk * kPvWaves + wave) * kPvTiles + k) * 32 + (lane & 31);
+        const int cc = min(ch[k], p.rv - 1);
+        zoff[k] = (size_t)(cc >> 4) * 1024 + (cc & 15) * 16 + 8 * half;
+    }
+    f32x16 acc[kPvRows][kPvTiles];
+#pragma unroll
+    for (int qi = 0; qi < kPvRows; ++qi)
+#pragma unroll
+        for (int k = 0; k < kPvTiles; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[qi][k][r] = 0.0f;
+
+    if (nb > 0) stage(0, blk_begin);
+    for (int i = 0; i < nb; ++i) {
+        const int blk = blk_begin + i, buf = i & 1;
+        __syncthreads();                     // block i staged; block i - 1's operands consumed
+        if (i + 1 < nb) stage(buf ^ 1, blk + 1);
+        const size_t bbase = block_id(p.pages, p.nblk_cap, bc, blk) * cgroups * 1024;
+        Fr z[kPvTiles][4];
+#pragma unroll
+        for (int k = 0; k < kPvTiles; ++k)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) z[k][ks] = load_frag<K>(p.zv, bbase + zoff[k] + ks * 256);
+        if ((blk + 1) * 64 > seq_len) {
+            // the group's last block: tokens past its longest row may hold anything (their
+            // probabilities are 0, but 0 * NaN is not): zero them
+#pragma unroll
+            for (int k = 0; k < kPvTiles; ++k)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (blk * 64 + 16 * ks + 8 * half + e >= seq_len) z[k][ks][e] = 0;
+        }
+#pragma unroll
+        for (int qi = 0; qi < kPvRows; ++qi)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int at = ((qi * 4 + ks) * 64 + lane) * 8;
+                const Fr ph = *reinterpret_cast<const Fr*>(&s_ph[buf][at]);
+                const Fr pl = *reinterpret_cast<const Fr*>(&s_pl[buf][at]);
+#pragma unroll
+                for (int k = 0; k < kPvTiles; ++k) {
+                    acc[qi][k] = mma32<K>(ph, z[k][ks], acc[qi][k]);
+                    acc[qi][k] = mma32<K>(pl, z[k][ks], acc[qi][k]);
+                }
+            }
+    }
+
+    // (M, L) of the split (one writer per (row, head)), then the wave's channels of Acc
+    if (chunk == 0 && tid < kPvRows * H) {
+        const int qi = tid / H, h = tid - qi * H;
+        float* ml = p.ws_ml + (((size_t)(row0 + qi) * p.S + split) * H + h) * 2;
+        ml[0] = s_M[qi][h];
+        ml[1] = s_L[qi][h];
+    }
+#pragma unroll
+    for (int k = 0; k < kPvTiles; ++k) {
+        if (ch[k] >= p.rv) continue;
+#pragma unroll
+        for (int qi = 0; qi < kPvRows; ++qi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int h = 8 * (r >> 2) + 4 * half + (r & 3);
+                if (h < H) p.ws_acc[(((size_t)(row0 + qi) * p.S + split) * H + h) * p.rv + ch[k]] = acc[qi][k][r];
+            }
+    }
+}
+
+hipError_t launch_prefill_values(const ValueParams& p, int elem, hipStream_t st) {
+    const dim3 grid(p.S, (p.rv + kPvChannels - 1) / kPvChannels, p.B / kPvRows);
+    if (elem == kF16) hipLaunchKernelGGL(prefill_values<kF16>, grid, dim3(64 * kPvWaves), 0, st, p);
+    else if (elem == kBF16) hipLaunchKernelGGL(prefill_values<kBF16>, grid, dim3(64 * kPvWaves), 0, st, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Output step for many query rows (Zhou notes, Algorithm 2 step 7 per row): out[r][h] =
+// (sum_s w_{r,h,s} Acc_s[r][h]) B_v[:, h*d:(h+1)*d] with the log-sum-exp split weights w
+// (normalised). One workgroup takes 128 rows of one head: wave w owns rows 32w .. 32w+31 and
+// all d output columns (d/32 MFMA accumulators). The head's B_v slice is staged in LDS per chunk
+// of 32 value channels (read once per 128 rows); each lane forms its row's merged latent values in
+// fp32 and feeds them as binary16 hi + lo parts (two MFMAs per fragment: fp32 accuracy).
+constexpr int kPpRows = 128;
+constexpr int kPpChunk = 32;
+constexpr int kPpMaxSplits = 64;
+
+template <int D, int K>
+__global__ __launch_bounds__(256, 2) void prefill_project(const ProjectParams p) {
+    constexpr int NT = D / 32;
+    using T = typename Elem<K>::storage;
+    using Fr = typename Elem<K>::frag;
+    // B_v rows of the chunk in B-operand fragment order: [nt][step][lane][8]
+    __shared__ __attribute__((aligned(16))) T s_bv[NT * 2 * 64 * 8];
+    __shared__ float s_w[kPpRows][kPpMaxSplits];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int r0 = blockIdx.x * kPpRows;
+    const int h = blockIdx.y;
+    const int S = p.S;
+    const size_t HD = (size_t)p.H * D;
+
+    // split weights of each row: w_s = 2^(M_s - M) / sum_s 2^(M_s - M) L_s (zeros for an empty row)
+    for (int rr = tid; rr < kPpRows; rr += 256) {
+        const int row = min(r0 + rr, p.B - 1);
+        const float* ml = p.ws_ml + ((size_t)row * S * p.H + h) * 2;
+        float M = -INFINITY;
+        for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(size_t)s * p.H * 2]);
+        if (M == -INFINITY) M = 0.0f;
+        float L = 0.0f;
+        for (int s = 0; s < S; ++s) L += __builtin_amdgcn_exp2f(ml[(size_t)s * p.H * 2] - M) * ml[(size_t)s * p.H * 2 + 1];
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        for (int s = 0; s < S; ++s) s_w[rr][s] = __builtin_amdgcn_exp2f(ml[(size_t)s * p.H * 2] - M) * inv;
+    }
+
+    const int rr = 32 * wave + (lane & 31);          // this lane's row of the A operand
+    const int row = min(r0 + rr, p.B - 1);
+    f32x16 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+
+    for (int c0 = 0; c0 < p.rv; c0 += kPpChunk) {
+        __syncthreads();                              // the previous chunk's fragments are read
+        // stage B_v[c0 .. c0+31][h*d .. h*d + d): fragment (nt, step), lane l holds column
+        // 32*nt + l%32 and channels c0 + 16*step + 8*(l/32) + jj; channels past rv_src are zero
+        for (int e = tid; e < NT * 2 * 64; e += 256) {
+            const int l = e & 63, st = (e >> 6) & 1, nt = e >> 7;
+            const int col = 32 * nt + (l & 31);
+            struct __attribute__((aligned(16))) Run { T v[8]; } run;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const int c = c0 + 16 * st + 8 * (l >> 5) + jj;
+                run.v[jj] = c < p.rv_src ? static_cast<const T*>(p.bv)[(size_t)c * HD + (size_t)h * D + col] : T(0);
+            }
+            *reinterpret_cast<Run*>(&s_bv[e * 8]) = run;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            // the lane's row: merged latent values of channels c0 + 16*st + 8*half .. + 7
+            const int cb = c0 + 16 * st + 8 * half;
+            f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (cb < p.rv) {
+                for (int s = 0; s < S; ++s) {
+                    const f32x4* src = reinterpret_cast<const f32x4*>(p.ws_acc + (((size_t)row * S + s) * p.H + h) * p.rv + cb);
+                    const float w = s_w[rr][s];
+                    a0 += w * src[0];
+                    a1 += w * src[1];
+                }
+            }
+            Fr ahi, alo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = e < 4 ? a0[e] : a1[e - 4];
+                if constexpr (K == kBF16) {
+                    const uint16_t hb = float_to_bf16_bits(v);
+                    ahi[e] = __builtin_bit_cast(__bf16, hb);
+                    alo[e] = __builtin_bit_cast(__bf16, float_to_bf16_bits(v - bf16_bits_to_float(hb)));
+                } else {
+                    ahi[e] = (_Float16)v;
+                    alo[e] = (_Float16)(v - (float)ahi[e]);
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const Fr bf = *reinterpret_cast<const Fr*>(&s_bv[((nt * 2 + st) * 64 + lane) * 8]);
+                acc[nt] = mma32<K>(ahi, bf, acc[nt]);
+                acc[nt] = mma32<K>(alo, bf, acc[nt]);
+            }
+        }
+    }
+    // acc[nt]: rows 32*wave + 8*(r/4) + 4*half + r%4, column 32*nt + lane%32
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int orow = r0 + 32 * wave + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (orow < p.B) p.out[((size_t)orow * p.H + h) * D + 32 * nt + (lane & 31)] = acc[nt][r];
+        }
+}
+
+hipError_t launch_prefill_project(const ProjectParams& p, int elem, hipStream_t st) {
+    if (p.S > kPpMaxSplits) return hipErrorInvalidValue;
+    const dim3 grid((p.B + kPpRows - 1) / kPpRows, p.H);
+    if (p.D == 128) {
+        if (elem == kF16) hipLaunchKernelGGL((prefill_project<128, kF16>), grid, dim3(256), 0, st, p);
+        else if (elem == kBF16) hipLaunchKernelGGL((prefill_project<128, kBF16>), grid, dim3(256), 0, st, p);
+        else return hipErrorInvalidValue;
+    } else if (p.D == 64) {
+        if (elem == kF16) hipLaunchKernelGGL((prefill_project<64, kF16>), grid, dim3(256), 0, st, p);
+        else if (elem == kBF16) hipLaunchKernelGGL((prefill_project<64, kBF16>), grid, dim3(256), 0, st, p);
+        else return hipErrorInvalidValue;
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void prefill_rows(const PrefillRowsParams p) {
     const int row = blockIdx.x * 256 + threadIdx.x;
     if (row >= p.B * p.chunk) return;

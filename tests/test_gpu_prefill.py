@@ -71,10 +71,12 @@ def _latent_case(dtype, d, ranks, rv, B, pos0, chunk, seed, scale_q=1.0):
 
 @pytest.mark.parametrize("dtype,d,chunk,pos0", [("f16", 128, 64, 0), ("f16", 128, 70, 37),
                                                 ("bf16", 128, 33, 130), ("f16", 64, 100, 5),
-                                                ("bf16", 64, 97, 64)])
+                                                ("bf16", 64, 97, 64), ("bf16", 128, 64, 10),
+                                                ("f16", 128, 64, 1000)])
 def test_prefill_latent_every_row(dtype, d, chunk, pos0):
     """Every row of small chunks: the first tokens of a prompt (pos0 0), a chunk after a cached
-    prefix, chunk lengths whose query grouping is 4 (64, 100), 2 (70) and 1 (33, 97)."""
+    prefix, chunk lengths whose query grouping is 4 (64, 100), 2 (70) and 1 (33, 97), and a
+    chunk after a 1000-token prefix (the value side then splits the sequence)."""
     ranks = [16, 48, 32, 64] if d == 128 else [16, 32, 48, 64]
     rv = 160
     B = 2
