@@ -136,6 +136,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 // Reductions over each 32-lane half of the wave (the first five steps of the wave-wide ones):
 // every lane gets the result of its own half.
+// 2^d for d = m_t - M, the difference of two integer tile maxima (d <= 0, an integer, or -inf
+// for a tile with no tokens): exact, where the hardware exp2 is an approximation
+__device__ __forceinline__ float tile_factor(float d) {
+    return d >= -149.0f ? ldexpf(1.0f, (int)d) : 0.0f;
+}
+
 __device__ __forceinline__ float half_max(float v) {
     v = fmaxf(v, dpp_mov<0xB1>(v));
     v = fmaxf(v, dpp_mov<0x4E>(v));

@@ -340,12 +340,16 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
             // lane = token of the block, so each half holds one 32-token tile
             float my = half ? sc[qi][1] : sc[qi][0];
             if (tok >= qlen[qi]) my = -INFINITY;
-            const float m = half_max(my);
+            // the tile maximum rounded up to an integer: rescaling a stored probability by
+            // 2^(m - M) between tiles is then exact; the tile sum adds the stored (rounded) values,
+            // so that numerator and denominator hold the same probabilities
+            float m = half_max(my);
+            if (m != -INFINITY) m = ceilf(m);
             // a tile wholly past the query's end: p = 0, l = 0
-            const float pr = m != -INFINITY ? __builtin_amdgcn_exp2f(my - m) : 0.0f;
-            const float l = half_sum(pr);
+            const PT pst = (PT)(m != -INFINITY ? __builtin_amdgcn_exp2f(my - m) : 0.0f);
+            const float l = half_sum((float)pst);
             const size_t row = (size_t)(row0 + qi) * H + h;
-            Pout[row * Tp + tok] = (PT)pr;
+            Pout[row * Tp + tok] = pst;
             // every lane stores (even lanes m, odd lanes l, to the same two words of its tile): no
             // branch, so the count of memory operations in flight stays static
             stats[(row * 2 * nblk + 2 * blk + half) * 2 + (lane & 1)] = (lane & 1) ? l : m;
@@ -430,42 +434,21 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
 // ------------------------------------------------------------------------------------------------
 template <int K> struct ProbFrag;
 
+// The tile maxima are integers, so the factor f = 2^(m_t - M) that brings a tile's stored
+// probabilities to the split's maximum is a power of two and the rescaled binary16 value is exact
+// (short of the subnormal range, where it is rounded once): one binary16 operand.
 template <> struct ProbFrag<kF16> {
     using Raw = f16x8;
     __device__ static Raw load(const void* P, size_t i) { return *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(P) + i); }
     __device__ static Raw zero() { Raw r; for (int e = 0; e < 8; ++e) r[e] = (_Float16)0.0f; return r; }
     struct Op { f16x8 v; };
     __device__ static Op scale(const Raw& r, float f) {
+        const _Float16 h = (_Float16)f;
         Op o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o.v[e] = (_Float16)((float)r[e] * f);
+        o.v = r * (f16x8){h, h, h, h, h, h, h, h};
         return o;
     }
     __device__ static f32x16 mma(const Op& a, const f16x8& z, f32x16 acc) { return mma32<kF16>(a.v, z, acc); }
-};
-
-// One query row per sequence (binary16 and mixed caches): the rescaled probability
-// p * 2^(m_t - M) as a binary16 hi + lo pair, so that the rescaling adds no second rounding to the
-// stored binary16 probability (the multi-query forms keep one operand: their registers are full).
-struct ProbFragF16Pair {
-    using Raw = f16x8;
-    __device__ static Raw load(const void* P, size_t i) { return ProbFrag<kF16>::load(P, i); }
-    __device__ static Raw zero() { return ProbFrag<kF16>::zero(); }
-    struct Op { f16x8 hi, lo; };
-    __device__ static Op scale(const Raw& r, float f) {
-        Op o;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = (float)r[e] * f;
-            o.hi[e] = (_Float16)v;
-            o.lo[e] = (_Float16)(v - (float)o.hi[e]);
-        }
-        return o;
-    }
-    __device__ static f32x16 mma(const Op& a, const f16x8& z, f32x16 acc) {
-        acc = mma32<kF16>(a.hi, z, acc);
-        return mma32<kF16>(a.lo, z, acc);
-    }
 };
 
 template <> struct ProbFrag<kBF16> {
@@ -529,10 +512,10 @@ __device__ __forceinline__ f16x8 q43_value_frag(const uint32_t (&run)[8], bool h
         for (int k = 0; k < 4; ++k) bits[k] = ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
     } else {
         const uint32_t w2 = run[ks] >> (8 * half);
-        const uint32_t w1 = run[4 + (ks >> 1)] >> (8 * (ks & 1) + 4 * half);
+        const uint32_t w1 = (run[4 + (ks >> 1)] >> (8 * (ks & 1) + 4 * half)) << 2;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            bits[k] = ((w2 >> (2 * k)) & 0x00030003u) | (((w1 >> k) & 0x00010001u) << 2) | 0x64006400u;
+            bits[k] = ((w2 >> (2 * k)) & 0x00030003u) | (((w1 >> k) & 0x00040004u) | 0x64006400u);
     }
     f16x8 out;
 #pragma unroll
@@ -560,7 +543,7 @@ template <int K, int NTW, bool QV, int NQ>
 __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
     using Fr = typename Elem<K>::frag;
     using Buf = ValBuf<K, NTW, QV>;
-    using PF = std::conditional_t<K == kF16 && NQ == 1, ProbFragF16Pair, ProbFrag<K>>;
+    using PF = ProbFrag<K>;
     constexpr int BPS = kMaxBlocksPerSplit / NQ;      // the planner caps splits at this many blocks
     __shared__ float s_f[NQ][kMaxHeads][2 * BPS];       // per 32-token tile
     __shared__ float s_M[NQ][kMaxHeads], s_L[NQ][kMaxHeads];
@@ -595,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void latent_values(const ValueParams p) {
         const float Mc = M != -INFINITY ? M : 0.0f;
         float L = 0.0f;
         for (int i = lane; i < 2 * nb; i += 64) {
-            const float f = __builtin_amdgcn_exp2f(st[2 * i] - Mc);
+            const float f = tile_factor(st[2 * i] - Mc);
             s_f[qi][h][i] = f;
             L += f * st[2 * i + 1];
         }

@@ -325,10 +325,11 @@ hipError_t launch_prefill_scores(const PrefillParams& p, int elem, hipStream_t s
 // section 5.3: all heads in one operand): Acc[row][h][c] = sum_n p_{row,h,n} 2^(m_t - M) Z_v[n][c]
 // over the split's blocks. One workgroup takes four query rows of one sequence and 512 value
 // channels; its eight waves own 64 channels each. Per 64-token block the probabilities of the four
-// rows (all heads) are rescaled by 2^(m_t - M) once, split into binary16 hi + lo parts and staged
-// in LDS in MFMA operand order (double-buffered), so every wave feeds them to its own channel
-// tile (two MFMAs per fragment) without repeating the rescaling. Writes (M, L, Acc) per split in
-// the decode workspace layout, read by the output step.
+// rows (all heads) are rescaled by 2^(m_t - M) once and staged in LDS in MFMA operand order
+// (double-buffered), so every wave feeds them to its own channel tiles without repeating the
+// rescaling. The tile maxima are integers, so the rescaled binary16 probability is exact (one
+// operand); a bfloat16 operand takes it as a hi + lo pair (two MFMAs per fragment). Writes
+// (M, L, Acc) per split in the decode workspace layout, read by the output step.
 constexpr int kPvWaves = 8;
 constexpr int kPvRows = 4;
 constexpr int kPvTiles = 2;                            // 32-channel tiles per wave
@@ -338,8 +339,9 @@ template <int K>
 __global__ __launch_bounds__(64 * kPvWaves, 1) void prefill_values(const ValueParams p) {
     using Fr = typename Elem<K>::frag;
     using T = typename Elem<K>::storage;
+    constexpr bool LO = K == kBF16;                     // a second (lo) operand part
     // [buffer][row][ks][lane][8]: lane l holds head l % 32, tokens 16*ks + 8*(l/32) + 0..7
-    __shared__ __attribute__((aligned(16))) T s_ph[2][kPvRows * 4 * 64 * 8], s_pl[2][kPvRows * 4 * 64 * 8];
+    __shared__ __attribute__((aligned(16))) T s_ph[2][kPvRows * 4 * 64 * 8], s_pl[2][LO ? kPvRows * 4 * 64 * 8 : 8];
     __shared__ float s_M[kPvRows][kMaxHeads], s_L[kPvRows][kMaxHeads];
 
     const int tid = threadIdx.x;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(64 * kPvWaves, 1) void prefill_values(const ValuePa
         M = wave_max(M);
         const float Mc = M != -INFINITY ? M : 0.0f;
         float L = 0.0f;
-        for (int i = lane; i < 2 * nb; i += 64) L += __builtin_amdgcn_exp2f(st[2 * i] - Mc) * st[2 * i + 1];
+        for (int i = lane; i < 2 * nb; i += 64) L += tile_factor(st[2 * i] - Mc) * st[2 * i + 1];
         L = wave_sum(L);
         if (lane == 0) { s_M[qi][h] = M; s_L[qi][h] = L; }
     }
@@ -385,24 +387,24 @@ __global__ __launch_bounds__(64 * kPvWaves, 1) void prefill_values(const ValuePa
             const f16x8 pv = *reinterpret_cast<const f16x8*>(static_cast<const _Float16*>(p.P) + prow);
             const float m = p.stats[(((size_t)(row0 + qi) * H + hh) * 2 * p.nblk + 2 * blk + (u >> 2)) * 2];
             const float M = s_M[qi][hh];
-            const float f = (h < H && m != -INFINITY && M != -INFINITY) ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-            struct __attribute__((aligned(16))) Run { T v[8]; } rh, rl;
+            const float f = h < H ? tile_factor(m - M) : 0.0f;
+            const int ks = u >> 1, l = h + 32 * (u & 1);
+            const int at = ((qi * 4 + ks) * 64 + l) * 8;
+            if constexpr (LO) {
+                struct __attribute__((aligned(16))) Run { T v[8]; } rh, rl;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float v = (float)pv[k] * f;
-                if constexpr (K == kBF16) {
+                for (int k = 0; k < 8; ++k) {
+                    const float v = (float)pv[k] * f;
                     const uint16_t hb = float_to_bf16_bits(v);
                     rh.v[k] = hb;
                     rl.v[k] = float_to_bf16_bits(v - bf16_bits_to_float(hb));
-                } else {
-                    rh.v[k] = (_Float16)v;
-                    rl.v[k] = (_Float16)(v - (float)rh.v[k]);
                 }
+                *reinterpret_cast<Run*>(&s_ph[buf][at]) = rh;
+                *reinterpret_cast<Run*>(&s_pl[buf][at]) = rl;
+            } else {
+                const _Float16 fh = (_Float16)f;
+                *reinterpret_cast<f16x8*>(&s_ph[buf][at]) = pv * (f16x8){fh, fh, fh, fh, fh, fh, fh, fh};
             }
-            const int ks = u >> 1, l = h + 32 * (u & 1);
-            const int at = ((qi * 4 + ks) * 64 + l) * 8;
-            *reinterpret_cast<Run*>(&s_ph[buf][at]) = rh;
-            *reinterpret_cast<Run*>(&s_pl[buf][at]) = rl;
         }
     };
 
@@ -452,11 +454,12 @@ __global__ __launch_bounds__(64 * kPvWaves, 1) void prefill_values(const ValuePa
             for (int ks = 0; ks < 4; ++ks) {
                 const int at = ((qi * 4 + ks) * 64 + lane) * 8;
                 const Fr ph = *reinterpret_cast<const Fr*>(&s_ph[buf][at]);
-                const Fr pl = *reinterpret_cast<const Fr*>(&s_pl[buf][at]);
 #pragma unroll
-                for (int k = 0; k < kPvTiles; ++k) {
-                    acc[qi][k] = mma32<K>(ph, z[k][ks], acc[qi][k]);
-                    acc[qi][k] = mma32<K>(pl, z[k][ks], acc[qi][k]);
+                for (int k = 0; k < kPvTiles; ++k) acc[qi][k] = mma32<K>(ph, z[k][ks], acc[qi][k]);
+                if constexpr (LO) {
+                    const Fr pl = *reinterpret_cast<const Fr*>(&s_pl[buf][at]);
+#pragma unroll
+                    for (int k = 0; k < kPvTiles; ++k) acc[qi][k] = mma32<K>(pl, z[k][ks], acc[qi][k]);
                 }
             }
     }
