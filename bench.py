@@ -53,13 +53,46 @@ DEFAULT_WORKLOAD = "longchat_b16_t32768_f16"
 MODEL_WORKLOAD = "model32_b32_t8192_f16"
 METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=16 T=32K"
 
-# Hardware-counter figures per launch from rocprofv3 runs of this bench's default command (the
-# summaries, with their commands, are the files named here): HBM bytes read + written
+# Hardware-counter figures per launch from rocprofv3 runs of this bench's command for the workload
+# (the summaries, with their commands, are the files named here): HBM bytes read + written
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a plain copy of known size gives), MfmaUtil
-# and VALUBusy (percent, rocprofv3's derived counters). Each entry carries the digest of the
-# kernel sources it was measured on; when the sources differ the figures are reported as null.
+# and VALUBusy (percent, rocprofv3's derived counters). Each workload's figures carry the digest of
+# the kernel sources they were measured on; when the sources differ they are reported as null.
 KERNEL_SOURCES = ("latent_decode.hip", "dense_decode.hip", "common.hpp")
 MEASURED = {
+    "longchat_b16_t32768_f16": {
+        "digest": "23f478f121632fa4",
+        "source": "profiles/latent_decode_counters_longchat_b16_t32768_f16.md",
+        "kernels": {
+            "latent_scores": {"traffic": 1435139659, "mfma_util_pct": 24.9, "valu_busy_pct": 75.3},
+            "latent_values": {"traffic": 1142569275, "mfma_util_pct": 8.0, "valu_busy_pct": 6.9},
+        },
+    },
+    "longchat_b16_t16384_f16": {
+        "digest": "23f478f121632fa4",
+        "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
+        "kernels": {
+            "latent_scores": {"traffic": 718569349, "mfma_util_pct": 22.9, "valu_busy_pct": 70.3},
+            "latent_values": {"traffic": 585721010, "mfma_util_pct": 6.8, "valu_busy_pct": 7.0},
+        },
+    },
+    "model32_b32_t8192_f16": {
+        "digest": "23f478f121632fa4",
+        "source": "profiles/model32_counters_b32_t8192_f16.md",
+        "kernels": {      # latent kernels: means over the 29 latent layers' launches
+            "latent_scores": {"traffic": 967539620, "mfma_util_pct": 22.4, "valu_busy_pct": 55.2},
+            "latent_values": {"traffic": 635032892, "mfma_util_pct": 6.0, "valu_busy_pct": 7.6},
+            "dense_attention": {"traffic": 4311022395, "mfma_util_pct": 0.0, "valu_busy_pct": 27.2},
+        },
+    },
+    "longchat_b16_t16384_q43": {
+        "digest": "23f478f121632fa4",
+        "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
+        "kernels": {
+            "latent_scores": {"traffic": 217546014, "mfma_util_pct": 13.1, "valu_busy_pct": 69.0},
+            "latent_values": {"traffic": 179067668, "mfma_util_pct": 9.9, "valu_busy_pct": 44.3},
+        },
+    },
 }
 
 
@@ -456,8 +489,9 @@ def measure_prefill(sk, buffers, synth, stream, hip, steps, batch=4, chunk=2048)
     """Prompt prefill through starkv_prefill_attn on the LongChat-shaped layer: `batch` sequences
     of `chunk` queries each at positions 0 .. chunk-1 over their own latents (binary16), timed with
     HIP events on the launch stream. Algorithmic work (the plain definition of latent attention,
-    causal): per (query, key, head) 2*d flop for the score and 2*r_v for the latent value sum,
-    per 32-query tile and key the key rebuild 2*d*R_k, per query the per-head output 2*H*r_v*d."""
+    causal): per (query, key, head) 2*d flop for the score and 2*r_v for the latent value sum, per
+    cached key its rebuild 2*d*R_k once (the kernel rebuilds a key tile for every 32-query tile
+    that reads it; that recomputation is not counted), per query the per-head output 2*H*r_v*d."""
     import torch
     w = synth.WORKLOADS["longchat_b16_t4096_f16"]
     ld = synth.draw_layer(w)
@@ -495,8 +529,7 @@ def measure_prefill(sk, buffers, synth, stream, hip, steps, batch=4, chunk=2048)
     if not bool(torch.isfinite(out).all()):
         raise SystemExit("non-finite prefill output")
     pairs = batch * chunk * (chunk + 1) // 2                  # causal (query, key) pairs
-    flop = (pairs * H * (2 * d + 2 * rv) + batch * ((chunk + 31) // 32) * chunk * 2 * d * Rk
-            + batch * chunk * 2 * H * rv * d)
+    flop = pairs * H * (2 * d + 2 * rv) + batch * chunk * 2 * d * Rk + batch * chunk * 2 * H * rv * d
     tf = flop / (us * 1e-6) / 1e12
     res = {"batch": batch, "chunk": chunk, "pos0": 0, "avg_us": us, "query_tokens_per_s": batch * chunk / (us * 1e-6),
            "alg_flop": flop, "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_F16_PEAK_TFLOPS,
@@ -799,11 +832,12 @@ def main(argv=None):
         roofline["mfma"] = {"achieved": mf / t_s / 1e12, "peak": MFMA_F16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": mf / t_s / 1e12 / MFMA_F16_PEAK_TFLOPS,
                             "flop_per_step": mf}
-    meas = MEASURED.get((desc["workload"], dom))
+    meas = MEASURED.get(desc["workload"])
     digest = kernel_source_digest()
-    if meas is not None and meas["digest"] == digest:
-        roofline["traffic"] = meas["traffic"]
-        roofline["counters"] = {k: meas[k] for k in ("source", "mfma_util_pct", "valu_busy_pct")}
+    if meas is not None and meas["digest"] == digest and dom in meas["kernels"]:
+        roofline["traffic"] = meas["kernels"][dom]["traffic"]
+        roofline["counters"] = {"source": meas["source"], "digest": digest,
+                                "kernels": meas["kernels"]}
     else:
         roofline["counters"] = {"source": None, "note": "no counter run on these kernel sources "
                                                         f"(digest {digest})"}
