@@ -18,7 +18,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "starkv_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# STARKV_ORACLE_LIB names another build of the same source (the sanitizer build of the tests)
+_LIB = os.environ.get("STARKV_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F64, F32, F16, BF16 = 0, 1, 2, 3
@@ -32,6 +33,18 @@ def build(force: bool = True) -> str:
                                "-ffp-contract=off", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(out: str) -> str:
+    """The same source with AddressSanitizer and UndefinedBehaviorSanitizer (gcc), for the
+    sanitizer test; load it through STARKV_ORACLE_LIB with the sanitizer runtimes preloaded."""
+    tmp = out + ".tmp"
+    subprocess.check_call(["gcc", "-O1", "-g", "-std=c11", "-fopenmp", "-fno-fast-math",
+                           "-ffp-contract=off", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                           "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, out)
+    return out
 
 
 def lib():

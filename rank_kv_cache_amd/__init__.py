@@ -44,7 +44,9 @@ EXPORTED_SYMBOLS = ["starkv_cache_bytes", "starkv_append_latents", "starkv_decod
                     "starkv_status_string", "starkv_version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libstarkv.so")
+# STARKV_LIBRARY names another build of the library (the host-sanitizer build of the tests); there
+# is no fallback: a missing library raises
+_LIB_PATH = os.environ.get("STARKV_LIBRARY") or os.path.join(_HERE, "libstarkv.so")
 _lib = None
 
 

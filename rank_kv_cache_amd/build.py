@@ -58,6 +58,32 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str) -> str:
+    """libstarkv.so with AddressSanitizer and UndefinedBehaviorSanitizer on the host code of the
+    C ABI layer (argument validation, planning, workspace layout; api.cpp), linked with the kernel
+    objects of the last build(). Device code is built as usual (the sanitizers apply to the host
+    pass only). Load it through STARKV_LIBRARY with the compiler's ASan runtime preloaded."""
+    objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s != "api.cpp"]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError(f"run build() first: {missing}")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_obj = out + ".api.o"
+    cmd = [HIPCC, *[f for f in COMMON if f != "-O3"], "-O1", "-g", *san, "-x", "hip", "-c",
+           os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for api.cpp (sanitized):\n{r.stderr}")
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, api_obj, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized):\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
