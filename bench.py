@@ -488,10 +488,11 @@ def measure_projections(sk, buffers, run, B, stream, hip, steps, model_dim=4096,
 def measure_prefill(sk, buffers, synth, stream, hip, steps, batch=4, chunk=2048):
     """Prompt prefill through starkv_prefill_attn on the LongChat-shaped layer: `batch` sequences
     of `chunk` queries each at positions 0 .. chunk-1 over their own latents (binary16), timed with
-    HIP events on the launch stream. Algorithmic work (the plain definition of latent attention,
-    causal): per (query, key, head) 2*d flop for the score and 2*r_v for the latent value sum, per
-    cached key its rebuild 2*d*R_k once (the kernel rebuilds a key tile for every 32-query tile
-    that reads it; that recomputation is not counted), per query the per-head output 2*H*r_v*d."""
+    HIP events on the launch stream. Algorithmic work: the cheaper of the two exact orders of the
+    plain definition of latent attention (causal) -- each cached key's rebuild 2*d*R_k and its
+    values per head 2*r_v*H*d once, then per (query, key, head) 2*d flop for the score and 2*d for
+    the value sum. (The latent order, values summed in latent space and B_v applied per query,
+    costs 2*r_v per (query, key, head) instead, 3.3x more at this shape; it is not counted.)"""
     import torch
     w = synth.WORKLOADS["longchat_b16_t4096_f16"]
     ld = synth.draw_layer(w)
@@ -529,7 +530,7 @@ def measure_prefill(sk, buffers, synth, stream, hip, steps, batch=4, chunk=2048)
     if not bool(torch.isfinite(out).all()):
         raise SystemExit("non-finite prefill output")
     pairs = batch * chunk * (chunk + 1) // 2                  # causal (query, key) pairs
-    flop = pairs * H * (2 * d + 2 * rv) + batch * chunk * 2 * d * Rk + batch * chunk * 2 * H * rv * d
+    flop = pairs * H * 4 * d + batch * chunk * (2 * d * Rk + 2 * rv * H * d)
     tf = flop / (us * 1e-6) / 1e12
     res = {"batch": batch, "chunk": chunk, "pos0": 0, "avg_us": us, "query_tokens_per_s": batch * chunk / (us * 1e-6),
            "alg_flop": flop, "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_F16_PEAK_TFLOPS,

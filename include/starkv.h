@@ -303,16 +303,19 @@ starkv_status starkv_decode_attn_project(const starkv_layer *layer, const starkv
  *   q:   [B][chunk][H][d] fp32, each query already rotated to its own position.
  *   bk, bv: as starkv_decode_attn.
  *   out: [B][chunk][H][d] fp32, per-head outputs before the output projection.
- * The key side runs query tiles on the matrix cores (keys rebuilt per 32-token tile, rotated in
- * fp32, query-key products as binary16 hi/lo parts); the value side sums probabilities times the
- * value latent for all heads of up to four queries at once, then applies B_v per head. Latent
- * layers with F16, BF16 or Q43 caches (Q43: sequence b must hold pos0 + chunk_lens[b] appended
- * tokens, or a multiple of 64 not above that). The workspace is
- * starkv_prefill_workspace_bytes(layer, batch, pos0, chunk) (0 for invalid or unsupported
- * requests); contents on entry are ignored.
+ * The keys (rotated to their positions in fp32) and the values of every head (Z_v B_v^h: for a
+ * chunk of queries this order costs 2 d instead of 2 r_v flop per query, key and head) of each
+ * 32-token tile up to pos0 + chunk_lens[b] are rebuilt once per call and kept in the workspace as
+ * binary16 hi/lo parts; attention then runs 32 queries per wave on the matrix cores (query-key
+ * products as hi/lo parts, an online softmax whose rescalings are exact powers of two) and writes
+ * each output once. Latent layers with F16, BF16 or Q43 caches (Q43: sequence b must hold
+ * pos0 + chunk_lens[b] appended tokens, or a multiple of 64 not above that). The workspace is
+ * starkv_prefill_workspace_bytes(layer, batch, pos0, chunk), about
+ * batch * (pos0 + chunk) * (2 (R_k + r_v) + 8 H d) bytes (0 for invalid or unsupported requests);
+ * contents on entry are ignored.
  * Errors: NULL, SHAPE (pos0 < 0, chunk < 1), CAPACITY (pos0 + chunk > capacity), DTYPE,
- * MISALIGNED, WORKSPACE, UNSUPPORTED (dense or F32 layers; pos0 + chunk above the decode length
- * limit for the query grouping). batch == 0 returns OK without enqueuing.
+ * MISALIGNED, WORKSPACE, UNSUPPORTED (dense or F32 layers; pos0 + chunk above 4,194,304 tokens;
+ * batch * chunk above 2^30). batch == 0 returns OK without enqueuing.
  */
 size_t starkv_prefill_workspace_bytes(const starkv_layer *layer, int32_t batch, int64_t pos0,
                                       int32_t chunk);

@@ -26,10 +26,8 @@ hipError_t launch_linear_store(const LinearStoreParams& p, int elem, hipStream_t
 hipError_t launch_merge(const MergeParams& p, hipStream_t st);
 hipError_t launch_project(const ProjectParams& p, int elem, hipStream_t st);
 hipError_t launch_row_fill(const RowFillParams& p, hipStream_t st);
-hipError_t launch_prefill_scores(const PrefillParams& p, int elem, hipStream_t st);
-hipError_t launch_prefill_rows(const PrefillRowsParams& p, hipStream_t st);
-hipError_t launch_prefill_project(const ProjectParams& p, int elem, hipStream_t st);
-hipError_t launch_prefill_values(const ValueParams& p, int elem, hipStream_t st);
+hipError_t launch_prefill_kv(const PrefillKVParams& p, int elem, hipStream_t st);
+hipError_t launch_prefill_attend(const PrefillFlashParams& p, hipStream_t st);
 hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
@@ -352,24 +350,31 @@ WorkspaceLayout workspace_layout(const LayerInfo& li, int B, int64_t seq_len, in
 // Prefill: query rows b * chunk + l, grouped nq at a time for the value kernel (4, 2 or 1: the
 // largest that divides the chunk, so that no group straddles two sequences); the decode workspace
 // of those rows plus per-row lengths, per-row fills and the group-to-sequence map.
+// Prefill workspace: the latent rows of tokens [0, pos0 + chunk) (binary16, or bfloat16 for a
+// bfloat16 cache), B_v in MFMA fragment order, then one key/value record of 256 * d bytes and two
+// exponents per (sequence, head, 32-token tile).
 struct PrefillLayout {
-    WorkspaceLayout w;
-    int nq = 1, rows = 0;
-    size_t row_len = 0, row_fill = 0, group_seq = 0, total = 0;
+    int64_t Tk = 0;
+    int ntiles = 0;
+    size_t zk_rows = 0, zv_rows = 0, bvf = 0, kv = 0, exps = 0, total = 0;
 };
 
 PrefillLayout prefill_layout(const LayerInfo& li, int B, int64_t pos0, int chunk) {
     PrefillLayout pl;
-    pl.nq = chunk % 4 == 0 ? 4 : chunk % 2 == 0 ? 2 : 1;
-    pl.rows = B * chunk;
-    pl.w = workspace_layout(li, pl.rows, pos0 + chunk, 0, pl.nq);
-    size_t off = pl.w.total;
-    pl.row_len = off;
-    off += align_up(static_cast<size_t>(pl.rows) * sizeof(int32_t));
-    pl.row_fill = off;
-    off += align_up(static_cast<size_t>(pl.rows) * sizeof(int32_t));
-    pl.group_seq = off;
-    off += align_up(static_cast<size_t>(pl.rows / pl.nq) * sizeof(int32_t));
+    pl.Tk = pos0 + chunk;
+    pl.ntiles = static_cast<int>((pl.Tk + 31) / 32);
+    const size_t b = static_cast<size_t>(B), T = static_cast<size_t>(pl.Tk);
+    size_t off = 0;
+    pl.zk_rows = off;
+    off += align_up(b * T * li.Rk * 2);
+    pl.zv_rows = off;
+    off += align_up(b * T * li.rv * 2);
+    pl.bvf = off;
+    off += align_up(static_cast<size_t>(li.rv) * li.H * li.D * 2);
+    pl.kv = off;
+    off += align_up(b * li.H * pl.ntiles * 256 * static_cast<size_t>(li.D));
+    pl.exps = off;
+    off += align_up(b * li.H * pl.ntiles * 2 * sizeof(int32_t));
     pl.total = off;
     return pl;
 }
@@ -1002,8 +1007,7 @@ static starkv_status prefill_check(const starkv_layer* layer, int32_t batch, int
     if (s != STARKV_OK) return s;
     if (batch < 0 || pos0 < 0 || chunk < 1) return STARKV_ERR_SHAPE;
     if (li->dense || li->cache_dt == STARKV_F32) return STARKV_ERR_UNSUPPORTED;
-    const PrefillLayout pl = prefill_layout(*li, batch, pos0, chunk);
-    if (pos0 + chunk > max_decode_len(*li, pl.nq)) return STARKV_ERR_UNSUPPORTED;
+    if (pos0 + chunk > max_decode_len(*li, 1)) return STARKV_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(batch) * chunk > (int64_t{1} << 30)) return STARKV_ERR_UNSUPPORTED;
     return STARKV_OK;
 }
@@ -1035,99 +1039,97 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
     if (!aligned16(workspace)) return STARKV_ERR_MISALIGNED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
-    const WorkspaceLayout& w = pl.w;
     const int ek = elem_kind(li.cache_dt);
-    const int stream_kind = li.q43 ? -1 : ek;
 
-    PrefillRowsParams rp;
-    rp.chunk_lens = chunk_lens;
-    rp.row_len = reinterpret_cast<int32_t*>(ws + pl.row_len);
-    rp.row_fill = reinterpret_cast<int32_t*>(ws + pl.row_fill);
-    rp.group_seq = reinterpret_cast<int32_t*>(ws + pl.group_seq);
-    rp.B = B;
-    rp.chunk = chunk;
-    rp.pos0 = static_cast<int>(pos0);
-    rp.nq = pl.nq;
-    if ((s = dev(launch_prefill_rows(rp, st))) != STARKV_OK) return s;
-
-    PrefillParams pp;
-    std::memset(&pp, 0, sizeof(pp));
-    pp.zk = cache->zk;
-    pp.bk = bk;
-    pp.q = q;
-    pp.P = ws + w.P;
-    pp.stats = reinterpret_cast<float*>(ws + w.stats);
-    pp.chunk_lens = chunk_lens;
-    pp.B = B;
-    pp.H = li.H;
-    pp.D = li.D;
-    pp.Rk = li.Rk;
-    pp.nblk_cap = cache->capacity / kTile;
-    pp.chunk = chunk;
-    pp.pos0 = static_cast<int>(pos0);
-    pp.nblk = w.nblk;
-    pp.Tp = w.nblk * kTile;
-    pp.pages = pages_of(cache);
-    pp.q_scale = q_scale_of(layer, li.D);
-    for (int h = 0; h <= li.H; ++h) pp.koff[h] = li.koff[h];
-    for (int h = 0; h < li.H; ++h) pp.rank[h] = li.rank[h];
-    for (int h = 0; h <= li.H; ++h) pp.soff[h] = li.soff[h];
-    for (int h = 0; h < li.H; ++h) pp.srank[h] = li.srank[h];
-    fill_rope(layer->rope_base, li.D, pp.rope_rev);
-    Q43Layout qk, qv;
-    if (li.q43) {
-        q43_layouts(li, &qk, &qv);
-        pp.zk_meta = cache->zk_meta;
-        pp.zk_tail = cache->zk_tail;
-        pp.ql = qk;
+    // 1. latent rows of tokens [0, pos0 + chunk_len(b)) of each sequence, token-major (mixed
+    //    4/3-bit groups dequantised to binary16 on the way)
+    for (int which = 0; which < 2; ++which) {
+        void* rows = ws + (which ? pl.zv_rows : pl.zk_rows);
+        if (li.q43) {
+            Q43Layout K, V;
+            q43_layouts(li, &K, &V);
+            Q43ReadParams r;
+            r.pages = pages_of(cache);
+            r.L = which ? V : K;
+            r.codes = which ? cache->zv : cache->zk;
+            r.meta = which ? cache->zv_meta : cache->zk_meta;
+            r.tail = which ? cache->zv_tail : cache->zk_tail;
+            r.out = rows;
+            r.B = B;
+            r.nblk_cap = cache->capacity / kTile;
+            r.t0 = 0;
+            r.t1 = pl.Tk;
+            r.full_tokens = pl.Tk / kTile * kTile;
+            r.chunk_lens = chunk_lens;
+            r.pos0 = pos0;
+            r.chunk = chunk;
+            if ((s = dev(launch_q43_readback(r, st))) != STARKV_OK) return s;
+        } else {
+            BlockXposeParams x;
+            x.pages = pages_of(cache);
+            x.src = which ? cache->zv : cache->zk;
+            x.dst = rows;
+            x.B = B;
+            x.C = which ? li.rv : li.Rk;
+            x.nblk_cap = cache->capacity / kTile;
+            x.t_begin = 0;
+            x.t_end = pl.Tk;
+            x.row0 = 0;
+            x.rows_per_seq = pl.Tk;
+            x.blk_first = 0;
+            x.to_blocks = 0;
+            x.layout = which;
+            x.chunk_lens = chunk_lens;
+            x.pos0 = pos0;
+            x.chunk = chunk;
+            if ((s = dev(launch_block_transpose(x, elem_bytes(li.cache_dt), st))) != STARKV_OK) return s;
+        }
     }
-    if ((s = dev(launch_prefill_scores(pp, stream_kind, st))) != STARKV_OK) return s;
 
-    ValueParams vp;
-    vp.pages = pages_of(cache);
-    vp.zv = cache->zv;
-    vp.P = pp.P;
-    vp.stats = pp.stats;
-    vp.ws_ml = reinterpret_cast<float*>(ws + w.ml);
-    vp.ws_acc = reinterpret_cast<float*>(ws + w.acc);
-    vp.B = pl.rows;
-    vp.H = li.H;
-    vp.rv = li.rv;
-    vp.nblk_cap = pp.nblk_cap;
-    vp.seq_len = static_cast<int>(pos0 + chunk);
-    vp.seq_lens = rp.row_len;
-    vp.seq_map = rp.group_seq;
-    vp.cache_batch = B;
-    vp.nblk = w.nblk;
-    vp.Tp = pp.Tp;
-    vp.S = w.vp.splits;
-    vp.blocks_per_split = w.vp.bps;
-    vp.zv_meta = cache->zv_meta;
-    vp.zv_tail = cache->zv_tail;
-    vp.row_fill = li.q43 ? rp.row_fill : nullptr;
-    vp.block_bytes = li.q43 ? qv.block_bytes : 0;
-    vp.n_hi = li.q43 ? qv.n_hi : 0;
-    // four rows per group on 16-bit latents: the prefill value kernel (probabilities rescaled once
-    // per block and shared by eight channel tiles); otherwise the multi-row decode value kernel
-    const hipError_t ve = (pl.nq == 4 && !li.q43)
-                              ? launch_prefill_values(vp, ek, st)
-                              : launch_latent_values(vp, stream_kind, w.vp.chunks, w.vp.ntw, pl.nq, st);
-    if ((s = dev(ve)) != STARKV_OK) return s;
-    ProjectParams pr;
-    pr.ws_ml = vp.ws_ml;
-    pr.ws_acc = vp.ws_acc;
-    pr.S = w.vp.splits;
-    pr.bv = bv;
-    pr.out = out;
-    pr.B = pl.rows;
-    pr.H = li.H;
-    pr.D = li.D;
-    pr.rv = li.rv;
-    pr.rv_src = li.rv_src;
-    // many rows: the matrix-core output step (B_v read once per 128 rows); few rows, or more
-    // splits than its weight table holds: the decode output step
-    if (pl.rows >= 128 && w.vp.splits <= 64) return dev(launch_prefill_project(pr, ek, st));
-    return dev(launch_project(pr, ek, st));
+    // 2. keys (rotated) and values (per head) of every 32-token tile, once
+    PrefillKVParams kp;
+    std::memset(&kp, 0, sizeof(kp));
+    kp.zk_rows = ws + pl.zk_rows;
+    kp.zv_rows = ws + pl.zv_rows;
+    kp.bk = bk;
+    kp.bv = bv;
+    kp.bvf = ws + pl.bvf;
+    kp.kv = ws + pl.kv;
+    kp.exps = reinterpret_cast<int32_t*>(ws + pl.exps);
+    kp.chunk_lens = chunk_lens;
+    kp.B = B;
+    kp.H = li.H;
+    kp.D = li.D;
+    kp.Rk = li.Rk;
+    kp.rv = li.rv;
+    kp.rv_src = li.rv_src;
+    kp.Tr = static_cast<int>(pl.Tk);
+    kp.ntiles = pl.ntiles;
+    kp.chunk = chunk;
+    kp.pos0 = static_cast<int>(pos0);
+    for (int h = 0; h <= li.H; ++h) kp.koff[h] = li.koff[h];
+    for (int h = 0; h < li.H; ++h) kp.rank[h] = li.rank[h];
+    for (int h = 0; h <= li.H; ++h) kp.soff[h] = li.soff[h];
+    for (int h = 0; h < li.H; ++h) kp.srank[h] = li.srank[h];
+    fill_rope(layer->rope_base, li.D, kp.rope_rev);
+    // mixed 4/3-bit rows are binary16, with binary16 factors
+    if ((s = dev(launch_prefill_kv(kp, li.q43 ? kF16 : ek, st))) != STARKV_OK) return s;
+
+    // 3. causal attention, 32 queries per wave, output written once
+    PrefillFlashParams fp;
+    fp.q = q;
+    fp.out = out;
+    fp.kv = kp.kv;
+    fp.exps = kp.exps;
+    fp.chunk_lens = chunk_lens;
+    fp.B = B;
+    fp.H = li.H;
+    fp.D = li.D;
+    fp.chunk = chunk;
+    fp.pos0 = static_cast<int>(pos0);
+    fp.ntiles = pl.ntiles;
+    fp.q_scale = q_scale_of(layer, li.D);
+    return dev(launch_prefill_attend(fp, st));
 }
 
 size_t starkv_decode_multi_workspace_bytes(const starkv_layer* layer, int32_t batch, int32_t nq,

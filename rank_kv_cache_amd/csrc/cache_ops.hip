@@ -65,17 +65,21 @@ __global__ __launch_bounds__(256) void block_transpose(const BlockXposeParams p)
             if (t >= p.t_begin && t < p.t_end) dst[gbase * 1024 + e] = tile[tok][ch];
         }
     } else {
+        // this sequence's end (a ragged prefill reads each sequence only up to its own fill)
+        const long long t_end = p.chunk_lens
+            ? min(p.t_end, p.pos0 + (long long)min(max(p.chunk_lens[b], 0), p.chunk)) : p.t_end;
+        if (tb >= t_end) return;                       // uniform: the whole block is past the end
         for (int e = threadIdx.x; e < ncg * 1024; e += 256) {
             int tok, ch;
             decode(e, &tok, &ch);
             const long long t = tb + tok;
-            if (t >= p.t_begin && t < p.t_end) tile[tok][ch] = src[gbase * 1024 + e];
+            if (t >= p.t_begin && t < t_end) tile[tok][ch] = src[gbase * 1024 + e];
         }
         __syncthreads();
         for (int e = threadIdx.x; e < 64 * 64; e += 256) {
             const int r = e >> 6, cc = e & 63;
             const long long t = tb + r;
-            if (t >= p.t_begin && t < p.t_end && c0 + cc < p.C)
+            if (t >= p.t_begin && t < t_end && c0 + cc < p.C)
                 dst[((size_t)b * p.rows_per_seq + (t - p.row0)) * p.C + c0 + cc] = tile[r][cc];
         }
     }

@@ -212,8 +212,15 @@ __global__ __launch_bounds__(256) void q43_readback(const Q43ReadParams p) {
     const long long tok = p.t0 + bt % n;
     const int b = (int)(bt / n);
     const int c = run * 8;
+    long long full = p.full_tokens;
+    if (p.chunk_lens) {
+        // this sequence's end: rows past it are not written, and none of its codes past it read
+        const long long end = p.pos0 + min(max(p.chunk_lens[b], 0), p.chunk);
+        if (tok >= end) return;
+        full = end >> 6 << 6;
+    }
     _Float16 v[8];
-    if (tok < p.full_tokens) {
+    if (tok < full) {
         const int g = (int)(tok >> 6), t = (int)(tok & 63);
         const size_t bid = block_id(p.pages, p.nblk_cap, b, g);
         const uint8_t* blk = static_cast<const uint8_t*>(p.codes) + bid * L.block_bytes;
