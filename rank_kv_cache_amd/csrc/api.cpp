@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "common.hpp"
+#include "prefill.hpp"
 
 namespace starkv {
 hipError_t launch_latent_scores(const ScoreParams& p, int elem, int groups, int splits, int maxks,

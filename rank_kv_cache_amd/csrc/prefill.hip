@@ -22,6 +22,7 @@
 //      sum goes to memory.
 
 #include "common.hpp"
+#include "prefill.hpp"
 
 namespace starkv {
 

@@ -170,3 +170,68 @@ def test_prefill_longchat_chunk_2048_sampled():
     _check_rows(got, pos0, [chunk],
                 lambda b, l, n: oracle.decode_latent(zk[:, :n], zv[:, :n], ld.bk, ld.bv, q[:, l], ranks)[0],
                 rows, "longchat chunk 2048")
+
+
+def test_prefill_q43_ragged():
+    """Mixed 4/3-bit cache filled per sequence to pos0 + chunk_len(b) (groups complete at different
+    tokens in different sequences, partial groups in the tails): every row against the oracle's
+    quantise / dequantise of that sequence's own rows; rows past a sequence's chunk are zero."""
+    from test_gpu_q43 import q43_layer
+    from test_gpu_ragged import _ragged_fill
+    from rank_kv_cache_amd import buffers
+    ranks, rv, d, B, pos0, chunk = [16, 64, 32, 48], 96, 128, 4, 100, 92
+    lens = [0, 45, 92, 7]
+    fills = [pos0 + n for n in lens]
+    cap = 256
+    ld, zk, zv, q = _latent_case("f16", d, ranks, rv, B, pos0, chunk, 650)
+    L = q43_layer(len(ranks), d, ranks, rv)
+    cache = buffers.alloc_cache(L, B, cap, fill=0xFF)
+    _ragged_fill(L, cache, zk, zv, fills)
+    got = _prefill(L, cache, pos0, chunk, q, ld.bk, ld.bv, chunk_lens=lens)
+    bits_k, bits_v = oracle.channel_bits(ranks, FRAC), oracle.channel_bits([rv], FRAC)
+    deq = []
+    for b, n in enumerate(fills):
+        ck, mk, tk = oracle.q43_pack(zk[b:b + 1, :n], bits_k, cap)
+        cv, mv, tv = oracle.q43_pack(zv[b:b + 1, :n], bits_v, cap)
+        deq.append((oracle.q43_unpack(ck, mk, tk, bits_k, n, cap), oracle.q43_unpack(cv, mv, tv, bits_v, n, cap)))
+    rows = [(b, l) for b in range(B) for l in range(chunk)]
+    _check_rows(got, pos0, lens,
+                lambda b, l, n: oracle.decode_latent(deq[b][0][:, :n], deq[b][1][:, :n], ld.bk, ld.bv,
+                                                     q[b:b + 1, l], ranks)[0],
+                rows, "q43 ragged fills")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "q43"])
+def test_prefill_paged(dtype):
+    """A paged cache (shuffled block table, poisoned spare pages) gives the same outputs as the
+    contiguous cache bit for bit, and matches the oracle; binary16 with ragged chunks, mixed
+    4/3-bit with full ones."""
+    from test_gpu_paged import paged_cache, _append_chunks
+    from test_gpu_q43 import q43_layer
+    from rank_kv_cache_amd import buffers
+    ranks, rv, d, B, pos0, chunk = [32, 16, 48], 80, 128, 3, 70, 64
+    T = pos0 + chunk
+    cap = 192
+    lens = [20, 64, 50] if dtype == "f16" else None
+    ld, zk, zv, q = _latent_case("f16", d, ranks, rv, B, pos0, chunk, 660 + (dtype == "q43"))
+    L = q43_layer(len(ranks), d, ranks, rv) if dtype == "q43" else latent_layer(len(ranks), d, ranks, rv, "f16")
+    flat = buffers.alloc_cache(L, B, cap, fill=0xFF)
+    paged, keep = paged_cache(L, B, cap, 661)
+    for c in (flat, paged):
+        _append_chunks(L, c, zk, zv, [pos0, chunk])
+    a = _prefill(L, flat, pos0, chunk, q, ld.bk, ld.bv, chunk_lens=lens)
+    b_ = _prefill(L, paged, pos0, chunk, q, ld.bk, ld.bv, chunk_lens=lens)
+    assert np.array_equal(a.view(np.uint32), b_.view(np.uint32))
+    lens_ = lens or [chunk] * B
+    if dtype == "q43":
+        bits_k, bits_v = oracle.channel_bits(ranks, FRAC), oracle.channel_bits([rv], FRAC)
+        ck, mk, tk = oracle.q43_pack(zk, bits_k, cap)
+        cv, mv, tv = oracle.q43_pack(zv, bits_v, cap)
+        rk_, rv_ = oracle.q43_unpack(ck, mk, tk, bits_k, T, cap), oracle.q43_unpack(cv, mv, tv, bits_v, T, cap)
+    else:
+        rk_, rv_ = zk, zv
+    rows = [(b, l) for b in range(B) for l in range(chunk)]
+    _check_rows(a, pos0, lens_,
+                lambda b, l, n: oracle.decode_latent(rk_[b:b + 1, :n], rv_[b:b + 1, :n], ld.bk, ld.bv,
+                                                     q[b:b + 1, l], ranks)[0],
+                rows, f"paged {dtype}")
