@@ -61,36 +61,36 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 KERNEL_SOURCES = ("latent_decode.hip", "dense_decode.hip", "common.hpp")
 MEASURED = {
     "longchat_b16_t32768_f16": {
-        "digest": "23f478f121632fa4",
+        "digest": "f23ffd8616d1e8a8",
         "source": "profiles/latent_decode_counters_longchat_b16_t32768_f16.md",
         "kernels": {
-            "latent_scores": {"traffic": 1435139659, "mfma_util_pct": 24.9, "valu_busy_pct": 75.3},
-            "latent_values": {"traffic": 1142569275, "mfma_util_pct": 8.0, "valu_busy_pct": 6.9},
+            "latent_scores": {"traffic": 1435267730, "mfma_util_pct": 24.2, "valu_busy_pct": 74.2},
+            "latent_values": {"traffic": 1142701177, "mfma_util_pct": 8.0, "valu_busy_pct": 7.0},
         },
     },
     "longchat_b16_t16384_f16": {
-        "digest": "23f478f121632fa4",
+        "digest": "f23ffd8616d1e8a8",
         "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
         "kernels": {
-            "latent_scores": {"traffic": 718569349, "mfma_util_pct": 22.9, "valu_busy_pct": 70.3},
-            "latent_values": {"traffic": 585721010, "mfma_util_pct": 6.8, "valu_busy_pct": 7.0},
+            "latent_scores": {"traffic": 718569645, "mfma_util_pct": 22.0, "valu_busy_pct": 68.6},
+            "latent_values": {"traffic": 585816177, "mfma_util_pct": 6.8, "valu_busy_pct": 7.0},
         },
     },
     "model32_b32_t8192_f16": {
-        "digest": "23f478f121632fa4",
+        "digest": "f23ffd8616d1e8a8",
         "source": "profiles/model32_counters_b32_t8192_f16.md",
         "kernels": {      # latent kernels: means over the 29 latent layers' launches
-            "latent_scores": {"traffic": 967539620, "mfma_util_pct": 22.4, "valu_busy_pct": 55.2},
-            "latent_values": {"traffic": 635032892, "mfma_util_pct": 6.0, "valu_busy_pct": 7.6},
-            "dense_attention": {"traffic": 4311022395, "mfma_util_pct": 0.0, "valu_busy_pct": 27.2},
+            "latent_scores": {"traffic": 967606991, "mfma_util_pct": 21.6, "valu_busy_pct": 53.6},
+            "latent_values": {"traffic": 635032252, "mfma_util_pct": 6.1, "valu_busy_pct": 7.7},
+            "dense_attention": {"traffic": 4311022011, "mfma_util_pct": 0.0, "valu_busy_pct": 27.2},
         },
     },
     "longchat_b16_t16384_q43": {
-        "digest": "23f478f121632fa4",
+        "digest": "f23ffd8616d1e8a8",
         "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
         "kernels": {
-            "latent_scores": {"traffic": 217546014, "mfma_util_pct": 13.1, "valu_busy_pct": 69.0},
-            "latent_values": {"traffic": 179067668, "mfma_util_pct": 9.9, "valu_busy_pct": 44.3},
+            "latent_scores": {"traffic": 217614782, "mfma_util_pct": 12.5, "valu_busy_pct": 65.1},
+            "latent_values": {"traffic": 179100596, "mfma_util_pct": 9.7, "valu_busy_pct": 43.8},
         },
     },
 }
