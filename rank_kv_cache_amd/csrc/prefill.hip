@@ -354,43 +354,33 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
     auto attend_tile = [&](int kt, int buf) __attribute__((always_inline)) {
             const _Float16* kb = reinterpret_cast<const _Float16*>(s_rec[buf]);
             const _Float16* vb = kb + KSTEPS * 2 * 64 * 8;
-            // three independent accumulation chains (hi*hi, hi*lo, lo*hi), summed at the end
-            f32x16 st, s1, s2;
+            f32x16 st;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] = s1[r] = s2[r] = 0.0f;
+            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
 #pragma unroll
             for (int step = 0; step < KSTEPS; ++step) {
                 const f16x8 kh = *reinterpret_cast<const f16x8*>(kb + ((2 * step) * 64 + lane) * 8);
                 const f16x8 kl = *reinterpret_cast<const f16x8*>(kb + ((2 * step + 1) * 64 + lane) * 8);
                 st = mma32<kF16>(kh, qh[step], st);
-                s1 = mma32<kF16>(kh, ql[step], s1);
-                s2 = mma32<kF16>(kl, qh[step], s2);
+                st = mma32<kF16>(kh, ql[step], st);
+                st = mma32<kF16>(kl, qh[step], st);
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[r] += s1[r] + s2[r];
             const int ek = s_ex[buf][0], ev = s_ex[buf][1];
-            const float un = ldexpf(1.0f, -(ek + eq));
+            const float un = ldexpf(1.0f, -(ek + eq));       // a power of two: scaling is exact
             // lane: query j, keys 32*kt + 8*(r/4) + 4*half + r%4. A tile wholly below the wave's
             // first query, with every query of the wave valid, needs no mask (wave-uniform).
-            float v[16];
+            const bool full = 32 * kt + 31 <= p.pos0 + l0 && l0 + 31 < clen;
+            bool ok[16];
             float tm = -INFINITY;
-            if (32 * kt + 31 <= p.pos0 + l0 && l0 + 31 < clen) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    v[r] = st[r] * un;
-                    tm = fmaxf(tm, v[r]);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kpos = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-                    v[r] = (qvalid && kpos <= qpos) ? st[r] * un : -INFINITY;
-                    tm = fmaxf(tm, v[r]);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int kpos = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+                ok[r] = full || (qvalid && kpos <= qpos);
+                tm = fmaxf(tm, ok[r] ? st[r] : -INFINITY);
             }
             {
                 const LanePair pr = swap32(tm);
-                tm = fmaxf(pr.a, pr.b);
+                tm = fmaxf(pr.a, pr.b) * un;
             }
             // the new running maximum, rounded up to an integer: the factors below are exact
             const float mn = tm == -INFINITY ? m : fmaxf(m, ceilf(tm));
@@ -399,7 +389,7 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
             f16x8 pf[2];
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                pf[r >> 3][r & 7] = (_Float16)(mn != -INFINITY ? __builtin_amdgcn_exp2f(v[r] - mn) : 0.0f);
+                pf[r >> 3][r & 7] = (_Float16)(ok[r] ? __builtin_amdgcn_exp2f(fmaf(st[r], un, -mn)) : 0.0f);
             // the sum of the stored values (fp32 sums of binary16 pairs), so that the normaliser
             // carries the same rounding as the weights
             float ls = 0.0f;
