@@ -235,6 +235,12 @@ starkv_status starkv_decode_attn_queries(const starkv_layer *layer, const starkv
  * most 4,194,304 / nq tokens (256 splits of 256 / nq blocks; the workspace size is 0 above it).
  * Errors: those of starkv_decode_attn with seq_len = max_len; SHAPE (nq < 1), UNSUPPORTED (other
  * nq, dense layers, F32 with nq > 1, max_len above the limit), MISALIGNED.
+ * Grouped query attention (G query heads per KV head; the reading notes' ledger counts KV heads):
+ * describe the H_kv KV heads in the layer (their ranks, B_k rows and B_v columns) and pass the
+ * query heads as rows: row b*G + g, head slot h holds query head h*G + g of sequence b, with
+ * nq = G (2 or 4; other G go through starkv_decode_attn_queries, one row per (sequence, g)). Each
+ * KV head's key is then rebuilt and rotated once for its G query heads, and its B_v slice applies
+ * to each of them.
  */
 size_t starkv_decode_multi_workspace_bytes(const starkv_layer *layer, int32_t batch, int32_t nq,
                                            int64_t max_len, int32_t num_splits);
