@@ -32,12 +32,13 @@ hipError_t launch_prefill_attend(const PrefillFlashParams& p, hipStream_t st);
 hipError_t launch_dense_split(const DenseDecodeParams& p, int elem, hipStream_t st);
 
 hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st);
-hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st);
+hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st,
+                                  bool frag_rows = false);
 hipError_t launch_append_small(const AppendSmallParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_padded_rows(const PaddedRowsParams& p, int elem_bytes, hipStream_t st);
 hipError_t launch_paged_rows(const PagedRowsParams& p, hipStream_t st);
 hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t st);
-hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st);
+hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st, bool frag_rows = false);
 hipError_t launch_hadamard_rotate(const HadamardParams& p, hipStream_t st);
 }  // namespace starkv
 
@@ -364,14 +365,16 @@ PrefillLayout prefill_layout(const LayerInfo& li, int B, int64_t pos0, int chunk
     PrefillLayout pl;
     pl.Tk = pos0 + chunk;
     pl.ntiles = static_cast<int>((pl.Tk + 31) / 32);
-    const size_t b = static_cast<size_t>(B), T = static_cast<size_t>(pl.Tk);
+    const size_t b = static_cast<size_t>(B);
     size_t off = 0;
+    // latent rows in fragment order: whole 32-token tiles per sequence
+    const size_t T32 = static_cast<size_t>(pl.ntiles) * 32;
     pl.zk_rows = off;
-    off += align_up(b * T * li.Rk * 2);
+    off += align_up(b * T32 * li.Rk * 2);
     pl.zv_rows = off;
-    off += align_up(b * T * li.rv * 2);
-    pl.bvf = off;
-    off += align_up(static_cast<size_t>(li.rv) * li.H * li.D * 2);
+    off += align_up(b * T32 * li.rv * 2);
+    pl.bvf = off;                                   // ranks padded with zero rows to a multiple of 64
+    off += align_up(static_cast<size_t>((li.rv + 63) / 64 * 64) * li.H * li.D * 2);
     pl.kv = off;
     off += align_up(b * li.H * pl.ntiles * 256 * static_cast<size_t>(li.D));
     pl.exps = off;
@@ -1042,8 +1045,8 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
     char* ws = static_cast<char*>(workspace);
     const int ek = elem_kind(li.cache_dt);
 
-    // 1. latent rows of tokens [0, pos0 + chunk_len(b)) of each sequence, token-major (mixed
-    //    4/3-bit groups dequantised to binary16 on the way)
+    // 1. latent rows of tokens [0, pos0 + chunk_len(b)) of each sequence, in MFMA fragment order
+    //    (32-token tiles of 8-channel runs; mixed 4/3-bit groups dequantised to binary16 on the way)
     for (int which = 0; which < 2; ++which) {
         void* rows = ws + (which ? pl.zv_rows : pl.zk_rows);
         if (li.q43) {
@@ -1064,7 +1067,7 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
             r.chunk_lens = chunk_lens;
             r.pos0 = pos0;
             r.chunk = chunk;
-            if ((s = dev(launch_q43_readback(r, st))) != STARKV_OK) return s;
+            if ((s = dev(launch_q43_readback(r, st, true))) != STARKV_OK) return s;
         } else {
             BlockXposeParams x;
             x.pages = pages_of(cache);
@@ -1076,14 +1079,14 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
             x.t_begin = 0;
             x.t_end = pl.Tk;
             x.row0 = 0;
-            x.rows_per_seq = pl.Tk;
+            x.rows_per_seq = static_cast<long long>(pl.ntiles) * 32;
             x.blk_first = 0;
             x.to_blocks = 0;
             x.layout = which;
             x.chunk_lens = chunk_lens;
             x.pos0 = pos0;
             x.chunk = chunk;
-            if ((s = dev(launch_block_transpose(x, elem_bytes(li.cache_dt), st))) != STARKV_OK) return s;
+            if ((s = dev(launch_block_transpose(x, elem_bytes(li.cache_dt), st, true))) != STARKV_OK) return s;
         }
     }
 
@@ -1104,7 +1107,7 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
     kp.Rk = li.Rk;
     kp.rv = li.rv;
     kp.rv_src = li.rv_src;
-    kp.Tr = static_cast<int>(pl.Tk);
+    kp.Tr = pl.ntiles * 32;
     kp.ntiles = pl.ntiles;
     kp.chunk = chunk;
     kp.pos0 = static_cast<int>(pos0);

@@ -28,7 +28,12 @@ __global__ __launch_bounds__(256) void copy_rows(const RowCopyParams p) {
 
 // Token-major rows <-> block layout (key or value latent), one (64-token block, 64-channel chunk,
 // sequence) per workgroup, staged through an LDS tile so both sides are accessed in order.
-template <typename E>
+// FR (blocks -> rows only): the rows side is in MFMA fragment order instead, 32-token tiles of
+// 8-channel runs: element (row r, channel c) of sequence b at
+// (((b * rows_per_seq / 32 + r / 32) * C / 8 + c / 8) * 32 + r % 32) * 8 + c % 8
+// (rows_per_seq a multiple of 32), so eight channels of one token are one 16-byte unit and the
+// 32 tokens of a tile are 512 contiguous bytes.
+template <typename E, bool FR>
 __global__ __launch_bounds__(256) void block_transpose(const BlockXposeParams p) {
     __shared__ E tile[64][65];                        // [token in block][channel in chunk]
     const int blk = p.blk_first + blockIdx.x;
@@ -76,11 +81,28 @@ __global__ __launch_bounds__(256) void block_transpose(const BlockXposeParams p)
             if (t >= p.t_begin && t < t_end) tile[tok][ch] = src[gbase * 1024 + e];
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-            const int r = e >> 6, cc = e & 63;
-            const long long t = tb + r;
-            if (t >= p.t_begin && t < t_end && c0 + cc < p.C)
-                dst[((size_t)b * p.rows_per_seq + (t - p.row0)) * p.C + c0 + cc] = tile[r][cc];
+        if constexpr (FR) {
+            // thread per (8-channel run, token): consecutive threads write consecutive 16-byte units
+            struct __attribute__((aligned(8 * sizeof(E)))) Run { E v[8]; };
+            for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+                const int r = (e & 31) + 32 * ((e >> 5) & 1), qq = e >> 6;
+                const long long t = tb + r;
+                if (t >= p.t_begin && t < t_end && c0 + 8 * qq < p.C) {
+                    Run v;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) v.v[k] = tile[r][8 * qq + k];
+                    const long long rr = t - p.row0;
+                    reinterpret_cast<Run*>(dst)[(((size_t)b * (p.rows_per_seq >> 5) + (rr >> 5)) * (p.C >> 3) +
+                                                 ((c0 >> 3) + qq)) * 32 + (rr & 31)] = v;
+                }
+            }
+        } else {
+            for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+                const int r = e >> 6, cc = e & 63;
+                const long long t = tb + r;
+                if (t >= p.t_begin && t < t_end && c0 + cc < p.C)
+                    dst[((size_t)b * p.rows_per_seq + (t - p.row0)) * p.C + c0 + cc] = tile[r][cc];
+            }
         }
     }
 }
@@ -204,14 +226,18 @@ hipError_t launch_copy_rows(const RowCopyParams& p, int B, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st) {
+hipError_t launch_block_transpose(const BlockXposeParams& p, int elem_bytes, hipStream_t st, bool frag_rows) {
     if (p.t_end <= p.t_begin) return hipSuccess;
+    if (frag_rows && (p.to_blocks || elem_bytes != 2 || (p.rows_per_seq & 31) || (p.row0 & 31) || (p.C & 7)))
+        return hipErrorInvalidValue;
     const int blk_last = (int)((p.t_end - 1) / 64);
     const dim3 grid(blk_last - p.blk_first + 1, (p.C + 63) / 64, p.B);
-    if (elem_bytes == 2)
-        hipLaunchKernelGGL(block_transpose<uint16_t>, grid, dim3(256), 0, st, p);
+    if (frag_rows)
+        hipLaunchKernelGGL((block_transpose<uint16_t, true>), grid, dim3(256), 0, st, p);
+    else if (elem_bytes == 2)
+        hipLaunchKernelGGL((block_transpose<uint16_t, false>), grid, dim3(256), 0, st, p);
     else if (elem_bytes == 4)
-        hipLaunchKernelGGL(block_transpose<uint32_t>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((block_transpose<uint32_t, false>), grid, dim3(256), 0, st, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

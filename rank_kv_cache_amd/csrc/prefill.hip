@@ -48,6 +48,9 @@ __device__ __forceinline__ int pf_scale_exp(float mx) {
     return max(-120, min(120, 14 - e));
 }
 
+// value ranks as staged for the preparation kernel: whole 64-rank chunks (B_v padded with zeros)
+__host__ __device__ __forceinline__ int pf_padded_rank(int rv) { return (rv + kPkChunk - 1) / kPkChunk * kPkChunk; }
+
 // tokens of sequence b that hold latents: [0, pos0 + chunk_len(b))
 __device__ __forceinline__ int pf_fill(const int32_t* chunk_lens, int b, int chunk, int pos0) {
     return pos0 + (chunk_lens ? min(max(chunk_lens[b], 0), chunk) : chunk);
@@ -64,7 +67,7 @@ struct __attribute__((aligned(16))) Run16 { uint16_t v[8]; };
 // 64 rows at a time and shared by the eight tiles.
 // ------------------------------------------------------------------------------------------------
 template <int D, int K>
-__global__ __launch_bounds__(64 * kPkWaves, 1) void prefill_kv(const PrefillKVParams p) {
+__global__ __launch_bounds__(64 * kPkWaves, 4) void prefill_kv(const PrefillKVParams p) {
     constexpr int NF = D / 2;            // RoPE frequencies
     constexpr int HMT = D / 64;          // m-tile pairs (mt, mt + HMT) of the rebuilt keys
     constexpr int MT = D / 32;
@@ -74,9 +77,10 @@ __global__ __launch_bounds__(64 * kPkWaves, 1) void prefill_kv(const PrefillKVPa
     using Fr = typename Elem<K>::frag;
     using T = typename Elem<K>::storage;
 
+    // B_k of the head during the key stage; afterwards two buffers of B_v^h chunks, in which
+    // rows c0 + 16*ks + 8*(l/32) + e of dim 32*n + l%32 sit at ((ks*NT + n)*64 + l)*8 + e
     __shared__ __attribute__((aligned(32))) T s_bk[kPfMaxFrag];
-    // B_v^h rows c0 + 16*ks + 8*(l/32) + e of dim 32*n + l%32 at ((ks*NT + n)*64 + l)*8 + e
-    __shared__ __attribute__((aligned(32))) T s_bv[kPkChunk * D];
+    static_assert(2 * kPkChunk * D <= kPfMaxFrag, "two value chunks fit where B_k was");
     // cos / sin of j*theta_i for lane l (j = l % 32), frequencies i = 32*pp + 8*g + 4*(l/32) + r:
     // entry [pp*4 + g][l] holds r = 0..3
     __shared__ __attribute__((aligned(16))) f32x4 s_cj[HMT * 4][64], s_sj[HMT * 4][64];
@@ -105,6 +109,40 @@ __global__ __launch_bounds__(64 * kPkWaves, 1) void prefill_kv(const PrefillKVPa
     const size_t rec = ((size_t)b * p.H + h) * p.ntiles + min(tile, p.ntiles - 1);
     _Float16* __restrict__ kout = reinterpret_cast<_Float16*>(static_cast<char*>(p.kv) + rec * (256 * D));
     _Float16* __restrict__ vout = kout + KSTEPS * 2 * 64 * 8;
+
+    // Value-stage staging: chunk c of B_v^h (rows 64c ..) is CKS*NT*64 16-byte runs, ITER per
+    // thread; the tile's Z_v fragments of chunk c are CKS per lane. Both are loaded one chunk
+    // ahead of their use, so that their latency overlaps the previous chunk's products.
+    constexpr int CKS = kPkChunk / 16;
+    constexpr int RUNS = CKS * NT * 64;
+    constexpr int ITER = RUNS / (64 * kPkWaves);
+    static_assert(ITER * 64 * kPkWaves == RUNS, "whole runs per thread");
+    const int nch = pf_padded_rank(p.rv) / kPkChunk;
+    const u32x4* __restrict__ bvsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.bvf)) +
+                                      (size_t)h * (pf_padded_rank(p.rv) >> 4) * NT * 64;
+    // B_v^h is padded with zero rows to whole chunks: every chunk is RUNS runs, and the staging
+    // needs neither bounds nor selects (either would let the compiler wait for the loads early).
+    auto bv_load = [&](int c, u32x4 (&v)[ITER]) {
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) v[i] = bvsrc[(size_t)c * RUNS + tid + i * 64 * kPkWaves];
+    };
+    auto bv_store = [&](int c, const u32x4 (&v)[ITER]) {
+        u32x4* dst = reinterpret_cast<u32x4*>(s_bk) + (c & 1) * RUNS;
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) dst[tid + i * 64 * kPkWaves] = v[i];
+    };
+    // The lane's key row, clamped into the fill: a key past the fill lies in the tile that holds
+    // the fill's last key, takes that key's values (so the tile's largest value, and its scale,
+    // are those of its real keys) and is causally masked for every query (probability exactly 0).
+    // In the fragment-order rows, 8 ranks of a key are one 16-byte unit and the 32 keys of a tile
+    // 512 contiguous bytes: each load of the wave reads 1 KB in two contiguous halves.
+    const int zr = min(n0 + j, fill - 1);
+    const T* __restrict__ zvrow = zv + (((size_t)(zr >> 5) * (p.rv >> 3) + half) * 32 + (zr & 31)) * 8;
+    auto zv_load = [&](int c, Fr (&a)[CKS]) {
+#pragma unroll
+        for (int ks = 0; ks < CKS; ++ks)
+            a[ks] = load_frag<K>(zvrow, (size_t)min(c * (kPkChunk / 8) + 2 * ks, (p.rv >> 3) - 2) * 256);
+    };
 
     if (tid < 64) s_rev[tid] = tid < NF ? p.rope_rev[tid] : 0.0;
     __syncthreads();
@@ -145,7 +183,9 @@ __global__ __launch_bounds__(64 * kPkWaves, 1) void prefill_kv(const PrefillKVPa
 #pragma unroll
         for (int ks = 0; ks < MAXKS; ++ks) {
             if (tok_ok) {
-                z[ks] = load_frag<K>(zk, (size_t)(n0 + j) * p.Rk + 16 * (kgrp + min(ks, nks - 1)) + 8 * half);
+                // fragment-order rows: 8 ranks of key j are one 16-byte unit, 32 keys 512 bytes
+                const int run = 2 * (kgrp + min(ks, nks - 1)) + half;
+                z[ks] = load_frag<K>(zk, (((size_t)tile * (p.Rk >> 3) + run) * 32 + j) * 8);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) z[ks][e] = 0;
@@ -214,30 +254,38 @@ __global__ __launch_bounds__(64 * kPkWaves, 1) void prefill_kv(const PrefillKVPa
     for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) va[n][r] = 0.0f;
-    for (int c0 = 0; c0 < p.rv; c0 += kPkChunk) {
-        const int cn = min(kPkChunk, p.rv - c0);              // a multiple of 16
-        __syncthreads();                                       // the previous chunk is consumed
-        {
-            const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const T*>(p.bvf) +
-                                                              ((size_t)h * (p.rv >> 4) + (c0 >> 4)) * NT * 64 * 8);
-            u32x4* dst = reinterpret_cast<u32x4*>(s_bv);
-            for (int it = tid; it < (cn >> 4) * NT * 64; it += 64 * kPkWaves) dst[it] = src[it];
+    // Two fragment buffers used in turn (the loop is unrolled by two), so that no register copy
+    // makes the next chunk's loads wait; no branch inside the loop (the last step loads and
+    // stages its clamped successor again, into the buffer nobody reads), so that the compiler's
+    // wait counts let each load run for a whole chunk. A wave past the fill computes on clamped
+    // rows and stores nothing.
+    Fr a0[CKS], a1[CKS];
+    u32x4 bq[ITER];
+    bv_load(0, bq);
+    zv_load(0, a0);
+    __syncthreads();                                           // every wave is done with B_k
+    bv_store(0, bq);
+    bv_load(min(1, nch - 1), bq);
+    __syncthreads();
+    // chunk c: B_v rows in LDS buffer c & 1, the next chunk's rows in bq, the tile's latent
+    // fragments in cur; the next chunk's fragments are loaded into nxt
+    auto vstep = [&](int c, const Fr (&cur)[CKS], Fr (&nxt)[CKS]) __attribute__((always_inline)) {
+        zv_load(min(c + 1, nch - 1), nxt);
+        const T* buf = s_bk + (c & 1) * (kPkChunk * D);
+#pragma unroll
+        for (int ks = 0; ks < CKS; ++ks) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                va[n] = mma32<K>(cur[ks], *reinterpret_cast<const Fr*>(buf + ((ks * NT + n) * 64 + lane) * 8), va[n]);
         }
+        // the other buffer was last read in chunk c - 1, before the previous barrier
+        bv_store(min(c + 1, nch - 1), bq);
+        bv_load(min(c + 2, nch - 1), bq);
         __syncthreads();
-        if (active) {
-            for (int ks = 0; ks < (cn >> 4); ++ks) {
-                Fr a;
-                if (tok_ok) {
-                    a = load_frag<K>(zv, (size_t)(n0 + j) * p.rv + c0 + 16 * ks + 8 * half);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a[e] = 0;
-                }
-#pragma unroll
-                for (int n = 0; n < NT; ++n)
-                    va[n] = mma32<K>(a, *reinterpret_cast<const Fr*>(s_bv + ((ks * NT + n) * 64 + lane) * 8), va[n]);
-            }
-        }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        vstep(c, a0, a1);
+        if (c + 1 < nch) vstep(c + 1, a1, a0);
     }
     if (active) {
         float mx = 0.0f;
@@ -472,13 +520,14 @@ template <int D>
 __global__ __launch_bounds__(256) void prefill_bv_frags(const PrefillKVParams p) {
     constexpr int NT = D / 32;
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long n_items = (long long)p.H * (p.rv >> 4) * NT * 64;
+    const int kst = pf_padded_rank(p.rv) >> 4;       // rank steps, zero rows past r_v
+    const long long n_items = (long long)p.H * kst * NT * 64;
     if (idx >= n_items) return;
     const int l = (int)(idx & 63);
     const long long f = idx >> 6;                     // (h, ks, n)
     const int n = (int)(f % NT);
-    const int ks = (int)((f / NT) % (p.rv >> 4));
-    const int h = (int)(f / NT / (p.rv >> 4));
+    const int ks = (int)((f / NT) % kst);
+    const int h = (int)(f / NT / kst);
     const uint16_t* bv = static_cast<const uint16_t*>(p.bv);
     const size_t col = (size_t)h * D + 32 * n + (l & 31);
     Run16 run;
@@ -492,7 +541,7 @@ __global__ __launch_bounds__(256) void prefill_bv_frags(const PrefillKVParams p)
 
 template <int D, int K>
 static hipError_t launch_kv_d(const PrefillKVParams& p, hipStream_t st) {
-    const long long n_items = (long long)p.H * (p.rv >> 4) * (D / 32) * 64;
+    const long long n_items = (long long)p.H * (pf_padded_rank(p.rv) >> 4) * (D / 32) * 64;
     hipLaunchKernelGGL(prefill_bv_frags<D>, dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0, st, p);
     const dim3 grid((p.ntiles + kPkWaves - 1) / kPkWaves, p.H, p.B);
     hipLaunchKernelGGL((prefill_kv<D, K>), grid, dim3(64 * kPkWaves), 0, st, p);

@@ -21,8 +21,11 @@ namespace starkv {
 //          e%4, scaled by 2^vexp;
 // and exps [2] (kexp, vexp) per record. Tokens at or past the sequence's fill are zero.
 struct PrefillKVParams {
-    const void* zk_rows;   // [B][Tr][Rk] latent rows (storage type; the layer's channel layout)
-    const void* zv_rows;   // [B][Tr][rv]
+    // latent rows (storage type; the layer's channel layout) of Tr = 32 * ntiles rows per sequence,
+    // in fragment order: (row r, channel c) of sequence b at
+    // (((b * ntiles + r / 32) * C / 8 + c / 8) * 32 + r % 32) * 8 + c % 8, C = Rk or rv
+    const void* zk_rows;
+    const void* zv_rows;
     const void* bk;        // key factors [R_k caller rows][D]
     const void* bv;        // value factor [rv_src][H*D]
     void* bvf;             // [H][rv/16][D/32][64][8]: B_v in B-operand fragment order (written here)

@@ -201,6 +201,9 @@ __device__ __forceinline__ _Float16 q43_dequant(int q, uint16_t s16, uint16_t z1
     return __builtin_fmaf16((_Float16)q, bits_f16(s16), bits_f16(z16));
 }
 
+// FR: rows in MFMA fragment order (32-token tiles of 8-channel runs, as block_transpose writes
+// them for prefill), t1 - t0 rounded up to 32 rows per sequence; else token-major [B][t1 - t0][C].
+template <bool FR>
 __global__ __launch_bounds__(256) void q43_readback(const Q43ReadParams p) {
     const Q43Layout& L = p.L;
     const int runs = L.C >> 3;
@@ -233,8 +236,15 @@ __global__ __launch_bounds__(256) void q43_readback(const Q43ReadParams p) {
         const _Float16* tail = static_cast<const _Float16*>(p.tail) + ((size_t)b * 64 + (tok & 63)) * L.C + c;
         for (int e = 0; e < 8; ++e) v[e] = tail[e];
     }
-    _Float16* dst = static_cast<_Float16*>(p.out) + (size_t)bt * L.C + c;
-    for (int e = 0; e < 8; ++e) dst[e] = v[e];
+    if constexpr (FR) {
+        struct __attribute__((aligned(16))) Run { _Float16 v[8]; } r;
+        for (int e = 0; e < 8; ++e) r.v[e] = v[e];
+        const long long rr = tok - p.t0, tiles = (n + 31) >> 5;
+        reinterpret_cast<Run*>(p.out)[(((size_t)b * tiles + (rr >> 5)) * runs + run) * 32 + (rr & 31)] = r;
+    } else {
+        _Float16* dst = static_cast<_Float16*>(p.out) + (size_t)bt * L.C + c;
+        for (int e = 0; e < 8; ++e) dst[e] = v[e];
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -314,10 +324,13 @@ hipError_t launch_q43_quantize(const Q43QuantParams& p, int ngroups, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st) {
+hipError_t launch_q43_readback(const Q43ReadParams& p, hipStream_t st, bool frag_rows) {
     const long long n = (long long)p.B * (p.t1 - p.t0) * (p.L.C / 8);
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(q43_readback, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+    if (frag_rows)
+        hipLaunchKernelGGL(q43_readback<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL(q43_readback<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
