@@ -362,32 +362,42 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
     const u32x4* __restrict__ recs = reinterpret_cast<const u32x4*>(p.kv) + ((size_t)b * p.H + h) * p.ntiles * (REC / 16);
     const int32_t* __restrict__ ex = p.exps + ((size_t)b * p.H + h) * p.ntiles * 2;
 
+    int eq;                              // the queries' power-of-two scale exponent
     // the wave's queries, scaled (softmax scale and log2 e, and a power of two for the 16-bit
     // parts) and split into the B operand of S^T: lane (query j, half), step (mt, s), entry e:
     // dim 32*mt + 16*s + 8*(e/4) + 4*half + e%4 (the key fragments' order)
-    float qm = 0.0f;
-    for (int e = lane; e < 32 * D; e += 64) {
-        const int qc = e / D, dim = e - qc * D;
-        if (l0 + qc < clen) qm = fmaxf(qm, fabsf(p.q[(((size_t)b * p.chunk + l0 + qc) * p.H + h) * D + dim] * p.q_scale));
-    }
-    qm = wave_max(qm);
-    const int eq = pf_scale_exp(qm);
-    const float qs = ldexpf(p.q_scale, eq);
+    // The two lanes of a query hold all of its dims between them, so the scale exponent comes
+    // from the loaded registers (all loads in flight at once) as the largest |q * scale| over
+    // the wave's valid queries.
     f16x8 qh[KSTEPS], ql[KSTEPS];
     {
         const float* qrow = p.q + (((size_t)b * p.chunk + min(lq, p.chunk - 1)) * p.H + h) * D;
+        f32x4 qv[KSTEPS][2];
 #pragma unroll
         for (int step = 0; step < KSTEPS; ++step) {
             const int base = 32 * (step >> 1) + 16 * (step & 1) + 4 * half;
-            const f32x4 lo4 = *reinterpret_cast<const f32x4*>(qrow + base);
-            const f32x4 hi4 = *reinterpret_cast<const f32x4*>(qrow + base + 8);
+            qv[step][0] = *reinterpret_cast<const f32x4*>(qrow + base);
+            qv[step][1] = *reinterpret_cast<const f32x4*>(qrow + base + 8);
+        }
+        float qm = 0.0f;
+        if (qvalid) {
+#pragma unroll
+            for (int step = 0; step < KSTEPS; ++step)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qm = fmaxf(qm, fabsf(qv[step][e >> 2][e & 3] * p.q_scale));
+        }
+        qm = wave_max(qm);
+        const int eq0 = pf_scale_exp(qm);
+        const float qs = ldexpf(p.q_scale, eq0);
+#pragma unroll
+        for (int step = 0; step < KSTEPS; ++step)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float v = qvalid ? (e < 4 ? lo4[e] : hi4[e - 4]) * qs : 0.0f;
+                const float v = qvalid ? qv[step][e >> 2][e & 3] * qs : 0.0f;
                 qh[step][e] = (_Float16)v;
                 ql[step][e] = (_Float16)(v - (float)qh[step][e]);
             }
-        }
+        eq = eq0;
     }
 
     float m = -INFINITY, l = 0.0f;       // running maximum (an integer, log2 units) and sum
@@ -405,13 +415,20 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
             f32x16 st;
 #pragma unroll
             for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+            // key fragments read one step ahead of their products
+            f16x8 kf[2][2];
+            kf[0][0] = *reinterpret_cast<const f16x8*>(kb + lane * 8);
+            kf[0][1] = *reinterpret_cast<const f16x8*>(kb + (64 + lane) * 8);
 #pragma unroll
             for (int step = 0; step < KSTEPS; ++step) {
-                const f16x8 kh = *reinterpret_cast<const f16x8*>(kb + ((2 * step) * 64 + lane) * 8);
-                const f16x8 kl = *reinterpret_cast<const f16x8*>(kb + ((2 * step + 1) * 64 + lane) * 8);
-                st = mma32<kF16>(kh, qh[step], st);
-                st = mma32<kF16>(kh, ql[step], st);
-                st = mma32<kF16>(kl, qh[step], st);
+                if (step + 1 < KSTEPS) {
+                    kf[(step + 1) & 1][0] = *reinterpret_cast<const f16x8*>(kb + ((2 * step + 2) * 64 + lane) * 8);
+                    kf[(step + 1) & 1][1] = *reinterpret_cast<const f16x8*>(kb + ((2 * step + 3) * 64 + lane) * 8);
+                }
+                __builtin_amdgcn_sched_barrier(0);             // keep the reads ahead of the products
+                st = mma32<kF16>(kf[step & 1][0], qh[step], st);
+                st = mma32<kF16>(kf[step & 1][0], ql[step], st);
+                st = mma32<kF16>(kf[step & 1][1], qh[step], st);
             }
             const int ek = s_ex[buf][0], ev = s_ex[buf][1];
             const float un = ldexpf(1.0f, -(ek + eq));       // a power of two: scaling is exact
@@ -458,15 +475,21 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[n][r] *= g;
             }
+            // value fragments, likewise one (dim tile, key half) ahead
+            f16x8 vf[2][2];
+            vf[0][0] = *reinterpret_cast<const f16x8*>(vb + lane * 8);
+            vf[0][1] = *reinterpret_cast<const f16x8*>(vb + (64 + lane) * 8);
 #pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const f16x8 vh = *reinterpret_cast<const f16x8*>(vb + (((n * 2 + t) * 2) * 64 + lane) * 8);
-                    const f16x8 vl = *reinterpret_cast<const f16x8*>(vb + (((n * 2 + t) * 2 + 1) * 64 + lane) * 8);
-                    acc[n] = mma32<kF16>(vh, pf[t], acc[n]);
-                    acc[n] = mma32<kF16>(vl, pf[t], acc[n]);
+            for (int u = 0; u < 2 * NT; ++u) {
+                if (u + 1 < 2 * NT) {
+                    vf[(u + 1) & 1][0] = *reinterpret_cast<const f16x8*>(vb + ((2 * u + 2) * 64 + lane) * 8);
+                    vf[(u + 1) & 1][1] = *reinterpret_cast<const f16x8*>(vb + ((2 * u + 3) * 64 + lane) * 8);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                const int n = u >> 1, t = u & 1;               // u = n * 2 + t
+                acc[n] = mma32<kF16>(vf[u & 1][0], pf[t], acc[n]);
+                acc[n] = mma32<kF16>(vf[u & 1][1], pf[t], acc[n]);
+            }
     };
 
     // Records are loaded one tile ahead: tile kt + 1's loads are issued (into registers) at the
