@@ -408,8 +408,9 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[n][r] = 0.0f;
 
-    // one key tile of the record in LDS buffer buf
-    auto attend_tile = [&](int kt, int buf) __attribute__((always_inline)) {
+    // one key tile of the record in LDS buffer buf; masked: the tile reaches past the wave's first
+    // query (or the wave holds queries past its chunk), so keys are compared with positions
+    auto attend_tile = [&](int kt, int buf, bool masked) __attribute__((always_inline)) {
             const _Float16* kb = reinterpret_cast<const _Float16*>(s_rec[buf]);
             const _Float16* vb = kb + KSTEPS * 2 * 64 * 8;
             f32x16 st;
@@ -431,18 +432,20 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
                 st = mma32<kF16>(kf[step & 1][1], qh[step], st);
             }
             const int ek = s_ex[buf][0], ev = s_ex[buf][1];
-            const float un = ldexpf(1.0f, -(ek + eq));       // a power of two: scaling is exact
-            // lane: query j, keys 32*kt + 8*(r/4) + 4*half + r%4. A tile wholly below the wave's
-            // first query, with every query of the wave valid, needs no mask (wave-uniform).
-            const bool full = 32 * kt + 31 <= p.pos0 + l0 && l0 + 31 < clen;
-            bool ok[16];
-            float tm = -INFINITY;
+            // a power of two (scaling is exact), kept above 0 so that a masked -inf stays -inf
+            const float un = ldexpf(1.0f, -min(ek + eq, 149));
+            // lane: query j, keys 32*kt + 8*(r/4) + 4*half + r%4. A masked product becomes -inf,
+            // whose weight below is exactly 0; only the wave's last tiles take this branch.
+            if (masked) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int kpos = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-                ok[r] = full || (qvalid && kpos <= qpos);
-                tm = fmaxf(tm, ok[r] ? st[r] : -INFINITY);
+                for (int r = 0; r < 16; ++r) {
+                    const int kpos = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (!(qvalid && kpos <= qpos)) st[r] = -INFINITY;
+                }
             }
+            float tm = st[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) tm = fmaxf(tm, st[r]);
             {
                 const LanePair pr = swap32(tm);
                 tm = fmaxf(pr.a, pr.b) * un;
@@ -451,10 +454,11 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
             const float mn = tm == -INFINITY ? m : fmaxf(m, ceilf(tm));
             const float fl = m == -INFINITY ? 0.0f : ldexpf(1.0f, (int)(m - mn));
             const float g = ldexpf(fl, ev - E);               // sums rescaled, values' frame moved to ev
+            // with no key seen yet (mn = -inf) every product here is -inf: offset 0 keeps exp2 at 0
+            const float mo = mn == -INFINITY ? 0.0f : mn;
             f16x8 pf[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                pf[r >> 3][r & 7] = (_Float16)(ok[r] ? __builtin_amdgcn_exp2f(fmaf(st[r], un, -mn)) : 0.0f);
+            for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(fmaf(st[r], un, -mo));
             // the sum of the stored values (fp32 sums of binary16 pairs), so that the normaliser
             // carries the same rounding as the weights
             float ls = 0.0f;
@@ -516,7 +520,11 @@ __global__ __launch_bounds__(64 * kPaWaves, 2) void prefill_attend(const Prefill
         const int buf = kt & 1;
         Pref nxt;
         if (kt + 1 < btiles) nxt = issue(kt + 1);
-        if (kt < wtiles) attend_tile(kt, buf);
+        if (kt < wtiles) {
+            // a tile wholly below the wave's first query, with every query of the wave valid,
+            // needs no mask (wave-uniform); only the wave's last tiles take the masked form
+            attend_tile(kt, buf, !(32 * kt + 31 <= p.pos0 + l0 && l0 + 31 < clen));
+        }
         if (kt + 1 < btiles) land(nxt, buf ^ 1);
         __syncthreads();
     }
