@@ -317,8 +317,9 @@ starkv_status starkv_decode_attn_project(const starkv_layer *layer, const starkv
  * each output once. Latent layers with F16, BF16 or Q43 caches (Q43: sequence b must hold
  * pos0 + chunk_lens[b] appended tokens, or a multiple of 64 not above that). The workspace is
  * starkv_prefill_workspace_bytes(layer, batch, pos0, chunk), about
- * batch * (pos0 + chunk) * (2 (R_k + r_v) + 8 H d) bytes (0 for invalid or unsupported requests);
- * contents on entry are ignored.
+ * batch * (pos0 + chunk) * (2 r_v + 8 H d) bytes, plus batch * (pos0 + chunk) * 2 R_k for Q43
+ * (16-bit key latents are read in place) (0 for invalid or unsupported requests); contents on
+ * entry are ignored.
  * Errors: NULL, SHAPE (pos0 < 0, chunk < 1), CAPACITY (pos0 + chunk > capacity), DTYPE,
  * MISALIGNED, WORKSPACE, UNSUPPORTED (dense or F32 layers; pos0 + chunk above 4,194,304 tokens;
  * batch * chunk above 2^30). batch == 0 returns OK without enqueuing.

@@ -369,8 +369,8 @@ PrefillLayout prefill_layout(const LayerInfo& li, int B, int64_t pos0, int chunk
     size_t off = 0;
     // latent rows in fragment order: whole 32-token tiles per sequence
     const size_t T32 = static_cast<size_t>(pl.ntiles) * 32;
-    pl.zk_rows = off;
-    off += align_up(b * T32 * li.Rk * 2);
+    pl.zk_rows = off;                               // 16-bit caches: keys read from the cache
+    if (li.q43) off += align_up(b * T32 * li.Rk * 2);
     pl.zv_rows = off;
     off += align_up(b * T32 * li.rv * 2);
     pl.bvf = off;                                   // ranks padded with zero rows to a multiple of 64
@@ -1046,8 +1046,9 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
     const int ek = elem_kind(li.cache_dt);
 
     // 1. latent rows of tokens [0, pos0 + chunk_len(b)) of each sequence, in MFMA fragment order
-    //    (32-token tiles of 8-channel runs; mixed 4/3-bit groups dequantised to binary16 on the way)
-    for (int which = 0; which < 2; ++which) {
+    //    (32-token tiles of 8-channel runs; mixed 4/3-bit groups dequantised to binary16 on the
+    //    way); 16-bit key latents need no copy (the cache's key layout is already fragment order)
+    for (int which = li.q43 ? 0 : 1; which < 2; ++which) {   // 16-bit keys: read in place
         void* rows = ws + (which ? pl.zv_rows : pl.zk_rows);
         if (li.q43) {
             Q43Layout K, V;
@@ -1095,6 +1096,11 @@ starkv_status starkv_prefill_attn(const starkv_layer* layer, const starkv_cache*
     std::memset(&kp, 0, sizeof(kp));
     kp.zk_rows = ws + pl.zk_rows;
     kp.zv_rows = ws + pl.zv_rows;
+    if (!li.q43) {
+        kp.zk_cache = cache->zk;
+        kp.pages = pages_of(cache);
+        kp.nblk_cap = cache->capacity / kTile;
+    }
     kp.bk = bk;
     kp.bv = bv;
     kp.bvf = ws + pl.bvf;

@@ -180,12 +180,20 @@ __global__ __launch_bounds__(64 * kPkWaves, 4) void prefill_kv(const PrefillKVPa
         pf_wave_sync();
         // latent fragments: lane column j = key n0 + j, eight ranks per lane (zero past the fill)
         Fr z[MAXKS];
+        // the tile's 64-token block in the cache (a 32-token tile never straddles two)
+        const size_t zblk = p.zk_cache ? block_id(p.pages, p.nblk_cap, b, n0 >> 6) : 0;
 #pragma unroll
         for (int ks = 0; ks < MAXKS; ++ks) {
             if (tok_ok) {
-                // fragment-order rows: 8 ranks of key j are one 16-byte unit, 32 keys 512 bytes
-                const int run = 2 * (kgrp + min(ks, nks - 1)) + half;
-                z[ks] = load_frag<K>(zk, (((size_t)tile * (p.Rk >> 3) + run) * 32 + j) * 8);
+                const int g = kgrp + min(ks, nks - 1);       // the 16-rank group
+                if (p.zk_cache) {
+                    // cache block layout: 16 ranks of each token contiguous, tokens in order
+                    z[ks] = load_frag<K>(static_cast<const T*>(p.zk_cache),
+                                         ((zblk * (p.Rk >> 4) + g) * 64 + ((n0 + j) & 63)) * 16 + 8 * half);
+                } else {
+                    // fragment-order rows: 8 ranks of key j are one 16-byte unit, 32 keys 512 bytes
+                    z[ks] = load_frag<K>(zk, (((size_t)tile * (p.Rk >> 3) + 2 * g + half) * 32 + j) * 8);
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) z[ks][e] = 0;

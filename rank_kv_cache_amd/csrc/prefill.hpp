@@ -24,8 +24,14 @@ struct PrefillKVParams {
     // latent rows (storage type; the layer's channel layout) of Tr = 32 * ntiles rows per sequence,
     // in fragment order: (row r, channel c) of sequence b at
     // (((b * ntiles + r / 32) * C / 8 + c / 8) * 32 + r % 32) * 8 + c % 8, C = Rk or rv
-    const void* zk_rows;
+    const void* zk_rows;   // unused when zk_cache is set
     const void* zv_rows;
+    // 16-bit caches: the key latents are read straight from the cache's block layout
+    // zk[block][R_k/16][64][16] (block = the pages' block of (b, token / 64)), where eight ranks of
+    // a token are already one 16-byte unit and the 32 tokens of a tile 1 KB; NULL: from zk_rows
+    const void* zk_cache = nullptr;
+    BlockMap pages;
+    int nblk_cap = 0;
     const void* bk;        // key factors [R_k caller rows][D]
     const void* bv;        // value factor [rv_src][H*D]
     void* bvf;             // [H][rv/16][D/32][64][8]: B_v in B-operand fragment order (written here)
