@@ -28,8 +28,8 @@
  *    fp16 scale and zero point.
  *
  * Readings where the pages are silent (RoPE convention, query position, softmax scale, the
- * quantiser's rounding rule, the packed byte layout, the Hadamard block size) are listed in
- * the design doc of this repository; each is restated next to the function that implements it.
+ * quantiser's rounding rule, the packed byte layout, the Hadamard block size) are each stated
+ * next to the function that implements it.
  *
  * Parity pins (tests/test_oracle_pins.py): every function here is checked against something
  * other than itself -- closed forms, library routines, brute force in 40-digit arithmetic,

@@ -348,8 +348,8 @@ _ROT_SEGS = np.array([[0, 3], [3, 2], [5, 6], [11, 12], [23, 8], [31, 24], [55, 
 
 def test_rotation_fp16_storage_rule():
     """orc_rotate_rows_f16 / orc_rotate_factor_f16 (Zhou notes, section 6.1 and Fig. 5: the latents
-    are rotated blockwise before they are quantised; the stored binary16 rule is a reading of
-    this build): every element is the exact signed sum times binary64(1/sqrt(b)), rounded to
+    are rotated blockwise before they are quantised; the pages do not fix the binary16 rounding
+    of the stored result, so the rule is a reading): every element is the exact signed sum times binary64(1/sqrt(b)), rounded to
     binary64 and then to binary16, bit for bit, for every block size 1 ... 64 — in particular
     2, 8 and 32, whose scale is not a power of two. A wrong sign or index of the Sylvester
     matrix, a transposed block, a binary32 intermediate or a binary32 1/sqrt(b) fails here."""
