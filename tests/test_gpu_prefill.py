@@ -92,6 +92,28 @@ def test_prefill_latent_every_row(dtype, d, chunk, pos0):
                 rows, f"{dtype} d={d} chunk={chunk} pos0={pos0}")
 
 
+@pytest.mark.parametrize("dtype,ranks,rv,chunk,pos0", [
+    ("f16", [24, 40, 12, 100], 100, 45, 19),
+    ("f16", [16, 48, 32, 64], 160, 1, 0),
+    ("bf16", [16, 48, 32, 64], 96, 1, 200),
+])
+def test_prefill_edge_shapes(dtype, ranks, rv, chunk, pos0):
+    """Key ranks off the 16-channel step and a value rank of 100 (stored rounded up to 112, the
+    value chunks then end in zero rows); a one-query chunk at position 0 (the first token attends
+    to itself alone) and after a 200-token prefix."""
+    d, B = 128, 2
+    ld, zk, zv, q = _latent_case(dtype, d, ranks, rv, B, pos0, chunk, 700 + chunk + pos0)
+    L = latent_layer(len(ranks), d, ranks, rv, dtype)
+    dev = DeviceLayer(L, zk, zv, ld.bk, ld.bv)
+    bf16 = dtype == "bf16"
+    got = _prefill(L, dev.cache, pos0, chunk, q, dev.bk, dev.bv, bf16=bf16)
+    rows = [(b, l) for b in range(B) for l in range(chunk)]
+    _check_rows(got, pos0, [chunk] * B,
+                lambda b, l, n: oracle.decode_latent(zk[b:b + 1, :n], zv[b:b + 1, :n], ld.bk, ld.bv,
+                                                     q[b:b + 1, l], ranks, bf16=bf16)[0],
+                rows, f"{dtype} ranks={ranks} rv={rv} chunk={chunk} pos0={pos0}")
+
+
 def test_prefill_ragged_chunks():
     """Per-sequence chunk lengths (0, 1, 31, 64 of a 64-query call): rows past a sequence's chunk
     are empty and give zeros."""
@@ -123,16 +145,17 @@ def test_prefill_peaked_attention():
                 rows, "peaked (q x 8)")
 
 
-@pytest.mark.parametrize("pos0,chunk", [(0, 128), (100, 92), (64, 64)])
-def test_prefill_q43(pos0, chunk):
+@pytest.mark.parametrize("pos0,chunk,d", [(0, 128, 128), (100, 92, 128), (64, 64, 128), (64, 64, 64)])
+def test_prefill_q43(pos0, chunk, d):
     """Mixed 4/3-bit cache holding exactly the prefix plus the chunk (so its partial last group is
-    in the tail): every row against the oracle's quantise / dequantise of the same rows."""
+    in the tail): every row against the oracle's quantise / dequantise of the same rows; head dims
+    128 and 64."""
     from test_gpu_q43 import _append, q43_layer
     from rank_kv_cache_amd import buffers
-    ranks, rv, d, B = [16, 64, 32, 48], 96, 128, 2
+    ranks, rv, B = ([16, 64, 32, 48] if d == 128 else [16, 32, 48, 64]), 96, 2
     T = pos0 + chunk
     cap = ((T + 63) // 64) * 64 + 64
-    ld, zk, zv, q = _latent_case("f16", d, ranks, rv, B, pos0, chunk, 630 + pos0)
+    ld, zk, zv, q = _latent_case("f16", d, ranks, rv, B, pos0, chunk, 630 + pos0 + d)
     L = q43_layer(len(ranks), d, ranks, rv)
     cache = buffers.alloc_cache(L, B, cap, fill=0xFF)
     _append(L, cache, zk, zv, [T])
@@ -147,7 +170,7 @@ def test_prefill_q43(pos0, chunk):
     _check_rows(got, pos0, [chunk] * B,
                 lambda b, l, n: oracle.decode_latent(deq[b][0][:, :n], deq[b][1][:, :n], ld.bk, ld.bv,
                                                      q[b:b + 1, l], ranks)[0],
-                rows, f"q43 pos0={pos0} chunk={chunk}")
+                rows, f"q43 d={d} pos0={pos0} chunk={chunk}")
 
 
 def test_prefill_longchat_chunk_2048_sampled():
