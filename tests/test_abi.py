@@ -328,6 +328,16 @@ def test_prefill_validation():
     assert pf(Cc=_cache(batch=0)) == 0
     assert sk.starkv_prefill_workspace_bytes(L, 2, -1, 20) == 0
     assert sk.starkv_prefill_workspace_bytes(L, 2, 0, 0) == 0
+    # the length limit (4,194,304 tokens of fill) and the query-count limit (batch * chunk <= 2^30)
+    big = _cache(capacity=1 << 23)
+    assert pf(Cc=big, pos0=(1 << 22) - 10, chunk=20) == 8
+    assert sk.starkv_prefill_workspace_bytes(L, 2, (1 << 22) - 10, 20) == 0
+    assert pf(Cc=_cache(batch=1 << 11, capacity=1 << 20), pos0=0, chunk=(1 << 19) + 64) == 8
+    # 16-bit key latents are read in place: only the mixed 4/3-bit layer stages key rows
+    q43 = _latent(cache_dtype=sk.Q43)
+    Rk, T = 16 + 32 + 48 + 64, 32
+    assert sk.starkv_prefill_workspace_bytes(q43, 2, 0, T) >= \
+        sk.starkv_prefill_workspace_bytes(L, 2, 0, T) + 2 * T * Rk * 2
 
 
 def test_decode_project_validation():
