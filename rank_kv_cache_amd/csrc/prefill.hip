@@ -131,9 +131,10 @@ __global__ __launch_bounds__(64 * kPkWaves, 4) void prefill_kv(const PrefillKVPa
 #pragma unroll
         for (int i = 0; i < ITER; ++i) dst[tid + i * 64 * kPkWaves] = v[i];
     };
-    // The lane's key row, clamped into the fill: a key past the fill lies in the tile that holds
-    // the fill's last key, takes that key's values (so the tile's largest value, and its scale,
-    // are those of its real keys) and is causally masked for every query (probability exactly 0).
+    // The lane's key row, clamped into the fill: a key past the fill in the tile that holds the
+    // fill's last key takes that key's values (so the tile's largest value, and its scale, are
+    // those of its real keys) and is causally masked for every query (probability exactly 0); a
+    // wave whose whole tile lies past the fill reads valid rows and stores nothing.
     // In the fragment-order rows, 8 ranks of a key are one 16-byte unit and the 32 keys of a tile
     // 512 contiguous bytes: each load of the wave reads 1 KB in two contiguous halves.
     const int zr = min(n0 + j, fill - 1);
