@@ -189,6 +189,11 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
 
     // ---- constant rotation by j*theta_i for this lane's column j and its frequencies ----
     // Frequencies held by the lane: i = 32*pp + 8*g + 4*half + r, pp < HMT, g < 4, r < 4.
+    // One query row: the rotation is kept in tangent form, (cos, tan = sin / cos), so that the
+    // rotate-and-dot of a rotary pair takes five operations instead of six:
+    // q1 (a c - b s) + q2 (a s + b c) = c (q1 (a - t b) + q2 (b + t a)). A cosine of exactly 0
+    // (or below 2^-60) is moved to +-2^-60, which changes the rotated pair by at most 2^-60 of it.
+    constexpr bool TANGENT = NQ == 1;
     float cj[HMT][4][4], sj[HMT][4][4];
 #pragma unroll
     for (int pp = 0; pp < HMT; ++pp)
@@ -199,6 +204,10 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
                 const int i = 32 * pp + 8 * g + 4 * half + r;
                 const double rev = (double)j * s_rev[i];
                 sincos_rev((float)(rev - floor(rev)), &cj[pp][g][r], &sj[pp][g][r]);
+                if constexpr (TANGENT) {
+                    if (fabsf(cj[pp][g][r]) < 0x1p-60f) cj[pp][g][r] = copysignf(0x1p-60f, cj[pp][g][r]);
+                    sj[pp][g][r] = sj[pp][g][r] / cj[pp][g][r];
+                }
             }
     __syncthreads();
 
@@ -306,12 +315,18 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
                         for (int r = 0; r < 4; ++r) {
                             const float a = acc0[4 * g + r], bb = acc1[4 * g + r];
                             const float c = cj[pp][g][r], sn = sj[pp][g][r];
-                            // the key rotated by j*theta, then its dot with each query
-                            const float ra = fmaf(-bb, sn, a * c), rb = fmaf(a, sn, bb * c);
+                            if constexpr (TANGENT) {
+                                // c (q1 (a - t b) + q2 (b + t a)), t = tan(j theta) in sj
+                                const float u = fmaf(-bb, sn, a), v = fmaf(a, sn, bb);
+                                sc[0][nt] = fmaf(c, fmaf(q1[0][r], u, q2[0][r] * v), sc[0][nt]);
+                            } else {
+                                // the key rotated by j*theta, then its dot with each query
+                                const float ra = fmaf(-bb, sn, a * c), rb = fmaf(a, sn, bb * c);
 #pragma unroll
-                            for (int qi = 0; qi < NQ; ++qi) {
-                                sc[qi][nt] = fmaf(q1[qi][r], ra, sc[qi][nt]);
-                                sc[qi][nt] = fmaf(q2[qi][r], rb, sc[qi][nt]);
+                                for (int qi = 0; qi < NQ; ++qi) {
+                                    sc[qi][nt] = fmaf(q1[qi][r], ra, sc[qi][nt]);
+                                    sc[qi][nt] = fmaf(q2[qi][r], rb, sc[qi][nt]);
+                                }
                             }
                         }
                     }
