@@ -61,36 +61,36 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 KERNEL_SOURCES = ("latent_decode.hip", "dense_decode.hip", "common.hpp")
 MEASURED = {
     "longchat_b16_t32768_f16": {
-        "digest": "f23ffd8616d1e8a8",
+        "digest": "d27dc45075513ef7",
         "source": "profiles/latent_decode_counters_longchat_b16_t32768_f16.md",
         "kernels": {
-            "latent_scores": {"traffic": 1435267730, "mfma_util_pct": 24.2, "valu_busy_pct": 74.2},
-            "latent_values": {"traffic": 1142701177, "mfma_util_pct": 8.0, "valu_busy_pct": 7.0},
+            "latent_scores": {"traffic": 1436869054, "mfma_util_pct": 24.8, "valu_busy_pct": 65.4},
+            "latent_values": {"traffic": 1142752152, "mfma_util_pct": 7.9, "valu_busy_pct": 6.6},
         },
     },
     "longchat_b16_t16384_f16": {
-        "digest": "f23ffd8616d1e8a8",
+        "digest": "d27dc45075513ef7",
         "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
         "kernels": {
-            "latent_scores": {"traffic": 718569645, "mfma_util_pct": 22.0, "valu_busy_pct": 68.6},
-            "latent_values": {"traffic": 585816177, "mfma_util_pct": 6.8, "valu_busy_pct": 7.0},
+            "latent_scores": {"traffic": 719175669, "mfma_util_pct": 21.9, "valu_busy_pct": 62.1},
+            "latent_values": {"traffic": 585730482, "mfma_util_pct": 6.7, "valu_busy_pct": 7.0},
         },
     },
     "model32_b32_t8192_f16": {
-        "digest": "f23ffd8616d1e8a8",
+        "digest": "d27dc45075513ef7",
         "source": "profiles/model32_counters_b32_t8192_f16.md",
         "kernels": {      # latent kernels: means over the 29 latent layers' launches
-            "latent_scores": {"traffic": 967606991, "mfma_util_pct": 21.6, "valu_busy_pct": 53.6},
-            "latent_values": {"traffic": 635032252, "mfma_util_pct": 6.1, "valu_busy_pct": 7.7},
-            "dense_attention": {"traffic": 4311022011, "mfma_util_pct": 0.0, "valu_busy_pct": 27.2},
+            "latent_scores": {"traffic": 966357486, "mfma_util_pct": 22.2, "valu_busy_pct": 50.8},
+            "latent_values": {"traffic": 634984110, "mfma_util_pct": 6.0, "valu_busy_pct": 7.6},
+            "dense_attention": {"traffic": 4311022026, "mfma_util_pct": 0.0, "valu_busy_pct": 27.2},
         },
     },
     "longchat_b16_t16384_q43": {
-        "digest": "f23ffd8616d1e8a8",
+        "digest": "d27dc45075513ef7",
         "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
         "kernels": {
-            "latent_scores": {"traffic": 217614782, "mfma_util_pct": 12.5, "valu_busy_pct": 65.1},
-            "latent_values": {"traffic": 179100596, "mfma_util_pct": 9.7, "valu_busy_pct": 43.8},
+            "latent_scores": {"traffic": 218148111, "mfma_util_pct": 13.3, "valu_busy_pct": 65.0},
+            "latent_values": {"traffic": 179099124, "mfma_util_pct": 9.9, "valu_busy_pct": 44.5},
         },
     },
 }
