@@ -172,20 +172,35 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // row's first bit in the window, n: 4-bit channels at the start of the group; sc / zc: the scales
 // and zero points of the eight channels, two per word. Each value is binary16(q*s + z) rounded
 // once (one fp16 FMA per pair); q is formed exactly as binary16(1024 + q) - 1024.
+// both 16-bit halves of x shifted right by s
+__device__ __forceinline__ uint32_t pk_shr16(uint32_t x, int s) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 v = __builtin_bit_cast(u16x2, x) >> (u16x2){(unsigned short)s, (unsigned short)s};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ f16x8 q43_key_frag(uint32_t w0, uint32_t w1, uint32_t w2, int sh, int n,
                                              int half, const u32x4& sc, const u32x4& zc) {
-    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
-    const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
-    const uint32_t low24 = (half ? __builtin_amdgcn_alignbit(hi, lo, 24) : lo) & 0xffffffu;
-    const int m = min(max(n - 8 * half, 0), 8);
-    const uint32_t ext = (hi >> (16 + 8 * half)) & ((1u << m) - 1u);
+    const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);    // row bits 0 .. 31
+    const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);    // row bits 32 .. 63
+    // the lane's eight 3-bit fields (row bits 24*half ..) and the fourth bits of those of its
+    // channels that are 4-bit (row bits 48 + 8*half ..)
+    const uint32_t L = __builtin_amdgcn_alignbit(hi, lo, 24 * half);
+    const uint32_t ext = __builtin_amdgcn_ubfe(hi, 16 + 8 * half, min(max(n - 8 * half, 0), 8));
+    // Channel pair (2k, 2k+1) goes to the low and high 16-bit halves. w_a holds fields 0.. in its
+    // low half and fields 1.. in its high half (pairs 0 and 1, the latter after a 6-bit shift of
+    // each half), w_b the same from field 4; v holds fourth bit e at bit 3 + e of the low half and
+    // at bit 2 + e of the high half, so a 2k-bit shift of each half brings pair k's to bit 3.
+    const uint32_t w_a = (L & 0xffffu) | ((L << 13) & 0xffff0000u);
+    const uint32_t w_b = ((L >> 12) & 0xffffu) | ((L << 1) & 0xffff0000u);
+    const uint32_t v = (ext << 3) | (ext << 18);
     f16x8 out;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int e = 2 * k;
-        const uint32_t q0 = ((low24 >> (3 * e)) & 7u) | (((ext >> e) & 1u) << 3);
-        const uint32_t q1 = ((low24 >> (3 * e + 3)) & 7u) | (((ext >> (e + 1)) & 1u) << 3);
-        const uint32_t bits = 0x64006400u | q0 | (q1 << 16);
+        const uint32_t w = pk_shr16(k < 2 ? w_a : w_b, (k & 1) * 6);
+        const uint32_t x = pk_shr16(v, e);
+        const uint32_t bits = (w & 0x00070007u) | (x & 0x00080008u) | 0x64006400u;
         const f16x2 qv = __builtin_bit_cast(f16x2, bits) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
         // vector elements are copied to scalars first: a bit cast applied directly to an
         // element of an ext_vector value has been compiled as a cast of element 0

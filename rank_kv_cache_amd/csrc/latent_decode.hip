@@ -54,13 +54,16 @@ template <int K, int MAXKS> struct KeyBuf {
 
 // Waves per score workgroup: twelve (three per SIMD, at most 168 VGPRs each) for 16-bit and
 // mixed 4/3-bit latents, else eight with a two-deep register pipeline over units.
+#ifndef STARKV_Q43_STAGE_WAVES
+#define STARKV_Q43_STAGE_WAVES 12
+#endif
 template <int K, int MAXKS, bool QK>
-constexpr int score_waves() { return K == kF32 ? 8 : 12; }
+constexpr int score_waves() { return K == kF32 ? 8 : (QK && MAXKS <= 4) ? STARKV_Q43_STAGE_WAVES : 12; }
 // With ranks above 64 (or code windows plus scales and zero points) at twelve waves, a unit's
 // latents for both 32-token column tiles do not fit the register budget: the second tile's
 // fragments are loaded once the first tile's MFMAs have consumed theirs.
 template <int K, int MAXKS, bool QK>
-constexpr bool score_split_loads() { return score_waves<K, MAXKS, QK>() == 12 && (QK || MAXKS > 4); }
+constexpr bool score_split_loads() { return QK || (score_waves<K, MAXKS, QK>() == 12 && MAXKS > 4); }
 // NQ queries of one sequence share each rebuilt, rotated key: eight waves (the per-query sums and
 // query tiles need the larger register budget), a smaller factor budget in LDS to make room for
 // NQ rotated queries per wave, and head groups of at most kMaxGroupHeadsMQ heads.
@@ -94,6 +97,12 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
     __shared__ int s_head[kMaxHeads], s_rank[kMaxHeads], s_kgrp[kMaxHeads];
     __shared__ int s_srank[kMaxHeads], s_soff[kMaxHeads];
     __shared__ int s_goff[QK ? kMaxHeads : 1][8], s_gn[QK ? kMaxHeads : 1][8];
+    // Mixed 4/3-bit codes, heads of rank <= 64: one unit's code run (at most 2048 bytes, read from
+    // the 16-byte boundary at or below its start, so at most 2056 bytes) and the head's scale and
+    // zero-point words, staged in a wave-private buffer one unit ahead.
+    constexpr bool STAGE = QK && MAXKS <= 4;
+    constexpr int kStCodeWords = 516, kStWords = kStCodeWords + 64;
+    __shared__ __attribute__((aligned(16))) uint32_t s_stage[STAGE ? NW : 1][STAGE ? kStWords : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -387,6 +396,64 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
             unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
                 return load_frag<K>(zk, base + (size_t)ks * 1024 + nt * 512);
             });
+        }
+    } else if constexpr (STAGE) {
+        // Mixed 4/3-bit codes, ranks <= 64: the next unit's code run and scale / zero-point words
+        // are loaded into registers before the current unit runs and written to the wave's LDS
+        // buffer after it, so the current unit decodes its fragments from LDS and waits on no
+        // global load. Every lane loads (indexes past the run are clamped to its last 16 bytes or
+        // word, inside the block's codes or the buffer's end padding), so the count of loads in
+        // flight is static.
+        struct Staged { u32x4 c0, c1; uint32_t tail, meta; int off0; };
+        auto stage_load = [&](int u) __attribute__((always_inline)) {
+            const int blk = blk_begin + wave + NW * (u / ng);
+            const int s = u - (u / ng) * ng;
+            const int nks = s_rank[s] >> 4;
+            const size_t bid = block_id(p.pages, p.nblk_cap, bc, blk);
+            const size_t start = bid * (size_t)p.ql.block_bytes + (size_t)s_goff[s][0];
+            const size_t end = bid * (size_t)p.ql.block_bytes + (size_t)(s_goff[s][nks - 1] + 8 * (48 + s_gn[s][nks - 1]));
+            const size_t c16 = start >> 4, last16 = (end - 1) >> 4;
+            const u32x4* code16 = reinterpret_cast<const u32x4*>(qcodes);
+            Staged st;
+            st.c0 = code16[min(c16 + (size_t)lane, last16)];
+            st.c1 = code16[min(c16 + 64 + (size_t)lane, last16)];
+            st.tail = qcodes[min(4 * c16 + 512 + (size_t)(lane & 3), (end - 1) >> 2)];
+            const uint32_t* mw = reinterpret_cast<const uint32_t*>(qmeta) + bid * (size_t)Rk;
+            st.meta = mw[(lane < 32 ? 0 : (Rk >> 1)) + 8 * s_kgrp[s] + min(lane & 31, 8 * nks - 1)];
+            st.off0 = (int)(start & 15);
+            return st;
+        };
+        // buffer words: [0, 516) codes from the 16-byte boundary, [516, 548) scales and
+        // [548, 580) zero points of the head's channels (two binary16 values per word)
+        auto stage_store = [&](const Staged& st) __attribute__((always_inline)) {
+            uint32_t* buf = s_stage[wave];
+            *reinterpret_cast<u32x4*>(buf + 4 * lane) = st.c0;
+            *reinterpret_cast<u32x4*>(buf + 256 + 4 * lane) = st.c1;
+            buf[512 + (lane & 3)] = st.tail;     // lanes with equal (lane & 3) store the same word
+            buf[kStCodeWords + lane] = st.meta;
+        };
+        int off0 = 0;    // the staged unit's start within its first 16 bytes (0 or 8)
+        if (nunits > 0) {
+            const Staged st = stage_load(0);
+            stage_store(st);
+            off0 = st.off0;
+        }
+        for (int u = 0; u < nunits; ++u) {
+            const Staged nx = stage_load(min(u + 1, nunits - 1));
+            const int blk = blk_begin + wave + NW * (u / ng);
+            const int s = u - (u / ng) * ng;
+            const uint32_t* buf = s_stage[wave];
+            const int g0 = s_goff[s][0];
+            unit(blk, s, [&](int nt, int ks) __attribute__((always_inline)) {
+                const int n = s_gn[s][ks];
+                const u32x4 sc = *reinterpret_cast<const u32x4*>(buf + kStCodeWords + 8 * ks + 4 * half);
+                const u32x4 zc = *reinterpret_cast<const u32x4*>(buf + kStCodeWords + 32 + 8 * ks + 4 * half);
+                const int rb = 8 * (off0 + s_goff[s][ks] - g0) + (int)__umul24(32 * nt + j, 48 + n);
+                const uint32_t* wp = buf + (rb >> 5);
+                return q43_key_frag(wp[0], wp[1], wp[2], rb & 31, n, half, sc, zc);
+            });
+            stage_store(nx);
+            off0 = nx.off0;
         }
     } else if constexpr (score_split_q<K, MAXKS, QK, NQ>()) {
         // Mixed 4/3-bit codes: the code window, scales and zero points of each fragment are
