@@ -167,11 +167,6 @@ __device__ __forceinline__ void sincos_rev(float x, float* c, float* s) {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Eight mixed 4/3-bit key codes of one token (one 16-channel group, channels 8*half .. +7) to an
-// fp16 MFMA operand fragment. w0..w2: the aligned 96-bit window holding the token's row, sh: the
-// row's first bit in the window, n: 4-bit channels at the start of the group; sc / zc: the scales
-// and zero points of the eight channels, two per word. Each value is binary16(q*s + z) rounded
-// once (one fp16 FMA per pair); q is formed exactly as binary16(1024 + q) - 1024.
 // both 16-bit halves of x shifted right by s
 __device__ __forceinline__ uint32_t pk_shr16(uint32_t x, int s) {
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -179,6 +174,11 @@ __device__ __forceinline__ uint32_t pk_shr16(uint32_t x, int s) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Eight mixed 4/3-bit key codes of one token (one 16-channel group, channels 8*half .. +7) to an
+// fp16 MFMA operand fragment. w0..w2: the aligned 96-bit window holding the token's row, sh: the
+// row's first bit in the window, n: 4-bit channels at the start of the group; sc / zc: the scales
+// and zero points of the eight channels, two per word. Each value is binary16(q*s + z) rounded
+// once (one fp16 FMA per pair); q is formed exactly as binary16(1024 + q) - 1024.
 __device__ __forceinline__ f16x8 q43_key_frag(uint32_t w0, uint32_t w1, uint32_t w2, int sh, int n,
                                              int half, const u32x4& sc, const u32x4& zc) {
     const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);    // row bits 0 .. 31
@@ -187,20 +187,23 @@ __device__ __forceinline__ f16x8 q43_key_frag(uint32_t w0, uint32_t w1, uint32_t
     // channels that are 4-bit (row bits 48 + 8*half ..)
     const uint32_t L = __builtin_amdgcn_alignbit(hi, lo, 24 * half);
     const uint32_t ext = __builtin_amdgcn_ubfe(hi, 16 + 8 * half, min(max(n - 8 * half, 0), 8));
-    // Channel pair (2k, 2k+1) goes to the low and high 16-bit halves. w_a holds fields 0.. in its
-    // low half and fields 1.. in its high half (pairs 0 and 1, the latter after a 6-bit shift of
-    // each half), w_b the same from field 4; v holds fourth bit e at bit 3 + e of the low half and
-    // at bit 2 + e of the high half, so a 2k-bit shift of each half brings pair k's to bit 3.
+    // Channel pair (2k, 2k+1) goes to the low and high 16-bit halves, code bits 0-2 and fourth
+    // bit 3. m_a holds fields 0.. in its low half and fields 1.. in its high half (pair 0; pair 1
+    // after a 6-bit shift of each half), m_b the same from field 4 (pairs 2 and 3). The fourth
+    // bits fill the slots those shifts leave free (bits 3 and 9 of each half): one 24-bit multiply
+    // by 2^3 + 2^18 + 2^7 + 2^22 moves bits 0..3 of a nibble to 3, 19, 9, 25 (no two partial
+    // products overlap, so no carries) and the merge keeps only those four bits.
     const uint32_t w_a = (L & 0xffffu) | ((L << 13) & 0xffff0000u);
     const uint32_t w_b = ((L >> 12) & 0xffffu) | ((L << 1) & 0xffff0000u);
-    const uint32_t v = (ext << 3) | (ext << 18);
+    constexpr uint32_t kSpread = (1u << 3) | (1u << 18) | (1u << 7) | (1u << 22);
+    constexpr uint32_t kSlots = 0x02080208u;
+    const uint32_t m_a = (__umul24(ext & 15u, kSpread) & kSlots) | (w_a & ~kSlots);
+    const uint32_t m_b = (__umul24(ext >> 4, kSpread) & kSlots) | (w_b & ~kSlots);
     f16x8 out;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int e = 2 * k;
-        const uint32_t w = pk_shr16(k < 2 ? w_a : w_b, (k & 1) * 6);
-        const uint32_t x = pk_shr16(v, e);
-        const uint32_t bits = (w & 0x00070007u) | (x & 0x00080008u) | 0x64006400u;
+        const uint32_t bits = (pk_shr16(k < 2 ? m_a : m_b, (k & 1) * 6) & 0x000f000fu) | 0x64006400u;
         const f16x2 qv = __builtin_bit_cast(f16x2, bits) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
         // vector elements are copied to scalars first: a bit cast applied directly to an
         // element of an ext_vector value has been compiled as a cast of element 0
