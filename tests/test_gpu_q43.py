@@ -333,16 +333,29 @@ def test_q43_decode_rank_mixes(ranks):
         assert np.all(np.isfinite(got)) and e <= 2e-3
 
 
-@pytest.mark.parametrize("frac,d", [(0.2, 128), (1.0, 128), (0.0, 128), (0.25, 64)])
-def test_q43_fractions_and_head_dim(frac, d):
+@pytest.mark.parametrize("frac,d,ranks", [(0.2, 128, [16, 48, 80, 32]), (0.2, 128, [16, 32, 64, 48, 32]),
+                                           (1.0, 128, [16, 48, 80, 32]), (0.0, 128, [16, 48, 80, 32]),
+                                           (0.25, 64, [16, 32, 48, 64])])
+def test_q43_fractions_and_head_dim(frac, d, ranks):
     """Quantisation variants the pages measure: the paper's 20 % at 4 bits (3.2 bits per value),
     uniform 4-bit (fraction 1), uniform 3-bit (fraction 0), and head_dim 64. Read-back must be
     bit-exact and decode within tolerance of the oracle's dequantisation, with the fraction passed
-    as the binary32 value the library receives."""
+    as the binary32 value the library receives. The second 20 % case keeps every rank at or below
+    64 (the score kernel's staged path) with odd counts of 4-bit channels, so head code runs start
+    8 bytes past a 16-byte boundary."""
     from rank_kv_cache_amd import buffers
     from gpu_support import rel_err
-    H, B = 4, 2
-    ranks = [16, 48, 80, 32] if d == 128 else [16, 32, 48, 64]
+    H, B = len(ranks), 2
+    if ranks == [16, 32, 64, 48, 32]:
+        # byte offset of each head's code run in a block: 16-channel groups of 48 + n bits per token
+        bits = oracle.channel_bits(ranks, float(np.float32(frac)))
+        starts, off, c = [], 0, 0
+        for r in ranks:
+            starts.append(off)
+            for g in range(r // 16):
+                off += 8 * (48 + int((bits[c + 16 * g:c + 16 * g + 16] == 4).sum()))
+            c += r
+        assert any(x % 16 == 8 for x in starts), starts
     rv = 208
     T, cap = 150, 192
     f32 = float(np.float32(frac))
