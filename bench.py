@@ -8,6 +8,7 @@ the three exempt layers attending over full-width fp16 K/V. Inputs are synthetic
 already resident in HBM when timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--scrub-mib N]
 
 Prints one JSON line. ``value`` is decode tokens per second (one new token per sequence per step,
 B / step time). ``roofline`` prices the dominant kernel (the one with the largest total time; all
@@ -670,6 +671,11 @@ def main(argv=None):
                          "projection and several queries per sequence (outside the step; they call "
                          "the decode kernels with other shapes, so a kernel trace of such a run "
                          "mixes those calls with the step's)")
+    ap.add_argument("--scrub-mib", type=int, default=0,
+                    help="before every warm-up and timed step, rewrite a buffer of this many MiB so "
+                         "that no cache line of the previous step survives in the last-level cache "
+                         "(256 MB); the step time is then taken from HIP events recorded after the "
+                         "rewrite, around the step alone")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, stream this many MiB through one elementwise copy "
                          "kernel (reads and writes that many bytes once): the reference for "
@@ -721,8 +727,14 @@ def main(argv=None):
     hip = HipEvents()
     nl = len(runs)
     ev = hip.create(3 * nl * a.steps)
+    scrub = torch.zeros(a.scrub_mib << 20, dtype=torch.uint8, device="cuda") if a.scrub_mib > 0 else None
+    sev = hip.create(2 * a.steps) if scrub is not None else []
 
     def step(i=None):
+        if scrub is not None:
+            scrub.bitwise_not_()
+            if i is not None:
+                hip.record(sev[2 * i], stream.cuda_stream)
         for li, r in enumerate(runs):
             sk.starkv_append_latents(r.layer, r.cache, r.T - 1, 1, r.new_k, r.new_v, stream=stream)
             if i is None:
@@ -734,6 +746,8 @@ def main(argv=None):
                                             a.splits, ws, ws_bytes, stream=stream,
                                             event_begin=ev[e], event_mid=ev[e + 1],
                                             event_end=ev[e + 2])
+        if scrub is not None and i is not None:
+            hip.record(sev[2 * i + 1], stream.cuda_stream)
 
     for _ in range(a.warmup):
         step()
@@ -768,6 +782,9 @@ def main(argv=None):
                 k_ms["latent_scores"][i] += hip.elapsed_ms(ev[e], ev[e + 1])
                 k_ms["latent_values"][i] += hip.elapsed_ms(ev[e + 1], ev[e + 2])
     hip.destroy(ev)
+    step_ms = [hip.elapsed_ms(sev[2 * i], sev[2 * i + 1]) for i in range(a.steps)] if sev else None
+    hip.destroy(sev)
+    del scrub
 
     for r in runs:
         res = r.out.cpu().numpy()
@@ -786,7 +803,8 @@ def main(argv=None):
                                                         min(a.steps, 10))
         prefill = measure_prefill(sk, buffers, synth, stream, hip, min(a.steps, 5))
 
-    ms_per_step = elapsed * 1e3 / a.steps
+    # with a scrub between steps the wall clock would include it: the steps' own HIP events instead
+    ms_per_step = statistics.fmean(step_ms) if step_ms else elapsed * 1e3 / a.steps
     kernels = {}
     for k in k_ms:
         if k_launches[k] == 0:
@@ -807,6 +825,8 @@ def main(argv=None):
                  "kv_hbm_frac_per_step": round(step_gbs / HBM_PEAK_GBS, 4),
                  "kv_gbs_stream_kernels": round(total_bytes / (stream_ms * 1e-3) / 1e9, 1),
                  "cached_tokens_per_s": B * runs[0].T / (ms_per_step * 1e-3)})
+    if a.scrub_mib > 0:
+        desc["scrub_mib_between_steps"] = a.scrub_mib
     dk = kernels[dom]
     roofline = {"bound": "hbm", "achieved": dk["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dk["gbs"] / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
