@@ -142,13 +142,29 @@ __device__ __forceinline__ float tile_factor(float d) {
     return d >= -149.0f ? ldexpf(1.0f, (int)d) : 0.0f;
 }
 
-__device__ __forceinline__ float half_max(float v) {
-    v = fmaxf(v, dpp_mov<0xB1>(v));
-    v = fmaxf(v, dpp_mov<0x4E>(v));
-    v = fmaxf(v, dpp_mov<0x141>(v));
-    v = fmaxf(v, dpp_mov<0x140>(v));
-    const LanePair p = swap16(v);
-    return fmaxf(p.a, p.b);
+// The maximum runs on integer keys of the float bits (non-negative values keep their bits,
+// negative ones have their magnitude bits flipped), which order like the values for every
+// non-NaN input including -inf; an integer maximum fuses with the DPP lane move, where a float
+// maximum is preceded by a canonicalising operation on each operand.
+__device__ __forceinline__ int float_order_key(float v) {
+    const int i = __float_as_int(v);
+    return i ^ (int)((uint32_t)(i >> 31) >> 1);
+}
+// v from another lane; the old value is the identity of a signed maximum, so that the move can
+// be folded into the maximum that consumes it
+template <int CTRL>
+__device__ __forceinline__ int dpp_max_src(int v) {
+    return __builtin_amdgcn_update_dpp((int)0x80000000, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float half_max(float x) {
+    int v = float_order_key(x);
+    v = max(v, dpp_max_src<0xB1>(v));
+    v = max(v, dpp_max_src<0x4E>(v));
+    v = max(v, dpp_max_src<0x141>(v));
+    v = max(v, dpp_max_src<0x140>(v));
+    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    const int m = max((int)r[0], (int)r[1]);
+    return __int_as_float(m ^ (int)((uint32_t)(m >> 31) >> 1));   // the key map is its own inverse
 }
 __device__ __forceinline__ float half_sum(float v) {
     v += dpp_mov<0xB1>(v);

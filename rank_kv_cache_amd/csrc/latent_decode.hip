@@ -248,7 +248,7 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
 
     // One unit: head slot s over 64-token block blk. frag(nt, ks) supplies the latent operand.
     auto unit = [&](int blk, int s, auto&& frag) __attribute__((always_inline)) {
-        const int h = s_head[s];
+        const int h = __builtin_amdgcn_readfirstlane(s_head[s]);   // s is wave-uniform
         const int nks = s_rank[s] >> 4;
         if (s == 0 && lane < NF) {
 #pragma unroll
@@ -367,16 +367,16 @@ __global__ __launch_bounds__((64 * score_waves_q<K, MAXKS, QK, NQ>()), 1) void l
             // the tile maximum rounded up to an integer: rescaling a stored probability by
             // 2^(m - M) between tiles is then exact; the tile sum adds the stored (rounded) values,
             // so that numerator and denominator hold the same probabilities
-            float m = half_max(my);
-            if (m != -INFINITY) m = ceilf(m);
+            const float m = ceilf(half_max(my));          // -inf stays -inf
             // a tile wholly past the query's end: p = 0, l = 0
             const PT pst = (PT)(m != -INFINITY ? __builtin_amdgcn_exp2f(my - m) : 0.0f);
             const float l = half_sum((float)pst);
+            // row and block are wave-uniform: the addresses are a scalar base plus the lane
             const size_t row = (size_t)(row0 + qi) * H + h;
-            Pout[row * Tp + tok] = pst;
+            (Pout + (row * Tp + (size_t)blk * 64))[lane] = pst;
             // every lane stores (even lanes m, odd lanes l, to the same two words of its tile): no
             // branch, so the count of memory operations in flight stays static
-            stats[(row * 2 * nblk + 2 * blk + half) * 2 + (lane & 1)] = (lane & 1) ? l : m;
+            (stats + (row * 2 * nblk + 2 * (size_t)blk) * 2)[2 * half + (lane & 1)] = (lane & 1) ? l : m;
         }
         wave_sync_lds();
     };
