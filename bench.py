@@ -62,36 +62,36 @@ METRIC = "decode attn tokens/sec and achieved latent-KV HBM GB/s (% of peak), B=
 KERNEL_SOURCES = ("latent_decode.hip", "dense_decode.hip", "common.hpp")
 MEASURED = {
     "longchat_b16_t32768_f16": {
-        "digest": "09362dc29ad13f76",
+        "digest": "70039981d02b5189",
         "source": "profiles/latent_decode_counters_longchat_b16_t32768_f16.md",
         "kernels": {
-            "latent_scores": {"traffic": 1436650616, "mfma_util_pct": 25.2, "valu_busy_pct": 67.5},
-            "latent_values": {"traffic": 1142681049, "mfma_util_pct": 8.2, "valu_busy_pct": 6.9},
+            "latent_scores": {"traffic": 1438133496, "mfma_util_pct": 25.6, "valu_busy_pct": 65.8},
+            "latent_values": {"traffic": 1142625440, "mfma_util_pct": 7.7, "valu_busy_pct": 6.6},
         },
     },
     "longchat_b16_t16384_f16": {
-        "digest": "09362dc29ad13f76",
+        "digest": "70039981d02b5189",
         "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
         "kernels": {
-            "latent_scores": {"traffic": 719057111, "mfma_util_pct": 22.9, "valu_busy_pct": 62.7},
-            "latent_values": {"traffic": 585752146, "mfma_util_pct": 6.8, "valu_busy_pct": 6.9},
+            "latent_scores": {"traffic": 719437768, "mfma_util_pct": 24.1, "valu_busy_pct": 63.6},
+            "latent_values": {"traffic": 585869984, "mfma_util_pct": 6.8, "valu_busy_pct": 7.0},
         },
     },
     "model32_b32_t8192_f16": {
-        "digest": "09362dc29ad13f76",
+        "digest": "70039981d02b5189",
         "source": "profiles/model32_counters_b32_t8192_f16.md",
         "kernels": {      # latent kernels: means over the 29 latent layers' launches
-            "latent_scores": {"traffic": 966359207, "mfma_util_pct": 22.0, "valu_busy_pct": 50.2},
-            "latent_values": {"traffic": 634997968, "mfma_util_pct": 6.1, "valu_busy_pct": 7.6},
-            "dense_attention": {"traffic": 4311021656, "mfma_util_pct": 0.0, "valu_busy_pct": 27.1},
+            "latent_scores": {"traffic": 963049756, "mfma_util_pct": 22.3, "valu_busy_pct": 49.6},
+            "latent_values": {"traffic": 635022727, "mfma_util_pct": 5.8, "valu_busy_pct": 7.3},
+            "dense_attention": {"traffic": 4311075335, "mfma_util_pct": 0.0, "valu_busy_pct": 26.1},
         },
     },
     "longchat_b16_t16384_q43": {
-        "digest": "09362dc29ad13f76",
+        "digest": "70039981d02b5189",
         "source": "profiles/latent_decode_counters_longchat_b16_t16384.md",
         "kernels": {
-            "latent_scores": {"traffic": 224537542, "mfma_util_pct": 14.9, "valu_busy_pct": 65.6},
-            "latent_values": {"traffic": 179115444, "mfma_util_pct": 9.9, "valu_busy_pct": 45.2},
+            "latent_scores": {"traffic": 240687280, "mfma_util_pct": 16.0, "valu_busy_pct": 69.8},
+            "latent_values": {"traffic": 179143104, "mfma_util_pct": 9.8, "valu_busy_pct": 44.7},
         },
     },
 }
