@@ -194,3 +194,38 @@ def test_append_chunks_and_readback():
     assert np.array_equal(rk2.view(np.uint16), zk[:, 37:171].view(np.uint16))
     assert np.array_equal(rv2.view(np.uint16), zv[:, 37:171].view(np.uint16))
     assert np.array_equal(bulk.decode(q), inc.decode(q))
+
+
+def test_all_negative_scores():
+    """Keys that point against the back-rotated query at every position: z_n solves
+    B^T z = -u_n R_n^T q in the least-squares sense (u_n in [0.3, 3]), so every score
+    (R_n^T q) . (B^T z_n) is minus a squared norm and each 32-token tile's maximum is negative
+    (the kernel takes the tile maxima over order-preserving integer keys of the float scores,
+    whose negative half has its magnitude bits flipped)."""
+    H, B, d, T, rv = 2, 1, 128, 300, 64
+    ranks = np.array([32, 48])
+    w = synth.Workload("n", batch=B, heads=H, head_dim=d, seq_len=T, dtype="f16", layer_seed=51,
+                       cache_seed=52, value_rank=rv, power=0.5)
+    ld = synth.draw_layer(w, key_ranks=ranks)
+    zk, zv = synth.draw_latent_cache(w, ld)
+    q = synth.draw_queries(53, 0, B, H, d)
+    rng = np.random.default_rng(54)
+    zk = zk.astype(np.float64)
+    off = 0
+    smax = -np.inf
+    for h, r in enumerate(ranks):
+        bh = np.asarray(ld.bk[off:off + r], dtype=np.float64)          # (r, d)
+        for n in range(T):
+            qn = oracle.rope(np.asarray(q[0, h], dtype=np.float64), -n)  # R_n^T q
+            zk[0, n, off:off + r] = -rng.uniform(0.3, 3.0) * np.linalg.lstsq(bh.T, qn, rcond=None)[0]
+        z16 = zk[0, :, off:off + r].astype(np.float16).astype(np.float64)
+        for n in range(T):
+            smax = max(smax, float(oracle.rope(np.asarray(q[0, h], dtype=np.float64), -n) @ (bh.T @ z16[n])))
+        off += r
+    zk = zk.astype(np.float16)
+    say(f"[negative] largest score {smax:.3f}")
+    assert smax < 0.0
+    dl = DeviceLayer(latent_layer(H, d, ranks, rv, "f16"), zk, zv, ld.bk, ld.bv)
+    e = rel_err(dl.decode(q), _oracle(ld, zk, zv, q, "f16"))
+    say(f"[negative] rel err {e:.3e}")
+    assert e <= TOL
